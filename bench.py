@@ -1,0 +1,324 @@
+#!/usr/bin/env python3
+"""Benchmark of the multi-LoRA hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: lora_build_segments,
+lora_shrink, and lora_expand / lora_expand_slice for every output of the
+workload.  Inputs live in HBM before timing starts.  Following the kernel
+micro-benchmark PR's method, a pool of distinct argument sets (>= 1 GiB, four
+times the 256 MB Infinity Cache) is cycled so that no step finds its data in
+cache, and the K timed steps are captured in one HIP graph (launch overhead
+of the Python binding stays out of the measurement) and replayed once between
+two events.
+
+Output: one JSON line on stdout.  value = algorithmic shrink + expand bytes of
+a step / step time (GB/s).  roofline = the dominant kernel, timed alone (a
+graph of K launches of that op over the pool, events on its stream) against
+the 8 TB/s HBM peak.  cpu_baseline = the fp64 oracle on the host cores on the
+same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config k]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "shrink+expand achieved HBM GB/s (BGMV) / MFMA TFLOP/s (SGMV), % roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class ArgSet:
+    """One set of device buffers for one step."""
+
+    def __init__(self, w, torch, lsb, src=None):
+        tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+        import numpy as np
+
+        def dev(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(tdt)
+
+        if src is None:
+            self.ids = torch.from_numpy(w.ids).cuda()
+            self.x = dev(w.x)
+            self.A = dev(w.A)
+            self.Bs = [[dev(s.B) for s in o.slices] for o in w.outputs]
+            self.ys = [dev(o.y0) for o in w.outputs]
+        else:
+            self.ids = src.ids.clone()
+            self.x = src.x.clone()
+            self.A = src.A.clone()
+            self.Bs = [[b.clone() for b in bl] for bl in src.Bs]
+            self.ys = [y.clone() for y in src.ys]
+        self.v = torch.zeros(w.T, w.r, dtype=torch.float32, device="cuda")
+        self.seg = lsb.Segments(self.ids, w.L)
+
+    def nbytes(self):
+        t = [self.ids, self.x, self.A, self.v] + [b for bl in self.Bs for b in bl] + self.ys
+        return sum(x.numel() * x.element_size() for x in t)
+
+
+def op_build(w, lsb, s, ws):
+    lsb.lora_build_segments(s.ids, w.L, seg=s.seg)
+
+
+def op_shrink(w, lsb, s, ws):
+    lsb.lora_shrink(s.x, s.A, s.seg, s.v, workspace=ws)
+
+
+def op_expand(w, lsb, s, ws):
+    for o, Bs, y in zip(w.outputs, s.Bs, s.ys):
+        if len(o.slices) == 1 and o.slices[0].col_off == 0:
+            lsb.lora_expand(s.v, Bs[0], s.seg, y, w.add)
+        else:
+            lsb.lora_expand_slice(s.v, Bs, [q.col_off for q in o.slices], s.seg, y, w.add)
+
+
+def step(w, lsb, s, ws):
+    op_build(w, lsb, s, ws)
+    op_shrink(w, lsb, s, ws)
+    op_expand(w, lsb, s, ws)
+
+
+def graph_time(torch, fn, sets, first, count):
+    """Captures `count` calls of fn over consecutive pool sets in one graph,
+    replays it once untimed, then once between two events.  Returns ms."""
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(count):
+            fn(sets[(first + i) % len(sets)])
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    del g
+    return ms
+
+
+def parity_check(w, torch, lsb, ws):
+    """Checks one fresh step against the oracle before anything is timed."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    s = ArgSet(w, torch, lsb)
+    step(w, lsb, s, ws)
+    torch.cuda.synchronize()
+    act = np.nonzero(w.active)[0].astype(np.int32)
+    v_ref = oracle.shrink(w.dtype, w.x, w.A, w.ids, rows=act)
+    vg = s.v.cpu().numpy().astype(np.float64)[act]
+    worst = float(np.max(np.abs(vg - v_ref) / (1e-2 * (1 + np.abs(v_ref))))) if act.size else 0.0
+    v_full = np.zeros((w.T, w.r))
+    v_full[act] = v_ref
+    for o, y in zip(w.outputs, s.ys):
+        cols = np.concatenate([np.arange(q.col_off, q.col_off + q.n) for q in o.slices])
+        ref = oracle.expand_slice(w.dtype, v_full, [q.B for q in o.slices], [q.col_off for q in o.slices],
+                                  w.ids, o.y0, w.add, rows=act)
+        yb = y.view(torch.int16).cpu().numpy().view(np.uint16)[act][:, cols]
+        got = W.bits_to_f32(yb, w.dtype).astype(np.float64)
+        if act.size:
+            worst = max(worst, float(np.max(np.abs(got - ref) / (1e-2 * (1 + np.abs(ref))))))
+    return worst
+
+
+def cpu_baseline(w, step_bytes):
+    """The fp64 oracle (as it is) on the host cores, over the same workload,
+    repeated to about 10 s of CPU work."""
+    import numpy as np
+    import oracle
+
+    def run():
+        oracle.build_segments(w.ids, w.L)
+        v = oracle.shrink(w.dtype, w.x, w.A, w.ids)
+        v = np.nan_to_num(v)
+        for o in w.outputs:
+            oracle.expand_slice(w.dtype, v, [q.B for q in o.slices], [q.col_off for q in o.slices],
+                                w.ids, o.y0, w.add)
+
+    t0 = time.perf_counter()
+    run()
+    t1 = time.perf_counter() - t0
+    reps = max(1, min(1000, int(math.ceil(10.0 / max(t1, 1e-6)))))
+    if t1 > 30.0:
+        reps = 1
+    t0 = time.perf_counter()
+    for _ in range(reps - 1):
+        run()
+    el = time.perf_counter() - t0 + (t1 if reps >= 1 else 0.0)
+    return {
+        "value": round(step_bytes * reps / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"the whole workload (metadata, shrink, expand of every output) run {reps}x "
+                  f"in {el:.1f} s, OpenMP over tokens",
+        "tokens_per_s": round(w.T * reps / el, 2),
+    }
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key, workload_name, src_hash):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if the
+    kernel source has not changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_key}_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+KERNEL_SOURCES = {
+    "build": ["lora_serving_build_amd/csrc/segments.hip"],
+    "shrink": ["lora_serving_build_amd/csrc/shrink.hip", "lora_serving_build_amd/csrc/tiles.h",
+               "lora_serving_build_amd/csrc/lora_device.h"],
+    "expand": ["lora_serving_build_amd/csrc/expand.hip", "lora_serving_build_amd/csrc/tiles.h",
+               "lora_serving_build_amd/csrc/lora_device.h"],
+}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="named workload 1..5 (default 2)")
+    ap.add_argument("--pool-gib", type=float, default=1.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the multi-LoRA path here has no multi-GPU mode "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import lora_serving_build_amd as lsb
+    import workloads as W
+
+    lsb.lib()
+    torch.cuda.set_device(0)
+    log(f"generating workload {args.config}")
+    w = W.config(args.config)
+    need = lsb.lora_shrink_workspace_bytes(w.T, w.L, w.H, w.r)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda") if need else None
+
+    worst = None
+    if not args.no_check:
+        log("parity check of one fresh step against the oracle")
+        worst = parity_check(w, torch, lsb, ws)
+        log(f"worst tolerance ratio {worst:.3g}")
+        if not worst <= 1.0:
+            print(json.dumps({"error": "parity check failed", "ratio": worst}))
+            sys.exit(1)
+
+    base = ArgSet(w, torch, lsb)
+    per_set = base.nbytes()
+    P = max(2, int(math.ceil(args.pool_gib * 2**30 / per_set)))
+    log(f"argument pool: {P} sets of {per_set / 2**20:.1f} MiB")
+    sets = [base] + [ArgSet(w, torch, lsb, src=base) for _ in range(P - 1)]
+    torch.cuda.synchronize()
+
+    fstep = lambda s: step(w, lsb, s, ws)
+    for i in range(args.warmup):
+        fstep(sets[i % P])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    log(f"timing {K} steps in one graph")
+    ms = graph_time(torch, fstep, sets, args.warmup, K)
+    ms_per_step = ms / K
+
+    shrink_b = w.shrink_bytes()
+    expand_b = w.expand_bytes()
+    step_bytes = shrink_b + expand_b
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # Per-op timing: each op alone, K launches over the pool in one graph.
+    ops = {}
+    for name, fn, nbytes, flops in (
+            ("build", op_build, 8 * w.T + 8 * (w.L + 1) + 16, 0),
+            ("shrink", op_shrink, shrink_b, w.shrink_flops()),
+            ("expand", op_expand, expand_b, w.expand_flops())):
+        t = graph_time(torch, lambda s, fn=fn: fn(w, lsb, s, ws), sets, args.warmup + K, K) / K
+        launches = 1 if name != "expand" else len(w.outputs)
+        ops[name] = {"us_per_op": round(t * 1e3, 3), "launches": launches, "bytes": nbytes,
+                     "GB_s": round(nbytes / (t * 1e-3) / 1e9, 1),
+                     "TFLOP_s": round(flops / (t * 1e-3) / 1e12, 2)}
+        log(f"{name}: {t * 1e3:.2f} us/op, {ops[name]['GB_s']} GB/s, {ops[name]['TFLOP_s']} TFLOP/s")
+    dom = max(("shrink", "expand"), key=lambda k: ops[k]["us_per_op"])
+    src_hash = source_hash(KERNEL_SOURCES[dom])
+    traffic = measured_traffic(dom, w.name, src_hash)
+    achieved = ops[dom]["bytes"] / (ops[dom]["us_per_op"] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "bytes_per_launch": ops[dom]["bytes"] // ops[dom]["launches"],
+                "us_per_launch": round(ops[dom]["us_per_op"] / ops[dom]["launches"], 3),
+                "source_hash": src_hash}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host")
+        cpu = cpu_baseline(w, step_bytes)
+
+    flops = w.shrink_flops() + w.expand_flops()
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.T, "active_tokens": w.T_a, "hidden": w.H,
+                   "rank": w.r, "num_loras": w.L, "distinct_loras": w.distinct,
+                   "outputs": [[q.n for q in o.slices] for o in w.outputs], "add_inputs": w.add,
+                   "pool_sets": P, "parallelism": "none"},
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
+        "mfma_frac": round(flops / (ms_per_step * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype], 5),
+        "tokens_per_s": round(w.T / (ms_per_step * 1e-3), 1),
+        "ops": ops,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parity_ratio": worst,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,164 @@
+/*
+ * liblora_mi355x: multi-LoRA gather-matmul (shrink / expand / expand_slice)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Problem statement (from the pages this library follows):
+ *  - vLLM PR "[misc] Add LoRA kernel micro benchmarks": one call computes a
+ *    whole m x k x n product in which every token uses the weight matrix that
+ *    its LoRA id selects out of num_loras; the ops are shrink, expand and
+ *    expand_slice in BGMV (one token per sequence) and SGMV (segments)
+ *    forms; expand optionally adds to the existing output (add_inputs); its
+ *    input is fp32 and its weights and output are fp16/bf16; expand_slice is
+ *    equivalent to one expand per output slice; shrink with split-K either
+ *    stores or accumulates, which makes repeated calls hard to check.
+ *  - vLLM PR "[Hardware][TPU][V1] Multi-LoRA Optimisations for the V1 TPU
+ *    backend", summary: shrink and expand as separate kernels; adapters used
+ *    by expand are pre-transposed once at load time.
+ *  - punica issue "The smallest rank supported is 16?": segments of tokens
+ *    sharing one adapter (SGMV) with BGMV as a strict subset; ranks other
+ *    than the supported bins are handled by zero padding.
+ *
+ * Mathematics.  For token t with adapter l = lora(t):
+ *   shrink:  v[t, j] = sum_{h < H} x[t, h] * A_l[h, j]            j < r
+ *   expand:  y[t, c] = (add_inputs ? y[t, c] : 0) + sum_{j < r} v[t, j] * B_l[j, c]
+ * lora(t) = -1 means "no adapter": such rows of v and y are never written.
+ *
+ * Memory layouts (all row-major, every pointer below is DEVICE memory unless
+ * marked host; the contraction index of both weights is contiguous):
+ *   x  [T][ldx]        fp16/bf16
+ *   A  [L][r][H]       fp16/bf16   (A_l stored transposed: row j holds A_l[:, j])
+ *   v  [T][ldv]        fp32
+ *   B  [L][n][r]       fp16/bf16   (B_l stored transposed: row c holds B_l[:, c])
+ *   y  [T][ldy]        fp16/bf16
+ * x, A, B and y share one dtype.
+ *
+ * Calls.  Every call is asynchronous on the given stream (a hipStream_t passed
+ * as void*; NULL = the default stream), copies nothing between host and device,
+ * never synchronises, and launches a fixed number of kernels whose geometry
+ * depends only on the scalar arguments, so calls can be captured in a HIP
+ * graph.  Host-checkable errors return a negative status before anything is
+ * launched; lora_last_error() then describes the problem.  Data-dependent
+ * problems (adapter ids outside [-1, L)) are not errors: such tokens are
+ * treated as -1 and counted.
+ *
+ * Precision.  Products are accumulated in fp32.  expand rounds once, to
+ * nearest even, when it writes y.  Inside expand the fp32 v is split into a
+ * high and a low fp16/bf16 part so that the matrix cores see v to about 16
+ * significant bits; with fp16 data, |v| must stay below 65504.
+ */
+#ifndef LORA_MI355X_H
+#define LORA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define LORA_OK 0
+#define LORA_ERR_INVALID_ARG (-1)  /* bad pointer, size, stride or slice layout      */
+#define LORA_ERR_UNSUPPORTED (-2)  /* outside the supported envelope (limits below)  */
+#define LORA_ERR_WORKSPACE (-3)    /* workspace missing or too small                 */
+#define LORA_ERR_HIP (-4)          /* the HIP runtime reported an error at launch    */
+
+/* Element types of x, A, B and y. */
+#define LORA_F16 0
+#define LORA_BF16 1
+
+/* Limits. */
+#define LORA_MAX_RANK 128     /* r in [1, 128]                                      */
+#define LORA_MAX_LORAS 2048   /* L in [1, 2048]                                     */
+#define LORA_MAX_SLICES 8     /* expand_slice: 1..8 slices                          */
+
+/* Segment metadata of one batch: tokens grouped by adapter (SGMV segments).
+ * A host struct whose pointers are caller-owned device buffers.  Built once
+ * per batch by lora_build_segments and then read by every shrink / expand
+ * of that batch.  Contents after a build:
+ *   sorted_token[T]  active tokens ordered by (adapter id, token index), then
+ *                    the tokens without an adapter in ascending order
+ *   seg_lora[L]      adapter id of segment s for s < S, then -1
+ *   seg_start[L+1]   first position in sorted_token of segment s; entries
+ *                    S..L hold T_a (the number of active tokens)
+ *   counts[4]        {S, T_a, longest segment, number of ids outside [-1, L)}
+ * Callers that already hold grouped batches may fill these buffers
+ * themselves, as long as they respect exactly these invariants. */
+typedef struct lora_segments {
+  int32_t num_tokens;          /* T >= 0                                       */
+  int32_t num_loras;           /* L in [1, LORA_MAX_LORAS]                      */
+  const int32_t *token_lora;   /* [T] adapter id of each token, -1 = none       */
+  int32_t *sorted_token;       /* [T]                                           */
+  int32_t *seg_lora;           /* [L]                                           */
+  int32_t *seg_start;          /* [L + 1]                                       */
+  int32_t *counts;             /* [4]                                           */
+} lora_segments;
+
+/* Builds the segment metadata of seg->token_lora into the other four
+ * buffers of *seg (one kernel, one workgroup).  The grouping follows the
+ * punica issue's SGMV segments; the order inside a segment is ascending token
+ * index, so the result is unique.  T = 0 and all-(-1) batches are valid.
+ * Errors: LORA_ERR_INVALID_ARG for a NULL seg or buffer (with T > 0) or
+ * T < 0; LORA_ERR_UNSUPPORTED for L outside [1, LORA_MAX_LORAS]. */
+int lora_build_segments(const lora_segments *seg, void *stream);
+
+/* Workspace bytes that lora_shrink needs for T tokens, L adapters, hidden
+ * size H and rank r (0 if it needs none).  The workspace holds split-K
+ * partial sums and per-tile arrival counters. */
+size_t lora_shrink_workspace_bytes(int32_t T, int32_t L, int32_t H, int32_t r);
+
+/* Zero-fills a workspace (a fill kernel on the stream; graph-safe). */
+int lora_workspace_clear(void *workspace, size_t bytes, void *stream);
+
+/* Shrink (micro-benchmark PR: bgmv_shrink / sgmv_shrink; TPU PR: the
+ * separate shrink kernel):  v[t, j] = sum_h x[t, h] * A_l[h, j], j < r, for
+ * every active token t, fp32 accumulation, fp32 result.  v rows of tokens
+ * without an adapter are not written.  The result overwrites v: any split of
+ * the H-sum across workgroups is reduced inside the call, in a fixed order,
+ * so repeated calls give identical bits.
+ *   x          [T][ldx] device, ldx >= H
+ *   A          [L][r][H] device
+ *   seg        metadata built for this batch (T, L taken from it)
+ *   v          [T][ldv] fp32 device, ldv >= r
+ *   workspace  device buffer of >= lora_shrink_workspace_bytes(T, L, H, r)
+ *              bytes that is all zero before its first use (lora_workspace_clear
+ *              or any zero fill); every call leaves it all zero again.  Calls
+ *              that run concurrently must not share a workspace.
+ * Errors: INVALID_ARG (NULL pointers, H < 1, ld too small, bad dtype),
+ * UNSUPPORTED (r outside [1, LORA_MAX_RANK]), WORKSPACE, HIP. */
+int lora_shrink(const void *x, int64_t ldx, const void *A, int32_t H, int32_t r,
+                const lora_segments *seg, float *v, int64_t ldv, void *workspace,
+                size_t workspace_bytes, int dtype, void *stream);
+
+/* Expand (micro-benchmark PR: bgmv_expand / sgmv_expand, add_inputs):
+ *   y[t, c] = (add_inputs ? y[t, c] : 0) + sum_{j<r} v[t, j] * B_l[j, c],  c < n
+ * for every active token; rows of tokens without an adapter and columns
+ * c >= n are not touched.  One rounding to the output type per element.
+ *   v  [T][ldv] fp32 device;  B  [L][n][r] device;  y  [T][ldy] device, ldy >= n.
+ * Same as lora_expand_slice with one slice at column 0. */
+int lora_expand(const float *v, int64_t ldv, const void *B, int32_t r, int32_t n,
+                const lora_segments *seg, void *y, int64_t ldy, int add_inputs,
+                int dtype, void *stream);
+
+/* Expand into column slices of a fused output (micro-benchmark PR:
+ * expand_slice, num_slices; equivalent to one expand per slice issued back to
+ * back).  Slice s uses weights B[s] ([L][n_s[s]][r], device), input
+ * v + s * v_slice_stride (elements; 0 = all slices share one v) and writes
+ * columns [col_off[s], col_off[s] + n_s[s]) of y.  B, n_s and col_off are
+ * HOST arrays of num_slices entries.  Slices must lie inside [0, ldy) and must
+ * not overlap; columns outside every slice are not touched.
+ * Errors: INVALID_ARG (NULL pointers, n_s < 1, overlapping or out-of-range
+ * slices), UNSUPPORTED (num_slices outside [1, LORA_MAX_SLICES], r range), HIP. */
+int lora_expand_slice(const float *v, int64_t ldv, int64_t v_slice_stride,
+                      const void *const *B, const int32_t *n_s, const int64_t *col_off,
+                      int32_t num_slices, int32_t r, const lora_segments *seg, void *y,
+                      int64_t ldy, int add_inputs, int dtype, void *stream);
+
+/* Message describing the last non-OK status returned on this thread. */
+const char *lora_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_MI355X_H */

@@ -1,0 +1,252 @@
+"""Python binding of liblora_mi355x (multi-LoRA shrink / expand on MI355X).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  PyTorch provides device memory and the current stream.  The entry
+points carry the C-ABI names of ``include/lora.h``:
+
+    lora_build_segments, lora_shrink, lora_expand, lora_expand_slice,
+    lora_shrink_workspace_bytes, lora_workspace_clear, lora_last_error
+
+If the shared library has not been built (``python -m
+lora_serving_build_amd.build``), every entry point raises: there is no
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "LoraError", "Segments", "lib", "lora_build_segments", "lora_shrink", "lora_expand",
+    "lora_expand_slice", "lora_shrink_workspace_bytes", "lora_workspace_clear",
+    "lora_last_error", "LORA_F16", "LORA_BF16", "LORA_MAX_RANK", "LORA_MAX_LORAS",
+    "LORA_MAX_SLICES", "library_path",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "liblora_mi355x.so")
+
+LORA_OK, LORA_ERR_INVALID_ARG, LORA_ERR_UNSUPPORTED, LORA_ERR_WORKSPACE, LORA_ERR_HIP = 0, -1, -2, -3, -4
+LORA_F16, LORA_BF16 = 0, 1
+LORA_MAX_RANK, LORA_MAX_LORAS, LORA_MAX_SLICES = 128, 2048, 8
+
+
+class LoraError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+
+
+class _CSegments(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32),
+        ("num_loras", ctypes.c_int32),
+        ("token_lora", ctypes.c_void_p),
+        ("sorted_token", ctypes.c_void_p),
+        ("seg_lora", ctypes.c_void_p),
+        ("seg_start", ctypes.c_void_p),
+        ("counts", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib() -> ctypes.CDLL:
+    """Loads liblora_mi355x.so; raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(library_path):
+                raise ImportError(
+                    f"{library_path} is missing: build it with "
+                    "`python -m lora_serving_build_amd.build` (hipcc, gfx950)")
+            L = ctypes.CDLL(library_path)
+            p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+            seg_p = ctypes.POINTER(_CSegments)
+            L.lora_build_segments.argtypes = [seg_p, p]
+            L.lora_shrink_workspace_bytes.argtypes = [i32, i32, i32, i32]
+            L.lora_shrink_workspace_bytes.restype = sz
+            L.lora_workspace_clear.argtypes = [p, sz, p]
+            L.lora_shrink.argtypes = [p, i64, p, i32, i32, seg_p, p, i64, p, sz, ctypes.c_int, p]
+            L.lora_expand.argtypes = [p, i64, p, i32, i32, seg_p, p, i64, ctypes.c_int, ctypes.c_int, p]
+            L.lora_expand_slice.argtypes = [p, i64, i64, p, p, p, i32, i32, seg_p, p, i64,
+                                            ctypes.c_int, ctypes.c_int, p]
+            L.lora_last_error.restype = ctypes.c_char_p
+            for f in ("lora_build_segments", "lora_workspace_clear", "lora_shrink", "lora_expand",
+                      "lora_expand_slice"):
+                getattr(L, f).restype = ctypes.c_int
+            _lib = L
+    return _lib
+
+
+def lora_last_error() -> str:
+    return lib().lora_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != LORA_OK:
+        raise LoraError(rc, lora_last_error())
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float16:
+        return LORA_F16
+    if t == torch.bfloat16:
+        return LORA_BF16
+    raise TypeError(f"unsupported dtype {t}: x, A, B and y must be float16 or bfloat16")
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _row_major(t: torch.Tensor, name: str):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with contiguous rows")
+    return t.stride(0)
+
+
+class Segments:
+    """Segment metadata buffers of one batch (device tensors) and the C
+    struct that points at them."""
+
+    def __init__(self, token_lora: torch.Tensor, num_loras: int):
+        if token_lora.dtype != torch.int32 or token_lora.dim() != 1 or not token_lora.is_cuda:
+            raise ValueError("token_lora must be a 1-D int32 CUDA tensor")
+        token_lora = token_lora.contiguous()
+        dev = token_lora.device
+        T = token_lora.shape[0]
+        self.token_lora = token_lora
+        self.num_loras = int(num_loras)
+        self.sorted_token = torch.empty(max(T, 1), dtype=torch.int32, device=dev)
+        self.seg_lora = torch.empty(self.num_loras, dtype=torch.int32, device=dev)
+        self.seg_start = torch.empty(self.num_loras + 1, dtype=torch.int32, device=dev)
+        self.counts = torch.empty(4, dtype=torch.int32, device=dev)
+        self.c = _CSegments(T, self.num_loras, token_lora.data_ptr(), self.sorted_token.data_ptr(),
+                            self.seg_lora.data_ptr(), self.seg_start.data_ptr(),
+                            self.counts.data_ptr())
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.c.num_tokens)
+
+    @property
+    def device(self) -> torch.device:
+        return self.token_lora.device
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def lora_build_segments(token_lora: torch.Tensor, num_loras: int,
+                        seg: Segments | None = None) -> Segments:
+    """Groups the batch's tokens by adapter id (see include/lora.h)."""
+    if seg is None:
+        seg = Segments(token_lora, num_loras)
+    _check(lib().lora_build_segments(seg.ref(), _stream(seg.device)))
+    return seg
+
+
+def lora_shrink_workspace_bytes(T: int, L: int, H: int, r: int) -> int:
+    return int(lib().lora_shrink_workspace_bytes(T, L, H, r))
+
+
+def lora_workspace_clear(ws: torch.Tensor):
+    _check(lib().lora_workspace_clear(ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
+                                      _stream(ws.device)))
+
+
+_ws_cache: dict = {}
+
+
+def _workspace(device: torch.device, nbytes: int) -> torch.Tensor | None:
+    """A zero-initialised workspace per (device, stream), grown on demand.
+    Every shrink leaves it zeroed again, so it is reused as is."""
+    if nbytes == 0:
+        return None
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros((nbytes + 255) // 256 * 256, dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def lora_shrink(x: torch.Tensor, A: torch.Tensor, seg: Segments, v: torch.Tensor,
+                workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """v[t, :r] = x[t, :H] . A_l for active tokens (A is [L][r][H]); v is fp32."""
+    if A.dim() != 3 or not A.is_contiguous():
+        raise ValueError("A must be a contiguous [L][r][H] tensor")
+    L, r, H = A.shape
+    if L != seg.num_loras:
+        raise ValueError(f"A holds {L} adapters, segments were built for {seg.num_loras}")
+    if v.dtype != torch.float32:
+        raise TypeError("v must be float32")
+    if x.dtype != A.dtype:
+        raise TypeError("x and A must share a dtype")
+    ldx = _row_major(x, "x")
+    ldv = _row_major(v, "v")
+    need = lora_shrink_workspace_bytes(seg.num_tokens, L, H, r)
+    if workspace is None:
+        workspace = _workspace(x.device, need)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().lora_shrink(ctypes.c_void_p(x.data_ptr()), ldx, ctypes.c_void_p(A.data_ptr()), H, r,
+                             seg.ref(), ctypes.c_void_p(v.data_ptr()), ldv, ws_ptr, ws_bytes,
+                             _dtype_code(x.dtype), _stream(x.device)))
+    return v
+
+
+def lora_expand(v: torch.Tensor, B: torch.Tensor, seg: Segments, y: torch.Tensor,
+                add_inputs: bool = True) -> torch.Tensor:
+    """y[t, :n] (+)= v[t, :r] . B_l for active tokens (B is [L][n][r])."""
+    if B.dim() != 3 or not B.is_contiguous():
+        raise ValueError("B must be a contiguous [L][n][r] tensor")
+    L, n, r = B.shape
+    if L != seg.num_loras:
+        raise ValueError(f"B holds {L} adapters, segments were built for {seg.num_loras}")
+    if v.dtype != torch.float32 or y.dtype != B.dtype:
+        raise TypeError("v must be float32 and y must share B's dtype")
+    ldv = _row_major(v, "v")
+    ldy = _row_major(y, "y")
+    _check(lib().lora_expand(ctypes.c_void_p(v.data_ptr()), ldv, ctypes.c_void_p(B.data_ptr()), r, n,
+                             seg.ref(), ctypes.c_void_p(y.data_ptr()), ldy, int(bool(add_inputs)),
+                             _dtype_code(y.dtype), _stream(y.device)))
+    return y
+
+
+def lora_expand_slice(v: torch.Tensor, Bs, col_offs, seg: Segments, y: torch.Tensor,
+                      add_inputs: bool = True, v_slice_stride: int = 0) -> torch.Tensor:
+    """For each slice s: y[t, off_s : off_s + n_s] (+)= v_s[t, :r] . B_s,l with
+    v_s = v shifted by s * v_slice_stride elements."""
+    Bs = list(Bs)
+    ns = len(Bs)
+    if ns != len(col_offs):
+        raise ValueError("one column offset per slice")
+    r = None
+    for b in Bs:
+        if b.dim() != 3 or not b.is_contiguous():
+            raise ValueError("every B must be a contiguous [L][n_s][r] tensor")
+        if b.shape[0] != seg.num_loras or b.dtype != y.dtype:
+            raise ValueError("every B must hold num_loras adapters in y's dtype")
+        if r is not None and b.shape[2] != r:
+            raise ValueError("all slices must share the rank")
+        r = b.shape[2]
+    if v.dtype != torch.float32:
+        raise TypeError("v must be float32")
+    ldv = _row_major(v, "v")
+    ldy = _row_major(y, "y")
+    ptrs = (ctypes.c_void_p * ns)(*[b.data_ptr() for b in Bs])
+    n_s = (ctypes.c_int32 * ns)(*[b.shape[1] for b in Bs])
+    offs = (ctypes.c_int64 * ns)(*[int(o) for o in col_offs])
+    _check(lib().lora_expand_slice(ctypes.c_void_p(v.data_ptr()), ldv, int(v_slice_stride), ptrs, n_s,
+                                   offs, ns, r, seg.ref(), ctypes.c_void_p(y.data_ptr()), ldy,
+                                   int(bool(add_inputs)), _dtype_code(y.dtype), _stream(y.device)))
+    return y

@@ -1,0 +1,198 @@
+// C-ABI of liblora_mi355x (declared in include/lora.h): argument validation,
+// dispatch to the gfx950 kernels, error reporting.  Nothing here allocates,
+// copies between host and device or synchronises.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "lora.h"
+#include "lora_kernels.h"
+
+namespace {
+
+thread_local char g_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_error, sizeof g_error, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_error[0] = '\0';
+  return LORA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(LORA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_dtype(int dtype, const char* fn) {
+  if (dtype != LORA_F16 && dtype != LORA_BF16)
+    return fail(LORA_ERR_INVALID_ARG, "%s: dtype %d is neither LORA_F16 nor LORA_BF16", fn, dtype);
+  return LORA_OK;
+}
+
+// Validates the metadata struct that shrink / expand read.
+int check_segments(const lora_segments* seg, const char* fn) {
+  if (!seg) return fail(LORA_ERR_INVALID_ARG, "%s: seg is NULL", fn);
+  if (seg->num_tokens < 0) return fail(LORA_ERR_INVALID_ARG, "%s: num_tokens %d < 0", fn, seg->num_tokens);
+  if (seg->num_loras < 1 || seg->num_loras > LORA_MAX_LORAS)
+    return fail(LORA_ERR_UNSUPPORTED, "%s: num_loras %d outside [1, %d]", fn, seg->num_loras,
+                LORA_MAX_LORAS);
+  if (!seg->seg_lora || !seg->seg_start || !seg->counts)
+    return fail(LORA_ERR_INVALID_ARG, "%s: segment buffers must not be NULL", fn);
+  if (seg->num_tokens > 0 && (!seg->token_lora || !seg->sorted_token))
+    return fail(LORA_ERR_INVALID_ARG, "%s: token buffers must not be NULL", fn);
+  return LORA_OK;
+}
+
+int check_rank(int32_t r, const char* fn) {
+  if (r < 1 || r > LORA_MAX_RANK)
+    return fail(LORA_ERR_UNSUPPORTED, "%s: rank %d outside [1, %d]", fn, r, LORA_MAX_RANK);
+  return LORA_OK;
+}
+
+lora::SegView view(const lora_segments* seg) {
+  lora::SegView s;
+  s.token_lora = seg->token_lora;
+  s.sorted_token = seg->sorted_token;
+  s.seg_lora = seg->seg_lora;
+  s.seg_start = seg->seg_start;
+  s.counts = seg->counts;
+  s.T = seg->num_tokens;
+  s.L = seg->num_loras;
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lora_build_segments(const lora_segments* seg, void* stream) {
+  static const char* fn = "lora_build_segments";
+  if (int e = check_segments(seg, fn)) return e;
+  hipError_t err = lora::launch_build_segments(seg->token_lora, seg->num_tokens, seg->num_loras,
+                                               seg->sorted_token, seg->seg_lora, seg->seg_start,
+                                               seg->counts, static_cast<hipStream_t>(stream));
+  return hip_status(err, fn);
+}
+
+size_t lora_shrink_workspace_bytes(int32_t T, int32_t L, int32_t H, int32_t r) {
+  if (T <= 0 || L < 1 || H < 1 || r < 1 || r > LORA_MAX_RANK) return 0;
+  const lora::ShrinkPlan p = lora::plan_shrink(T, L, H, r);
+  return p.partial_bytes + p.counter_bytes;
+}
+
+int lora_workspace_clear(void* workspace, size_t bytes, void* stream) {
+  static const char* fn = "lora_workspace_clear";
+  if (bytes == 0) return ok();
+  if (!workspace) return fail(LORA_ERR_INVALID_ARG, "%s: workspace is NULL", fn);
+  if (!aligned16(workspace) || (bytes & 15u))
+    return fail(LORA_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned and sized", fn);
+  return hip_status(lora::launch_fill_zero(workspace, bytes, static_cast<hipStream_t>(stream)), fn);
+}
+
+int lora_shrink(const void* x, int64_t ldx, const void* A, int32_t H, int32_t r,
+                const lora_segments* seg, float* v, int64_t ldv, void* workspace,
+                size_t workspace_bytes, int dtype, void* stream) {
+  static const char* fn = "lora_shrink";
+  if (int e = check_dtype(dtype, fn)) return e;
+  if (int e = check_segments(seg, fn)) return e;
+  if (int e = check_rank(r, fn)) return e;
+  if (H < 1) return fail(LORA_ERR_INVALID_ARG, "%s: H %d < 1", fn, H);
+  if (ldx < H) return fail(LORA_ERR_INVALID_ARG, "%s: ldx %lld < H %d", fn, (long long)ldx, H);
+  if (ldv < r) return fail(LORA_ERR_INVALID_ARG, "%s: ldv %lld < r %d", fn, (long long)ldv, r);
+  const int32_t T = seg->num_tokens;
+  if (T == 0) return ok();
+  if (!x || !A || !v) return fail(LORA_ERR_INVALID_ARG, "%s: x, A and v must not be NULL", fn);
+  const lora::ShrinkPlan plan = lora::plan_shrink(T, seg->num_loras, H, r);
+  const size_t need = plan.partial_bytes + plan.counter_bytes;
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(LORA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace))
+      return fail(LORA_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned", fn);
+  }
+  const bool vec = (H % 8 == 0) && (ldx % 8 == 0) && aligned16(x) && aligned16(A) &&
+                   (ldv % 4 == 0) && aligned16(v);
+  hipError_t err = lora::launch_shrink(view(seg), static_cast<const uint16_t*>(x), ldx,
+                                       static_cast<const uint16_t*>(A), H, r, v, ldv, workspace,
+                                       plan, dtype, vec, static_cast<hipStream_t>(stream));
+  return hip_status(err, fn);
+}
+
+int lora_expand_slice(const float* v, int64_t ldv, int64_t v_slice_stride, const void* const* B,
+                      const int32_t* n_s, const int64_t* col_off, int32_t num_slices, int32_t r,
+                      const lora_segments* seg, void* y, int64_t ldy, int add_inputs, int dtype,
+                      void* stream) {
+  static const char* fn = "lora_expand_slice";
+  if (int e = check_dtype(dtype, fn)) return e;
+  if (int e = check_segments(seg, fn)) return e;
+  if (int e = check_rank(r, fn)) return e;
+  if (num_slices < 1 || num_slices > LORA_MAX_SLICES)
+    return fail(LORA_ERR_UNSUPPORTED, "%s: num_slices %d outside [1, %d]", fn, num_slices,
+                LORA_MAX_SLICES);
+  if (!B || !n_s || !col_off)
+    return fail(LORA_ERR_INVALID_ARG, "%s: B, n_s and col_off must not be NULL", fn);
+  if (ldv < r) return fail(LORA_ERR_INVALID_ARG, "%s: ldv %lld < r %d", fn, (long long)ldv, r);
+  if (v_slice_stride < 0)
+    return fail(LORA_ERR_INVALID_ARG, "%s: v_slice_stride %lld < 0", fn, (long long)v_slice_stride);
+  lora::ExpandSliceDesc desc[LORA_MAX_SLICES];
+  int order[LORA_MAX_SLICES];
+  for (int s = 0; s < num_slices; ++s) {
+    if (!B[s]) return fail(LORA_ERR_INVALID_ARG, "%s: B[%d] is NULL", fn, s);
+    if (n_s[s] < 1) return fail(LORA_ERR_INVALID_ARG, "%s: n_s[%d] = %d < 1", fn, s, n_s[s]);
+    if (col_off[s] < 0 || col_off[s] + n_s[s] > ldy)
+      return fail(LORA_ERR_INVALID_ARG, "%s: slice %d columns [%lld, %lld) outside [0, ldy=%lld)",
+                  fn, s, (long long)col_off[s], (long long)(col_off[s] + n_s[s]), (long long)ldy);
+    desc[s].B = static_cast<const uint16_t*>(B[s]);
+    desc[s].n = n_s[s];
+    desc[s].col_off = col_off[s];
+    order[s] = s;
+  }
+  std::sort(order, order + num_slices, [&](int a, int b) { return col_off[a] < col_off[b]; });
+  for (int i = 1; i < num_slices; ++i) {
+    const int a = order[i - 1], b = order[i];
+    if (col_off[a] + n_s[a] > col_off[b])
+      return fail(LORA_ERR_INVALID_ARG, "%s: slices %d and %d overlap", fn, a, b);
+  }
+  const int32_t T = seg->num_tokens;
+  if (T == 0) return ok();
+  if (!v || !y) return fail(LORA_ERR_INVALID_ARG, "%s: v and y must not be NULL", fn);
+  bool vec = (r % 8 == 0) && (ldv % 4 == 0) && (v_slice_stride % 4 == 0) && aligned16(v) &&
+             (ldy % 8 == 0) && aligned16(y);
+  for (int s = 0; s < num_slices; ++s) vec = vec && aligned16(B[s]) && (col_off[s] % 8 == 0);
+  hipError_t err = lora::launch_expand(view(seg), v, ldv, v_slice_stride, desc, num_slices, r,
+                                       static_cast<uint16_t*>(y), ldy, add_inputs ? 1 : 0, dtype,
+                                       vec, static_cast<hipStream_t>(stream));
+  return hip_status(err, fn);
+}
+
+int lora_expand(const float* v, int64_t ldv, const void* B, int32_t r, int32_t n,
+                const lora_segments* seg, void* y, int64_t ldy, int add_inputs, int dtype,
+                void* stream) {
+  const void* Bs[1] = {B};
+  const int32_t ns[1] = {n};
+  const int64_t off[1] = {0};
+  int rc = lora_expand_slice(v, ldv, 0, Bs, ns, off, 1, r, seg, y, ldy, add_inputs, dtype, stream);
+  if (rc != LORA_OK) {
+    // Report under this entry point's name.
+    char tmp[512];
+    snprintf(tmp, sizeof tmp, "lora_expand: %s", g_error);
+    snprintf(g_error, sizeof g_error, "%s", tmp);
+  }
+  return rc;
+}
+
+const char* lora_last_error(void) { return g_error; }
+
+}  // extern "C"

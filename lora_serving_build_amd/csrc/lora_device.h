@@ -1,0 +1,137 @@
+// Device-side building blocks shared by the gfx950 kernels: vector types,
+// 16-bit conversions, the 16x16x32 matrix-core op and wave/block scans.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lora {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- 16-bit <-> fp32
+// DT 0 = IEEE binary16, DT 1 = bfloat16.  Widening is exact; narrowing rounds
+// to nearest even (bf16 by rounding the binary32 pattern; NaN stays NaN).
+template <int DT>
+__device__ __forceinline__ float to_f32(uint32_t bits16) {
+  if constexpr (DT == 0) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+  } else {
+    return __uint_as_float(bits16 << 16);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t from_f32(float f) {
+  if constexpr (DT == 0) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+  } else {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  }
+}
+
+// Packs two 16-bit patterns into one dword (lo = first element).
+__device__ __forceinline__ uint32_t pack2(uint32_t a, uint32_t b) { return a | (b << 16); }
+
+// ---------------------------------------------------------------- matrix core
+// D(16x16, fp32) += A(16x32) * B(32x16) with 8 elements of A and B per lane.
+// Whatever the hardware's internal k numbering, slot (lane / 16, element e) of
+// A meets slot (lane / 16, element e) of B, so both operands only have to
+// place the same k in the same slot.  Lane i of D holds rows 4 * (i / 16) + 0..3
+// of column i % 16.
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (DT == 0) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+}
+
+// ---------------------------------------------------------------- loads
+// Loads 8 consecutive 16-bit elements p[0..8) as 4 dwords.  Elements at or
+// beyond `limit` (counted from p) read as zero.  VEC: p is 16-byte aligned
+// whenever the whole chunk is in range.
+template <bool VEC>
+__device__ __forceinline__ u32x4 load8_16(const uint16_t* __restrict__ p, int limit) {
+  if (VEC && limit >= 8) return *reinterpret_cast<const u32x4*>(p);
+  uint32_t e[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) e[i] = (i < limit) ? (uint32_t)p[i] : 0u;
+  u32x4 r;
+  r.x = pack2(e[0], e[1]);
+  r.y = pack2(e[2], e[3]);
+  r.z = pack2(e[4], e[5]);
+  r.w = pack2(e[6], e[7]);
+  return r;
+}
+
+// Loads 8 consecutive floats (elements beyond `limit` read as zero).
+template <bool VEC>
+__device__ __forceinline__ void load8_f32(const float* __restrict__ p, int limit, float out[8]) {
+  if (VEC && limit >= 8) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out[i] = (i < limit) ? p[i] : 0.0f;
+}
+
+// ---------------------------------------------------------------- scans
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    int y = __shfl_up(x, d, kWave);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// Exclusive prefix sum over all threads of a block of NT threads.  `scratch`
+// holds NT / 64 + 1 ints of LDS.  Returns the exclusive prefix; *total gets the
+// block total.  Contains __syncthreads(); every thread must call it.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_sum(int x, int* scratch, int* total) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  int inc = wave_inclusive_sum(x);
+  if (lane == kWave - 1) scratch[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    int w = (lane < NW) ? scratch[lane] : 0;
+    int wi = wave_inclusive_sum(w);
+    if (lane < NW) scratch[lane] = wi - w;
+    if (lane == NW - 1) scratch[NW] = wi;
+  }
+  __syncthreads();
+  int excl = scratch[wave] + inc - x;
+  *total = scratch[NW];
+  __syncthreads();
+  return excl;
+}
+
+// XCD-aware renumbering: workgroups are dealt round-robin to the 8 XCDs, so
+// for a grid that is a multiple of 8 this maps consecutive logical ids onto
+// one XCD (and its L2).
+__device__ __forceinline__ int xcd_logical_id(int wg, int grid) {
+  if ((grid & 7) != 0) return wg;
+  return (wg & 7) * (grid >> 3) + (wg >> 3);
+}
+
+}  // namespace lora

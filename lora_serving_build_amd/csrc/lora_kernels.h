@@ -1,0 +1,63 @@
+// Launchers of the gfx950 kernels, called by the C-ABI layer (lora_api.hip)
+// after it has validated every argument.  They return the hipError_t of the
+// launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lora {
+
+constexpr int kMaxSlices = 8;
+constexpr int kMaxRank = 128;
+constexpr int kMaxLoras = 2048;
+
+// Token tile of the segment kernels: 4 waves x 16 tokens.
+constexpr int kTileTokens = 64;
+// Columns per expand work item (per wave: 16 tokens x 64 columns).
+constexpr int kExpandCols = 64;
+// H elements one shrink K-step covers (4 lane groups x 32 elements).
+constexpr int kShrinkKStep = 128;
+
+struct SegView {
+  const int32_t* token_lora;
+  const int32_t* sorted_token;
+  const int32_t* seg_lora;
+  const int32_t* seg_start;
+  const int32_t* counts;
+  int32_t T;
+  int32_t L;
+};
+
+hipError_t launch_build_segments(const int32_t* token_lora, int32_t T, int32_t L,
+                                 int32_t* sorted_token, int32_t* seg_lora,
+                                 int32_t* seg_start, int32_t* counts, hipStream_t s);
+
+struct ShrinkPlan {
+  int32_t ksplit;       // number of H chunks reduced across workgroups
+  int32_t kchunk;       // H elements per chunk (multiple of kShrinkKStep)
+  int32_t max_tiles;    // upper bound on token tiles
+  int32_t grid;         // persistent workgroups
+  size_t partial_bytes; // split-K partial sums in the workspace
+  size_t counter_bytes; // per-tile arrival counters in the workspace
+};
+
+ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r);
+
+hipError_t launch_shrink(const SegView& seg, const uint16_t* x, int64_t ldx, const uint16_t* A,
+                         int32_t H, int32_t r, float* v, int64_t ldv, void* workspace,
+                         const ShrinkPlan& plan, int dtype, bool vec, hipStream_t s);
+
+struct ExpandSliceDesc {
+  const uint16_t* B;
+  int32_t n;
+  int64_t col_off;
+};
+
+hipError_t launch_expand(const SegView& seg, const float* v, int64_t ldv, int64_t v_slice_stride,
+                         const ExpandSliceDesc* slices, int32_t num_slices, int32_t r,
+                         uint16_t* y, int64_t ldy, int add, int dtype, bool vec, hipStream_t s);
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+
+}  // namespace lora

@@ -1,0 +1,144 @@
+"""The C-ABI library: it loads, exports every symbol that include/lora.h
+declares, and rejects host-checkable errors before launching anything.  CPU
+only: every call here returns from argument validation, no kernel runs."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import lora_serving_build_amd as lsb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+           if f.endswith(".h")]
+
+FAKE = ctypes.c_void_p(0x100000)   # never dereferenced: validation fails first
+
+
+def declared_functions():
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(lora_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for f in ("lora_build_segments", "lora_shrink", "lora_expand", "lora_expand_slice",
+              "lora_shrink_workspace_bytes", "lora_workspace_clear", "lora_last_error"):
+        assert f in names
+
+
+@pytest.mark.parametrize("name", declared_functions())
+def test_library_exports_symbol(name):
+    lib = lsb.lib()
+    assert hasattr(lib, name)
+
+
+def _seg(T=16, L=4, token=True):
+    return lsb._CSegments(T, L, FAKE.value if token else None, FAKE.value, FAKE.value, FAKE.value,
+                          FAKE.value)
+
+
+def _expect(rc, code, text):
+    assert rc == code, (rc, lsb.lora_last_error())
+    assert text in lsb.lora_last_error()
+
+
+def test_build_segments_validation():
+    lib = lsb.lib()
+    _expect(lib.lora_build_segments(None, None), lsb.LORA_ERR_INVALID_ARG, "seg is NULL")
+    s = _seg(T=-1)
+    _expect(lib.lora_build_segments(ctypes.byref(s), None), lsb.LORA_ERR_INVALID_ARG, "num_tokens")
+    for L in (0, lsb.LORA_MAX_LORAS + 1):
+        s = _seg(L=L)
+        _expect(lib.lora_build_segments(ctypes.byref(s), None), lsb.LORA_ERR_UNSUPPORTED, "num_loras")
+    s = _seg(token=False)
+    _expect(lib.lora_build_segments(ctypes.byref(s), None), lsb.LORA_ERR_INVALID_ARG, "token buffers")
+
+
+def test_shrink_validation():
+    lib = lsb.lib()
+    s = _seg()
+    sp = ctypes.byref(s)
+    call = lambda **k: lib.lora_shrink(k.get("x", FAKE), k.get("ldx", 64), k.get("A", FAKE), k.get("H", 64),
+                                       k.get("r", 16), k.get("seg", sp), k.get("v", FAKE), k.get("ldv", 16),
+                                       k.get("ws", FAKE), k.get("wsb", 1 << 30), k.get("dt", 0), None)
+    _expect(call(dt=2), lsb.LORA_ERR_INVALID_ARG, "dtype")
+    _expect(call(r=0), lsb.LORA_ERR_UNSUPPORTED, "rank")
+    _expect(call(r=129), lsb.LORA_ERR_UNSUPPORTED, "rank")
+    _expect(call(H=0), lsb.LORA_ERR_INVALID_ARG, "H 0")
+    _expect(call(ldx=63), lsb.LORA_ERR_INVALID_ARG, "ldx")
+    _expect(call(ldv=15), lsb.LORA_ERR_INVALID_ARG, "ldv")
+    _expect(call(x=None), lsb.LORA_ERR_INVALID_ARG, "must not be NULL")
+    need = lsb.lora_shrink_workspace_bytes(16, 4, 4096, 16)
+    assert need > 0
+    _expect(call(H=4096, ldx=4096, wsb=need - 1), lsb.LORA_ERR_WORKSPACE, "workspace")
+    _expect(call(H=4096, ldx=4096, ws=None), lsb.LORA_ERR_WORKSPACE, "workspace")
+    _expect(call(seg=None), lsb.LORA_ERR_INVALID_ARG, "seg is NULL")
+    # T = 0 is valid and launches nothing.
+    s0 = _seg(T=0)
+    assert call(seg=ctypes.byref(s0)) == lsb.LORA_OK
+
+
+def test_workspace_size_is_zero_when_not_split():
+    # Large batches need no split of H, hence no workspace.
+    assert lsb.lora_shrink_workspace_bytes(0, 4, 4096, 16) == 0
+    assert lsb.lora_shrink_workspace_bytes(65536, 4, 4096, 16) == 0
+    assert lsb.lora_shrink_workspace_bytes(256, 4, 4096, 16) > 0
+
+
+def _slice_call(lib, sp, Bs, ns, offs, ldy=64, r=16, stride=0, dt=0, nsl=None):
+    k = len(ns) if nsl is None else nsl
+    B = (ctypes.c_void_p * max(len(Bs), 1))(*Bs)
+    n = (ctypes.c_int32 * max(len(ns), 1))(*ns)
+    o = (ctypes.c_int64 * max(len(offs), 1))(*offs)
+    return lib.lora_expand_slice(FAKE, 16, stride, B, n, o, k, r, sp, FAKE, ldy, 1, dt, None)
+
+
+def test_expand_slice_validation():
+    lib = lsb.lib()
+    s = _seg()
+    sp = ctypes.byref(s)
+    F = FAKE.value
+    _expect(_slice_call(lib, sp, [F], [32], [0], nsl=0), lsb.LORA_ERR_UNSUPPORTED, "num_slices")
+    _expect(_slice_call(lib, sp, [F] * 9, [4] * 9, list(range(0, 36, 4)), nsl=9),
+            lsb.LORA_ERR_UNSUPPORTED, "num_slices")
+    _expect(_slice_call(lib, sp, [F, F], [32, 32], [0, 16]), lsb.LORA_ERR_INVALID_ARG, "overlap")
+    _expect(_slice_call(lib, sp, [F, F], [32, 32], [32, 0], ldy=63), lsb.LORA_ERR_INVALID_ARG, "outside")
+    _expect(_slice_call(lib, sp, [F], [0], [0]), lsb.LORA_ERR_INVALID_ARG, "n_s[0]")
+    _expect(_slice_call(lib, sp, [F], [8], [-8]), lsb.LORA_ERR_INVALID_ARG, "outside")
+    _expect(_slice_call(lib, sp, [None], [8], [0]), lsb.LORA_ERR_INVALID_ARG, "B[0] is NULL")
+    _expect(_slice_call(lib, sp, [F], [8], [0], r=200), lsb.LORA_ERR_UNSUPPORTED, "rank")
+    _expect(_slice_call(lib, sp, [F], [8], [0], stride=-1), lsb.LORA_ERR_INVALID_ARG, "v_slice_stride")
+    _expect(_slice_call(lib, sp, [F], [8], [0], dt=5), lsb.LORA_ERR_INVALID_ARG, "dtype")
+    # Slices given out of column order but disjoint are fine (T = 0: no launch).
+    s0 = _seg(T=0)
+    assert _slice_call(lib, ctypes.byref(s0), [F, F], [16, 16], [16, 0], ldy=32) == lsb.LORA_OK
+
+
+def test_expand_reports_under_its_name():
+    lib = lsb.lib()
+    s = _seg()
+    rc = lib.lora_expand(FAKE, 16, FAKE, 16, 0, ctypes.byref(s), FAKE, 64, 1, 0, None)
+    assert rc == lsb.LORA_ERR_INVALID_ARG
+    assert lsb.lora_last_error().startswith("lora_expand:")
+
+
+def test_workspace_clear_validation():
+    lib = lsb.lib()
+    assert lib.lora_workspace_clear(None, 0, None) == lsb.LORA_OK
+    _expect(lib.lora_workspace_clear(None, 16, None), lsb.LORA_ERR_INVALID_ARG, "NULL")
+    _expect(lib.lora_workspace_clear(ctypes.c_void_p(0x100008), 16, None), lsb.LORA_ERR_INVALID_ARG,
+            "aligned")
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(lsb, "_lib", None)
+    monkeypatch.setattr(lsb, "library_path", str(tmp_path / "absent.so"))
+    with pytest.raises(ImportError):
+        lsb.lib()

@@ -1,0 +1,377 @@
+"""GPU parity: the HIP path (through the C-ABI) against the fp64 oracle.
+
+Every test builds seeded inputs with ``workloads``, runs
+lora_build_segments -> lora_shrink -> lora_expand[_slice] on the GPU and
+compares with the oracle run on the same bits:
+  * metadata bit for bit,
+  * v and y within |gpu - oracle| <= 1e-2 (1 + |oracle|) ("chained": the
+    oracle's own fp64 v feeds its expand; "isolated": the GPU's fp32 v does),
+  * integer-valued inputs bit for bit against the oracle rounded once,
+  * rows of tokens without an adapter and columns outside the slices
+    untouched, bit for bit.
+The five named workloads run at full size; the largest is compared on a
+sample of rows (plus every untouched row in full).
+"""
+import numpy as np
+import pytest
+import torch
+
+import lora_serving_build_amd as lsb
+import oracle
+import workloads as W
+from parity_util import (DeviceWorkload, check_neg_rows, check_outside_slices, decode, dev_bits,
+                         host_bits, seg_host, sentinel_v, tol_ratio, V_SENTINEL)
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def _slice_cols(o):
+    return np.concatenate([np.arange(s.col_off, s.col_off + s.n) for s in o.slices])
+
+
+def compare_with_oracle(dw: DeviceWorkload, rows=None, isolated=True):
+    """Returns the worst tolerance ratios (v, y chained, y isolated)."""
+    w = dw.w
+    act_rows = np.nonzero(w.active)[0].astype(np.int32)
+    rows = act_rows if rows is None else np.asarray(rows, np.int32)
+    v_gpu = dw.v.cpu().numpy().astype(np.float64)
+    v_or = oracle.shrink(w.dtype, w.x, w.A, w.ids, rows=rows)
+    rv = tol_ratio(v_gpu[rows, :w.r], v_or)
+    v_full = np.zeros((w.T, w.r))
+    v_full[rows] = v_or
+    ry = ryi = 0.0
+    for o, y in zip(w.outputs, dw.ys):
+        Bs = [s.B for s in o.slices]
+        offs = [s.col_off for s in o.slices]
+        cols = _slice_cols(o)
+        got = decode(host_bits(y.index_select(0, torch.from_numpy(rows).long().cuda())), w.dtype)[:, cols]
+        ref = oracle.expand_slice(w.dtype, v_full, Bs, offs, w.ids, o.y0, w.add, rows=rows)
+        ry = max(ry, tol_ratio(got, ref))
+        if isolated:
+            ref_i = oracle.expand_slice(w.dtype, np.ascontiguousarray(v_gpu[:, :w.r]), Bs, offs, w.ids,
+                                        o.y0, w.add, rows=rows)
+            ryi = max(ryi, tol_ratio(got, ref_i))
+    return rv, ry, ryi
+
+
+# ---------------------------------------------------------------- metadata
+META_CASES = [(0, 1, "uniform"), (1, 1, "uniform"), (1, 4, "neg"), (7, 3, "uniform"),
+              (64, 4, "uniform"), (257, 4, "neg"), (1000, 64, "bad"), (513, 1, "uniform"),
+              (300, 16, "allneg"), (129, 5, "one"), (2048, 200, "bad"), (5000, 2048, "neg"),
+              (20000, 7, "uniform"), (3000, 3, "sorted")]
+
+
+@pytest.mark.parametrize("T,L,kind", META_CASES)
+def test_segments_bit_exact(T, L, kind):
+    _announce(f"segments T={T} L={L} {kind}")
+    rng = np.random.default_rng(T * 17 + L)
+    ids = rng.integers(0, L, size=T).astype(np.int32)
+    if kind == "neg":
+        ids[rng.random(T) < 0.3] = -1
+    elif kind == "bad":
+        m = rng.random(T)
+        ids[m < 0.1] = -1
+        ids[(m >= 0.1) & (m < 0.15)] = L + 3
+        ids[(m >= 0.15) & (m < 0.2)] = -7
+    elif kind == "allneg":
+        ids[:] = -1
+    elif kind == "one":
+        ids[:] = L - 1
+    elif kind == "sorted":
+        ids.sort()
+    seg = lsb.lora_build_segments(torch.from_numpy(ids).cuda(), L)
+    torch.cuda.synchronize()
+    got = seg_host(seg)
+    ref = oracle.build_segments(ids, L)
+    for g, r in zip(got, ref):
+        assert np.array_equal(g, r)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_segments_of_named_workloads(k, named):
+    w = named(k)
+    _announce(f"segments of {w.name}")
+    seg = lsb.lora_build_segments(torch.from_numpy(w.ids).cuda(), w.L)
+    torch.cuda.synchronize()
+    for g, r in zip(seg_host(seg), oracle.build_segments(w.ids, w.L)):
+        assert np.array_equal(g, r)
+
+
+# ---------------------------------------------------------------- named workloads
+@pytest.fixture(scope="module")
+def named():
+    cache = {}
+
+    def get(k):
+        if k not in cache:
+            cache.clear()
+            cache[k] = W.config(k)
+        return cache[k]
+    return get
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
+def test_named_workload_parity(k, named):
+    w = named(k)
+    _announce(f"parity {w.name}")
+    dw = DeviceWorkload(w)
+    seg = dw.run()
+    for g, r in zip(seg_host(seg), oracle.build_segments(w.ids, w.L)):
+        assert np.array_equal(g, r)
+    rv, ry, ryi = compare_with_oracle(dw)
+    print(f"  tolerance ratios: v {rv:.3g}  y {ry:.3g}  y(isolated) {ryi:.3g}")
+    assert rv <= 1 and ry <= 1 and ryi <= 1
+    check_neg_rows(dw)
+    check_outside_slices(dw)
+
+
+@pytest.mark.timeout(900)
+def test_largest_workload_sampled(named):
+    """The 8192-token, H = 8192, r = 64, 64-adapter layer: every untouched row
+    in full, and v / y on a sample of rows (segment boundaries + random)."""
+    w = named(5)
+    _announce(f"parity (sampled) {w.name}")
+    dw = DeviceWorkload(w)
+    seg = dw.run()
+    st, sl, ss, cn = seg_host(seg)
+    for g, r in zip((st, sl, ss, cn), oracle.build_segments(w.ids, w.L)):
+        assert np.array_equal(g, r)
+    S = cn[0]
+    bounds = np.unique(np.concatenate([st[ss[:S]], st[np.maximum(ss[1:S + 1] - 1, 0)]]))
+    rng = np.random.default_rng(5)
+    act = np.nonzero(w.active)[0]
+    rows = np.unique(np.concatenate([bounds, rng.choice(act, 192, replace=False)])).astype(np.int32)
+    rv, ry, ryi = compare_with_oracle(dw, rows=rows)
+    print(f"  rows {rows.size}; tolerance ratios: v {rv:.3g}  y {ry:.3g}  y(isolated) {ryi:.3g}")
+    assert rv <= 1 and ry <= 1 and ryi <= 1
+    check_neg_rows(dw)
+
+
+# ---------------------------------------------------------------- exactness
+INT_CASES = [
+    ("f16", 200, 256, 16, 4, [[256]], 1),
+    ("bf16", 333, 512, 20, 5, [[64, 48, 100]], (1, 40)),
+    ("bf16", 97, 1024, 128, 3, [[128]], 1),
+    ("f16", 1000, 128, 8, 64, [[72, 8]], (1, 8)),
+    ("bf16", 64, 2049, 2, 2, [[33]], 4),
+]
+
+
+@pytest.mark.parametrize("dtype,T,H,r,L,slices,sl", INT_CASES)
+def test_integer_inputs_bit_exact(dtype, T, H, r, L, slices, sl):
+    """Integer inputs keep every fp32 partial sum exact, so the GPU must equal
+    the oracle's exact value rounded once to the output type."""
+    _announce(f"integer exact {dtype} T={T} H={H} r={r} L={L} slices={slices}")
+    w = W.make("int", dtype, T, H, r, L, slices, seed=T + H + r, seq_len=sl, neg_frac=0.15,
+               integer=True)
+    dw = DeviceWorkload(w)
+    dw.run()
+    act = np.nonzero(w.active)[0]
+    v_or = oracle.shrink(w.dtype, w.x, w.A, w.ids)
+    v_gpu = dw.v.cpu().numpy()
+    assert np.array_equal(v_gpu[act].astype(np.float64), v_or[act])
+    for o, y in zip(w.outputs, dw.ys):
+        ref = oracle.expand_slice(w.dtype, np.nan_to_num(v_or), [s.B for s in o.slices],
+                                  [s.col_off for s in o.slices], w.ids, o.y0, w.add)
+        ref_bits = W.f32_to_bits(ref.astype(np.float32), dtype) if dtype == "bf16" else \
+            ref.astype(np.float16).view(np.uint16)
+        got = host_bits(y)[:, _slice_cols(o)]
+        assert np.array_equal(got[act], ref_bits[act])
+    check_neg_rows(dw)
+    check_outside_slices(dw)
+
+
+# ---------------------------------------------------------------- shapes and edges
+EDGE_CASES = [
+    # dtype, T, H, r, L, slices, seq_len, neg_frac, id_dist
+    ("f16", 1, 64, 16, 1, [[64]], 1, 0.0, "uniform"),
+    ("bf16", 77, 2049, 20, 3, [[2049]], (1, 9), 0.2, "uniform"),   # odd H, r: scalar path
+    ("f16", 130, 1024, 2, 4, [[100]], 1, 0.1, "uniform"),           # ragged n
+    ("bf16", 515, 4096, 128, 8, [[1024, 512]], (1, 100), 0.1, "uniform"),
+    ("bf16", 300, 512, 64, 1, [[512]], (1, 300), 0.0, "uniform"),   # one adapter
+    ("f16", 4099, 256, 32, 300, [[256]], (1, 3), 0.05, "zipf"),     # many short segments
+    ("bf16", 2000, 16384, 16, 4, [[1024]], 8, 0.0, "uniform"),      # widest H of the sweep
+    ("f16", 260, 1024, 48, 6, [[40, 24, 8, 128]], (1, 50), 0.3, "uniform"),
+]
+
+
+@pytest.mark.parametrize("dtype,T,H,r,L,slices,sl,neg,dist", EDGE_CASES)
+def test_edge_shapes(dtype, T, H, r, L, slices, sl, neg, dist):
+    _announce(f"edge {dtype} T={T} H={H} r={r} L={L} slices={slices} seq={sl} neg={neg} {dist}")
+    w = W.make("edge", dtype, T, H, r, L, slices, seed=T * 3 + r, seq_len=sl, neg_frac=neg,
+               id_dist=dist)
+    dw = DeviceWorkload(w)
+    dw.run()
+    rv, ry, ryi = compare_with_oracle(dw)
+    print(f"  tolerance ratios: v {rv:.3g}  y {ry:.3g}  y(isolated) {ryi:.3g}")
+    assert rv <= 1 and ry <= 1 and ryi <= 1
+    check_neg_rows(dw)
+    check_outside_slices(dw)
+
+
+def test_empty_and_all_negative_batches():
+    _announce("empty and all -1 batches")
+    for T, neg in ((0, 0.0), (50, 1.0)):
+        w = W.make("e", "bf16", T, 256, 16, 3, [[64]], seed=9, neg_frac=neg) if T else None
+        if T == 0:
+            ids = torch.empty(0, dtype=torch.int32, device="cuda")
+            seg = lsb.lora_build_segments(ids, 3)
+            x = torch.empty(0, 256, dtype=torch.bfloat16, device="cuda")
+            A = torch.zeros(3, 16, 256, dtype=torch.bfloat16, device="cuda")
+            v = torch.empty(0, 16, device="cuda")
+            lsb.lora_shrink(x, A, seg, v)
+            B = torch.zeros(3, 64, 16, dtype=torch.bfloat16, device="cuda")
+            y = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
+            lsb.lora_expand(v, B, seg, y)
+            torch.cuda.synchronize()
+            assert seg.counts.cpu().tolist() == [0, 0, 0, 0]
+            assert seg.seg_lora.cpu().tolist() == [-1, -1, -1]
+            assert seg.seg_start.cpu().tolist() == [0, 0, 0, 0]
+        else:
+            assert not w.active.any()
+            dw = DeviceWorkload(w)
+            dw.run()
+            check_neg_rows(dw)
+
+
+def test_strided_rows():
+    """x with ldx > H, v with ldv > r and y with ldy wider than the slices."""
+    _announce("strided rows")
+    w = W.make("s", "bf16", 150, 512, 16, 4, [[256]], seed=12, seq_len=(1, 20), neg_frac=0.1)
+    x_wide = np.zeros((w.T, 520), np.uint16)
+    x_wide[:, :512] = w.x
+    xd = dev_bits(x_wide, w.dtype)[:, :512]
+    A = dev_bits(w.A, w.dtype)
+    ids = torch.from_numpy(w.ids).cuda()
+    seg = lsb.lora_build_segments(ids, w.L)
+    v = sentinel_v(w.T, 16, ldv=24)[:, :16]
+    lsb.lora_shrink(xd, A, seg, v)
+    y0_wide = W.normal_bits(np.random.default_rng(1), (w.T, 272), 1.0, w.dtype)
+    y = dev_bits(y0_wide, w.dtype)
+    B = dev_bits(w.outputs[0].slices[0].B, w.dtype)
+    lsb.lora_expand_slice(v, [B], [8], seg, y, True)
+    torch.cuda.synchronize()
+    act = np.nonzero(w.active)[0]
+    v_or = oracle.shrink(w.dtype, w.x, w.A, w.ids)
+    vg = v.cpu().numpy().astype(np.float64)
+    assert tol_ratio(vg[act], v_or[act]) <= 1
+    ref = oracle.expand(w.dtype, np.nan_to_num(v_or), w.outputs[0].slices[0].B, w.ids, y0_wide, 8, True)
+    got = decode(host_bits(y), w.dtype)
+    assert tol_ratio(got[act][:, 8:264], ref[act]) <= 1
+    outside = np.r_[0:8, 264:272]
+    assert np.array_equal(host_bits(y)[:, outside], y0_wide[:, outside])
+    inact = np.nonzero(~w.active)[0]
+    assert np.array_equal(host_bits(y)[inact], y0_wide[inact])
+
+
+def test_expand_slice_equals_separate_expands():
+    """expand_slice gives the same bits as one lora_expand per slice into a
+    column view (the micro-benchmark PR emulates slices that way)."""
+    _announce("expand_slice vs separate expands")
+    w = W.make("q", "bf16", 700, 1024, 32, 6, [[256, 64, 64]], seed=21, seq_len=(1, 30), neg_frac=0.1)
+    dw = DeviceWorkload(w)
+    dw.run()
+    y2 = dev_bits(w.outputs[0].y0, w.dtype)
+    for s, B in zip(w.outputs[0].slices, dw.Bs[0]):
+        lsb.lora_expand(dw.v, B, dw.seg, y2[:, s.col_off:s.col_off + s.n], True)
+    torch.cuda.synchronize()
+    assert torch.equal(dw.ys[0].view(torch.int16), y2.view(torch.int16))
+
+
+def test_v_slice_stride():
+    """Per-slice v through v_slice_stride against the oracle."""
+    _announce("v_slice_stride")
+    w = W.make("vs", "f16", 200, 256, 16, 3, [[128, 64]], seed=31, seq_len=(1, 10), neg_frac=0.1)
+    ids = torch.from_numpy(w.ids).cuda()
+    seg = lsb.lora_build_segments(ids, w.L)
+    vh = np.random.default_rng(2).standard_normal((w.T, 32)).astype(np.float32)
+    v = torch.from_numpy(vh).cuda()
+    y = dev_bits(w.outputs[0].y0, w.dtype)
+    Bs = [dev_bits(s.B, w.dtype) for s in w.outputs[0].slices]
+    lsb.lora_expand_slice(v, Bs, [0, 128], seg, y, True, v_slice_stride=16)
+    torch.cuda.synchronize()
+    ref = oracle.expand_slice(w.dtype, vh.astype(np.float64), [s.B for s in w.outputs[0].slices],
+                              [0, 128], w.ids, w.outputs[0].y0, True, v_slice_stride=16)
+    act = w.active
+    assert tol_ratio(decode(host_bits(y), w.dtype)[act], ref[act]) <= 1
+
+
+def test_add_inputs_false():
+    _announce("add_inputs = False")
+    w = W.make("na", "bf16", 400, 1024, 16, 4, [[512]], seed=41, seq_len=(1, 16), neg_frac=0.2,
+               add=False)
+    dw = DeviceWorkload(w)
+    dw.run()
+    rv, ry, ryi = compare_with_oracle(dw)
+    assert rv <= 1 and ry <= 1 and ryi <= 1
+    check_neg_rows(dw)
+
+
+def _rank_pairs():
+    import os
+    pairs = []
+    with open(os.path.join(os.path.dirname(__file__), "golden", "rank_bins.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                a, b = line.split()
+                pairs.append((int(a), int(b)))
+    return pairs + [(8, 128), (45, 128)]
+
+
+@pytest.mark.parametrize("r_true,r_pad", _rank_pairs())
+def test_rank_padding(r_true, r_pad):
+    """Zero-padding the rank (punica issue's mitigation) gives the oracle's
+    true-rank result within tolerance, and the same bits as the unpadded run."""
+    _announce(f"rank padding {r_true} -> {r_pad}")
+    w = W.make("rp", "bf16", 300, 1024, r_true, 5, [[512]], seed=r_true, seq_len=(1, 20), neg_frac=0.1)
+    Ap = np.zeros((w.L, r_pad, w.H), np.uint16)
+    Ap[:, :r_true] = w.A
+    B = w.outputs[0].slices[0].B
+    Bp = np.zeros((w.L, B.shape[1], r_pad), np.uint16)
+    Bp[:, :, :r_true] = B
+    ids = torch.from_numpy(w.ids).cuda()
+    seg = lsb.lora_build_segments(ids, w.L)
+    x = dev_bits(w.x, w.dtype)
+    outs = []
+    for A_, B_, rr in ((w.A, B, r_true), (Ap, Bp, r_pad)):
+        v = sentinel_v(w.T, rr)
+        lsb.lora_shrink(x, dev_bits(A_, w.dtype), seg, v)
+        y = dev_bits(w.outputs[0].y0, w.dtype)
+        lsb.lora_expand(v, dev_bits(B_, w.dtype), seg, y, True)
+        torch.cuda.synchronize()
+        outs.append((v.cpu().numpy(), host_bits(y)))
+    act = w.active
+    v_or = oracle.shrink(w.dtype, w.x, w.A, w.ids)
+    ref = oracle.expand(w.dtype, np.nan_to_num(v_or), B, w.ids, w.outputs[0].y0, 0, True)
+    for vg, yb in outs:
+        assert tol_ratio(vg[act, :r_true].astype(np.float64), v_or[act]) <= 1
+        assert tol_ratio(decode(yb, w.dtype)[act], ref[act]) <= 1
+    assert np.all(outs[1][0][act, r_true:] == 0)
+    assert np.array_equal(outs[0][1], outs[1][1])
+
+
+def test_shrink_repeatable_and_workspace_reuse():
+    """Split-K shrink overwrites v and leaves its workspace zeroed: repeated
+    calls give identical bits, also after a call on a different batch."""
+    _announce("shrink repeatability")
+    big = W.make("rep", "f16", 256, 4096, 16, 4, [[64]], seed=51)
+    small = W.make("rep2", "f16", 40, 4096, 16, 4, [[64]], seed=52, neg_frac=0.2, seq_len=(1, 5))
+    assert lsb.lora_shrink_workspace_bytes(256, 4, 4096, 16) > 0
+    res = []
+    for w in (big, small, big):
+        ids = torch.from_numpy(w.ids).cuda()
+        seg = lsb.lora_build_segments(ids, w.L)
+        v = sentinel_v(w.T, 16)
+        lsb.lora_shrink(dev_bits(w.x, w.dtype), dev_bits(w.A, w.dtype), seg, v)
+        lsb.lora_shrink(dev_bits(w.x, w.dtype), dev_bits(w.A, w.dtype), seg, v)
+        torch.cuda.synchronize()
+        res.append(v.cpu().numpy().view(np.uint32).copy())
+        act = w.active
+        v_or = oracle.shrink(w.dtype, w.x, w.A, w.ids)
+        assert tol_ratio(v.cpu().numpy()[act].astype(np.float64), v_or[act]) <= 1
+        assert np.all(res[-1][~act] == V_SENTINEL)
+    assert np.array_equal(res[0], res[2])
