@@ -103,27 +103,26 @@ typedef struct lora_segments {
 int lora_build_segments(const lora_segments *seg, void *stream);
 
 /* Workspace bytes that lora_shrink needs for T tokens, L adapters, hidden
- * size H and rank r (0 if it needs none).  The workspace holds split-K
- * partial sums and per-tile arrival counters. */
+ * size H and rank r (0 if it needs none).  Only batches with too few token
+ * tiles to occupy the GPU split the H-sum across workgroups; the workspace
+ * then holds one fp32 partial row per token and H chunk. */
 size_t lora_shrink_workspace_bytes(int32_t T, int32_t L, int32_t H, int32_t r);
-
-/* Zero-fills a workspace (a fill kernel on the stream; graph-safe). */
-int lora_workspace_clear(void *workspace, size_t bytes, void *stream);
 
 /* Shrink (micro-benchmark PR: bgmv_shrink / sgmv_shrink; TPU PR: the
  * separate shrink kernel):  v[t, j] = sum_h x[t, h] * A_l[h, j], j < r, for
  * every active token t, fp32 accumulation, fp32 result.  v rows of tokens
  * without an adapter are not written.  The result overwrites v: any split of
- * the H-sum across workgroups is reduced inside the call, in a fixed order,
- * so repeated calls give identical bits.
+ * the H-sum across waves or workgroups is reduced inside the call in a
+ * fixed order, so repeated calls give identical bits.  When the H-sum is
+ * split across workgroups the call launches a second, small kernel.
  *   x          [T][ldx] device, ldx >= H
  *   A          [L][r][H] device
  *   seg        metadata built for this batch (T, L taken from it)
  *   v          [T][ldv] fp32 device, ldv >= r
  *   workspace  device buffer of >= lora_shrink_workspace_bytes(T, L, H, r)
- *              bytes that is all zero before its first use (lora_workspace_clear
- *              or any zero fill); every call leaves it all zero again.  Calls
- *              that run concurrently must not share a workspace.
+ *              bytes, 16-byte aligned (may be NULL when that size is 0); its
+ *              contents need no initialisation.  Calls that run concurrently
+ *              must not share a workspace.
  * Errors: INVALID_ARG (NULL pointers, H < 1, ld too small, bad dtype),
  * UNSUPPORTED (r outside [1, LORA_MAX_RANK]), WORKSPACE, HIP. */
 int lora_shrink(const void *x, int64_t ldx, const void *A, int32_t H, int32_t r,

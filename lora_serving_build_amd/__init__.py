@@ -5,7 +5,7 @@ kernels.  PyTorch provides device memory and the current stream.  The entry
 points carry the C-ABI names of ``include/lora.h``:
 
     lora_build_segments, lora_shrink, lora_expand, lora_expand_slice,
-    lora_shrink_workspace_bytes, lora_workspace_clear, lora_last_error
+    lora_shrink_workspace_bytes, lora_last_error
 
 If the shared library has not been built (``python -m
 lora_serving_build_amd.build``), every entry point raises: there is no
@@ -21,8 +21,7 @@ import torch
 
 __all__ = [
     "LoraError", "Segments", "lib", "lora_build_segments", "lora_shrink", "lora_expand",
-    "lora_expand_slice", "lora_shrink_workspace_bytes", "lora_workspace_clear",
-    "lora_last_error", "LORA_F16", "LORA_BF16", "LORA_MAX_RANK", "LORA_MAX_LORAS",
+    "lora_expand_slice", "lora_shrink_workspace_bytes", "lora_last_error", "LORA_F16", "LORA_BF16", "LORA_MAX_RANK", "LORA_MAX_LORAS",
     "LORA_MAX_SLICES", "library_path",
 ]
 
@@ -73,14 +72,12 @@ def lib() -> ctypes.CDLL:
             L.lora_build_segments.argtypes = [seg_p, p]
             L.lora_shrink_workspace_bytes.argtypes = [i32, i32, i32, i32]
             L.lora_shrink_workspace_bytes.restype = sz
-            L.lora_workspace_clear.argtypes = [p, sz, p]
             L.lora_shrink.argtypes = [p, i64, p, i32, i32, seg_p, p, i64, p, sz, ctypes.c_int, p]
             L.lora_expand.argtypes = [p, i64, p, i32, i32, seg_p, p, i64, ctypes.c_int, ctypes.c_int, p]
             L.lora_expand_slice.argtypes = [p, i64, i64, p, p, p, i32, i32, seg_p, p, i64,
                                             ctypes.c_int, ctypes.c_int, p]
             L.lora_last_error.restype = ctypes.c_char_p
-            for f in ("lora_build_segments", "lora_workspace_clear", "lora_shrink", "lora_expand",
-                      "lora_expand_slice"):
+            for f in ("lora_build_segments", "lora_shrink", "lora_expand", "lora_expand_slice"):
                 getattr(L, f).restype = ctypes.c_int
             _lib = L
     return _lib
@@ -158,23 +155,18 @@ def lora_shrink_workspace_bytes(T: int, L: int, H: int, r: int) -> int:
     return int(lib().lora_shrink_workspace_bytes(T, L, H, r))
 
 
-def lora_workspace_clear(ws: torch.Tensor):
-    _check(lib().lora_workspace_clear(ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
-                                      _stream(ws.device)))
-
-
 _ws_cache: dict = {}
 
 
 def _workspace(device: torch.device, nbytes: int) -> torch.Tensor | None:
-    """A zero-initialised workspace per (device, stream), grown on demand.
-    Every shrink leaves it zeroed again, so it is reused as is."""
+    """A workspace per (device, stream), grown on demand.  Calls on one stream
+    run in order, so they can share it."""
     if nbytes == 0:
         return None
     key = (device.index, torch.cuda.current_stream(device).cuda_stream)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros((nbytes + 255) // 256 * 256, dtype=torch.uint8, device=device)
+        ws = torch.empty((nbytes + 255) // 256 * 256, dtype=torch.uint8, device=device)
         _ws_cache[key] = ws
     return ws
 

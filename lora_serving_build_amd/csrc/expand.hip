@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kExpandThreads) void expand_sgmv_kernel(ExpandArgs 
   const int g = lane >> 4;  // lane group
 
   int S;
-  const int mtiles = build_tile_prefix<kExpandThreads>(a.seg, s_tile_start, s_scan, &S);
+  const int mtiles = build_tile_prefix<kExpandThreads>(a.seg, kTileTokens, s_tile_start, s_scan, &S);
   const int ctiles = a.col_tile_start[a.num_slices];
   const int n_items = mtiles * ctiles;
   const int grid = gridDim.x;
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kExpandThreads) void expand_sgmv_kernel(ExpandArgs 
     const int nq = a.slices[q].n;
 
     int p0 = 0, p_end = 0, l = 0;
-    if (!tile_range(a.seg, s_tile_start, S, mt, &p0, &p_end, &l)) continue;
+    if (!tile_range(a.seg, kTileTokens, s_tile_start, S, mt, &p0, &p_end, &l)) continue;
     const int pw = p0 + wave * 16;
     if (pw >= p_end) continue;
     const int t_raw = (pw + m < p_end) ? a.seg.sorted_token[pw + m] : -1;
@@ -74,6 +74,16 @@ __global__ __launch_bounds__(kExpandThreads) void expand_sgmv_kernel(ExpandArgs 
 
     const float* vrow = a.v + (int64_t)t * a.ldv + (int64_t)q * a.v_slice_stride;
     const uint16_t* Bl = a.slices[q].B + (int64_t)l * nq * a.r;
+    const int c0 = n0 + g * 16;
+    const int ncols = nq - c0;
+    uint16_t* yrow = a.y + (int64_t)t * a.ldy + a.slices[q].col_off + c0;
+    // The y row is the largest and coldest input: start its load first.
+    const bool yvec = VEC && tok_ok && ncols >= 16;
+    u32x4 w[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+    if (yvec && a.add) {
+      w[0] = reinterpret_cast<const u32x4*>(yrow)[0];
+      w[1] = reinterpret_cast<const u32x4*>(yrow)[1];
+    }
 
     f32x4 acc[4];
 #pragma unroll
@@ -111,10 +121,7 @@ __global__ __launch_bounds__(kExpandThreads) void expand_sgmv_kernel(ExpandArgs 
     }
 
     // Lane (m, g) holds columns n0 + 16g + 4qq + e of token t.
-    const int c0 = n0 + g * 16;
-    const int ncols = nq - c0;
     if (!tok_ok || ncols <= 0) continue;
-    uint16_t* yrow = a.y + (int64_t)t * a.ldy + a.slices[q].col_off + c0;
     float out[16];
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
@@ -123,12 +130,9 @@ __global__ __launch_bounds__(kExpandThreads) void expand_sgmv_kernel(ExpandArgs 
       out[qq * 4 + 2] = acc[qq].z;
       out[qq * 4 + 3] = acc[qq].w;
     }
-    if (VEC && ncols >= 16) {
+    if (yvec) {
       u32x4* yp = reinterpret_cast<u32x4*>(yrow);
-      u32x4 w[2];
       if (a.add) {
-        w[0] = yp[0];
-        w[1] = yp[1];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const uint32_t d[4] = {w[hh].x, w[hh].y, w[hh].z, w[hh].w};

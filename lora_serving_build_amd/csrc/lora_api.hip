@@ -91,15 +91,6 @@ size_t lora_shrink_workspace_bytes(int32_t T, int32_t L, int32_t H, int32_t r) {
   return p.partial_bytes + p.counter_bytes;
 }
 
-int lora_workspace_clear(void* workspace, size_t bytes, void* stream) {
-  static const char* fn = "lora_workspace_clear";
-  if (bytes == 0) return ok();
-  if (!workspace) return fail(LORA_ERR_INVALID_ARG, "%s: workspace is NULL", fn);
-  if (!aligned16(workspace) || (bytes & 15u))
-    return fail(LORA_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned and sized", fn);
-  return hip_status(lora::launch_fill_zero(workspace, bytes, static_cast<hipStream_t>(stream)), fn);
-}
-
 int lora_shrink(const void* x, int64_t ldx, const void* A, int32_t H, int32_t r,
                 const lora_segments* seg, float* v, int64_t ldv, void* workspace,
                 size_t workspace_bytes, int dtype, void* stream) {

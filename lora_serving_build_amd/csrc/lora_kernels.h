@@ -12,8 +12,10 @@ constexpr int kMaxSlices = 8;
 constexpr int kMaxRank = 128;
 constexpr int kMaxLoras = 2048;
 
-// Token tile of the segment kernels: 4 waves x 16 tokens.
+// Token tile of the expand kernel: 4 waves x 16 tokens.
 constexpr int kTileTokens = 64;
+// Largest token tile of the shrink kernel (4 token groups of 16).
+constexpr int kMaxShrinkTile = 64;
 // Columns per expand work item (per wave: 16 tokens x 64 columns).
 constexpr int kExpandCols = 64;
 // H elements one shrink K-step covers (4 lane groups x 32 elements).
@@ -34,12 +36,15 @@ hipError_t launch_build_segments(const int32_t* token_lora, int32_t T, int32_t L
                                  int32_t* seg_start, int32_t* counts, hipStream_t s);
 
 struct ShrinkPlan {
-  int32_t ksplit;       // number of H chunks reduced across workgroups
+  int32_t mw, jg, kw;   // waves per workgroup: token groups x rank groups x H slices
+  int32_t jtw;          // 16-row tiles of r per wave (1 or 2)
+  int32_t rp;           // rank padded to the rank groups
+  int32_t ksplit;       // number of H chunks split across workgroups
   int32_t kchunk;       // H elements per chunk (multiple of kShrinkKStep)
   int32_t max_tiles;    // upper bound on token tiles
   int32_t grid;         // persistent workgroups
-  size_t partial_bytes; // split-K partial sums in the workspace
-  size_t counter_bytes; // per-tile arrival counters in the workspace
+  size_t partial_bytes; // workspace for per-chunk partial rows (ksplit > 1)
+  size_t counter_bytes; // unused (0)
 };
 
 ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r);
@@ -57,7 +62,5 @@ struct ExpandSliceDesc {
 hipError_t launch_expand(const SegView& seg, const float* v, int64_t ldv, int64_t v_slice_stride,
                          const ExpandSliceDesc* slices, int32_t num_slices, int32_t r,
                          uint16_t* y, int64_t ldy, int add, int dtype, bool vec, hipStream_t s);
-
-hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
 }  // namespace lora

@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for f in ("lora_build_segments", "lora_shrink", "lora_expand", "lora_expand_slice",
-              "lora_shrink_workspace_bytes", "lora_workspace_clear", "lora_last_error"):
+              "lora_shrink_workspace_bytes", "lora_last_error"):
         assert f in names
 
 
@@ -86,7 +86,7 @@ def test_shrink_validation():
 
 
 def test_workspace_size_is_zero_when_not_split():
-    # Large batches need no split of H, hence no workspace.
+    # Large batches need no split of H across workgroups, hence no workspace.
     assert lsb.lora_shrink_workspace_bytes(0, 4, 4096, 16) == 0
     assert lsb.lora_shrink_workspace_bytes(65536, 4, 4096, 16) == 0
     assert lsb.lora_shrink_workspace_bytes(256, 4, 4096, 16) > 0
@@ -127,14 +127,6 @@ def test_expand_reports_under_its_name():
     rc = lib.lora_expand(FAKE, 16, FAKE, 16, 0, ctypes.byref(s), FAKE, 64, 1, 0, None)
     assert rc == lsb.LORA_ERR_INVALID_ARG
     assert lsb.lora_last_error().startswith("lora_expand:")
-
-
-def test_workspace_clear_validation():
-    lib = lsb.lib()
-    assert lib.lora_workspace_clear(None, 0, None) == lsb.LORA_OK
-    _expect(lib.lora_workspace_clear(None, 16, None), lsb.LORA_ERR_INVALID_ARG, "NULL")
-    _expect(lib.lora_workspace_clear(ctypes.c_void_p(0x100008), 16, None), lsb.LORA_ERR_INVALID_ARG,
-            "aligned")
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

@@ -324,8 +324,12 @@ def _rank_pairs():
 
 @pytest.mark.parametrize("r_true,r_pad", _rank_pairs())
 def test_rank_padding(r_true, r_pad):
-    """Zero-padding the rank (punica issue's mitigation) gives the oracle's
-    true-rank result within tolerance, and the same bits as the unpadded run."""
+    """Zero-padding the rank (punica issue's mitigation): the padded run gives
+    the oracle's true-rank result within tolerance, its padded v columns are
+    exactly zero, and expand fed the same v gives the same bits for the true and
+    the padded rank (the extra products are exact zeros).  Shrink may split the
+    H-sum differently for different ranks, so chained results are compared
+    within tolerance only."""
     _announce(f"rank padding {r_true} -> {r_pad}")
     w = W.make("rp", "bf16", 300, 1024, r_true, 5, [[512]], seed=r_true, seq_len=(1, 20), neg_frac=0.1)
     Ap = np.zeros((w.L, r_pad, w.H), np.uint16)
@@ -336,22 +340,31 @@ def test_rank_padding(r_true, r_pad):
     ids = torch.from_numpy(w.ids).cuda()
     seg = lsb.lora_build_segments(ids, w.L)
     x = dev_bits(w.x, w.dtype)
-    outs = []
+    act = w.active
+    v_or = oracle.shrink(w.dtype, w.x, w.A, w.ids)
+    ref = oracle.expand(w.dtype, np.nan_to_num(v_or), B, w.ids, w.outputs[0].y0, 0, True)
+    vs = []
     for A_, B_, rr in ((w.A, B, r_true), (Ap, Bp, r_pad)):
         v = sentinel_v(w.T, rr)
         lsb.lora_shrink(x, dev_bits(A_, w.dtype), seg, v)
         y = dev_bits(w.outputs[0].y0, w.dtype)
         lsb.lora_expand(v, dev_bits(B_, w.dtype), seg, y, True)
         torch.cuda.synchronize()
-        outs.append((v.cpu().numpy(), host_bits(y)))
-    act = w.active
-    v_or = oracle.shrink(w.dtype, w.x, w.A, w.ids)
-    ref = oracle.expand(w.dtype, np.nan_to_num(v_or), B, w.ids, w.outputs[0].y0, 0, True)
-    for vg, yb in outs:
+        vg = v.cpu().numpy()
         assert tol_ratio(vg[act, :r_true].astype(np.float64), v_or[act]) <= 1
-        assert tol_ratio(decode(yb, w.dtype)[act], ref[act]) <= 1
-    assert np.all(outs[1][0][act, r_true:] == 0)
-    assert np.array_equal(outs[0][1], outs[1][1])
+        assert tol_ratio(decode(host_bits(y), w.dtype)[act], ref[act]) <= 1
+        vs.append(v)
+    assert np.all(vs[1].cpu().numpy()[act, r_true:] == 0)
+    # Same v into both expands: identical bits.
+    v_pad = torch.zeros(w.T, r_pad, device="cuda")
+    v_pad[:, :r_true] = vs[0]
+    ys = []
+    for vv, B_ in ((vs[0], B), (v_pad, Bp)):
+        y = dev_bits(w.outputs[0].y0, w.dtype)
+        lsb.lora_expand(vv, dev_bits(B_, w.dtype), seg, y, True)
+        ys.append(y)
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0].view(torch.int16), ys[1].view(torch.int16))
 
 
 def test_shrink_repeatable_and_workspace_reuse():
