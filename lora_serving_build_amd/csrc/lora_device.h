@@ -41,6 +41,35 @@ __device__ __forceinline__ uint32_t from_f32(float f) {
 // Packs two 16-bit patterns into one dword (lo = first element).
 __device__ __forceinline__ uint32_t pack2(uint32_t a, uint32_t b) { return a | (b << 16); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Rounds two floats to nearest even and packs them (a in the low half): one
+// v_cvt_pk_{bf16,f16}_f32 on gfx950.
+template <int DT>
+__device__ __forceinline__ uint32_t cvt_pack2(float a, float b) {
+  const f32x2 f = f32x2{a, b};
+  if constexpr (DT == 0) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+  }
+}
+
+// Widens the two 16-bit values of a packed dword.
+template <int DT>
+__device__ __forceinline__ void unpack2(uint32_t d, float* lo, float* hi) {
+  if constexpr (DT == 0) {
+    const f16x2 h = __builtin_bit_cast(f16x2, d);
+    *lo = (float)h.x;
+    *hi = (float)h.y;
+  } else {
+    *lo = __uint_as_float(d << 16);
+    *hi = __uint_as_float(d & 0xffff0000u);
+  }
+}
+
 // ---------------------------------------------------------------- matrix core
 // D(16x16, fp32) += A(16x32) * B(32x16) with 8 elements of A and B per lane.
 // Whatever the hardware's internal k numbering, slot (lane / 16, element e) of
@@ -61,10 +90,12 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 // ---------------------------------------------------------------- loads
 // Loads 8 consecutive 16-bit elements p[0..8) as 4 dwords.  Elements at or
 // beyond `limit` (counted from p) read as zero.  VEC: p is 16-byte aligned
-// whenever the whole chunk is in range.
+// and limit is a multiple of 8, so a chunk is either whole or absent.
 template <bool VEC>
 __device__ __forceinline__ u32x4 load8_16(const uint16_t* __restrict__ p, int limit) {
-  if (VEC && limit >= 8) return *reinterpret_cast<const u32x4*>(p);
+  if constexpr (VEC) {
+    return limit >= 8 ? *reinterpret_cast<const u32x4*>(p) : u32x4{0u, 0u, 0u, 0u};
+  }
   uint32_t e[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) e[i] = (i < limit) ? (uint32_t)p[i] : 0u;
@@ -76,10 +107,30 @@ __device__ __forceinline__ u32x4 load8_16(const uint16_t* __restrict__ p, int li
   return r;
 }
 
-// Loads 8 consecutive floats (elements beyond `limit` read as zero).
+// Branch-free load of the 8 16-bit elements row[off..off+8) for the vector
+// path: the address is clamped into [0, end - 8] so the load is always legal,
+// and the value is replaced by zeros when !ok or off >= end.  Keeping loads
+// out of divergent branches lets the compiler count outstanding loads instead
+// of draining them all before the matrix ops.  Needs end >= 8 and 16-byte
+// aligned chunks (end, off multiples of 8).
+__device__ __forceinline__ u32x4 load8_16_masked(const uint16_t* __restrict__ row, int off,
+                                                 int end, bool ok) {
+  const int safe = off < end ? off : end - 8;
+  const u32x4 v = *reinterpret_cast<const u32x4*>(row + safe);
+  const bool keep = ok && off < end;
+  return u32x4{keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u};
+}
+
+// Loads 8 consecutive floats (elements beyond `limit` read as zero).  VEC: p
+// is 16-byte aligned and limit is a multiple of 8.
 template <bool VEC>
 __device__ __forceinline__ void load8_f32(const float* __restrict__ p, int limit, float out[8]) {
-  if (VEC && limit >= 8) {
+  if constexpr (VEC) {
+    if (limit < 8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) out[i] = 0.0f;
+      return;
+    }
     f32x4 a = *reinterpret_cast<const f32x4*>(p);
     f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
     out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;

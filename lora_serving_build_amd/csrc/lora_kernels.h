@@ -16,8 +16,8 @@ constexpr int kMaxLoras = 2048;
 constexpr int kTileTokens = 64;
 // Largest token tile of the shrink kernel (4 token groups of 16).
 constexpr int kMaxShrinkTile = 64;
-// Columns per expand work item (per wave: 16 tokens x 64 columns).
-constexpr int kExpandCols = 64;
+// Columns per expand work item (per wave: 16 tokens x 128 columns).
+constexpr int kExpandCols = 128;
 // H elements one shrink K-step covers (4 lane groups x 32 elements).
 constexpr int kShrinkKStep = 128;
 

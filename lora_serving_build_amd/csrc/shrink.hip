@@ -1,19 +1,21 @@
 // Shrink on segments (SGMV form): v[t, j] = sum_h x[t, h] * A_l[h, j].
 //
-// One workgroup of 16 waves takes one token tile of one segment at a time
-// (persistent grid).  The 16 waves are arranged as
-//   mw token groups (16 tokens each) x jg rank groups x kw slices of H,
-// with mw * jg * kw = 16.  Per H step of 128 every lane loads 64 contiguous
-// bytes of its token's x row and of one A_l row (lane group g = lane / 16
-// covers elements 32g..32g+31) and 16x16x32 matrix-core ops accumulate the
-// transposed product D[j][token] in fp32.  The kw partial tiles of a token
-// group meet in LDS and are added in slice order, so the result does not
-// depend on timing; there is no device-scope fence or atomic on the path.
+// One workgroup of four waves owns a 64-token tile of one segment and a range
+// of H (the whole of H unless the batch has too few tiles to fill the GPU).
+// H is walked in blocks of 128: the block of x (64 rows x 256 B) and of A_l
+// (r rows x 256 B) is loaded cooperatively -- 16 lanes per row, so one load
+// instruction covers 4 rows x 256 contiguous bytes -- into registers one
+// block ahead, then written to a double-buffered LDS tile.  A_l is thus read
+// from L2 once per 64 tokens instead of once per 16, and the matrix cores take
+// their operands from LDS (row pitch padded to 272 B, which spreads the 16 rows
+// of an operand read over all banks).  Wave w multiplies tokens 16w..16w+15
+// against all of r with 16x16x32 ops, accumulating the transposed product
+// D[j][token] in fp32, so each lane ends with four consecutive j of one token.
 //
-// Batches with too few tiles to occupy the chip also split H across
-// workgroups (ks chunks).  Each chunk then writes its fp32 partial tile to the
-// workspace (indexed by sorted position) and a second small kernel adds the ks
-// partials in chunk order and writes v: the kernel boundary orders the two.
+// When H is split across workgroups (ks chunks), each chunk writes its fp32
+// partial rows to the workspace (indexed by sorted position) and a second
+// small kernel adds the ks partials in chunk order and writes v: the kernel
+// boundary orders the two, and the sum order is fixed.
 #include "lora_device.h"
 #include "lora_kernels.h"
 #include "tiles.h"
@@ -22,8 +24,11 @@ namespace lora {
 
 namespace {
 
-constexpr int kShrinkWaves = 16;
-constexpr int kShrinkThreads = kShrinkWaves * kWave;
+constexpr int kShrinkThreads = 256;
+constexpr int kSkTile = 64;              // tokens per tile (4 waves x 16)
+constexpr int kSkKB = kShrinkKStep;      // H elements per LDS block
+constexpr int kSkPitch = kSkKB + 8;      // 16-bit elements per LDS row
+constexpr int kSkChunks = kSkKB / 8;     // 16-byte chunks per row and block
 
 struct ShrinkArgs {
   SegView seg;
@@ -36,9 +41,8 @@ struct ShrinkArgs {
   int64_t ldv;
   float* partial;  // [ks][T][rp] when ks > 1
   int32_t ks;
-  int32_t kchunk;  // H elements per workgroup chunk (multiple of kShrinkKStep)
-  int32_t mw, jg, kw;
-  int32_t rp;      // padded rank of the partial rows (= jg * JTW * 16)
+  int32_t kchunk;  // H elements per workgroup chunk (multiple of kSkKB)
+  int32_t rp;      // padded rank of the partial rows (16 * NJT)
 };
 
 // Stores four consecutive j values of one row (j0 = first), clipped at r.
@@ -54,38 +58,41 @@ __device__ __forceinline__ void store4(float* p, int j0, int r, f32x4 val) {
   if (j0 + 3 < r) p[3] = val.w;
 }
 
-// JTW = 16-row tiles of r per wave (1 or 2).
-template <int DT, bool VEC, int JTW>
+// NJT = 16-row tiles of r (r <= 16 * NJT).  VEC: 16-byte aligned rows with H
+// and ldx multiples of 8 (otherwise element-wise loads).
+template <int DT, bool VEC, int NJT>
 __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkArgs a) {
+  constexpr int RP = 16 * NJT;
+  constexpr int XL = kSkTile * kSkChunks / kShrinkThreads;  // x chunks per thread per block (4)
+  constexpr int AL = RP * kSkChunks / kShrinkThreads;       // A chunks per thread per block (NJT)
+  __shared__ __align__(16) uint16_t s_x[2][kSkTile * kSkPitch];
+  __shared__ __align__(16) uint16_t s_a[2][RP * kSkPitch];
   __shared__ int32_t s_tile_start[kMaxLoras + 1];
-  __shared__ int32_t s_scan[kShrinkWaves + 1];
-  __shared__ int32_t s_tok[kMaxShrinkTile];
-  __shared__ f32x4 s_red[kShrinkWaves * 16 * JTW * 4];
+  __shared__ int32_t s_scan[kShrinkThreads / kWave + 1];
+  __shared__ int32_t s_tok[kSkTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int m = lane & 15;  // token column of D / row of A inside a 16-row tile
-  const int g = lane >> 4;  // lane group
-  const int kw = a.kw, jg = a.jg, mw = a.mw;
-  const int kg = wave % kw;
-  const int jgi = (wave / kw) % jg;
-  const int mg = wave / (kw * jg);
-  const int tile_tokens = 16 * mw;
-  constexpr int CH = JTW * 4;  // f32x4 chunks per (wave, token) row of s_red
+  const int g = lane >> 4;  // lane group: which 8 of the 32 elements of an op
+  // Cooperative load layout: chunk c = tid + 256 i, row c / 16, 16-byte column c % 16.
+  const int lrow = tid >> 4;
+  const int lcol = (tid & 15) * 8;
 
   int S;
-  const int tiles = build_tile_prefix<kShrinkThreads>(a.seg, tile_tokens, s_tile_start, s_scan, &S);
+  const int tiles = build_tile_prefix<kShrinkThreads>(a.seg, kSkTile, s_tile_start, s_scan, &S);
   const int n_items = tiles * a.ks;
   const int grid = gridDim.x;
 
   for (int item = xcd_logical_id(blockIdx.x, grid); item < n_items; item += grid) {
-    // Consecutive items share the chunk of H and walk the tiles of a segment.
+    // Consecutive items share the chunk of H and walk the tiles of a segment,
+    // so neighbouring workgroups of an XCD read the same A_l block.
     const int ksi = item / tiles;
     const int tile = item - ksi * tiles;
     int p0 = 0, p_end = 0, l = 0;
-    const bool ok = tile_range(a.seg, tile_tokens, s_tile_start, S, tile, &p0, &p_end, &l);
-    if (tid < tile_tokens) {
+    const bool ok = tile_range(a.seg, kSkTile, s_tile_start, S, tile, &p0, &p_end, &l);
+    if (tid < kSkTile) {
       int t = -1;
       if (ok && p0 + tid < p_end) {
         t = a.seg.sorted_token[p0 + tid];
@@ -94,70 +101,96 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkArgs a) {
       s_tok[tid] = t;
     }
     __syncthreads();
-
     const int kbeg = ksi * a.kchunk;
     const int kend = min(a.H, kbeg + a.kchunk);
-    int wspan = (kend - kbeg + kw - 1) / kw;
-    wspan = (wspan + kShrinkKStep - 1) / kShrinkKStep * kShrinkKStep;
-    const int k0 = kbeg + kg * wspan;
-    const int k1 = min(kend, k0 + wspan);
-    const int t = s_tok[mg * 16 + m];
-    const bool tok_ok = t >= 0;
-    const bool wave_live = ok && p0 + mg * 16 < p_end;
+    const int t_any = s_tok[0];
+    // Rows of this thread's loads.  A missing token reads some valid row: its
+    // output column is dropped.  Rows j >= r read row 0: output rows dropped.
+    const uint16_t* xsrc[XL];
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+      const int tt = s_tok[lrow + 16 * i];
+      xsrc[i] = a.x + (int64_t)(tt >= 0 ? tt : (t_any >= 0 ? t_any : 0)) * a.ldx;
+    }
+    const uint16_t* Al = a.A + (int64_t)l * a.r * a.H;
+    const uint16_t* asrc[AL];
+#pragma unroll
+    for (int i = 0; i < AL; ++i) {
+      const int j = lrow + 16 * i;
+      asrc[i] = Al + (int64_t)(j < a.r ? j : 0) * a.H;
+    }
 
-    f32x4 acc[JTW];
+    u32x4 rx[XL], ra[AL];
+    auto gload = [&](int kb) {
+      // Elements at or beyond kend read as zero (only the last block has any).
+      const int off = kb + lcol;
 #pragma unroll
-    for (int jj = 0; jj < JTW; ++jj) acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < XL; ++i) {
+        if constexpr (VEC)
+          rx[i] = load8_16_masked(xsrc[i], off, kend, ok);
+        else
+          rx[i] = ok ? load8_16<false>(xsrc[i] + off, kend - off) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int i = 0; i < AL; ++i) {
+        if constexpr (VEC)
+          ra[i] = load8_16_masked(asrc[i], off, kend, ok);
+        else
+          ra[i] = ok ? load8_16<false>(asrc[i] + off, kend - off) : u32x4{0u, 0u, 0u, 0u};
+      }
+    };
+    auto swrite = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < XL; ++i)
+        *reinterpret_cast<u32x4*>(&s_x[buf][(lrow + 16 * i) * kSkPitch + lcol]) = rx[i];
+#pragma unroll
+      for (int i = 0; i < AL; ++i)
+        *reinterpret_cast<u32x4*>(&s_a[buf][(lrow + 16 * i) * kSkPitch + lcol]) = ra[i];
+    };
 
-    if (wave_live) {
-      const uint16_t* xrow = a.x + (int64_t)(tok_ok ? t : 0) * a.ldx;
-      const uint16_t* Al = a.A + (int64_t)l * a.r * a.H;
-      for (int k = k0; k < k1; k += kShrinkKStep) {
-        const int kl = k + g * 32;
-        u32x4 xv[4];
+    f32x4 acc[NJT];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          xv[i] = tok_ok ? load8_16<VEC>(xrow + kl + i * 8, k1 - (kl + i * 8))
-                         : u32x4{0u, 0u, 0u, 0u};
+    for (int jt = 0; jt < NJT; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool wave_live = ok && p0 + wave * 16 < p_end;
+    const int nblk = kend > kbeg ? (kend - kbeg + kSkKB - 1) / kSkKB : 0;
+
+    if (nblk > 0) {
+      gload(kbeg);
+      swrite(0);
+    }
+    __syncthreads();
+    for (int b = 0; b < nblk; ++b) {
+      const int buf = b & 1;
+      if (b + 1 < nblk) gload(kbeg + (b + 1) * kSkKB);  // in flight during the ops below
+      if (wave_live) {
+        const uint16_t* xs = &s_x[buf][(wave * 16 + m) * kSkPitch + 8 * g];
+        const uint16_t* as = &s_a[buf][m * kSkPitch + 8 * g];
 #pragma unroll
-        for (int jj = 0; jj < JTW; ++jj) {
-          const int j = (jgi * JTW + jj) * 16 + m;
-          const uint16_t* arow = Al + (int64_t)j * a.H;
+        for (int kk = 0; kk < kSkKB; kk += 32) {
+          const u32x4 xop = *reinterpret_cast<const u32x4*>(xs + kk);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const u32x4 av = (j < a.r) ? load8_16<VEC>(arow + kl + i * 8, k1 - (kl + i * 8))
-                                       : u32x4{0u, 0u, 0u, 0u};
-            acc[jj] = mfma16x16x32<DT>(av, xv[i], acc[jj]);
+          for (int jt = 0; jt < NJT; ++jt) {
+            const u32x4 aop = *reinterpret_cast<const u32x4*>(as + jt * 16 * kSkPitch + kk);
+            acc[jt] = mfma16x16x32<DT>(aop, xop, acc[jt]);
           }
         }
       }
+      if (b + 1 < nblk) swrite(buf ^ 1);
+      __syncthreads();
     }
-    // Lane (m, g) holds D[j = 16 jj + 4 g + e][token m] of its rank group.
-#pragma unroll
-    for (int jj = 0; jj < JTW; ++jj) s_red[(wave * 16 + m) * CH + jj * 4 + g] = acc[jj];
-    __syncthreads();
 
-    // Add the kw slices of H in order and write v (or the chunk's partial).
-    const int chunks_per_tok = jg * CH;
-    const int n_out = tile_tokens * chunks_per_tok;
-    for (int o = tid; o < n_out; o += kShrinkThreads) {
-      const int tokl = o / chunks_per_tok;
-      const int c = o - tokl * chunks_per_tok;
-      const int jgo = c / CH;
-      const int cc = c - jgo * CH;
-      const int mgo = tokl >> 4;
-      const int mm = tokl & 15;
-      const int tt = s_tok[tokl];
-      if (tt < 0) continue;
-      f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int wbase = (mgo * jg + jgo) * kw;
-      for (int q = 0; q < kw; ++q) sum += s_red[((wbase + q) * 16 + mm) * CH + cc];
-      const int j0 = jgo * JTW * 16 + (cc >> 2) * 16 + (cc & 3) * 4;
-      if (a.ks == 1) {
-        store4<VEC>(a.v + (int64_t)tt * a.ldv + j0, j0, a.r, sum);
-      } else {
-        float* part = a.partial + ((int64_t)ksi * a.seg.T + (p0 + tokl)) * a.rp + j0;
-        *reinterpret_cast<f32x4*>(part) = sum;
+    // Lane (m, g) holds D[j = 16 jt + 4 g + e][token 16 wave + m].
+    const int tt = s_tok[wave * 16 + m];
+    if (wave_live && tt >= 0) {
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt) {
+        const int j0 = jt * 16 + 4 * g;
+        if (a.ks == 1) {
+          store4<VEC>(a.v + (int64_t)tt * a.ldv + j0, j0, a.r, acc[jt]);
+        } else {
+          float* part = a.partial + ((int64_t)ksi * a.seg.T + (p0 + wave * 16 + m)) * a.rp + j0;
+          *reinterpret_cast<f32x4*>(part) = acc[jt];
+        }
       }
     }
     __syncthreads();
@@ -188,11 +221,21 @@ __global__ __launch_bounds__(256) void shrink_reduce_kernel(SegView seg, const f
 }
 
 template <int DT, bool VEC>
-hipError_t launch_typed(const ShrinkArgs& args, int jtw, int grid, hipStream_t s) {
-  if (jtw == 1)
-    hipLaunchKernelGGL((shrink_kernel<DT, VEC, 1>), dim3(grid), dim3(kShrinkThreads), 0, s, args);
-  else
-    hipLaunchKernelGGL((shrink_kernel<DT, VEC, 2>), dim3(grid), dim3(kShrinkThreads), 0, s, args);
+hipError_t launch_typed(const ShrinkArgs& args, int njt, int grid, hipStream_t s) {
+  switch (njt) {
+    case 1:
+      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 1>), dim3(grid), dim3(kShrinkThreads), 0, s, args);
+      break;
+    case 2:
+      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 2>), dim3(grid), dim3(kShrinkThreads), 0, s, args);
+      break;
+    case 4:
+      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 4>), dim3(grid), dim3(kShrinkThreads), 0, s, args);
+      break;
+    default:
+      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 8>), dim3(grid), dim3(kShrinkThreads), 0, s, args);
+      break;
+  }
   return hipGetLastError();
 }
 
@@ -207,43 +250,31 @@ int env_int(const char* name, int dflt) {
 
 ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r) {
   ShrinkPlan p{};
-  const int njt = (r + 15) / 16;
-  p.jtw = njt == 1 ? 1 : 2;
-  const int need_jg = (njt + p.jtw - 1) / p.jtw;
-  p.jg = need_jg <= 1 ? 1 : need_jg <= 2 ? 2 : 4;
-  p.rp = p.jg * p.jtw * 16;
-  // Token groups per workgroup: larger tiles reuse A_l across more tokens;
-  // keep about one workgroup per CU or more.
-  int mw = 1;
-  while (mw * 2 * p.jg <= kShrinkWaves && mw * 2 <= kMaxShrinkTile / 16 &&
-         (int64_t)T >= (int64_t)4096 * mw * 2)
-    mw *= 2;
-  mw = env_int("LORA_SHRINK_MW", mw);
-  while (mw & (mw - 1)) mw &= mw - 1;  // powers of two only: mw * jg * kw must be 16
-  if (mw > kMaxShrinkTile / 16) mw = kMaxShrinkTile / 16;
-  if (mw * p.jg > kShrinkWaves) mw = kShrinkWaves / p.jg;
-  p.mw = mw;
-  p.kw = kShrinkWaves / (p.mw * p.jg);
-  const int64_t tt = 16 * (int64_t)p.mw;
-  const int64_t tiles = T > 0 ? (T + tt - 1) / tt + (L < T ? L : T) : 0;
+  const int njt0 = (r + 15) / 16;
+  p.jtw = njt0 <= 1 ? 1 : njt0 <= 2 ? 2 : njt0 <= 4 ? 4 : 8;  // rank tiles (template)
+  p.rp = 16 * p.jtw;
+  p.mw = kSkTile / 16;
+  p.jg = 1;
+  p.kw = 1;
+  const int64_t tiles = T > 0 ? (T + kSkTile - 1) / kSkTile + (L < T ? L : T) : 0;
   p.max_tiles = (int32_t)tiles;
-  // Split H across workgroups only when the tiles alone leave most CUs idle,
-  // and never below one H step per wave.
+  // Split H across workgroups when the tiles alone leave CUs idle; keep at
+  // least two LDS blocks per chunk.
   int64_t ks = 1;
-  if (tiles > 0 && tiles < 128) ks = (256 + tiles - 1) / tiles;
-  const int64_t ks_max = H / ((int64_t)p.kw * kShrinkKStep);
+  if (tiles > 0 && tiles < 384) ks = (512 + tiles - 1) / tiles;
+  const int64_t ks_max = (H + 2 * kSkKB - 1) / (2 * kSkKB);
   if (ks > ks_max) ks = ks_max;
   if (ks < 1) ks = 1;
   ks = env_int("LORA_SHRINK_KSPLIT", (int)ks);
   int64_t chunk = (H + ks - 1) / ks;
-  chunk = (chunk + kShrinkKStep - 1) / kShrinkKStep * kShrinkKStep;
+  chunk = (chunk + kSkKB - 1) / kSkKB * kSkKB;
   ks = (H + chunk - 1) / chunk;
   p.ksplit = (int32_t)ks;
   p.kchunk = (int32_t)chunk;
   p.partial_bytes = ks > 1 ? (size_t)(ks * (int64_t)T * p.rp * 4) : 0;
   p.counter_bytes = 0;
   int64_t items = tiles * ks;
-  int64_t grid = items < 512 ? items : 512;
+  int64_t grid = items < 1024 ? items : 1024;
   grid = (grid + 7) / 8 * 8;
   if (grid < 8) grid = 8;
   p.grid = (int32_t)grid;
@@ -265,9 +296,6 @@ hipError_t launch_shrink(const SegView& seg, const uint16_t* x, int64_t ldx, con
   a.partial = plan.ksplit > 1 ? reinterpret_cast<float*>(workspace) : nullptr;
   a.ks = plan.ksplit;
   a.kchunk = plan.kchunk;
-  a.mw = plan.mw;
-  a.jg = plan.jg;
-  a.kw = plan.kw;
   a.rp = plan.rp;
   hipError_t e;
   if (dtype == 0)
