@@ -5,7 +5,7 @@ kernels.  PyTorch provides device memory and the current stream.  The entry
 points carry the C-ABI names of ``include/lora.h``:
 
     lora_build_segments, lora_shrink, lora_expand, lora_expand_slice,
-    lora_shrink_workspace_bytes, lora_last_error
+    lora_shrink_workspace_bytes, lora_set_path, lora_last_error
 
 If the shared library has not been built (``python -m
 lora_serving_build_amd.build``), every entry point raises: there is no
@@ -21,7 +21,8 @@ import torch
 
 __all__ = [
     "LoraError", "Segments", "lib", "lora_build_segments", "lora_shrink", "lora_expand",
-    "lora_expand_slice", "lora_shrink_workspace_bytes", "lora_last_error", "LORA_F16", "LORA_BF16", "LORA_MAX_RANK", "LORA_MAX_LORAS",
+    "lora_expand_slice", "lora_shrink_workspace_bytes", "lora_last_error", "lora_set_path",
+    "PATH_AUTO", "PATH_BGMV", "PATH_SGMV", "LORA_F16", "LORA_BF16", "LORA_MAX_RANK", "LORA_MAX_LORAS",
     "LORA_MAX_SLICES", "library_path",
 ]
 
@@ -77,10 +78,24 @@ def lib() -> ctypes.CDLL:
             L.lora_expand_slice.argtypes = [p, i64, i64, p, p, p, i32, i32, seg_p, p, i64,
                                             ctypes.c_int, ctypes.c_int, p]
             L.lora_last_error.restype = ctypes.c_char_p
+            L.lora_set_path.argtypes = [ctypes.c_int]
+            L.lora_set_path.restype = ctypes.c_int
             for f in ("lora_build_segments", "lora_shrink", "lora_expand", "lora_expand_slice"):
                 getattr(L, f).restype = ctypes.c_int
             _lib = L
     return _lib
+
+
+PATH_AUTO, PATH_BGMV, PATH_SGMV = 0, 1, 2
+
+
+def lora_set_path(mode: int) -> int:
+    """Selects the kernel path (0 auto, 1 per-token BGMV, 2 segment SGMV);
+    returns the previous mode."""
+    rc = lib().lora_set_path(int(mode))
+    if rc < 0:
+        raise LoraError(rc, lora_last_error())
+    return rc
 
 
 def lora_last_error() -> str:

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "lora.h"
 #include "lora_kernels.h"
@@ -60,6 +61,31 @@ int check_rank(int32_t r, const char* fn) {
   return LORA_OK;
 }
 
+// Kernel path: 0 = automatic, 1 = per-token (BGMV), 2 = segment tiles (SGMV).
+std::atomic<int> g_path{0};
+
+// Automatic choice, from timings of both kernel families on decode batches
+// (H = 4096, 4 adapters, MI355X): the per-token shrink wins up to about 512
+// tokens at rank 16 -- each token gets a workgroup of its own, while tiles
+// would need the H-sum split across workgroups and a second launch -- but the
+// per-token expand only for the smallest batches, because there a 64-token
+// tile shares one staged weight block and the per-token kernel re-reads it.
+// Larger ranks favour the tiles for both ops.
+constexpr int32_t kBgmvShrinkMaxTokens = 512;
+constexpr int32_t kBgmvExpandMaxTokens = 32;
+constexpr int32_t kBgmvAutoMaxRank = 16;
+
+enum class Op { kShrink, kExpand };
+
+bool use_bgmv(Op op, int32_t T, int32_t r) {
+  const int mode = g_path.load(std::memory_order_relaxed);
+  if (r > lora::kBgmvMaxRank) return false;
+  if (mode == 1) return true;
+  if (mode == 2) return false;
+  if (r > kBgmvAutoMaxRank) return false;
+  return T <= (op == Op::kShrink ? kBgmvShrinkMaxTokens : kBgmvExpandMaxTokens);
+}
+
 lora::SegView view(const lora_segments* seg) {
   lora::SegView s;
   s.token_lora = seg->token_lora;
@@ -104,6 +130,16 @@ int lora_shrink(const void* x, int64_t ldx, const void* A, int32_t H, int32_t r,
   const int32_t T = seg->num_tokens;
   if (T == 0) return ok();
   if (!x || !A || !v) return fail(LORA_ERR_INVALID_ARG, "%s: x, A and v must not be NULL", fn);
+  if (g_path.load(std::memory_order_relaxed) == 1 && r > lora::kBgmvMaxRank)
+    return fail(LORA_ERR_UNSUPPORTED, "%s: the per-token path takes r <= %d", fn, lora::kBgmvMaxRank);
+  const bool vec = (H % 8 == 0) && (ldx % 8 == 0) && aligned16(x) && aligned16(A) &&
+                   (ldv % 4 == 0) && aligned16(v);
+  if (use_bgmv(Op::kShrink, T, r)) {
+    hipError_t err = lora::launch_bgmv_shrink(view(seg), static_cast<const uint16_t*>(x), ldx,
+                                              static_cast<const uint16_t*>(A), H, r, v, ldv, dtype,
+                                              vec, static_cast<hipStream_t>(stream));
+    return hip_status(err, fn);
+  }
   const lora::ShrinkPlan plan = lora::plan_shrink(T, seg->num_loras, H, r);
   const size_t need = plan.partial_bytes + plan.counter_bytes;
   if (need > 0) {
@@ -113,8 +149,6 @@ int lora_shrink(const void* x, int64_t ldx, const void* A, int32_t H, int32_t r,
     if (!aligned16(workspace))
       return fail(LORA_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned", fn);
   }
-  const bool vec = (H % 8 == 0) && (ldx % 8 == 0) && aligned16(x) && aligned16(A) &&
-                   (ldv % 4 == 0) && aligned16(v);
   hipError_t err = lora::launch_shrink(view(seg), static_cast<const uint16_t*>(x), ldx,
                                        static_cast<const uint16_t*>(A), H, r, v, ldv, workspace,
                                        plan, dtype, vec, static_cast<hipStream_t>(stream));
@@ -162,6 +196,14 @@ int lora_expand_slice(const float* v, int64_t ldv, int64_t v_slice_stride, const
   bool vec = (r % 8 == 0) && (ldv % 4 == 0) && (v_slice_stride % 4 == 0) && aligned16(v) &&
              (ldy % 8 == 0) && aligned16(y);
   for (int s = 0; s < num_slices; ++s) vec = vec && aligned16(B[s]) && (col_off[s] % 8 == 0);
+  if (g_path.load(std::memory_order_relaxed) == 1 && r > lora::kBgmvMaxRank)
+    return fail(LORA_ERR_UNSUPPORTED, "%s: the per-token path takes r <= %d", fn, lora::kBgmvMaxRank);
+  if (use_bgmv(Op::kExpand, T, r)) {
+    hipError_t err = lora::launch_bgmv_expand(view(seg), v, ldv, v_slice_stride, desc, num_slices, r,
+                                              static_cast<uint16_t*>(y), ldy, add_inputs ? 1 : 0,
+                                              dtype, vec, static_cast<hipStream_t>(stream));
+    return hip_status(err, fn);
+  }
   hipError_t err = lora::launch_expand(view(seg), v, ldv, v_slice_stride, desc, num_slices, r,
                                        static_cast<uint16_t*>(y), ldy, add_inputs ? 1 : 0, dtype,
                                        vec, static_cast<hipStream_t>(stream));
@@ -182,6 +224,12 @@ int lora_expand(const float* v, int64_t ldv, const void* B, int32_t r, int32_t n
     snprintf(g_error, sizeof g_error, "%s", tmp);
   }
   return rc;
+}
+
+int lora_set_path(int mode) {
+  if (mode < 0 || mode > 2)
+    return fail(LORA_ERR_INVALID_ARG, "lora_set_path: mode %d is not 0, 1 or 2", mode);
+  return g_path.exchange(mode);
 }
 
 const char* lora_last_error(void) { return g_error; }

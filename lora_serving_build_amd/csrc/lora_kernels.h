@@ -59,6 +59,17 @@ struct ExpandSliceDesc {
   int64_t col_off;
 };
 
+// Per-token (BGMV) kernels for decode-shaped batches; r <= kBgmvMaxRank.
+constexpr int kBgmvMaxRank = 64;
+
+hipError_t launch_bgmv_shrink(const SegView& seg, const uint16_t* x, int64_t ldx, const uint16_t* A,
+                              int32_t H, int32_t r, float* v, int64_t ldv, int dtype, bool vec,
+                              hipStream_t s);
+
+hipError_t launch_bgmv_expand(const SegView& seg, const float* v, int64_t ldv, int64_t v_slice_stride,
+                              const ExpandSliceDesc* slices, int32_t num_slices, int32_t r,
+                              uint16_t* y, int64_t ldy, int add, int dtype, bool vec, hipStream_t s);
+
 hipError_t launch_expand(const SegView& seg, const float* v, int64_t ldv, int64_t v_slice_stride,
                          const ExpandSliceDesc* slices, int32_t num_slices, int32_t r,
                          uint16_t* y, int64_t ldy, int add, int dtype, bool vec, hipStream_t s);

@@ -77,8 +77,12 @@ def test_shrink_validation():
     _expect(call(x=None), lsb.LORA_ERR_INVALID_ARG, "must not be NULL")
     need = lsb.lora_shrink_workspace_bytes(16, 4, 4096, 16)
     assert need > 0
-    _expect(call(H=4096, ldx=4096, wsb=need - 1), lsb.LORA_ERR_WORKSPACE, "workspace")
-    _expect(call(H=4096, ldx=4096, ws=None), lsb.LORA_ERR_WORKSPACE, "workspace")
+    prev = lib.lora_set_path(2)          # the segment path is the one that needs a workspace
+    try:
+        _expect(call(H=4096, ldx=4096, wsb=need - 1), lsb.LORA_ERR_WORKSPACE, "workspace")
+        _expect(call(H=4096, ldx=4096, ws=None), lsb.LORA_ERR_WORKSPACE, "workspace")
+    finally:
+        lib.lora_set_path(prev)
     _expect(call(seg=None), lsb.LORA_ERR_INVALID_ARG, "seg is NULL")
     # T = 0 is valid and launches nothing.
     s0 = _seg(T=0)
@@ -92,12 +96,12 @@ def test_workspace_size_is_zero_when_not_split():
     assert lsb.lora_shrink_workspace_bytes(256, 4, 4096, 16) > 0
 
 
-def _slice_call(lib, sp, Bs, ns, offs, ldy=64, r=16, stride=0, dt=0, nsl=None):
+def _slice_call(lib, sp, Bs, ns, offs, ldy=64, r=16, stride=0, dt=0, nsl=None, ldv=16):
     k = len(ns) if nsl is None else nsl
     B = (ctypes.c_void_p * max(len(Bs), 1))(*Bs)
     n = (ctypes.c_int32 * max(len(ns), 1))(*ns)
     o = (ctypes.c_int64 * max(len(offs), 1))(*offs)
-    return lib.lora_expand_slice(FAKE, 16, stride, B, n, o, k, r, sp, FAKE, ldy, 1, dt, None)
+    return lib.lora_expand_slice(FAKE, ldv, stride, B, n, o, k, r, sp, FAKE, ldy, 1, dt, None)
 
 
 def test_expand_slice_validation():
@@ -113,7 +117,7 @@ def test_expand_slice_validation():
     _expect(_slice_call(lib, sp, [F], [0], [0]), lsb.LORA_ERR_INVALID_ARG, "n_s[0]")
     _expect(_slice_call(lib, sp, [F], [8], [-8]), lsb.LORA_ERR_INVALID_ARG, "outside")
     _expect(_slice_call(lib, sp, [None], [8], [0]), lsb.LORA_ERR_INVALID_ARG, "B[0] is NULL")
-    _expect(_slice_call(lib, sp, [F], [8], [0], r=200), lsb.LORA_ERR_UNSUPPORTED, "rank")
+    _expect(_slice_call(lib, sp, [F], [8], [0], r=200, ldv=200), lsb.LORA_ERR_UNSUPPORTED, "rank")
     _expect(_slice_call(lib, sp, [F], [8], [0], stride=-1), lsb.LORA_ERR_INVALID_ARG, "v_slice_stride")
     _expect(_slice_call(lib, sp, [F], [8], [0], dt=5), lsb.LORA_ERR_INVALID_ARG, "dtype")
     # Slices given out of column order but disjoint are fine (T = 0: no launch).
@@ -134,3 +138,28 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(lsb, "library_path", str(tmp_path / "absent.so"))
     with pytest.raises(ImportError):
         lsb.lib()
+
+
+def test_set_path_validation():
+    lib = lsb.lib()
+    prev = lib.lora_set_path(0)
+    assert prev in (0, 1, 2)
+    _expect(lib.lora_set_path(3), lsb.LORA_ERR_INVALID_ARG, "mode 3")
+    _expect(lib.lora_set_path(-1), lsb.LORA_ERR_INVALID_ARG, "mode -1")
+    assert lib.lora_set_path(2) == 0
+    assert lib.lora_set_path(1) == 2
+    assert lib.lora_set_path(prev) == 1
+
+
+def test_forced_bgmv_rejects_large_rank_before_launch():
+    lib = lsb.lib()
+    s = _seg()
+    prev = lib.lora_set_path(1)
+    try:
+        rc = lib.lora_shrink(FAKE, 4096, FAKE, 4096, 128, ctypes.byref(s), FAKE, 128, FAKE, 1 << 30, 0,
+                             None)
+        _expect(rc, lsb.LORA_ERR_UNSUPPORTED, "per-token path")
+        rc = _slice_call(lib, ctypes.byref(s), [FAKE.value], [8], [0], r=128, ldy=64, ldv=128)
+        _expect(rc, lsb.LORA_ERR_UNSUPPORTED, "per-token path")
+    finally:
+        lib.lora_set_path(prev)

@@ -323,7 +323,7 @@ def _rank_pairs():
 
 
 @pytest.mark.parametrize("r_true,r_pad", _rank_pairs())
-def test_rank_padding(r_true, r_pad):
+def test_rank_padding(r_true, r_pad, force_path):
     """Zero-padding the rank (punica issue's mitigation): the padded run gives
     the oracle's true-rank result within tolerance, its padded v columns are
     exactly zero, and expand fed the same v gives the same bits for the true and
@@ -355,16 +355,19 @@ def test_rank_padding(r_true, r_pad):
         assert tol_ratio(decode(host_bits(y), w.dtype)[act], ref[act]) <= 1
         vs.append(v)
     assert np.all(vs[1].cpu().numpy()[act, r_true:] == 0)
-    # Same v into both expands: identical bits.
+    # Same v into both expands, on one kernel family at a time: identical bits.
     v_pad = torch.zeros(w.T, r_pad, device="cuda")
     v_pad[:, :r_true] = vs[0]
-    ys = []
-    for vv, B_ in ((vs[0], B), (v_pad, Bp)):
-        y = dev_bits(w.outputs[0].y0, w.dtype)
-        lsb.lora_expand(vv, dev_bits(B_, w.dtype), seg, y, True)
-        ys.append(y)
-    torch.cuda.synchronize()
-    assert torch.equal(ys[0].view(torch.int16), ys[1].view(torch.int16))
+    modes = [lsb.PATH_SGMV] + ([lsb.PATH_BGMV] if r_pad <= 64 else [])
+    for mode in modes:
+        force_path(mode)
+        ys = []
+        for vv, B_ in ((vs[0], B), (v_pad, Bp)):
+            y = dev_bits(w.outputs[0].y0, w.dtype)
+            lsb.lora_expand(vv, dev_bits(B_, w.dtype), seg, y, True)
+            ys.append(y)
+        torch.cuda.synchronize()
+        assert torch.equal(ys[0].view(torch.int16), ys[1].view(torch.int16)), f"path {mode}"
 
 
 def test_shrink_repeatable_and_workspace_reuse():
@@ -388,3 +391,90 @@ def test_shrink_repeatable_and_workspace_reuse():
         assert tol_ratio(v.cpu().numpy()[act].astype(np.float64), v_or[act]) <= 1
         assert np.all(res[-1][~act] == V_SENTINEL)
     assert np.array_equal(res[0], res[2])
+
+
+# ---------------------------------------------------------------- BGMV and SGMV paths
+@pytest.fixture
+def force_path():
+    def setter(mode):
+        lsb.lora_set_path(mode)
+    yield setter
+    lsb.lora_set_path(lsb.PATH_AUTO)
+
+
+PATH_CASES = [
+    # dtype, T, H, r, L, slices, seq_len, neg_frac
+    ("f16", 16, 1024, 16, 4, [[1024]], 1, 0.0),
+    ("f16", 256, 4096, 16, 4, [[4096]], 1, 0.0),
+    ("bf16", 300, 2048, 32, 7, [[512, 256, 256]], (1, 20), 0.1),
+    ("bf16", 130, 1536, 64, 3, [[1000]], (1, 9), 0.2),
+    ("f16", 77, 2049, 20, 3, [[300]], (1, 9), 0.2),      # scalar path
+    ("bf16", 1100, 1024, 8, 40, [[256, 64]], (1, 4), 0.05),
+]
+
+
+@pytest.mark.parametrize("mode", [lsb.PATH_BGMV, lsb.PATH_SGMV])
+@pytest.mark.parametrize("dtype,T,H,r,L,slices,sl,neg", PATH_CASES)
+def test_each_path_matches_oracle(force_path, mode, dtype, T, H, r, L, slices, sl, neg):
+    """Both kernel families, forced, against the oracle (BGMV semantics are a
+    strict subset of SGMV, so either must give the oracle's result)."""
+    _announce(f"path {mode} {dtype} T={T} H={H} r={r} L={L} slices={slices}")
+    force_path(mode)
+    w = W.make("path", dtype, T, H, r, L, slices, seed=T + 17 * r, seq_len=sl, neg_frac=neg)
+    dw = DeviceWorkload(w)
+    dw.run()
+    rv, ry, ryi = compare_with_oracle(dw)
+    print(f"  tolerance ratios: v {rv:.3g}  y {ry:.3g}  y(isolated) {ryi:.3g}")
+    assert rv <= 1 and ry <= 1 and ryi <= 1
+    check_neg_rows(dw)
+    check_outside_slices(dw)
+
+
+@pytest.mark.parametrize("mode", [lsb.PATH_BGMV, lsb.PATH_SGMV])
+@pytest.mark.parametrize("dtype,T,H,r,L,slices,sl", [
+    ("f16", 200, 256, 16, 4, [[256]], 1),
+    ("bf16", 333, 512, 24, 5, [[64, 48, 100]], (1, 40)),
+    ("bf16", 90, 2048, 64, 3, [[136]], (1, 5)),
+])
+def test_each_path_integer_exact(force_path, mode, dtype, T, H, r, L, slices, sl):
+    _announce(f"integer exact, path {mode} {dtype} T={T} H={H} r={r}")
+    force_path(mode)
+    w = W.make("int", dtype, T, H, r, L, slices, seed=T + H, seq_len=sl, neg_frac=0.15, integer=True)
+    dw = DeviceWorkload(w)
+    dw.run()
+    act = np.nonzero(w.active)[0]
+    v_or = oracle.shrink(w.dtype, w.x, w.A, w.ids)
+    assert np.array_equal(dw.v.cpu().numpy()[act].astype(np.float64), v_or[act])
+    for o, y in zip(w.outputs, dw.ys):
+        ref = oracle.expand_slice(w.dtype, np.nan_to_num(v_or), [s.B for s in o.slices],
+                                  [s.col_off for s in o.slices], w.ids, o.y0, w.add)
+        ref_bits = W.f32_to_bits(ref.astype(np.float32), dtype) if dtype == "bf16" else \
+            ref.astype(np.float16).view(np.uint16)
+        assert np.array_equal(host_bits(y)[:, _slice_cols(o)][act], ref_bits[act])
+    check_neg_rows(dw)
+
+
+def test_bgmv_and_sgmv_agree(force_path):
+    """The per-token and the segment kernels on the same batch agree with each
+    other within the tolerance (punica issue: BGMV is a subset of SGMV)."""
+    _announce("bgmv vs sgmv on one batch")
+    w = W.make("agree", "bf16", 400, 4096, 16, 4, [[4096, 1024]], seed=77, seq_len=(1, 8),
+               neg_frac=0.1)
+    outs = []
+    for mode in (lsb.PATH_BGMV, lsb.PATH_SGMV):
+        force_path(mode)
+        dw = DeviceWorkload(w)
+        dw.run()
+        outs.append((dw.v.cpu().numpy().astype(np.float64), decode(host_bits(dw.ys[0]), w.dtype)))
+    act = w.active
+    assert tol_ratio(outs[0][0][act], outs[1][0][act]) <= 1
+    assert tol_ratio(outs[0][1][act], outs[1][1][act]) <= 1
+
+
+def test_forced_bgmv_rejects_large_rank(force_path):
+    force_path(lsb.PATH_BGMV)
+    w = W.make("big", "bf16", 32, 256, 128, 2, [[64]], seed=3)
+    dw = DeviceWorkload(w)
+    with pytest.raises(lsb.LoraError) as e:
+        dw.run()
+    assert e.value.code == lsb.LORA_ERR_UNSUPPORTED
