@@ -157,7 +157,7 @@ def cpu_baseline(w, step_bytes):
     t0 = time.perf_counter()
     run()
     t1 = time.perf_counter() - t0
-    reps = max(1, min(1000, int(math.ceil(10.0 / max(t1, 1e-6)))))
+    reps = max(1, min(100000, int(math.ceil(10.0 / max(t1, 1e-6)))))
     if t1 > 30.0:
         reps = 1
     t0 = time.perf_counter()
@@ -175,6 +175,114 @@ def cpu_baseline(w, step_bytes):
     }
 
 
+OP_KERNELS = {  # kernel-name fragments of each op (rocprofv3 names)
+    "build": ("build_segments_kernel",),
+    "shrink": ("shrink_kernel", "shrink_reduce_kernel"),
+    "expand": ("expand_kernel",),
+}
+COPY_PROBE_BYTES = 256 << 20
+
+
+def op_of(kernel_name):
+    for op, frags in OP_KERNELS.items():
+        if any(f in kernel_name for f in frags):
+            return op
+    return None
+
+
+def summarize_profiles(args):
+    """Turns rocprofv3 CSV output of this script into the short summaries kept
+    under profiles/: a kernel-trace table, and per-op HBM traffic from the
+    FETCH_SIZE / WRITE_SIZE runs scaled by a copy of known size."""
+    import csv
+    import collections
+    import workloads as W
+    w = W.config(args.config)
+    name = w.name
+    out_dir = os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    lines = [f"# rocprofv3 kernel trace: {name}", "",
+             "command (from the repository root, on one MI355X):",
+             f"  rocprofv3 --kernel-trace --stats -d <dir> -o run --output-format csv -- "
+             f"python bench.py --config {args.config} --no-cpu-baseline",
+             "", "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    stats = list(csv.DictReader(open(args.trace)))
+    op_avg = {}
+    for r in stats:
+        kn = r["Name"]
+        op = op_of(kn)
+        if op is None and "copy" not in kn.lower():
+            continue
+        short = kn.replace("void ", "").replace("lora::(anonymous namespace)::", "").split("(")[0]
+        lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | "
+                     f"{float(r['MinNs'])/1e3:.2f} | {float(r['MaxNs'])/1e3:.2f} |")
+        if op:
+            op_avg.setdefault(op, []).append((kn, float(r["AverageNs"]) / 1e3, int(r["Calls"])))
+    lines += ["", "Per op (average launch duration; algorithmic bytes per call):"]
+    nbytes = {"shrink": w.shrink_bytes(), "expand": w.expand_bytes()}
+    calls_per_op = {"shrink": 1, "expand": len(w.outputs), "build": 1}
+    for op, rows in sorted(op_avg.items()):
+        tot_us = sum(a for _, a, _ in rows)
+        line = f"- {op}: {tot_us:.2f} us summed over its kernels' average launches"
+        if op in nbytes:
+            per_launch = nbytes[op] / calls_per_op[op]
+            avg_launch = sum(a * c for _, a, c in rows) / max(1, sum(c for _, _, c in rows))
+            line += (f"; {per_launch / 2**20:.3f} MiB per launch, average launch {avg_launch:.2f} us "
+                     f"-> {per_launch / (avg_launch * 1e-6) / 1e9:.1f} GB/s")
+        lines.append(line)
+    with open(os.path.join(out_dir, f"trace_{name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("wrote", os.path.join(out_dir, f"trace_{name}.md"))
+    if not (args.fetch and args.write):
+        return
+
+    def per_op(path, counter):
+        rows = list(csv.DictReader(open(path)))
+        tot = collections.defaultdict(float)
+        steps = 0
+        copy_vals = []
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            kn = r["Kernel_Name"]
+            val = float(r["Counter_Value"])  # KiB per dispatch
+            op = op_of(kn)
+            if op == "build":
+                steps += 1
+            if op:
+                tot[op] += val
+            elif "neg_kernel" in kn:
+                copy_vals.append(val)
+        return {k: v / max(1, steps) for k, v in tot.items()}, copy_vals, steps
+
+    fetch, fcopy, steps = per_op(args.fetch, "FETCH_SIZE")
+    write, wcopy, _ = per_op(args.write, "WRITE_SIZE")
+    if not fcopy or not wcopy:
+        raise SystemExit("no copy probe dispatch found: run the --pmc passes with --traffic-probe")
+    f_fetch = max(fcopy) * 1024 / COPY_PROBE_BYTES
+    f_write = max(wcopy) * 1024 / COPY_PROBE_BYTES
+    rec = {"workload": name, "steps_profiled": steps,
+           "copy_probe_bytes": COPY_PROBE_BYTES,
+           "fetch_scale": round(f_fetch, 4), "write_scale": round(f_write, 4),
+           "ops": {}}
+    for op in sorted(set(fetch) | set(write)):
+        b = fetch.get(op, 0.0) * 1024 / f_fetch + write.get(op, 0.0) * 1024 / f_write
+        alg = {"shrink": w.shrink_bytes(), "expand": w.expand_bytes()}.get(op)
+        rec["ops"][op] = {"bytes_per_call": int(b), "fetch_kib": round(fetch.get(op, 0.0), 1),
+                          "write_kib": round(write.get(op, 0.0), 1),
+                          "algorithmic_bytes": alg,
+                          "source_hash": source_hash(KERNEL_SOURCES[op])}
+    rec["commands"] = [
+        f"rocprofv3 --pmc FETCH_SIZE -d <dir> -o run --output-format csv -- python bench.py "
+        f"--config {args.config} --no-cpu-baseline --traffic-probe",
+        f"rocprofv3 --pmc WRITE_SIZE -d <dir> -o run --output-format csv -- python bench.py "
+        f"--config {args.config} --no-cpu-baseline --traffic-probe"]
+    path = os.path.join(out_dir, f"traffic_{name}.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print("wrote", path)
+
+
 def source_hash(paths):
     h = hashlib.sha256()
     for p in paths:
@@ -183,25 +291,25 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel_key, workload_name, src_hash):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if the
-    kernel source has not changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_key}_{workload_name}.json")
+def measured_traffic(op, workload_name, src_hash, launches):
+    """HBM bytes per launch of an op from the committed rocprofv3 counter
+    summary, if the op's kernel sources have not changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        rec = json.load(f)
-    if rec.get("source_hash") != src_hash:
+        rec = json.load(f).get("ops", {}).get(op)
+    if not rec or rec.get("source_hash") != src_hash:
         return None
-    return rec.get("bytes_per_launch")
+    return rec["bytes_per_call"] // launches
 
 
+_COMMON = ["lora_serving_build_amd/csrc/lora_device.h", "lora_serving_build_amd/csrc/tiles.h",
+           "lora_serving_build_amd/csrc/lora_kernels.h", "lora_serving_build_amd/csrc/lora_api.hip"]
 KERNEL_SOURCES = {
-    "build": ["lora_serving_build_amd/csrc/segments.hip"],
-    "shrink": ["lora_serving_build_amd/csrc/shrink.hip", "lora_serving_build_amd/csrc/tiles.h",
-               "lora_serving_build_amd/csrc/lora_device.h"],
-    "expand": ["lora_serving_build_amd/csrc/expand.hip", "lora_serving_build_amd/csrc/tiles.h",
-               "lora_serving_build_amd/csrc/lora_device.h"],
+    "build": ["lora_serving_build_amd/csrc/segments.hip"] + _COMMON,
+    "shrink": ["lora_serving_build_amd/csrc/shrink.hip", "lora_serving_build_amd/csrc/bgmv.hip"] + _COMMON,
+    "expand": ["lora_serving_build_amd/csrc/expand.hip", "lora_serving_build_amd/csrc/bgmv.hip"] + _COMMON,
 }
 
 
@@ -214,7 +322,17 @@ def main():
     ap.add_argument("--pool-gib", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="also run one plain copy of 256 MiB (calibrates FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--summarize-profiles", action="store_true",
+                    help="write profiles/ summaries from rocprofv3 CSVs (--trace, --fetch, --write)")
+    ap.add_argument("--trace")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the multi-LoRA path here has no multi-GPU mode "
@@ -275,9 +393,18 @@ def main():
                      "GB_s": round(nbytes / (t * 1e-3) / 1e9, 1),
                      "TFLOP_s": round(flops / (t * 1e-3) / 1e12, 2)}
         log(f"{name}: {t * 1e3:.2f} us/op, {ops[name]['GB_s']} GB/s, {ops[name]['TFLOP_s']} TFLOP/s")
+    if args.traffic_probe:
+        # A plain streaming kernel of known size (reads and writes 256 MiB
+        # once each): the yardstick for the FETCH_SIZE / WRITE_SIZE counters.
+        src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     dom = max(("shrink", "expand"), key=lambda k: ops[k]["us_per_op"])
     src_hash = source_hash(KERNEL_SOURCES[dom])
-    traffic = measured_traffic(dom, w.name, src_hash)
+    traffic = measured_traffic(dom, w.name, src_hash, ops[dom]["launches"])
     achieved = ops[dom]["bytes"] / (ops[dom]["us_per_op"] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
