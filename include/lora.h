@@ -155,11 +155,11 @@ int lora_expand_slice(const float *v, int64_t ldv, int64_t v_slice_stride,
 
 /* Kernel path (punica issue: BGMV, one adapter per input, is a strict subset
  * of SGMV, segments of inputs sharing an adapter; both compute the same
- * result).  0 = automatic: with r <= 16, shrink of at most 512 tokens and
- * expand of at most 32 tokens take the per-token (BGMV) kernels, everything
- * else the segment-tile (SGMV) kernels; 1 = always per-token (r <= 64, else
- * LORA_ERR_UNSUPPORTED); 2 = always segment tiles.  Process-wide, meant for tests and measurement.  Returns the
- * previous mode, or LORA_ERR_INVALID_ARG for an unknown mode. */
+ * result).  0 = automatic: with r <= 16, shrink and expand of at most 512
+ * tokens take the per-token (BGMV) kernels, everything else the segment-tile
+ * (SGMV) kernels; 1 = always per-token (r <= 64, else LORA_ERR_UNSUPPORTED);
+ * 2 = always segment tiles.  Process-wide, meant for tests and measurement.
+ * Returns the previous mode, or LORA_ERR_INVALID_ARG for an unknown mode. */
 int lora_set_path(int mode);
 
 /* Message describing the last non-OK status returned on this thread. */

@@ -2,24 +2,23 @@
 //
 // The punica issue describes BGMV as each input using its own model, with the
 // speed-up coming from spreading many small products over many compute units.
-// Here one workgroup takes one token at a time, in token order, and streams
-// that token's adapter rows with lane-contiguous 16-byte loads: every load
-// instruction of a wave covers 1 KB of one row.  These kernels read only
-// token_lora: for a small batch, the sorted metadata would add dependent
-// round trips before the first weight load, and every adapter of the batch
-// fits in L2 anyway.  Rows that do not depend on the adapter (x, y, v) are
-// loaded before the adapter id arrives.  The whole H-sum of a token stays
-// inside its workgroup, so no partial sums leave it.
+// Here one workgroup takes one token at a time, in token order.  These kernels
+// read only token_lora: for a small batch, the sorted metadata would add
+// dependent round trips before the first weight load, and every adapter of the
+// batch fits in L2 anyway.  Rows that do not depend on the adapter (x, y, v)
+// are loaded before the adapter id is needed.  The whole H-sum of a token
+// stays inside its workgroup, so no partial sums leave it.
 //
-// shrink: lane i of the workgroup owns elements 8 (i + 256 k) .. +8 of H;
-//   v_dot2 (two 16-bit products into fp32) accumulates x . A_l[j] for each j,
-//   then a wave butterfly and an LDS step across the four waves add them up.
-// expand: the token's v row is split once into hi + lo 16-bit parts (held in
-//   scalar registers, as it is the same for the whole workgroup); lane i owns
-//   8 consecutive output columns, whose B_l^T rows are 8 r contiguous elements,
-//   and adds v_dot2(hi) + v_dot2(lo) per pair of ranks (the element-wise path
-//   for unaligned shapes does the same arithmetic); y is read and written 16
-//   bytes per lane and rounded once.
+// shrink: lane i of the workgroup owns elements 8 (i + 256 k) .. +8 of H (each
+//   wave instruction reads 1 KB of one row); v_dot2 (two 16-bit products into
+//   fp32) accumulates x . A_l[j] for each j; a transposing wave reduction and
+//   an LDS step across the four waves add them up.
+// expand: the token's v is split into hi + lo 16-bit parts; each output
+//   column is the balanced pairwise sum of per-8-rank group dot products (see
+//   group_dot), rounded once when added to y.  The aligned kernel for
+//   r = 8, 16, 32, 64 reads the weight block front to back, 1 KB per wave
+//   instruction; the general kernel covers every other shape with the same
+//   arithmetic.
 #include "lora_device.h"
 #include "lora_kernels.h"
 
@@ -63,16 +62,14 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   }
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
-
 // Adapter of token t as a uniform value; -1 when the token has none (ids
 // outside [0, L) count as none).  t is the same for the whole workgroup.
+// token_lora is read-only for the whole launch, so the load goes through the
+// constant address space: a scalar load, counted apart from the vector loads
+// in flight, so waiting for the id does not wait for them.
 __device__ __forceinline__ int token_adapter(const SegView& seg, int t) {
-  const int l = __builtin_amdgcn_readfirstlane(seg.token_lora[t]);
+  typedef const __attribute__((address_space(4))) int32_t* const_ptr;
+  const int l = __builtin_amdgcn_readfirstlane(*(const_ptr)(uintptr_t)(seg.token_lora + t));
   return (l >= 0 && l < seg.L) ? l : -1;
 }
 
@@ -135,11 +132,11 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_shrink_kernel(BgShrinkArgs a)
       }
     }
     if (l < 0) continue;  // uniform: no adapter, v row left as it is
-#pragma unroll
-    for (int j = 0; j < RT; ++j) {
-      const float s = wave_sum(acc[j]);
-      if (lane == 0) s_red[wave][j] = s;
-    }
+    // Transposing wave reduction: lane i ends with the wave's total of rank
+    // i >> (6 - log2 RT); one lane of each group writes it.
+    wave_transpose_sum<RT>(acc);
+    constexpr int kShift = 6 - log2_of<RT>();
+    if ((lane & ((1 << kShift) - 1)) == 0) s_red[wave][lane >> kShift] = acc[0];
     __syncthreads();
     if (tid < a.r && tid < RT) {
       float s = 0.f;
@@ -151,8 +148,37 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_shrink_kernel(BgShrinkArgs a)
   }
 }
 
+// Splits two fp32 values into a packed high 16-bit pair and the packed 16-bit
+// rounding of the remainders (the remainder of a non-finite value is 0).
+template <int DT>
+__device__ __forceinline__ void split_hilo(float f0, float f1, uint32_t* hi, uint32_t* lo) {
+  *hi = cvt_pack2<DT>(f0, f1);
+  float h0, h1;
+  unpack2<DT>(*hi, &h0, &h1);
+  *lo = cvt_pack2<DT>(__builtin_isfinite(h0) ? f0 - h0 : 0.f, __builtin_isfinite(h1) ? f1 - h1 : 0.f);
+}
+
+// Products of one group of 8 ranks with one column's 8 weights: rank pairs in
+// order, each pair's high part then its low part.  Both expand kernels build
+// a column from these group sums and add the groups in a balanced pairwise
+// tree, so a rank zero-padded to more groups gives the same bits.
+template <int DT>
+__device__ __forceinline__ float group_dot(const uint32_t* vh, const uint32_t* vl, u32x4 b) {
+  float s = 0.f;
+  s = dot2<DT>(vh[0], b.x, s);
+  s = dot2<DT>(vl[0], b.x, s);
+  s = dot2<DT>(vh[1], b.y, s);
+  s = dot2<DT>(vl[1], b.y, s);
+  s = dot2<DT>(vh[2], b.z, s);
+  s = dot2<DT>(vl[2], b.z, s);
+  s = dot2<DT>(vh[3], b.w, s);
+  s = dot2<DT>(vl[3], b.w, s);
+  return s;
+}
+
 // Output columns c0..c0+7 of one slice for one token: returns them in out[].
-template <int DT, bool VEC, int RT>
+// NG = rank groups of 8 (r <= 8 NG, a power of two).
+template <int DT, bool VEC, int NG>
 __device__ __forceinline__ void bg_expand_cols(const uint16_t* Bl, int nq, int r, int c0,
                                                const uint32_t* vhi, const uint32_t* vlo,
                                                float out[8]) {
@@ -160,29 +186,28 @@ __device__ __forceinline__ void bg_expand_cols(const uint16_t* Bl, int nq, int r
   for (int e = 0; e < 8; ++e) {
     const int c = c0 + e < nq ? c0 + e : nq - 1;  // past the slice: dropped by the caller
     const uint16_t* brow = Bl + (int64_t)c * r;
-    // Same pairwise arithmetic on both paths (ranks >= r are zeros), so
-    // zero-padding the rank does not change a single bit.
-    float s = 0.f;
-    if constexpr (VEC) {
+    float p[NG];
 #pragma unroll
-      for (int kk = 0; kk < RT; kk += 8) {
-        const u32x4 bv = load8_16<true>(brow + kk, r - kk);
-        const uint32_t b4[4] = {bv.x, bv.y, bv.z, bv.w};
+    for (int g = 0; g < NG; ++g) {
+      u32x4 b;
+      if constexpr (VEC) {
+        b = load8_16<true>(brow + 8 * g, r - 8 * g);  // r % 8 == 0: whole group or zeros
+      } else {
+        uint32_t d[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          s = dot2<DT>(vhi[kk / 2 + i], b4[i], s);
-          s = dot2<DT>(vlo[kk / 2 + i], b4[i], s);
+          const int k = 8 * g + 2 * i;
+          d[i] = pack2(k < r ? (uint32_t)brow[k] : 0u, k + 1 < r ? (uint32_t)brow[k + 1] : 0u);
         }
+        b = u32x4{d[0], d[1], d[2], d[3]};
       }
-    } else {
-      // Element-wise loads; the same pairs in the same order.
-      for (int kk = 0; kk < r; kk += 2) {
-        const uint32_t b = pack2(brow[kk], kk + 1 < r ? (uint32_t)brow[kk + 1] : 0u);
-        s = dot2<DT>(vhi[kk / 2], b, s);
-        s = dot2<DT>(vlo[kk / 2], b, s);
-      }
+      p[g] = group_dot<DT>(vhi + 4 * g, vlo + 4 * g, b);
     }
-    out[e] = s;
+#pragma unroll
+    for (int m = 1; m < NG; m *= 2)
+#pragma unroll
+      for (int g = 0; g < NG; g += 2 * m) p[g] = p[g] + p[g + m];
+    out[e] = p[0];
   }
 }
 
@@ -216,7 +241,8 @@ __device__ __forceinline__ void bg_store_cols(uint16_t* yrow, int nq, int c0, in
   }
 }
 
-// RT = ranks handled (r <= RT, RT a multiple of 8).
+// General per-token expand: any r <= RT, any alignment.  Lane i owns 8
+// consecutive output columns and reads their weight rows itself.
 template <int DT, bool VEC, int RT>
 __global__ __launch_bounds__(kBgThreads) void bgmv_expand_kernel(BgExpandArgs a) {
   constexpr int BLK = kBgThreads * 8;
@@ -234,15 +260,9 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_expand_kernel(BgExpandArgs a)
       // hi / lo 16-bit pairs of v (ranks >= r are zero).
       uint32_t vhi[RT / 2], vlo[RT / 2];
 #pragma unroll
-      for (int k = 0; k < RT / 2; ++k) {
-        const float f0 = 2 * k < a.r ? vrow[2 * k] : 0.f;
-        const float f1 = 2 * k + 1 < a.r ? vrow[2 * k + 1] : 0.f;
-        vhi[k] = cvt_pack2<DT>(f0, f1);
-        float h0, h1;
-        unpack2<DT>(vhi[k], &h0, &h1);
-        vlo[k] = cvt_pack2<DT>(__builtin_isfinite(h0) ? f0 - h0 : 0.f,
-                               __builtin_isfinite(h1) ? f1 - h1 : 0.f);
-      }
+      for (int k = 0; k < RT / 2; ++k)
+        split_hilo<DT>(2 * k < a.r ? vrow[2 * k] : 0.f, 2 * k + 1 < a.r ? vrow[2 * k + 1] : 0.f,
+                       &vhi[k], &vlo[k]);
       // Up to two column blocks per trip; their y loads are issued first.
       for (int c0 = tid * 8; c0 < nq; c0 += UNR * BLK) {
         u32x4 yv[UNR];
@@ -255,10 +275,119 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_expand_kernel(BgExpandArgs a)
         float out[UNR][8];
 #pragma unroll
         for (int u = 0; u < UNR; ++u)
-          if (c0 + u * BLK < nq) bg_expand_cols<DT, VEC, RT>(Bl, nq, a.r, c0 + u * BLK, vhi, vlo, out[u]);
+          if (c0 + u * BLK < nq)
+            bg_expand_cols<DT, VEC, RT / 8>(Bl, nq, a.r, c0 + u * BLK, vhi, vlo, out[u]);
 #pragma unroll
         for (int u = 0; u < UNR; ++u)
           if (c0 + u * BLK < nq) bg_store_cols<DT, VEC>(yrow, nq, c0 + u * BLK, a.add, yv[u], out[u]);
+      }
+    }
+  }
+}
+
+// Per-token expand for r = 8 G (G = 1, 2, 4, 8) on aligned data.  A token's
+// weight block B_l is read front to back: load k of lane i takes 16-byte chunk
+// 64 k + i of the current stretch, so each wave instruction reads 1 KB of
+// consecutive memory.  Chunk c holds ranks 8 (c % G) .. +8 of column c / G;
+// the G lanes of a column add their group sums over DPP (the same balanced
+// tree as the general kernel), one of them parks the column total in a
+// wave-private LDS row, and the wave then reads the row back 8 columns per
+// lane for 16-byte y updates.  A wave handles RPI rounds of 512 columns at
+// once; y rows and v are loaded before the adapter id is needed.
+constexpr int kRoundCols = kWave * 8;
+
+template <int DT, int G>
+__global__ __launch_bounds__(kBgThreads) void bgmv_expand_fast_kernel(BgExpandArgs a) {
+  constexpr int LG = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
+  constexpr int RPI = G <= 2 ? 2 : 1;        // rounds of 512 columns per trip
+  constexpr int K = 8 * G;                   // weight loads per lane and round
+  constexpr int KB = K < 16 ? K : 16;        // loads per batch (register bound)
+  constexpr int CPI = kWave / G;             // columns per load instruction
+  constexpr int NW = kBgThreads / kWave;
+  __shared__ __align__(16) float s_out[NW][RPI * kRoundCols];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int part = lane & (G - 1);
+  float* so = s_out[wave];
+
+  for (int t = blockIdx.x; t < a.seg.T; t += gridDim.x) {
+    for (int q = 0; q < a.num_slices; ++q) {
+      const int nq = a.slices[q].n;
+      const float* vrow = a.v + (int64_t)t * a.ldv + (int64_t)q * a.v_slice_stride + part * 8;
+      uint16_t* yrow = a.y + (int64_t)t * a.ldy + a.slices[q].col_off;
+      for (int R0 = wave * RPI; R0 * kRoundCols < nq; R0 += NW * RPI) {
+        // y and v do not depend on the adapter: they are in flight while the
+        // (scalar) adapter id arrives, and only the id is waited for before
+        // the weight loads go out.
+        const int l = token_adapter(a.seg, t);
+        u32x4 yv[RPI];
+#pragma unroll
+        for (int u = 0; u < RPI; ++u) {
+          const int c0 = (R0 + u) * kRoundCols + lane * 8;
+          yv[u] = (a.add && c0 + 8 <= nq) ? *reinterpret_cast<const u32x4*>(yrow + c0)
+                                          : u32x4{0u, 0u, 0u, 0u};
+        }
+        f32x4 va = *reinterpret_cast<const f32x4*>(vrow);
+        f32x4 vb = *reinterpret_cast<const f32x4*>(vrow + 4);
+        if (l < 0) break;  // uniform: the row of y stays as it is
+        const uint16_t* Bl = a.slices[q].B + (int64_t)l * nq * (8 * G);
+        const int64_t nchunks = (int64_t)nq * G;
+        u32x4 b[RPI][KB];
+#pragma unroll
+        for (int u = 0; u < RPI; ++u) {
+          const int64_t base = (int64_t)(R0 + u) * kRoundCols * G + lane;
+#pragma unroll
+          for (int k = 0; k < KB; ++k) {
+            // Chunks past the slice read chunk 0; their columns are never stored.
+            const int64_t idx = base + (int64_t)k * kWave;
+            b[u][k] = *reinterpret_cast<const u32x4*>(Bl + (idx < nchunks ? idx : 0) * 8);
+          }
+        }
+        // All first-batch weight loads are in flight before any arithmetic;
+        // the opaque moves keep the split of v from being hoisted above them.
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" : "+v"(va), "+v"(vb));
+        uint32_t vh[4], vl[4];
+        split_hilo<DT>(va.x, va.y, &vh[0], &vl[0]);
+        split_hilo<DT>(va.z, va.w, &vh[1], &vl[1]);
+        split_hilo<DT>(vb.x, vb.y, &vh[2], &vl[2]);
+        split_hilo<DT>(vb.z, vb.w, &vh[3], &vl[3]);
+#pragma unroll
+        for (int u = 0; u < RPI; ++u) {
+          const int64_t base = (int64_t)(R0 + u) * kRoundCols * G + lane;
+#pragma unroll
+          for (int kb = 0; kb < K; kb += KB) {
+            if (kb > 0) {
+#pragma unroll
+              for (int k = 0; k < KB; ++k) {
+                const int64_t idx = base + (int64_t)(kb + k) * kWave;
+                b[u][k] = *reinterpret_cast<const u32x4*>(Bl + (idx < nchunks ? idx : 0) * 8);
+              }
+            }
+#pragma unroll
+            for (int k = 0; k < KB; ++k) {
+              float p = group_dot<DT>(vh, vl, b[u][k]);
+              if constexpr (G >= 2) p = p + lane_xor<0>(p, lane);
+              if constexpr (G >= 4) p = p + lane_xor<1>(p, lane);
+              if constexpr (G >= 8) p = p + lane_xor<2>(p, lane);
+              if (part == 0) so[u * kRoundCols + (kb + k) * CPI + (lane >> LG)] = p;
+            }
+          }
+        }
+        // LDS operations of one wave execute in order: wave-scope fences
+        // only keep the compiler from moving them.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int u = 0; u < RPI; ++u) {
+          const int c0 = (R0 + u) * kRoundCols + lane * 8;
+          const f32x4 o0 = *reinterpret_cast<const f32x4*>(so + u * kRoundCols + lane * 8);
+          const f32x4 o1 = *reinterpret_cast<const f32x4*>(so + u * kRoundCols + lane * 8 + 4);
+          float out[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+          if (c0 < nq) bg_store_cols<DT, true>(yrow, nq, c0, a.add, yv[u], out);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
     }
   }
@@ -307,6 +436,18 @@ hipError_t launch_bgmv_expand(const SegView& seg, const float* v, int64_t ldv, i
   a.ldy = ldy;
   a.add = add;
   const int grid = bg_grid(seg.T);
+  if (vec && (r == 8 || r == 16 || r == 32 || r == 64)) {
+#define LORA_BG_FAST(DT_)                                                                            \
+  switch (r) {                                                                                       \
+    case 8: hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 1>), dim3(grid), dim3(kBgThreads), 0, s, a); break; \
+    case 16: hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 2>), dim3(grid), dim3(kBgThreads), 0, s, a); break; \
+    case 32: hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 4>), dim3(grid), dim3(kBgThreads), 0, s, a); break; \
+    default: hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 8>), dim3(grid), dim3(kBgThreads), 0, s, a); break; \
+  }
+    if (dtype == 0) { LORA_BG_FAST(0) } else { LORA_BG_FAST(1) }
+#undef LORA_BG_FAST
+    return hipGetLastError();
+  }
 #define LORA_BG_EXPAND(DT_, VEC_)                                                                     \
   if (r <= 16)                                                                                       \
     hipLaunchKernelGGL((bgmv_expand_kernel<DT_, VEC_, 16>), dim3(grid), dim3(kBgThreads), 0, s, a);  \

@@ -72,7 +72,7 @@ std::atomic<int> g_path{0};
 // tile shares one staged weight block and the per-token kernel re-reads it.
 // Larger ranks favour the tiles for both ops.
 constexpr int32_t kBgmvShrinkMaxTokens = 512;
-constexpr int32_t kBgmvExpandMaxTokens = 32;
+constexpr int32_t kBgmvExpandMaxTokens = 512;
 constexpr int32_t kBgmvAutoMaxRank = 16;
 
 enum class Op { kShrink, kExpand };

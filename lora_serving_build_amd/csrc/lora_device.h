@@ -177,6 +177,78 @@ __device__ __forceinline__ int block_exclusive_sum(int x, int* scratch, int* tot
   return excl;
 }
 
+// ---------------------------------------------------------------- wave reductions
+// Value of lane (lane ^ (1 << B)) for B <= 3, i.e. inside one row of 16 lanes,
+// through DPP: quad permutations for bits 0 and 1, two row shifts for bit 2,
+// a row rotation by 8 for bit 3.
+template <int B>
+__device__ __forceinline__ float lane_xor(float v, int lane) {
+  static_assert(B >= 0 && B <= 3, "DPP exchange stays inside a row");
+  const int i = __float_as_int(v);
+  if constexpr (B == 0) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, i, 0xB1, 0xF, 0xF, true));  // [1,0,3,2]
+  } else if constexpr (B == 1) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, i, 0x4E, 0xF, 0xF, true));  // [2,3,0,1]
+  } else if constexpr (B == 2) {
+    const int up = __builtin_amdgcn_update_dpp(0, i, 0x104, 0xF, 0xF, true);    // from lane + 4
+    const int down = __builtin_amdgcn_update_dpp(0, i, 0x114, 0xF, 0xF, true);  // from lane - 4
+    return __int_as_float((lane & 4) ? down : up);
+  } else {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, i, 0x128, 0xF, 0xF, true));  // rotate 8
+  }
+}
+
+// One step of a transposing reduction over lane bit B: lanes with bit B clear
+// keep (a + a of the partner lane), lanes with it set keep (b + b of the
+// partner).  Bits 5 and 4 use the gfx950 lane-swap instructions, which move
+// half of each operand across 32- or 16-lane boundaries in one VALU op.
+template <int B>
+__device__ __forceinline__ float pair_step(float a, float b, int lane) {
+  if constexpr (B == 5 || B == 4) {
+    const auto s = B == 5 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false)
+                          : __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+  } else {
+    const bool hi = (lane >> B) & 1;
+    const float keep = hi ? b : a;
+    const float send = hi ? a : b;
+    return keep + lane_xor<B>(send, lane);
+  }
+}
+
+template <int B, int M>
+__device__ __forceinline__ void transpose_step(float* x, int lane) {
+  if constexpr (M >= 2) {
+#pragma unroll
+    for (int i = 0; i < M / 2; ++i) x[i] = pair_step<B>(x[i], x[i + M / 2], lane);
+  } else {
+    static_assert(B <= 3, "at least four values per lane");
+    x[0] = x[0] + lane_xor<B>(x[0], lane);
+  }
+}
+
+// Sums each of the N per-lane values x[0..N) over the 64 lanes of a wave
+// (N a power of two, 4 <= N <= 64), in about N + 6 cross-lane operations
+// instead of 6 N.  Afterwards x[0] of lane l holds the wave total of value
+// (l >> (6 - log2 N)) & (N - 1); the lanes that share those bits hold the same
+// total.  The order of the additions is fixed, so the result is reproducible.
+template <int N>
+__device__ __forceinline__ void wave_transpose_sum(float (&x)[N]) {
+  static_assert(N >= 4 && N <= 64 && (N & (N - 1)) == 0, "N: power of two in [4, 64]");
+  const int lane = threadIdx.x & (kWave - 1);
+  transpose_step<5, N>(x, lane);
+  transpose_step<4, N / 2>(x, lane);
+  transpose_step<3, (N / 4 > 1 ? N / 4 : 1)>(x, lane);
+  transpose_step<2, (N / 8 > 1 ? N / 8 : 1)>(x, lane);
+  transpose_step<1, (N / 16 > 1 ? N / 16 : 1)>(x, lane);
+  transpose_step<0, (N / 32 > 1 ? N / 32 : 1)>(x, lane);
+}
+
+template <int N>
+constexpr int log2_of() {
+  return N <= 1 ? 0 : 1 + log2_of<N / 2>();
+}
+
 // XCD-aware renumbering: workgroups are dealt round-robin to the 8 XCDs, so
 // for a grid that is a multiple of 8 this maps consecutive logical ids onto
 // one XCD (and its L2).
