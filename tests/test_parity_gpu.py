@@ -62,7 +62,8 @@ def compare_with_oracle(dw: DeviceWorkload, rows=None, isolated=True):
 META_CASES = [(0, 1, "uniform"), (1, 1, "uniform"), (1, 4, "neg"), (7, 3, "uniform"),
               (64, 4, "uniform"), (257, 4, "neg"), (1000, 64, "bad"), (513, 1, "uniform"),
               (300, 16, "allneg"), (129, 5, "one"), (2048, 200, "bad"), (5000, 2048, "neg"),
-              (20000, 7, "uniform"), (3000, 3, "sorted")]
+              (20000, 7, "uniform"), (3000, 3, "sorted"), (8192, 64, "bad"), (8193, 64, "bad"),
+              (40000, 300, "bad"), (9000, 1500, "bad")]
 
 
 @pytest.mark.parametrize("T,L,kind", META_CASES)
