@@ -9,12 +9,18 @@
 // same 16 weights, so one 16x16x32 op adds B^T (hi + lo) and v keeps about 16
 // significant bits.  Per chunk, the weight block (128 rows of B_l^T, one
 // contiguous 128 x r run in memory) is loaded by the whole workgroup with
-// linear 16-byte loads one chunk ahead and staged in LDS, so all waves share
-// one copy.  The product is computed transposed, D[c][token], and goes through
-// a per-wave fp32 tile in LDS so that the read-modify-write of y -- the bulk
-// of the traffic -- uses 16 lanes per row and 256 contiguous bytes per row and
-// instruction.  The next chunk's y is loaded during the current chunk; y is
-// rounded once, to nearest even.
+// linear 16-byte loads one chunk ahead and staged in LDS (two buffers up to
+// r = 64, so one barrier per chunk), so all waves share one copy.
+//
+// The product is computed transposed, D[c][token]: lane (m, g) of op tile q
+// holds columns 16 q + 4 g .. +4 of token m.  One lane-row swap between the
+// op tiles 2p and 2p + 1 leaves every lane with 8 consecutive columns of its
+// token (row g: columns 32 p + {0, 16, 8, 24}[g] .. +8), so y is read and
+// written straight from registers, 16 bytes per lane (16 rows x 64 bytes per
+// instruction) -- the bulk of the traffic, with no staging tile.  The next
+// chunk's y is loaded during the current chunk; y is rounded once, to nearest
+// even.  LDS stays small enough for four workgroups per CU, which keeps about
+// 64 KB of y in flight per CU.
 #include "lora_device.h"
 #include "lora_kernels.h"
 #include "tiles.h"
@@ -40,34 +46,48 @@ struct ExpandArgs {
   int32_t add;
 };
 
-constexpr int kEpiPitch = kExpandCols + 4;  // floats per row of a wave's staging tile
+template <int NKS>
+struct ExpandLds {
+  static constexpr int RK = 16 * NKS;            // padded rank
+  static constexpr int BP = RK + 8;              // 16-bit elements per LDS weight row
+  static constexpr int NB = NKS <= 4 ? 2 : 1;    // weight buffers
+  static constexpr size_t weight_bytes = (size_t)NB * kExpandCols * BP * 2;
+  // weights, then the tile table (3 (L + 1) ints) and scan scratch
+  static size_t bytes(int L) { return weight_bytes + 4 * (3 * ((size_t)L + 1) + 8); }
+};
 
-// NKS = 16-wide steps of r (r <= 16 * NKS).  VEC: 16-byte aligned rows, r and
+// Column offset (inside a 32-column pair of op tiles) of the 8 columns a lane
+// of lane group g holds after the swap.
+__device__ __forceinline__ int pair_col(int g) { return 8 * (((g & 1) << 1) | (g >> 1)); }
+
+// NKS = 16-wide steps of r (r <= 16 * NKS).  TB = 16-token blocks per wave
+// (tile = 64 TB tokens; two blocks share every weight operand read from LDS
+// and halve the weight traffic per token).  VEC: 16-byte aligned rows, r and
 // the slice offsets multiples of 8, ldy a multiple of 8.
-template <int DT, bool VEC, int NKS>
-__global__ __launch_bounds__(kExpandThreads) void expand_kernel(ExpandArgs a) {
-  constexpr int RK = 16 * NKS;                   // padded rank
-  constexpr int BP = RK + 8;                     // 16-bit elements per LDS weight row
-  constexpr int PPR = RK / 8;                    // 16-byte pieces per weight row
-  constexpr int BL = kExpandCols * PPR / kExpandThreads;  // pieces per thread per chunk
-  constexpr int NQ = kExpandCols / 16;           // 16-column op tiles per chunk
-  __shared__ __align__(16) uint16_t s_b[kExpandCols * BP];
-  __shared__ __align__(16) float s_epi[kExpandThreads / kWave][16 * kEpiPitch];
-  __shared__ int32_t s_tile_start[kMaxLoras + 1];
-  __shared__ int32_t s_scan[kExpandThreads / kWave + 1];
-  __shared__ int32_t s_tok[kTileTokens];
+template <int DT, bool VEC, int NKS, int TB>
+__global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <= 2 ? 4 : 3)) void expand_kernel(ExpandArgs a) {
+  using Lds = ExpandLds<NKS>;
+  constexpr int BP = Lds::BP;
+  constexpr int NB = Lds::NB;
+  constexpr int TT = kTileTokens * TB;                       // tokens per tile
+  constexpr int PPR = Lds::RK / 8;                           // 16-byte pieces per weight row
+  constexpr int BL = kExpandCols * PPR / kExpandThreads;     // pieces per thread per chunk
+  constexpr int NQ = kExpandCols / 16;                       // 16-column op tiles per chunk
+  constexpr int NP = NQ / 2;                                 // op tile pairs
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* s_b = reinterpret_cast<uint16_t*>(smem);
+  int32_t* s_table = reinterpret_cast<int32_t*>(smem + Lds::weight_bytes);
+  int32_t* s_scan = s_table + 3 * (a.seg.L + 1);
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int m = lane & 15;  // token of the ops / weight row inside a 16-row tile
   const int g = lane >> 4;  // lane group
-  const int er = lane >> 4;        // epilogue: rows er + 4 i of the wave's 16 tokens
-  const int ec = (lane & 15) * 8;  // epilogue: 8 consecutive columns
-  float* epi = s_epi[wave];
+  const int pc = pair_col(g);
 
-  int S;
-  const int mtiles = build_tile_prefix<kExpandThreads>(a.seg, kTileTokens, s_tile_start, s_scan, &S);
+  const TileTable table = build_tile_table<kExpandThreads>(a.seg, TT, s_table, s_scan);
+  const int mtiles = table.tiles;
   const int nruns = a.run_start[a.num_slices];
   const int n_items = mtiles * nruns;
   const int grid = gridDim.x;
@@ -84,50 +104,9 @@ __global__ __launch_bounds__(kExpandThreads) void expand_kernel(ExpandArgs a) {
     const int c_end = min(c_beg + a.cpr, (nq + kExpandCols - 1) / kExpandCols);
 
     int p0 = 0, p_end = 0, l = 0;
-    const bool ok = tile_range(a.seg, kTileTokens, s_tile_start, S, mt, &p0, &p_end, &l);
-    if (tid < kTileTokens) {
-      int t = -1;
-      if (ok && p0 + tid < p_end) {
-        t = a.seg.sorted_token[p0 + tid];
-        if (t < 0 || t >= a.seg.T) t = -1;
-      }
-      s_tok[tid] = t;
-    }
-    __syncthreads();
-    const bool wave_live = ok && p0 + wave * 16 < p_end;
+    const bool ok = tile_range_lds(table, a.seg.T, a.seg.L, TT, mt, &p0, &p_end, &l);
     const uint16_t* Bl = a.slices[q].B + (int64_t)l * nq * a.r;
     uint16_t* ybase = a.y + a.slices[q].col_off;
-
-    // v of this wave's 16 tokens as hi / lo operands, once per item.
-    u32x4 bop[NKS];
-    {
-      const int t = s_tok[wave * 16 + m];
-      const bool tok_ok = wave_live && t >= 0;
-      const float* vrow = a.v + (int64_t)(tok_ok ? t : 0) * a.ldv + (int64_t)q * a.v_slice_stride;
-#pragma unroll
-      for (int st = 0; st < NKS; ++st) {
-        const int rk = st * 16 + (g & 1) * 8;
-        float vv[8];
-        if (tok_ok) {
-          load8_f32<VEC>(vrow + rk, a.r - rk, vv);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) vv[e] = 0.f;
-        }
-        uint32_t w4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t hi = cvt_pack2<DT>(vv[2 * e], vv[2 * e + 1]);
-          float h0, h1;
-          unpack2<DT>(hi, &h0, &h1);
-          const float l0 = __builtin_isfinite(h0) ? vv[2 * e] - h0 : 0.f;
-          const float l1 = __builtin_isfinite(h1) ? vv[2 * e + 1] - h1 : 0.f;
-          const uint32_t lo = cvt_pack2<DT>(l0, l1);
-          w4[e] = g < 2 ? hi : lo;
-        }
-        bop[st] = u32x4{w4[0], w4[1], w4[2], w4[3]};
-      }
-    }
 
     // Weight chunk loader: piece p = tid + 256 i is row p / PPR, columns
     // 8 (p % PPR) .. +8 of the chunk's B_l^T rows.  Rows past the slice read
@@ -141,116 +120,214 @@ __global__ __launch_bounds__(kExpandThreads) void expand_kernel(ExpandArgs a) {
         const int col = (p - row * PPR) * 8;
         int n = c * kExpandCols + row;
         n = n < nq ? n : nq - 1;
-        if constexpr (VEC)
-          rb[i] = load8_16<true>(Bl + (int64_t)n * a.r + col, a.r - col);
-        else
+        if constexpr (VEC) {
+          // r % 8 == 0: a piece is whole or past r.  The load is unconditional
+          // (clamped into the row) so the compiler can count loads in flight
+          // exactly; pieces past r are zeroed only when r < RK, in a uniform
+          // branch.
+          const int cs = col < a.r ? col : a.r - 8;
+          rb[i] = *reinterpret_cast<const u32x4*>(Bl + (int64_t)n * a.r + cs);
+        } else {
           rb[i] = load8_16<false>(Bl + (int64_t)n * a.r + col, a.r - col);
+        }
       }
     };
-    auto swrite_b = [&]() {
+    // Pieces past r (vector path) are zeroed here, when the chunk is written
+    // to LDS, not next to their loads: a select next to a load would make the
+    // wave wait for it at once.
+    auto swrite_b = [&](int buf) {
 #pragma unroll
       for (int i = 0; i < BL; ++i) {
         const int p = tid + kExpandThreads * i;
         const int row = p / PPR;
         const int col = (p - row * PPR) * 8;
-        *reinterpret_cast<u32x4*>(&s_b[row * BP + col]) = rb[i];
+        u32x4 w = rb[i];
+        if (VEC && col >= a.r) w = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(&s_b[(buf * kExpandCols + row) * BP + col]) = w;
       }
     };
-    // y rows of this lane for chunk c (vector path only; zeros otherwise).
-    auto gload_y = [&](int c, u32x4* yv) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        yv[i] = u32x4{0u, 0u, 0u, 0u};
-        if constexpr (VEC) {
-          const int tt = s_tok[wave * 16 + er + 4 * i];
-          const int col = c * kExpandCols + ec;
-          if (a.add && wave_live && tt >= 0 && nq - col >= 8)
-            yv[i] = *reinterpret_cast<const u32x4*>(ybase + (int64_t)tt * a.ldy + col);
-        }
-      }
-    };
+    // The first chunk's weights depend only on the adapter: issue them before
+    // the token list arrives.
+    if (ok && c_beg < c_end) gload_b(c_beg);
 
-    u32x4 ycur[4], ynext[4];
-    if (c_beg < c_end) {
-      gload_b(c_beg);
-      swrite_b();
-      gload_y(c_beg, ycur);
+    // Wave w takes tokens [16 TB w, 16 TB (w + 1)) of the tile, block b the
+    // 16 tokens from 16 (TB w + b); every lane reads its own token id.
+    bool blk_live[TB], tok_ok[TB];
+    int tok[TB];
+    uint16_t* yrow[TB];
+#pragma unroll
+    for (int b = 0; b < TB; ++b) {
+      const int pos = p0 + 16 * (TB * wave + b) + m;
+      blk_live[b] = ok && p0 + 16 * (TB * wave + b) < p_end;
+      int t = (ok && pos < p_end) ? a.seg.sorted_token[pos] : -1;
+      t = (t >= 0 && t < a.seg.T) ? t : -1;
+      tok[b] = t;
+      tok_ok[b] = blk_live[b] && t >= 0;
+      yrow[b] = ybase + (int64_t)(tok_ok[b] ? t : 0) * a.ldy;
     }
-    __syncthreads();
-    for (int c = c_beg; c < c_end; ++c) {
-      const bool has_next = c + 1 < c_end;
-      if (has_next) {
-        gload_b(c + 1);
-        gload_y(c + 1, ynext);
-      }
-      if (wave_live) {
-        f32x4 acc[NQ];
+    const bool wave_live = blk_live[0];
+
+    // y of this lane for chunk c: pair p covers columns 32 p + pc .. +8.  The
+    // vector path loads unconditionally (rows of inactive lanes point at row
+    // 0 and columns are clamped into the slice, n % 8 == 0), so the compiler
+    // counts the loads in flight exactly; values that no store uses are
+    // simply ignored.
+    auto gload_y = [&](int c, u32x4 (*yv)[NP]) {
 #pragma unroll
-        for (int qq = 0; qq < NQ; ++qq) acc[qq] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int b = 0; b < TB; ++b) {
 #pragma unroll
-        for (int st = 0; st < NKS; ++st) {
-#pragma unroll
-          for (int qq = 0; qq < NQ; ++qq) {
-            const u32x4 aop = *reinterpret_cast<const u32x4*>(
-                &s_b[(qq * 16 + m) * BP + st * 16 + (g & 1) * 8]);
-            acc[qq] = mfma16x16x32<DT>(aop, bop[st], acc[qq]);
+        for (int p = 0; p < NP; ++p) {
+          yv[b][p] = u32x4{0u, 0u, 0u, 0u};
+          if constexpr (VEC) {
+            const int col = c * kExpandCols + 32 * p + pc;
+            const int cs = col + 8 <= nq ? col : nq - 8;
+            yv[b][p] = *reinterpret_cast<const u32x4*>(yrow[b] + cs);
           }
         }
-        // Lane (m, g) holds columns 16 qq + 4 g + e of token row m.
+      }
+    };
+    // v of each block's 16 tokens as hi / lo operands, once per item.  All
+    // loads go out before any is used (addresses clamped into the row, ranks
+    // >= r replaced by zeros afterwards).
+    u32x4 bop[TB][NKS];
+    {
+      f32x4 vraw[TB][NKS][2];
 #pragma unroll
-        for (int qq = 0; qq < NQ; ++qq)
-          *reinterpret_cast<f32x4*>(epi + m * kEpiPitch + qq * 16 + 4 * g) = acc[qq];
-        // Only this wave reads its staging tile; LDS operations of one wave
-        // execute in order, so a wavefront-scope fence is enough.
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int col = c * kExpandCols + ec;
-        const int cvalid = nq - col;
-        if (cvalid > 0) {
+      for (int b = 0; b < TB; ++b) {
+        const float* vrow = a.v + (int64_t)(tok_ok[b] ? tok[b] : 0) * a.ldv + (int64_t)q * a.v_slice_stride;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = er + 4 * i;
-            const int tt = s_tok[wave * 16 + row];
-            if (tt < 0) continue;
-            const f32x4 o0 = *reinterpret_cast<const f32x4*>(epi + row * kEpiPitch + ec);
-            const f32x4 o1 = *reinterpret_cast<const f32x4*>(epi + row * kEpiPitch + ec + 4);
-            float out[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
-            uint16_t* yp = ybase + (int64_t)tt * a.ldy + col;
-            if (VEC && cvalid >= 8) {
-              if (a.add) {
-                const uint32_t d[4] = {ycur[i].x, ycur[i].y, ycur[i].z, ycur[i].w};
+        for (int st = 0; st < NKS; ++st) {
+          const int rk = st * 16 + (g & 1) * 8;
+          if constexpr (VEC) {
+            const int rs = rk + 8 <= a.r ? rk : 0;
+            vraw[b][st][0] = *reinterpret_cast<const f32x4*>(vrow + rs);
+            vraw[b][st][1] = *reinterpret_cast<const f32x4*>(vrow + rs + 4);
+          } else {
+            float vv[8];
+            load8_f32<false>(vrow + rk, a.r - rk, vv);
+            vraw[b][st][0] = f32x4{vv[0], vv[1], vv[2], vv[3]};
+            vraw[b][st][1] = f32x4{vv[4], vv[5], vv[6], vv[7]};
+          }
+        }
+      }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  float y0, y1;
-                  unpack2<DT>(d[e], &y0, &y1);
-                  out[2 * e] += y0;
-                  out[2 * e + 1] += y1;
-                }
+      for (int b = 0; b < TB; ++b) {
+#pragma unroll
+        for (int st = 0; st < NKS; ++st) {
+          const int rk = st * 16 + (g & 1) * 8;
+          const bool keep = tok_ok[b] && (VEC ? rk + 8 <= a.r : true);
+          const float vv[8] = {vraw[b][st][0].x, vraw[b][st][0].y, vraw[b][st][0].z, vraw[b][st][0].w,
+                               vraw[b][st][1].x, vraw[b][st][1].y, vraw[b][st][1].z, vraw[b][st][1].w};
+          uint32_t w4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float f0 = keep ? vv[2 * e] : 0.f, f1 = keep ? vv[2 * e + 1] : 0.f;
+            const uint32_t hi = cvt_pack2<DT>(f0, f1);
+            float h0, h1;
+            unpack2<DT>(hi, &h0, &h1);
+            const float l0 = __builtin_isfinite(h0) ? f0 - h0 : 0.f;
+            const float l1 = __builtin_isfinite(h1) ? f1 - h1 : 0.f;
+            const uint32_t lo = cvt_pack2<DT>(l0, l1);
+            w4[e] = g < 2 ? hi : lo;
+          }
+          bop[b][st] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+        }
+      }
+    }
+
+    if (ok && c_beg < c_end) swrite_b(0);
+    __syncthreads();
+    // One chunk: the next chunk's weights and this chunk's y go out first,
+    // the products run from LDS while they are in flight, then one wait and
+    // the y update.  The latency of y is covered by the other workgroups on
+    // the CU (up to four), not by a longer prefetch: a longer prefetch would
+    // not survive the compiler's conservative load counting across the loop.
+    auto chunk = [&](int c) {
+      const int buf = NB == 2 ? ((c - c_beg) & 1) : 0;
+      const bool has_next = c + 1 < c_end;
+      if (has_next) gload_b(c + 1);
+      u32x4 ycur[TB][NP];
+      gload_y(c, ycur);
+      // Nothing below may be scheduled between these loads.
+      __builtin_amdgcn_sched_barrier(0);
+      if (wave_live) {
+        const uint16_t* sb = s_b + buf * kExpandCols * BP;
+        // Two halves of 64 columns keep fewer accumulators live at a time.
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          f32x4 acc[TB][NQ / 2];
+#pragma unroll
+          for (int b = 0; b < TB; ++b)
+#pragma unroll
+            for (int qq = 0; qq < NQ / 2; ++qq) acc[b][qq] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int st = 0; st < NKS; ++st) {
+#pragma unroll
+            for (int qq = 0; qq < NQ / 2; ++qq) {
+              const int row = (h * (NQ / 2) + qq) * 16 + m;
+              const u32x4 aop = *reinterpret_cast<const u32x4*>(&sb[row * BP + st * 16 + (g & 1) * 8]);
+#pragma unroll
+              for (int b = 0; b < TB; ++b) acc[b][qq] = mfma16x16x32<DT>(aop, bop[b][st], acc[b][qq]);
+            }
+          }
+#pragma unroll
+          for (int b = 0; b < TB; ++b) {
+            if (!tok_ok[b]) continue;
+#pragma unroll
+            for (int pp = 0; pp < NP / 2; ++pp) {
+              const int p = h * (NP / 2) + pp;
+              float out[8];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[b][2 * pp][e]),
+                                                                 __float_as_uint(acc[b][2 * pp + 1][e]), false, false);
+                out[e] = __uint_as_float(sw[0]);
+                out[4 + e] = __uint_as_float(sw[1]);
               }
-              *reinterpret_cast<u32x4*>(yp) =
-                  u32x4{cvt_pack2<DT>(out[0], out[1]), cvt_pack2<DT>(out[2], out[3]),
-                        cvt_pack2<DT>(out[4], out[5]), cvt_pack2<DT>(out[6], out[7])};
-            } else {
+              const int col = c * kExpandCols + 32 * p + pc;
+              const int cvalid = nq - col;
+              if (cvalid <= 0) continue;
+              uint16_t* yp = yrow[b] + col;
+              if constexpr (VEC) {  // n % 8 == 0: the lane's 8 columns are all in the slice
+                if (a.add) {
+                  const uint32_t d[4] = {ycur[b][p].x, ycur[b][p].y, ycur[b][p].z, ycur[b][p].w};
 #pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                if (e < cvalid) {
-                  float o = out[e];
-                  if (a.add) o += to_f32<DT>(yp[e]);
-                  yp[e] = (uint16_t)(cvt_pack2<DT>(o, 0.f) & 0xffffu);
+                  for (int e = 0; e < 4; ++e) {
+                    float y0, y1;
+                    unpack2<DT>(d[e], &y0, &y1);
+                    out[2 * e] += y0;
+                    out[2 * e + 1] += y1;
+                  }
+                }
+                *reinterpret_cast<u32x4*>(yp) =
+                    u32x4{cvt_pack2<DT>(out[0], out[1]), cvt_pack2<DT>(out[2], out[3]),
+                          cvt_pack2<DT>(out[4], out[5]), cvt_pack2<DT>(out[6], out[7])};
+              } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                  if (e < cvalid) {
+                    float o = out[e];
+                    if (a.add) o += to_f32<DT>(yp[e]);
+                    yp[e] = (uint16_t)(cvt_pack2<DT>(o, 0.f) & 0xffffu);
+                  }
                 }
               }
             }
           }
         }
       }
-      __syncthreads();  // every wave is done with this chunk's weights
-      if (has_next) {
-        swrite_b();
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ycur[i] = ynext[i];
+      if constexpr (NB == 2) {
+        // The other buffer was last read in the previous chunk, which every
+        // wave finished before the barrier that ended it.
+        if (has_next) swrite_b(buf ^ 1);
+        __syncthreads();
+      } else {
+        __syncthreads();  // every wave is done with this chunk's weights
+        if (has_next) swrite_b(0);
+        __syncthreads();
       }
-      __syncthreads();
-    }
+    };
+    for (int c = c_beg; c < c_end; ++c) chunk(c);
   }
 }
 
@@ -269,12 +346,22 @@ hipError_t launch_expand(const SegView& seg, const float* v, int64_t ldv, int64_
   a.y = y;
   a.ldy = ldy;
   a.add = add;
-  const int64_t mt_max = seg.T > 0 ? (seg.T + kTileTokens - 1) / kTileTokens + (seg.L < seg.T ? seg.L : seg.T) : 0;
+  const int nks = r <= 16 ? 1 : r <= 32 ? 2 : r <= 64 ? 4 : 8;
+  // 64-token tiles measured faster than 128-token ones on the named
+  // workloads; the two-block form (r <= 64) stays selectable for tuning.
+  int tb = 1;
+  if (const char* e = getenv("LORA_EXPAND_TB")) {
+    const long f = atol(e);
+    if (f == 1 || f == 2) tb = (int)f;
+  }
+  if (nks == 8) tb = 1;
+  const int64_t tt = (int64_t)kTileTokens * tb;
+  const int64_t mt_max = seg.T > 0 ? (seg.T + tt - 1) / tt + (seg.L < seg.T ? seg.L : seg.T) : 0;
   int64_t chunks = 0;
   for (int q = 0; q < num_slices; ++q) chunks += (slices[q].n + kExpandCols - 1) / kExpandCols;
   // Chunks per run: long runs amortise an item's set-up and keep each y row
   // streaming, but leave a few items per resident workgroup.
-  int64_t cpr = mt_max * chunks / 2048;
+  int64_t cpr = mt_max * chunks / 4096;
   if (cpr > 16) cpr = 16;
   if (cpr < 1) cpr = 1;
   if (const char* e = getenv("LORA_EXPAND_CPR")) {
@@ -291,22 +378,36 @@ hipError_t launch_expand(const SegView& seg, const float* v, int64_t ldv, int64_
   }
   a.run_start[num_slices] = runs;
   int64_t items = mt_max * runs;
-  // Two resident workgroups per CU (LDS bound).
-  int64_t grid = items < 512 ? items : 512;
+  const size_t lds = nks == 1 ? ExpandLds<1>::bytes(seg.L)
+                     : nks == 2 ? ExpandLds<2>::bytes(seg.L)
+                     : nks == 4 ? ExpandLds<4>::bytes(seg.L) : ExpandLds<8>::bytes(seg.L);
+  // Persistent workgroups: as many as fit on the 256 CUs (LDS and register
+  // bound), at most four per CU.
+  int64_t per_cu = (int64_t)(160 * 1024 / lds);
+  const int64_t reg_cu = tb == 2 || nks == 8 ? 2 : (nks <= 2 ? 4 : 3);
+  per_cu = per_cu < 1 ? 1 : (per_cu > reg_cu ? reg_cu : per_cu);
+  int64_t grid = items < 256 * per_cu ? items : 256 * per_cu;
   grid = (grid + 7) / 8 * 8;
   if (grid < 8) grid = 8;
-  const int nks = r <= 16 ? 1 : r <= 32 ? 2 : r <= 64 ? 4 : 8;
-#define LORA_EXPAND_LAUNCH(DT_, VEC_)                                                                \
+#define LORA_EXPAND_LAUNCH(DT_, VEC_, TB_)                                                           \
   switch (nks) {                                                                                    \
-    case 1: hipLaunchKernelGGL((expand_kernel<DT_, VEC_, 1>), dim3(grid), dim3(kExpandThreads), 0, s, a); break; \
-    case 2: hipLaunchKernelGGL((expand_kernel<DT_, VEC_, 2>), dim3(grid), dim3(kExpandThreads), 0, s, a); break; \
-    case 4: hipLaunchKernelGGL((expand_kernel<DT_, VEC_, 4>), dim3(grid), dim3(kExpandThreads), 0, s, a); break; \
-    default: hipLaunchKernelGGL((expand_kernel<DT_, VEC_, 8>), dim3(grid), dim3(kExpandThreads), 0, s, a); break; \
+    case 1: hipLaunchKernelGGL((expand_kernel<DT_, VEC_, 1, TB_>), dim3(grid), dim3(kExpandThreads), lds, s, a); break; \
+    case 2: hipLaunchKernelGGL((expand_kernel<DT_, VEC_, 2, TB_>), dim3(grid), dim3(kExpandThreads), lds, s, a); break; \
+    case 4: hipLaunchKernelGGL((expand_kernel<DT_, VEC_, 4, TB_>), dim3(grid), dim3(kExpandThreads), lds, s, a); break; \
+    default: hipLaunchKernelGGL((expand_kernel<DT_, VEC_, 8, 1>), dim3(grid), dim3(kExpandThreads), lds, s, a); break; \
   }
-  if (dtype == 0) {
-    if (vec) { LORA_EXPAND_LAUNCH(0, true) } else { LORA_EXPAND_LAUNCH(0, false) }
+  if (tb == 2) {
+    if (dtype == 0) {
+      if (vec) { LORA_EXPAND_LAUNCH(0, true, 2) } else { LORA_EXPAND_LAUNCH(0, false, 2) }
+    } else {
+      if (vec) { LORA_EXPAND_LAUNCH(1, true, 2) } else { LORA_EXPAND_LAUNCH(1, false, 2) }
+    }
   } else {
-    if (vec) { LORA_EXPAND_LAUNCH(1, true) } else { LORA_EXPAND_LAUNCH(1, false) }
+    if (dtype == 0) {
+      if (vec) { LORA_EXPAND_LAUNCH(0, true, 1) } else { LORA_EXPAND_LAUNCH(0, false, 1) }
+    } else {
+      if (vec) { LORA_EXPAND_LAUNCH(1, true, 1) } else { LORA_EXPAND_LAUNCH(1, false, 1) }
+    }
   }
 #undef LORA_EXPAND_LAUNCH
   return hipGetLastError();

@@ -195,7 +195,8 @@ int lora_expand_slice(const float* v, int64_t ldv, int64_t v_slice_stride, const
   if (!v || !y) return fail(LORA_ERR_INVALID_ARG, "%s: v and y must not be NULL", fn);
   bool vec = (r % 8 == 0) && (ldv % 4 == 0) && (v_slice_stride % 4 == 0) && aligned16(v) &&
              (ldy % 8 == 0) && aligned16(y);
-  for (int s = 0; s < num_slices; ++s) vec = vec && aligned16(B[s]) && (col_off[s] % 8 == 0);
+  for (int s = 0; s < num_slices; ++s)
+    vec = vec && aligned16(B[s]) && (col_off[s] % 8 == 0) && (n_s[s] % 8 == 0);
   if (g_path.load(std::memory_order_relaxed) == 1 && r > lora::kBgmvMaxRank)
     return fail(LORA_ERR_UNSUPPORTED, "%s: the per-token path takes r <= %d", fn, lora::kBgmvMaxRank);
   if (use_bgmv(Op::kExpand, T, r)) {

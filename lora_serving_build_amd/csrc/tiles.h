@@ -74,4 +74,67 @@ __device__ __forceinline__ bool tile_range(const SegView& seg, int tile_tokens,
   return true;
 }
 
+// LDS copy of everything a tile lookup needs, so that mapping a work item to
+// its tokens costs no global round trip: tile_start[0..S], seg_start[0..S],
+// seg_lora[0..S).  Each array holds L + 1 ints.
+struct TileTable {
+  int32_t* tile_start;
+  int32_t* seg_start;
+  int32_t* seg_lora;
+  int S;
+  int tiles;
+};
+
+// Fills a TileTable from the metadata (same clamping as build_tile_prefix).
+// Every thread of the block must call it.
+template <int NT>
+__device__ TileTable build_tile_table(const SegView& seg, int tile_tokens, int32_t* lds,
+                                      int32_t* scratch) {
+  TileTable tt;
+  tt.tile_start = lds;
+  tt.seg_start = lds + seg.L + 1;
+  tt.seg_lora = lds + 2 * (seg.L + 1);
+  int S = seg.counts[0];
+  S = S < 0 ? 0 : (S > seg.L ? seg.L : S);
+  for (int s = threadIdx.x; s <= S; s += NT) tt.seg_start[s] = seg.seg_start[s];
+  for (int s = threadIdx.x; s < S; s += NT) tt.seg_lora[s] = seg.seg_lora[s];
+  __syncthreads();
+  const int per = (S + NT - 1) / NT;
+  const int lo = min((int)threadIdx.x * per, S);
+  const int hi = min(lo + per, S);
+  int mine = 0;
+  for (int s = lo; s < hi; ++s) {
+    const int len = tt.seg_start[s + 1] - tt.seg_start[s];
+    mine += len > 0 ? (len + tile_tokens - 1) / tile_tokens : 0;
+  }
+  int total;
+  int run = block_exclusive_sum<NT>(mine, scratch, &total);
+  for (int s = lo; s < hi; ++s) {
+    tt.tile_start[s] = run;
+    const int len = tt.seg_start[s + 1] - tt.seg_start[s];
+    run += len > 0 ? (len + tile_tokens - 1) / tile_tokens : 0;
+  }
+  if (threadIdx.x == 0) tt.tile_start[S] = total;
+  __syncthreads();
+  tt.S = S;
+  tt.tiles = total;
+  return tt;
+}
+
+// tile_range on a TileTable (LDS only).
+__device__ __forceinline__ bool tile_range_lds(const TileTable& tt, int T, int L, int tile_tokens,
+                                               int tile, int* p0, int* p_end, int* lora_id) {
+  const int s = tile_segment(tt.tile_start, tt.S, tile);
+  const int start = tt.seg_start[s];
+  const int end = tt.seg_start[s + 1];
+  const int b = start + (tile - tt.tile_start[s]) * tile_tokens;
+  const int e = min(b + tile_tokens, end);
+  const int l = tt.seg_lora[s];
+  if (b < 0 || e > T || b >= e || l < 0 || l >= L) return false;
+  *p0 = b;
+  *p_end = e;
+  *lora_id = l;
+  return true;
+}
+
 }  // namespace lora
