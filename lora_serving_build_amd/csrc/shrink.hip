@@ -2,15 +2,22 @@
 //
 // One workgroup of four waves owns a 64-token tile of one segment and a range
 // of H (the whole of H unless the batch has too few tiles to fill the GPU).
-// H is walked in blocks of 128: the block of x (64 rows x 256 B) and of A_l
-// (r rows x 256 B) is loaded cooperatively -- 16 lanes per row, so one load
-// instruction covers 4 rows x 256 contiguous bytes -- into registers one
-// block ahead, then written to a double-buffered LDS tile.  A_l is thus read
-// from L2 once per 64 tokens instead of once per 16, and the matrix cores take
-// their operands from LDS (row pitch padded to 272 B, which spreads the 16 rows
-// of an operand read over all banks).  Wave w multiplies tokens 16w..16w+15
-// against all of r with 16x16x32 ops, accumulating the transposed product
-// D[j][token] in fp32, so each lane ends with four consecutive j of one token.
+// Wave w multiplies tokens 16w..16w+15 against all of r with 16x16x32 ops,
+// accumulating the transposed product D[j][token] in fp32, so each lane ends
+// with four consecutive j of one token.  H is walked in blocks of 128:
+//  - x is private to a wave, so each lane loads its own operand straight into
+//    registers (token m of the wave, 8 consecutive h per 32-wide k step: one
+//    load instruction covers 16 rows x 64 contiguous bytes), one block ahead,
+//    in two register sets that the loop alternates (no copy waits for a load);
+//  - A_l is shared by the four waves: its block (r rows x 256 B, 16 lanes per
+//    row) is loaded cooperatively one block ahead and written to a
+//    double-buffered LDS tile (row pitch padded to 272 B, which spreads the 16
+//    rows of an operand read over all banks), so A_l is read from L2 once per
+//    64 tokens.
+// Loads are unconditional (addresses clamped into the chunk): values past the
+// end of the chunk are zeroed where they are used, so the compiler can count
+// the loads in flight exactly.  LDS holds only A and the tile table, which
+// leaves room for four workgroups per CU.
 //
 // When H is split across workgroups (ks chunks), each chunk writes its fp32
 // partial rows to the workspace (indexed by sorted position) and a second
@@ -26,9 +33,9 @@ namespace {
 
 constexpr int kShrinkThreads = 256;
 constexpr int kSkTile = 64;              // tokens per tile (4 waves x 16)
-constexpr int kSkKB = kShrinkKStep;      // H elements per LDS block
-constexpr int kSkPitch = kSkKB + 8;      // 16-bit elements per LDS row
-constexpr int kSkChunks = kSkKB / 8;     // 16-byte chunks per row and block
+constexpr int kSkKB = kShrinkKStep;      // H elements per block
+constexpr int kSkPitch = kSkKB + 8;      // 16-bit elements per LDS row of A
+constexpr int kSkChunks = kSkKB / 8;     // 16-byte pieces per row and block
 
 struct ShrinkArgs {
   SegView seg;
@@ -43,6 +50,13 @@ struct ShrinkArgs {
   int32_t ks;
   int32_t kchunk;  // H elements per workgroup chunk (multiple of kSkKB)
   int32_t rp;      // padded rank of the partial rows (16 * NJT)
+};
+
+template <int NJT>
+struct ShrinkLds {
+  static constexpr size_t a_bytes = (size_t)2 * 16 * NJT * kSkPitch * 2;
+  // A blocks, then the tile table (3 (L + 1) ints) and scan scratch
+  static size_t bytes(int L) { return a_bytes + 4 * (3 * ((size_t)L + 1) + 8); }
 };
 
 // Stores four consecutive j values of one row (j0 = first), clipped at r.
@@ -61,27 +75,26 @@ __device__ __forceinline__ void store4(float* p, int j0, int r, f32x4 val) {
 // NJT = 16-row tiles of r (r <= 16 * NJT).  VEC: 16-byte aligned rows with H
 // and ldx multiples of 8 (otherwise element-wise loads).
 template <int DT, bool VEC, int NJT>
-__global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkArgs a) {
+__global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kernel(ShrinkArgs a) {
   constexpr int RP = 16 * NJT;
-  constexpr int XL = kSkTile * kSkChunks / kShrinkThreads;  // x chunks per thread per block (4)
-  constexpr int AL = RP * kSkChunks / kShrinkThreads;       // A chunks per thread per block (NJT)
-  __shared__ __align__(16) uint16_t s_x[2][kSkTile * kSkPitch];
-  __shared__ __align__(16) uint16_t s_a[2][RP * kSkPitch];
-  __shared__ int32_t s_tile_start[kMaxLoras + 1];
-  __shared__ int32_t s_scan[kShrinkThreads / kWave + 1];
-  __shared__ int32_t s_tok[kSkTile];
+  constexpr int AL = RP * kSkChunks / kShrinkThreads;  // A pieces per thread per block (NJT)
+  constexpr int KS = kSkKB / 32;                        // 32-wide k steps per block
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* s_a = reinterpret_cast<uint16_t*>(smem);    // [2][RP * kSkPitch]
+  int32_t* s_table = reinterpret_cast<int32_t*>(smem + ShrinkLds<NJT>::a_bytes);
+  int32_t* s_scan = s_table + 3 * (a.seg.L + 1);
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int m = lane & 15;  // token column of D / row of A inside a 16-row tile
   const int g = lane >> 4;  // lane group: which 8 of the 32 elements of an op
-  // Cooperative load layout: chunk c = tid + 256 i, row c / 16, 16-byte column c % 16.
+  // Cooperative A layout: piece c = tid + 256 i, row c / 16, 16-byte column c % 16.
   const int lrow = tid >> 4;
   const int lcol = (tid & 15) * 8;
 
-  int S;
-  const int tiles = build_tile_prefix<kShrinkThreads>(a.seg, kSkTile, s_tile_start, s_scan, &S);
+  const TileTable table = build_tile_table<kShrinkThreads>(a.seg, kSkTile, s_table, s_scan);
+  const int tiles = table.tiles;
   const int n_items = tiles * a.ks;
   const int grid = gridDim.x;
 
@@ -91,27 +104,17 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkArgs a) {
     const int ksi = item / tiles;
     const int tile = item - ksi * tiles;
     int p0 = 0, p_end = 0, l = 0;
-    const bool ok = tile_range(a.seg, kSkTile, s_tile_start, S, tile, &p0, &p_end, &l);
-    if (tid < kSkTile) {
-      int t = -1;
-      if (ok && p0 + tid < p_end) {
-        t = a.seg.sorted_token[p0 + tid];
-        if (t < 0 || t >= a.seg.T) t = -1;
-      }
-      s_tok[tid] = t;
-    }
-    __syncthreads();
+    const bool ok = tile_range_lds(table, a.seg.T, a.seg.L, kSkTile, tile, &p0, &p_end, &l);
     const int kbeg = ksi * a.kchunk;
     const int kend = min(a.H, kbeg + a.kchunk);
-    const int t_any = s_tok[0];
-    // Rows of this thread's loads.  A missing token reads some valid row: its
-    // output column is dropped.  Rows j >= r read row 0: output rows dropped.
-    const uint16_t* xsrc[XL];
-#pragma unroll
-    for (int i = 0; i < XL; ++i) {
-      const int tt = s_tok[lrow + 16 * i];
-      xsrc[i] = a.x + (int64_t)(tt >= 0 ? tt : (t_any >= 0 ? t_any : 0)) * a.ldx;
-    }
+    const int pos = p0 + wave * 16 + m;
+    int t = (ok && pos < p_end) ? a.seg.sorted_token[pos] : -1;
+    t = (t >= 0 && t < a.seg.T) ? t : -1;
+    const bool tok_ok = t >= 0;
+    const bool wave_live = ok && p0 + wave * 16 < p_end;
+    // A missing token reads row 0 (its output column is dropped).  Rows
+    // j >= r of A read row 0 (output rows dropped).
+    const uint16_t* xrow = a.x + (int64_t)(tok_ok ? t : 0) * a.ldx;
     const uint16_t* Al = a.A + (int64_t)l * a.r * a.H;
     const uint16_t* asrc[AL];
 #pragma unroll
@@ -120,80 +123,101 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkArgs a) {
       asrc[i] = Al + (int64_t)(j < a.r ? j : 0) * a.H;
     }
 
-    u32x4 rx[XL], ra[AL];
-    auto gload = [&](int kb) {
-      // Elements at or beyond kend read as zero (only the last block has any).
+    u32x4 ra[AL];
+    auto gload_a = [&](int kb) {
       const int off = kb + lcol;
 #pragma unroll
-      for (int i = 0; i < XL; ++i) {
-        if constexpr (VEC)
-          rx[i] = load8_16_masked(xsrc[i], off, kend, ok);
-        else
-          rx[i] = ok ? load8_16<false>(xsrc[i] + off, kend - off) : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
       for (int i = 0; i < AL; ++i) {
-        if constexpr (VEC)
-          ra[i] = load8_16_masked(asrc[i], off, kend, ok);
-        else
+        if constexpr (VEC) {
+          const int oc = off < kend ? off : kend - 8;  // kend is a multiple of 8 here
+          ra[i] = *reinterpret_cast<const u32x4*>(asrc[i] + oc);
+        } else {
           ra[i] = ok ? load8_16<false>(asrc[i] + off, kend - off) : u32x4{0u, 0u, 0u, 0u};
+        }
       }
     };
-    auto swrite = [&](int buf) {
+    // Zeroes the pieces past the chunk when the block goes to LDS.
+    auto swrite_a = [&](int buf, int kb) {
+      const int off = kb + lcol;
 #pragma unroll
-      for (int i = 0; i < XL; ++i)
-        *reinterpret_cast<u32x4*>(&s_x[buf][(lrow + 16 * i) * kSkPitch + lcol]) = rx[i];
+      for (int i = 0; i < AL; ++i) {
+        u32x4 w = ra[i];
+        if (!(ok && off < kend)) w = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(&s_a[(buf * RP + lrow + 16 * i) * kSkPitch + lcol]) = w;
+      }
+    };
+    auto gload_x = [&](int kb, u32x4* xr) {
 #pragma unroll
-      for (int i = 0; i < AL; ++i)
-        *reinterpret_cast<u32x4*>(&s_a[buf][(lrow + 16 * i) * kSkPitch + lcol]) = ra[i];
+      for (int kk = 0; kk < KS; ++kk) {
+        const int off = kb + 32 * kk + 8 * g;
+        if constexpr (VEC) {
+          const int oc = off < kend ? off : kend - 8;
+          xr[kk] = *reinterpret_cast<const u32x4*>(xrow + oc);
+        } else {
+          xr[kk] = tok_ok ? load8_16<false>(xrow + off, kend - off) : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
     };
 
     f32x4 acc[NJT];
 #pragma unroll
     for (int jt = 0; jt < NJT; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const bool wave_live = ok && p0 + wave * 16 < p_end;
     const int nblk = kend > kbeg ? (kend - kbeg + kSkKB - 1) / kSkKB : 0;
 
-    if (nblk > 0) {
-      gload(kbeg);
-      swrite(0);
-    }
-    __syncthreads();
-    for (int b = 0; b < nblk; ++b) {
+    // One block: the next block's A and x go out first, then the ops of this
+    // one from LDS (A) and registers (x).
+    auto block = [&](int b, u32x4* xcur, u32x4* xnext) {
       const int buf = b & 1;
-      if (b + 1 < nblk) gload(kbeg + (b + 1) * kSkKB);  // in flight during the ops below
+      const int kb = kbeg + b * kSkKB;
+      const bool has_next = b + 1 < nblk;
+      // Issued on every block (the last one reads clamped addresses and drops
+      // the data): a load that only some paths issue would make the compiler
+      // assume none and wait for everything before the ops below.
+      gload_a(kb + kSkKB);
+      gload_x(kb + kSkKB, xnext);
+      __builtin_amdgcn_sched_barrier(0);
       if (wave_live) {
-        const uint16_t* xs = &s_x[buf][(wave * 16 + m) * kSkPitch + 8 * g];
-        const uint16_t* as = &s_a[buf][m * kSkPitch + 8 * g];
+        const uint16_t* as = &s_a[(buf * RP + m) * kSkPitch + 8 * g];
 #pragma unroll
-        for (int kk = 0; kk < kSkKB; kk += 32) {
-          const u32x4 xop = *reinterpret_cast<const u32x4*>(xs + kk);
+        for (int kk = 0; kk < KS; ++kk) {
+          // Elements past the chunk (last block only) are zero.
+          const u32x4 xop = (kb + 32 * kk + 8 * g < kend) ? xcur[kk] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
           for (int jt = 0; jt < NJT; ++jt) {
-            const u32x4 aop = *reinterpret_cast<const u32x4*>(as + jt * 16 * kSkPitch + kk);
+            const u32x4 aop = *reinterpret_cast<const u32x4*>(as + jt * 16 * kSkPitch + 32 * kk);
             acc[jt] = mfma16x16x32<DT>(aop, xop, acc[jt]);
           }
         }
       }
-      if (b + 1 < nblk) swrite(buf ^ 1);
+      if (has_next) swrite_a(buf ^ 1, kb + kSkKB);
       __syncthreads();
+    };
+
+    u32x4 xa[KS], xb[KS];
+    if (nblk > 0) {
+      gload_a(kbeg);
+      gload_x(kbeg, xa);
+      swrite_a(0, kbeg);
+    }
+    __syncthreads();
+    for (int b = 0; b < nblk; b += 2) {
+      block(b, xa, xb);
+      if (b + 1 < nblk) block(b + 1, xb, xa);
     }
 
     // Lane (m, g) holds D[j = 16 jt + 4 g + e][token 16 wave + m].
-    const int tt = s_tok[wave * 16 + m];
-    if (wave_live && tt >= 0) {
+    if (wave_live && tok_ok) {
 #pragma unroll
       for (int jt = 0; jt < NJT; ++jt) {
         const int j0 = jt * 16 + 4 * g;
         if (a.ks == 1) {
-          store4<VEC>(a.v + (int64_t)tt * a.ldv + j0, j0, a.r, acc[jt]);
+          store4<VEC>(a.v + (int64_t)t * a.ldv + j0, j0, a.r, acc[jt]);
         } else {
-          float* part = a.partial + ((int64_t)ksi * a.seg.T + (p0 + wave * 16 + m)) * a.rp + j0;
+          float* part = a.partial + ((int64_t)ksi * a.seg.T + pos) * a.rp + j0;
           *reinterpret_cast<f32x4*>(part) = acc[jt];
         }
       }
     }
-    __syncthreads();
   }
 }
 
@@ -220,20 +244,27 @@ __global__ __launch_bounds__(256) void shrink_reduce_kernel(SegView seg, const f
   }
 }
 
+size_t shrink_lds_bytes(int njt, int L) {
+  return njt == 1 ? ShrinkLds<1>::bytes(L)
+         : njt == 2 ? ShrinkLds<2>::bytes(L)
+         : njt == 4 ? ShrinkLds<4>::bytes(L) : ShrinkLds<8>::bytes(L);
+}
+
 template <int DT, bool VEC>
 hipError_t launch_typed(const ShrinkArgs& args, int njt, int grid, hipStream_t s) {
+  const size_t lds = shrink_lds_bytes(njt, args.seg.L);
   switch (njt) {
     case 1:
-      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 1>), dim3(grid), dim3(kShrinkThreads), 0, s, args);
+      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 1>), dim3(grid), dim3(kShrinkThreads), lds, s, args);
       break;
     case 2:
-      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 2>), dim3(grid), dim3(kShrinkThreads), 0, s, args);
+      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 2>), dim3(grid), dim3(kShrinkThreads), lds, s, args);
       break;
     case 4:
-      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 4>), dim3(grid), dim3(kShrinkThreads), 0, s, args);
+      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 4>), dim3(grid), dim3(kShrinkThreads), lds, s, args);
       break;
     default:
-      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 8>), dim3(grid), dim3(kShrinkThreads), 0, s, args);
+      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 8>), dim3(grid), dim3(kShrinkThreads), lds, s, args);
       break;
   }
   return hipGetLastError();
@@ -274,7 +305,12 @@ ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r) {
   p.partial_bytes = ks > 1 ? (size_t)(ks * (int64_t)T * p.rp * 4) : 0;
   p.counter_bytes = 0;
   int64_t items = tiles * ks;
-  int64_t grid = items < 1024 ? items : 1024;
+  // Persistent workgroups: as many as are resident at once (LDS and register
+  // bound: four per CU up to r = 64, two beyond).
+  int64_t per_cu = (int64_t)(160 * 1024 / shrink_lds_bytes(p.jtw, L));
+  const int64_t reg_cu = p.jtw <= 4 ? 4 : 2;
+  per_cu = per_cu < 1 ? 1 : (per_cu > reg_cu ? reg_cu : per_cu);
+  int64_t grid = items < 256 * per_cu ? items : 256 * per_cu;
   grid = (grid + 7) / 8 * 8;
   if (grid < 8) grid = 8;
   p.grid = (int32_t)grid;
