@@ -157,7 +157,7 @@ def cpu_baseline(w, step_bytes):
     t0 = time.perf_counter()
     run()
     t1 = time.perf_counter() - t0
-    reps = max(1, min(100000, int(math.ceil(10.0 / max(t1, 1e-6)))))
+    reps = max(1, min(100000, int(math.ceil(12.0 / max(t1, 1e-6)))))
     if t1 > 30.0:
         reps = 1
     t0 = time.perf_counter()
@@ -176,9 +176,9 @@ def cpu_baseline(w, step_bytes):
 
 
 OP_KERNELS = {  # kernel-name fragments of each op (rocprofv3 names)
-    "build": ("build_segments_kernel",),
-    "shrink": ("shrink_kernel", "shrink_reduce_kernel"),
-    "expand": ("expand_kernel",),
+    "build": ("build_segments",),
+    "shrink": ("shrink",),
+    "expand": ("expand",),
 }
 COPY_PROBE_BYTES = 256 << 20
 
@@ -218,17 +218,16 @@ def summarize_profiles(args):
                      f"{float(r['MinNs'])/1e3:.2f} | {float(r['MaxNs'])/1e3:.2f} |")
         if op:
             op_avg.setdefault(op, []).append((kn, float(r["AverageNs"]) / 1e3, int(r["Calls"])))
-    lines += ["", "Per op (average launch duration; algorithmic bytes per call):"]
+    steps = sum(c for _, _, c in op_avg.get("build", [])) or 1
+    lines += ["", f"Per op and step ({steps} steps traced; every kernel of the op counted, "
+              "algorithmic bytes of the op):"]
     nbytes = {"shrink": w.shrink_bytes(), "expand": w.expand_bytes()}
-    calls_per_op = {"shrink": 1, "expand": len(w.outputs), "build": 1}
     for op, rows in sorted(op_avg.items()):
-        tot_us = sum(a for _, a, _ in rows)
-        line = f"- {op}: {tot_us:.2f} us summed over its kernels' average launches"
+        per_step = sum(a * c for _, a, c in rows) / steps
+        line = f"- {op}: {per_step:.2f} us per step"
         if op in nbytes:
-            per_launch = nbytes[op] / calls_per_op[op]
-            avg_launch = sum(a * c for _, a, c in rows) / max(1, sum(c for _, _, c in rows))
-            line += (f"; {per_launch / 2**20:.3f} MiB per launch, average launch {avg_launch:.2f} us "
-                     f"-> {per_launch / (avg_launch * 1e-6) / 1e9:.1f} GB/s")
+            line += (f"; {nbytes[op] / 2**20:.3f} MiB -> "
+                     f"{nbytes[op] / (per_step * 1e-6) / 1e9:.1f} GB/s")
         lines.append(line)
     with open(os.path.join(out_dir, f"trace_{name}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
