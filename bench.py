@@ -282,6 +282,59 @@ def summarize_profiles(args):
     print("wrote", path)
 
 
+SWEEP_POINTS = (  # (kind, tokens, hidden, rank): the micro-benchmark grid, thinned
+    [(k, T, H, r) for k in ("bgmv", "sgmv") for T in (16, 256, 2048, 8192)
+     for H in (4096, 16384) for r in (16, 64)]
+    + [("sgmv", 65536, 16384, 16)])  # the review thread's bs 8192 x seq 8 example
+
+
+def sweep(args):
+    """Shrink and expand alone on the micro-benchmark sweep shapes: 4 adapters,
+    ids sorted, one token per sequence (bgmv) or eight (sgmv), expand r -> H
+    with add_inputs.  Ids come from the shared generator; the tensors are drawn
+    on the GPU (seeded) because host generation of the large points takes
+    longer than timing them.  One JSON line per point and op."""
+    import torch
+    import lora_serving_build_amd as lsb
+    import workloads as W
+    torch.cuda.set_device(0)
+    dt = torch.float16
+    gen = torch.Generator(device="cuda")
+    for kind, T, H, r in SWEEP_POINTS:
+        L = 4
+        ids_w = W.sweep_point(kind, T, 8, 8, L=L)  # same id draw as the full-size point
+        ids = torch.from_numpy(ids_w.ids).cuda()
+        per_set = (T * H * 2) * 2 + L * r * H * 2 * 2 + T * r * 4
+        P = max(2, min(64, int(math.ceil(args.pool_gib * 2**30 / per_set))))
+        gen.manual_seed(T * 131 + H * 7 + r)
+        sets = []
+        for _ in range(P):
+            sets.append(dict(
+                x=torch.randn(T, H, generator=gen, device="cuda").to(dt),
+                A=(torch.randn(L, r, H, generator=gen, device="cuda") / math.sqrt(H)).to(dt),
+                B=(torch.randn(L, H, r, generator=gen, device="cuda") / math.sqrt(r)).to(dt),
+                y=torch.randn(T, H, generator=gen, device="cuda").to(dt),
+                v=torch.zeros(T, r, device="cuda"),
+                seg=lsb.lora_build_segments(ids, L)))
+        need = lsb.lora_shrink_workspace_bytes(T, L, H, r)
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        K = min(P, 20) if T * H < 2**27 else 8
+        shrink_b = T * H * 2 + L * r * H * 2 + T * r * 4
+        expand_b = T * r * 4 + L * r * H * 2 + 2 * T * H * 2
+        for op, fn, nb in (
+                ("shrink", lambda s: lsb.lora_shrink(s["x"], s["A"], s["seg"], s["v"], workspace=ws), shrink_b),
+                ("expand", lambda s: lsb.lora_expand(s["v"], s["B"], s["seg"], s["y"], True), expand_b)):
+            us = graph_time(torch, fn, sets, 0, K) / K * 1e3
+            gbs = nb / (us * 1e-6) / 1e9
+            print(json.dumps({"sweep": kind, "tokens": T, "hidden": H, "rank": r, "num_loras": L,
+                              "op": op, "us": round(us, 2), "GB_s": round(gbs, 1),
+                              "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                              "algorithmic_MiB": round(nb / 2**20, 2), "pool_sets": P}), flush=True)
+        del sets, ws
+        torch.cuda.empty_cache()
+
+
 def source_hash(paths):
     h = hashlib.sha256()
     for p in paths:
@@ -325,12 +378,17 @@ def main():
                     help="also run one plain copy of 256 MiB (calibrates FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--summarize-profiles", action="store_true",
                     help="write profiles/ summaries from rocprofv3 CSVs (--trace, --fetch, --write)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time shrink and expand alone on the micro-benchmark sweep shapes")
     ap.add_argument("--trace")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
     args = ap.parse_args()
     if args.summarize_profiles:
         summarize_profiles(args)
+        return
+    if args.sweep:
+        sweep(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
