@@ -455,6 +455,52 @@ def test_each_path_integer_exact(force_path, mode, dtype, T, H, r, L, slices, sl
     check_neg_rows(dw)
 
 
+PLAN_VARIANTS = [
+    # (environment overrides of the launch plan, dtype, T, H, r, L, slices)
+    ({"LORA_SHRINK_KSPLIT": "1"}, "bf16", 300, 2048, 32, 7, [[512, 256, 256]]),
+    ({"LORA_SHRINK_KSPLIT": "2"}, "f16", 300, 2048, 32, 7, [[512, 256, 256]]),
+    ({"LORA_SHRINK_KSPLIT": "5"}, "bf16", 500, 4096, 64, 9, [[1024]]),
+    ({"LORA_EXPAND_TB": "2"}, "bf16", 700, 1024, 64, 5, [[2048, 512]]),
+    ({"LORA_EXPAND_TB": "2"}, "f16", 300, 1024, 16, 3, [[1000]]),
+    ({"LORA_EXPAND_TB": "2"}, "bf16", 300, 512, 128, 3, [[384]]),
+    ({"LORA_EXPAND_CPR": "1"}, "bf16", 400, 1024, 32, 6, [[1536, 256]]),
+    ({"LORA_EXPAND_CPR": "3"}, "f16", 400, 1024, 32, 6, [[1536, 256]]),
+    ({"LORA_EXPAND_CPR": "40"}, "bf16", 400, 1024, 32, 6, [[1536, 256]]),
+]
+
+
+@pytest.mark.parametrize("env,dtype,T,H,r,L,slices", PLAN_VARIANTS)
+@pytest.mark.parametrize("integer", [False, True])
+def test_plan_variants(force_path, monkeypatch, env, dtype, T, H, r, L, slices, integer):
+    """Launch plans the defaults never pick (other H splits, 128-token expand
+    tiles, other column runs), selected through the library's tuning
+    overrides, still give the oracle's result; with integer inputs, its exact
+    bits."""
+    _announce(f"plan {env} {dtype} T={T} H={H} r={r} L={L} slices={slices} integer={integer}")
+    for k, val in env.items():
+        monkeypatch.setenv(k, val)
+    force_path(lsb.PATH_SGMV)
+    w = W.make("plan", dtype, T, H, r, L, slices, seed=T + r + (7 if integer else 0), seq_len=(1, 40),
+               neg_frac=0.1, integer=integer)
+    dw = DeviceWorkload(w)
+    dw.run()
+    if integer:
+        act = np.nonzero(w.active)[0]
+        v_or = oracle.shrink(w.dtype, w.x, w.A, w.ids)
+        assert np.array_equal(dw.v.cpu().numpy()[act].astype(np.float64), v_or[act])
+        for o, y in zip(w.outputs, dw.ys):
+            ref = oracle.expand_slice(w.dtype, np.nan_to_num(v_or), [s.B for s in o.slices],
+                                      [s.col_off for s in o.slices], w.ids, o.y0, w.add)
+            ref_bits = W.f32_to_bits(ref.astype(np.float32), dtype) if dtype == "bf16" else \
+                ref.astype(np.float16).view(np.uint16)
+            assert np.array_equal(host_bits(y)[:, _slice_cols(o)][act], ref_bits[act])
+    else:
+        rv, ry, ryi = compare_with_oracle(dw)
+        assert rv <= 1 and ry <= 1 and ryi <= 1
+    check_neg_rows(dw)
+    check_outside_slices(dw)
+
+
 def test_bgmv_and_sgmv_agree(force_path):
     """The per-token and the segment kernels on the same batch agree with each
     other within the tolerance (punica issue: BGMV is a subset of SGMV)."""
