@@ -235,6 +235,10 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
       }
     }
 
+    // y of the first chunk depends only on the tokens: it goes out here,
+    // with v, instead of one barrier later.
+    u32x4 yfirst[TB][NP];
+    if (c_beg < c_end) gload_y(c_beg, yfirst);
     if (ok && c_beg < c_end) swrite_b(0);
     __syncthreads();
     // One chunk: the next chunk's weights and this chunk's y go out first,
@@ -242,12 +246,19 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
     // the y update.  The latency of y is covered by the other workgroups on
     // the CU (up to four), not by a longer prefetch: a longer prefetch would
     // not survive the compiler's conservative load counting across the loop.
-    auto chunk = [&](int c) {
+    auto chunk = [&](int c, bool first) {
       const int buf = NB == 2 ? ((c - c_beg) & 1) : 0;
       const bool has_next = c + 1 < c_end;
       if (has_next) gload_b(c + 1);
       u32x4 ycur[TB][NP];
-      gload_y(c, ycur);
+      if (first) {
+#pragma unroll
+        for (int b = 0; b < TB; ++b)
+#pragma unroll
+          for (int p = 0; p < NP; ++p) ycur[b][p] = yfirst[b][p];
+      } else {
+        gload_y(c, ycur);
+      }
       // Nothing below may be scheduled between these loads.
       __builtin_amdgcn_sched_barrier(0);
       if (wave_live) {
@@ -327,7 +338,8 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
         __syncthreads();
       }
     };
-    for (int c = c_beg; c < c_end; ++c) chunk(c);
+    if (c_beg < c_end) chunk(c_beg, true);
+    for (int c = c_beg + 1; c < c_end; ++c) chunk(c, false);
   }
 }
 

@@ -94,10 +94,12 @@ __device__ TileTable build_tile_table(const SegView& seg, int tile_tokens, int32
   tt.tile_start = lds;
   tt.seg_start = lds + seg.L + 1;
   tt.seg_lora = lds + 2 * (seg.L + 1);
+  // All L + 1 entries are copied (they exist whatever S is), so these loads
+  // go out together with the load of S instead of one round trip after it.
   int S = seg.counts[0];
+  for (int s = threadIdx.x; s <= seg.L; s += NT) tt.seg_start[s] = seg.seg_start[s];
+  for (int s = threadIdx.x; s < seg.L; s += NT) tt.seg_lora[s] = seg.seg_lora[s];
   S = S < 0 ? 0 : (S > seg.L ? seg.L : S);
-  for (int s = threadIdx.x; s <= S; s += NT) tt.seg_start[s] = seg.seg_start[s];
-  for (int s = threadIdx.x; s < S; s += NT) tt.seg_lora[s] = seg.seg_lora[s];
   __syncthreads();
   const int per = (S + NT - 1) / NT;
   const int lo = min((int)threadIdx.x * per, S);
