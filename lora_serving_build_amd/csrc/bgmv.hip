@@ -50,6 +50,7 @@ struct BgExpandArgs {
   uint16_t* y;
   int64_t ldy;
   int32_t add;
+  int32_t cb;  // column blocks per token (aligned kernel)
 };
 
 template <int DT>
@@ -293,13 +294,15 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_expand_kernel(BgExpandArgs a)
 // tree as the general kernel), one of them parks the column total in a
 // wave-private LDS row, and the wave then reads the row back 8 columns per
 // lane for 16-byte y updates.  A wave handles RPI rounds of 512 columns at
-// once; y rows and v are loaded before the adapter id is needed.
+// once; y rows and v are loaded before the adapter id is needed.  A token's
+// columns are spread over cb workgroups (work item = (token, column block)),
+// so a small batch still fills the chip: in every slice, block b takes the
+// rounds whose index divided by 4 RPI is b modulo cb.
 constexpr int kRoundCols = kWave * 8;
 
-template <int DT, int G>
+template <int DT, int G, int RPI>
 __global__ __launch_bounds__(kBgThreads) void bgmv_expand_fast_kernel(BgExpandArgs a) {
   constexpr int LG = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
-  constexpr int RPI = G <= 2 ? 2 : 1;        // rounds of 512 columns per trip
   constexpr int K = 8 * G;                   // weight loads per lane and round
   constexpr int KB = K < 16 ? K : 16;        // loads per batch (register bound)
   constexpr int CPI = kWave / G;             // columns per load instruction
@@ -310,12 +313,15 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_expand_fast_kernel(BgExpandAr
   const int part = lane & (G - 1);
   float* so = s_out[wave];
 
-  for (int t = blockIdx.x; t < a.seg.T; t += gridDim.x) {
+  const int items = a.seg.T * a.cb;
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int t = it / a.cb;
+    const int cb = it - t * a.cb;
     for (int q = 0; q < a.num_slices; ++q) {
       const int nq = a.slices[q].n;
       const float* vrow = a.v + (int64_t)t * a.ldv + (int64_t)q * a.v_slice_stride + part * 8;
       uint16_t* yrow = a.y + (int64_t)t * a.ldy + a.slices[q].col_off;
-      for (int R0 = wave * RPI; R0 * kRoundCols < nq; R0 += NW * RPI) {
+      for (int R0 = (cb * NW + wave) * RPI; R0 * kRoundCols < nq; R0 += a.cb * NW * RPI) {
         // y and v do not depend on the adapter: they are in flight while the
         // (scalar) adapter id arrives, and only the id is waited for before
         // the weight loads go out.
@@ -435,19 +441,49 @@ hipError_t launch_bgmv_expand(const SegView& seg, const float* v, int64_t ldv, i
   a.y = y;
   a.ldy = ldy;
   a.add = add;
-  const int grid = bg_grid(seg.T);
   if (vec && (r == 8 || r == 16 || r == 32 || r == 64)) {
+    // Rounds of 512 columns in the widest slice, and workgroups per token
+    // that give each wave RPI rounds of it.  Two rounds per wave keep more
+    // bytes in flight; one round doubles the workgroups of a small batch.
+    constexpr int nw = kBgThreads / kWave;
+    int64_t rounds = 1;
+    for (int q = 0; q < num_slices; ++q) {
+      const int64_t rq = (slices[q].n + kRoundCols - 1) / kRoundCols;
+      rounds = rq > rounds ? rq : rounds;
+    }
+    const int64_t T = seg.T > 0 ? seg.T : 1;
+    int rpi = r <= 16 ? 2 : 1;
+    if (rpi == 2 && T * ((rounds + 2 * nw - 1) / (2 * nw)) < 256) rpi = 1;
+    if (const char* e = getenv("LORA_BGMV_RPI")) {
+      const long f = atol(e);
+      if (f == 1 || (f == 2 && r <= 16)) rpi = (int)f;
+    }
+    int64_t cb = (rounds + (int64_t)nw * rpi - 1) / ((int64_t)nw * rpi);
+    if (const char* e = getenv("LORA_BGMV_CB")) {
+      const long f = atol(e);
+      if (f >= 1 && f < cb) cb = f;
+    }
+    a.cb = (int32_t)cb;
+    int64_t grid = T * cb;
+    if (grid > 8192) grid = 8192;
 #define LORA_BG_FAST(DT_)                                                                            \
-  switch (r) {                                                                                       \
-    case 8: hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 1>), dim3(grid), dim3(kBgThreads), 0, s, a); break; \
-    case 16: hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 2>), dim3(grid), dim3(kBgThreads), 0, s, a); break; \
-    case 32: hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 4>), dim3(grid), dim3(kBgThreads), 0, s, a); break; \
-    default: hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 8>), dim3(grid), dim3(kBgThreads), 0, s, a); break; \
+  switch (r) {                                                                                      \
+    case 8:                                                                                         \
+      if (rpi == 2) hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 1, 2>), dim3(grid), dim3(kBgThreads), 0, s, a); \
+      else hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 1, 1>), dim3(grid), dim3(kBgThreads), 0, s, a); \
+      break;                                                                                        \
+    case 16:                                                                                        \
+      if (rpi == 2) hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 2, 2>), dim3(grid), dim3(kBgThreads), 0, s, a); \
+      else hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 2, 1>), dim3(grid), dim3(kBgThreads), 0, s, a); \
+      break;                                                                                        \
+    case 32: hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 4, 1>), dim3(grid), dim3(kBgThreads), 0, s, a); break; \
+    default: hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 8, 1>), dim3(grid), dim3(kBgThreads), 0, s, a); break; \
   }
     if (dtype == 0) { LORA_BG_FAST(0) } else { LORA_BG_FAST(1) }
 #undef LORA_BG_FAST
     return hipGetLastError();
   }
+  const int grid = bg_grid(seg.T);
 #define LORA_BG_EXPAND(DT_, VEC_)                                                                     \
   if (r <= 16)                                                                                       \
     hipLaunchKernelGGL((bgmv_expand_kernel<DT_, VEC_, 16>), dim3(grid), dim3(kBgThreads), 0, s, a);  \

@@ -4,10 +4,11 @@
 // Work item = (run of 128-column chunks of one slice, 64-token tile of one
 // segment).  The four waves of a workgroup each take 16 tokens of the tile.
 // Per item, each wave converts its tokens' fp32 v once into the matrix-core
-// operand: v is split into hi = round(v) and lo = round(v - hi) in the data
-// type, lane groups 0 and 1 carry hi and groups 2 and 3 carry lo against the
-// same 16 weights, so one 16x16x32 op adds B^T (hi + lo) and v keeps about 16
-// significant bits.  Per chunk, the weight block (128 rows of B_l^T, one
+// operands: v is split into hi = round(v) and lo = round(v - hi) in the data
+// type, so v keeps about 16 significant bits.  For r <= 16, lane groups 0 and
+// 1 carry hi and groups 2 and 3 carry lo against the same 16 weights, so one
+// 16x16x32 op adds B^T (hi + lo).  For larger r, one weight operand covers 32
+// ranks and two ops apply it to hi and to lo, which halves the LDS reads.  Per chunk, the weight block (128 rows of B_l^T, one
 // contiguous 128 x r run in memory) is loaded by the whole workgroup with
 // linear 16-byte loads one chunk ahead and staged in LDS (two buffers up to
 // r = 64, so one barrier per chunk), so all waves share one copy.
@@ -74,6 +75,7 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
   constexpr int BL = kExpandCols * PPR / kExpandThreads;     // pieces per thread per chunk
   constexpr int NQ = kExpandCols / 16;                       // 16-column op tiles per chunk
   constexpr int NP = NQ / 2;                                 // op tile pairs
+  constexpr bool kPack = NKS >= 2;                           // 32 ranks per weight operand
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* s_b = reinterpret_cast<uint16_t*>(smem);
   int32_t* s_table = reinterpret_cast<int32_t*>(smem + Lds::weight_bytes);
@@ -188,16 +190,20 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
     };
     // v of each block's 16 tokens as hi / lo operands, once per item.  All
     // loads go out before any is used (addresses clamped into the row, ranks
-    // >= r replaced by zeros afterwards).
+    // >= r replaced by zeros afterwards).  For r <= 16 one operand holds hi
+    // (lane groups 0, 1) and lo (groups 2, 3) of the same 16 ranks; for larger
+    // r, operand 2 p holds hi and 2 p + 1 lo of ranks 32 p .. +32, so one
+    // weight operand read from LDS feeds two products.
     u32x4 bop[TB][NKS];
     {
-      f32x4 vraw[TB][NKS][2];
+      constexpr int NV = kPack ? NKS / 2 : NKS;  // 8-rank groups per lane
+      f32x4 vraw[TB][NV][2];
 #pragma unroll
       for (int b = 0; b < TB; ++b) {
         const float* vrow = a.v + (int64_t)(tok_ok[b] ? tok[b] : 0) * a.ldv + (int64_t)q * a.v_slice_stride;
 #pragma unroll
-        for (int st = 0; st < NKS; ++st) {
-          const int rk = st * 16 + (g & 1) * 8;
+        for (int st = 0; st < NV; ++st) {
+          const int rk = kPack ? st * 32 + g * 8 : st * 16 + (g & 1) * 8;
           if constexpr (VEC) {
             const int rs = rk + 8 <= a.r ? rk : 0;
             vraw[b][st][0] = *reinterpret_cast<const f32x4*>(vrow + rs);
@@ -213,12 +219,12 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
 #pragma unroll
       for (int b = 0; b < TB; ++b) {
 #pragma unroll
-        for (int st = 0; st < NKS; ++st) {
-          const int rk = st * 16 + (g & 1) * 8;
+        for (int st = 0; st < NV; ++st) {
+          const int rk = kPack ? st * 32 + g * 8 : st * 16 + (g & 1) * 8;
           const bool keep = tok_ok[b] && (VEC ? rk + 8 <= a.r : true);
           const float vv[8] = {vraw[b][st][0].x, vraw[b][st][0].y, vraw[b][st][0].z, vraw[b][st][0].w,
                                vraw[b][st][1].x, vraw[b][st][1].y, vraw[b][st][1].z, vraw[b][st][1].w};
-          uint32_t w4[4];
+          uint32_t h4[4], l4[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float f0 = keep ? vv[2 * e] : 0.f, f1 = keep ? vv[2 * e + 1] : 0.f;
@@ -227,10 +233,15 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
             unpack2<DT>(hi, &h0, &h1);
             const float l0 = __builtin_isfinite(h0) ? f0 - h0 : 0.f;
             const float l1 = __builtin_isfinite(h1) ? f1 - h1 : 0.f;
-            const uint32_t lo = cvt_pack2<DT>(l0, l1);
-            w4[e] = g < 2 ? hi : lo;
+            h4[e] = hi;
+            l4[e] = cvt_pack2<DT>(l0, l1);
           }
-          bop[b][st] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+          if constexpr (kPack) {
+            bop[b][2 * st] = u32x4{h4[0], h4[1], h4[2], h4[3]};
+            bop[b][2 * st + 1] = u32x4{l4[0], l4[1], l4[2], l4[3]};
+          } else {
+            bop[b][st] = g < 2 ? u32x4{h4[0], h4[1], h4[2], h4[3]} : u32x4{l4[0], l4[1], l4[2], l4[3]};
+          }
         }
       }
     }
@@ -271,14 +282,27 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
           for (int b = 0; b < TB; ++b)
 #pragma unroll
             for (int qq = 0; qq < NQ / 2; ++qq) acc[b][qq] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if constexpr (kPack) {
 #pragma unroll
-          for (int st = 0; st < NKS; ++st) {
+            for (int st = 0; st < NKS / 2; ++st) {
+#pragma unroll
+              for (int qq = 0; qq < NQ / 2; ++qq) {
+                const int row = (h * (NQ / 2) + qq) * 16 + m;
+                const u32x4 aop = *reinterpret_cast<const u32x4*>(&sb[row * BP + st * 32 + g * 8]);
+#pragma unroll
+                for (int b = 0; b < TB; ++b) {
+                  acc[b][qq] = mfma16x16x32<DT>(aop, bop[b][2 * st], acc[b][qq]);
+                  acc[b][qq] = mfma16x16x32<DT>(aop, bop[b][2 * st + 1], acc[b][qq]);
+                }
+              }
+            }
+          } else {
 #pragma unroll
             for (int qq = 0; qq < NQ / 2; ++qq) {
               const int row = (h * (NQ / 2) + qq) * 16 + m;
-              const u32x4 aop = *reinterpret_cast<const u32x4*>(&sb[row * BP + st * 16 + (g & 1) * 8]);
+              const u32x4 aop = *reinterpret_cast<const u32x4*>(&sb[row * BP + (g & 1) * 8]);
 #pragma unroll
-              for (int b = 0; b < TB; ++b) acc[b][qq] = mfma16x16x32<DT>(aop, bop[b][st], acc[b][qq]);
+              for (int b = 0; b < TB; ++b) acc[b][qq] = mfma16x16x32<DT>(aop, bop[b][0], acc[b][qq]);
             }
           }
 #pragma unroll

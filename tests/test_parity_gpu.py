@@ -456,30 +456,37 @@ def test_each_path_integer_exact(force_path, mode, dtype, T, H, r, L, slices, sl
 
 
 PLAN_VARIANTS = [
-    # (environment overrides of the launch plan, dtype, T, H, r, L, slices)
-    ({"LORA_SHRINK_KSPLIT": "1"}, "bf16", 300, 2048, 32, 7, [[512, 256, 256]]),
-    ({"LORA_SHRINK_KSPLIT": "2"}, "f16", 300, 2048, 32, 7, [[512, 256, 256]]),
-    ({"LORA_SHRINK_KSPLIT": "5"}, "bf16", 500, 4096, 64, 9, [[1024]]),
-    ({"LORA_EXPAND_TB": "2"}, "bf16", 700, 1024, 64, 5, [[2048, 512]]),
-    ({"LORA_EXPAND_TB": "2"}, "f16", 300, 1024, 16, 3, [[1000]]),
-    ({"LORA_EXPAND_TB": "2"}, "bf16", 300, 512, 128, 3, [[384]]),
-    ({"LORA_EXPAND_CPR": "1"}, "bf16", 400, 1024, 32, 6, [[1536, 256]]),
-    ({"LORA_EXPAND_CPR": "3"}, "f16", 400, 1024, 32, 6, [[1536, 256]]),
-    ({"LORA_EXPAND_CPR": "40"}, "bf16", 400, 1024, 32, 6, [[1536, 256]]),
+    # (environment overrides of the launch plan, kernel path, dtype, T, H, r, L, slices)
+    ({"LORA_SHRINK_KSPLIT": "1"}, "sgmv", "bf16", 300, 2048, 32, 7, [[512, 256, 256]]),
+    ({"LORA_SHRINK_KSPLIT": "2"}, "sgmv", "f16", 300, 2048, 32, 7, [[512, 256, 256]]),
+    ({"LORA_SHRINK_KSPLIT": "5"}, "sgmv", "bf16", 500, 4096, 64, 9, [[1024]]),
+    ({"LORA_EXPAND_TB": "2"}, "sgmv", "bf16", 700, 1024, 64, 5, [[2048, 512]]),
+    ({"LORA_EXPAND_TB": "2"}, "sgmv", "f16", 300, 1024, 16, 3, [[1000]]),
+    ({"LORA_EXPAND_TB": "2"}, "sgmv", "bf16", 300, 512, 128, 3, [[384]]),
+    ({"LORA_EXPAND_CPR": "1"}, "sgmv", "bf16", 400, 1024, 32, 6, [[1536, 256]]),
+    ({"LORA_EXPAND_CPR": "3"}, "sgmv", "f16", 400, 1024, 32, 6, [[1536, 256]]),
+    ({"LORA_EXPAND_CPR": "40"}, "sgmv", "bf16", 400, 1024, 32, 6, [[1536, 256]]),
+    # per-token expand: rounds of 512 columns per wave and column blocks per token
+    ({"LORA_BGMV_RPI": "2"}, "bgmv", "f16", 20, 1024, 16, 3, [[4096, 1024]]),
+    ({"LORA_BGMV_RPI": "2"}, "bgmv", "bf16", 9, 512, 8, 3, [[2048, 4096]]),
+    ({"LORA_BGMV_RPI": "1", "LORA_BGMV_CB": "1"}, "bgmv", "bf16", 37, 1024, 16, 4, [[3072, 1024, 1024]]),
+    ({"LORA_BGMV_CB": "2"}, "bgmv", "bf16", 5, 1024, 32, 3, [[8192]]),
+    ({}, "bgmv", "f16", 3, 1024, 64, 2, [[16384, 512]]),
+    ({}, "bgmv", "bf16", 600, 1024, 16, 5, [[14336, 14336]]),
 ]
 
 
-@pytest.mark.parametrize("env,dtype,T,H,r,L,slices", PLAN_VARIANTS)
+@pytest.mark.parametrize("env,path,dtype,T,H,r,L,slices", PLAN_VARIANTS)
 @pytest.mark.parametrize("integer", [False, True])
-def test_plan_variants(force_path, monkeypatch, env, dtype, T, H, r, L, slices, integer):
+def test_plan_variants(force_path, monkeypatch, env, path, dtype, T, H, r, L, slices, integer):
     """Launch plans the defaults never pick (other H splits, 128-token expand
-    tiles, other column runs), selected through the library's tuning
-    overrides, still give the oracle's result; with integer inputs, its exact
-    bits."""
-    _announce(f"plan {env} {dtype} T={T} H={H} r={r} L={L} slices={slices} integer={integer}")
+    tiles, other column runs, other per-token column blocks), selected through
+    the library's tuning overrides, still give the oracle's result; with
+    integer inputs, its exact bits."""
+    _announce(f"plan {env} {path} {dtype} T={T} H={H} r={r} L={L} slices={slices} integer={integer}")
     for k, val in env.items():
         monkeypatch.setenv(k, val)
-    force_path(lsb.PATH_SGMV)
+    force_path(lsb.PATH_SGMV if path == "sgmv" else lsb.PATH_BGMV)
     w = W.make("plan", dtype, T, H, r, L, slices, seed=T + r + (7 if integer else 0), seq_len=(1, 40),
                neg_frac=0.1, integer=integer)
     dw = DeviceWorkload(w)
