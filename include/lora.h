@@ -155,8 +155,10 @@ int lora_expand_slice(const float *v, int64_t ldv, int64_t v_slice_stride,
 
 /* Kernel path (punica issue: BGMV, one adapter per input, is a strict subset
  * of SGMV, segments of inputs sharing an adapter; both compute the same
- * result).  0 = automatic: with r <= 16, shrink and expand of at most 512
- * tokens take the per-token (BGMV) kernels, everything else the segment-tile
+ * result).  0 = automatic: batches of at most 512 tokens may take the
+ * per-token (BGMV) kernels -- a shrink when a cost fitted to measured times of
+ * both families (from T, H and r) favours it, an expand when r <= 16 and
+ * T n <= 4M or r <= 32 and T n <= 1M -- everything else the segment-tile
  * (SGMV) kernels; 1 = always per-token (r <= 64, else LORA_ERR_UNSUPPORTED);
  * 2 = always segment tiles.  Process-wide, meant for tests and measurement.
  * Returns the previous mode, or LORA_ERR_INVALID_ARG for an unknown mode. */

@@ -2,17 +2,19 @@
 //
 // The punica issue describes BGMV as each input using its own model, with the
 // speed-up coming from spreading many small products over many compute units.
-// Here one workgroup takes one token at a time, in token order.  These kernels
+// Here a workgroup takes one token (with a small batch, one block of its ranks
+// or of its output columns) at a time, in token order.  These kernels
 // read only token_lora: for a small batch, the sorted metadata would add
 // dependent round trips before the first weight load, and every adapter of the
 // batch fits in L2 anyway.  Rows that do not depend on the adapter (x, y, v)
 // are loaded before the adapter id is needed.  The whole H-sum of a token
 // stays inside its workgroup, so no partial sums leave it.
 //
-// shrink: lane i of the workgroup owns elements 8 (i + 256 k) .. +8 of H (each
-//   wave instruction reads 1 KB of one row); v_dot2 (two 16-bit products into
-//   fp32) accumulates x . A_l[j] for each j; a transposing wave reduction and
-//   an LDS step across the four waves add them up.
+// shrink: a workgroup takes one token and a block of up to 16 ranks; lane i
+//   owns elements 8 (i + 256 k) .. +8 of H (each wave instruction reads 1 KB
+//   of one row); v_dot2 (two 16-bit products into fp32) accumulates
+//   x . A_l[j] for each j; a transposing wave reduction and an LDS step across
+//   the four waves add them up.
 // expand: the token's v is split into hi + lo 16-bit parts; each output
 //   column is the balanced pairwise sum of per-8-rank group dot products (see
 //   group_dot), rounded once when added to y.  The aligned kernel for
@@ -37,6 +39,7 @@ struct BgShrinkArgs {
   int32_t r;
   float* v;
   int64_t ldv;
+  int32_t jb;  // rank blocks per token
 };
 
 struct BgExpandArgs {
@@ -74,18 +77,24 @@ __device__ __forceinline__ int token_adapter(const SegView& seg, int t) {
   return (l >= 0 && l < seg.L) ? l : -1;
 }
 
-// RT = rows of A handled (r <= RT).  Lane i owns elements 8 (i + 256 k) .. +8
-// of H; up to two blocks of 2048 elements are in flight per trip.
+// Work item = (token, block of RT ranks): a small batch is spread over
+// T ceil(r / RT) workgroups, each of which reads the token's x row (again, from
+// L2, for every block after the first) and RT rows of A.  Lane i owns elements
+// 8 (i + 256 k) .. +8 of H; UNR blocks of 2048 elements are in flight per trip,
+// more when RT is small.
 template <int DT, bool VEC, int RT>
 __global__ __launch_bounds__(kBgThreads) void bgmv_shrink_kernel(BgShrinkArgs a) {
   constexpr int BLK = kBgThreads * 8;
-  constexpr int UNR = RT <= 16 ? 2 : 1;  // blocks per trip (register bound)
+  constexpr int UNR = RT <= 4 ? 8 : RT <= 8 ? 4 : 2;  // blocks per trip (register bound)
   __shared__ float s_red[kBgThreads / kWave][RT];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
+  const int items = a.seg.T * a.jb;
 
-  for (int t = blockIdx.x; t < a.seg.T; t += gridDim.x) {
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int t = it / a.jb;
+    const int j0 = (it - t * a.jb) * RT;
     const uint16_t* xrow = a.x + (int64_t)t * a.ldx;
     float acc[RT];
 #pragma unroll
@@ -104,8 +113,8 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_shrink_kernel(BgShrinkArgs a)
         const uint16_t* Al = a.A + (int64_t)l * a.r * a.H;
 #pragma unroll
         for (int j = 0; j < RT; ++j) {
-          // Rows j >= r read row 0 and are never stored.
-          const uint16_t* arow = Al + (int64_t)(j < a.r ? j : 0) * a.H;
+          // Rows j0 + j >= r read row 0 and are never stored.
+          const uint16_t* arow = Al + (int64_t)(j0 + j < a.r ? j0 + j : 0) * a.H;
           float s = acc[j];
 #pragma unroll
           for (int u = 0; u < UNR; ++u) {
@@ -128,22 +137,22 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_shrink_kernel(BgShrinkArgs a)
           const float xf = to_f32<DT>(xrow[h]);
 #pragma unroll
           for (int j = 0; j < RT; ++j)
-            if (j < a.r) acc[j] += xf * to_f32<DT>(Al[(int64_t)j * a.H + h]);
+            if (j0 + j < a.r) acc[j] += xf * to_f32<DT>(Al[(int64_t)(j0 + j) * a.H + h]);
         }
       }
     }
     if (l < 0) continue;  // uniform: no adapter, v row left as it is
     // Transposing wave reduction: lane i ends with the wave's total of rank
-    // i >> (6 - log2 RT); one lane of each group writes it.
+    // j0 + (i >> (6 - log2 RT)); one lane of each group writes it.
     wave_transpose_sum<RT>(acc);
     constexpr int kShift = 6 - log2_of<RT>();
     if ((lane & ((1 << kShift) - 1)) == 0) s_red[wave][lane >> kShift] = acc[0];
     __syncthreads();
-    if (tid < a.r && tid < RT) {
+    if (tid < RT && j0 + tid < a.r) {
       float s = 0.f;
 #pragma unroll
       for (int w = 0; w < kBgThreads / kWave; ++w) s += s_red[w][tid];
-      a.v[(int64_t)t * a.ldv + tid] = s;
+      a.v[(int64_t)t * a.ldv + j0 + tid] = s;
     }
     __syncthreads();
   }
@@ -406,18 +415,35 @@ int bg_grid(int32_t T) {
 
 }  // namespace
 
+int bgmv_shrink_ranks(int64_t T, int32_t r) {
+  // Measured on MI355X (4 adapters, H = 1024 .. 16384): the best choice is
+  // the largest block that still gives 256 workgroups; fewer ranks per
+  // workgroup re-read x from L2 more often for no gain in parallelism.
+  int rt = 16;
+  while (rt > 4 && (rt / 2 >= r || T * ((r + rt - 1) / rt) < 256)) rt /= 2;
+  if (const char* e = getenv("LORA_BGMV_SHRINK_RT")) {
+    const long f = atol(e);
+    if (f == 4 || f == 8 || f == 16) rt = (int)f;
+  }
+  return rt;
+}
+
 hipError_t launch_bgmv_shrink(const SegView& seg, const uint16_t* x, int64_t ldx, const uint16_t* A,
                               int32_t H, int32_t r, float* v, int64_t ldv, int dtype, bool vec,
                               hipStream_t s) {
-  BgShrinkArgs a{seg, x, ldx, A, H, r, v, ldv};
-  const int grid = bg_grid(seg.T);
+  BgShrinkArgs a{seg, x, ldx, A, H, r, v, ldv, 1};
+  const int64_t T = seg.T > 0 ? seg.T : 1;
+  const int rt = bgmv_shrink_ranks(T, r);
+  a.jb = (r + rt - 1) / rt;
+  int64_t grid = T * a.jb;
+  if (grid > 8192) grid = 8192;
 #define LORA_BG_SHRINK(DT_, VEC_)                                                                     \
-  if (r <= 16)                                                                                       \
+  if (rt == 16)                                                                                      \
     hipLaunchKernelGGL((bgmv_shrink_kernel<DT_, VEC_, 16>), dim3(grid), dim3(kBgThreads), 0, s, a);  \
-  else if (r <= 32)                                                                                  \
-    hipLaunchKernelGGL((bgmv_shrink_kernel<DT_, VEC_, 32>), dim3(grid), dim3(kBgThreads), 0, s, a);  \
+  else if (rt == 8)                                                                                  \
+    hipLaunchKernelGGL((bgmv_shrink_kernel<DT_, VEC_, 8>), dim3(grid), dim3(kBgThreads), 0, s, a);   \
   else                                                                                               \
-    hipLaunchKernelGGL((bgmv_shrink_kernel<DT_, VEC_, 64>), dim3(grid), dim3(kBgThreads), 0, s, a);
+    hipLaunchKernelGGL((bgmv_shrink_kernel<DT_, VEC_, 4>), dim3(grid), dim3(kBgThreads), 0, s, a);
   if (dtype == 0) {
     if (vec) { LORA_BG_SHRINK(0, true) } else { LORA_BG_SHRINK(0, false) }
   } else {
@@ -443,8 +469,9 @@ hipError_t launch_bgmv_expand(const SegView& seg, const float* v, int64_t ldv, i
   a.add = add;
   if (vec && (r == 8 || r == 16 || r == 32 || r == 64)) {
     // Rounds of 512 columns in the widest slice, and workgroups per token
-    // that give each wave RPI rounds of it.  Two rounds per wave keep more
-    // bytes in flight; one round doubles the workgroups of a small batch.
+    // that give each wave RPI rounds of it.  One round per wave (twice the
+    // workgroups of two) measured faster on 16- and 256-token batches; two
+    // rounds stay selectable for r <= 16.
     constexpr int nw = kBgThreads / kWave;
     int64_t rounds = 1;
     for (int q = 0; q < num_slices; ++q) {
@@ -452,8 +479,7 @@ hipError_t launch_bgmv_expand(const SegView& seg, const float* v, int64_t ldv, i
       rounds = rq > rounds ? rq : rounds;
     }
     const int64_t T = seg.T > 0 ? seg.T : 1;
-    int rpi = r <= 16 ? 2 : 1;
-    if (rpi == 2 && T * ((rounds + 2 * nw - 1) / (2 * nw)) < 256) rpi = 1;
+    int rpi = 1;
     if (const char* e = getenv("LORA_BGMV_RPI")) {
       const long f = atol(e);
       if (f == 1 || (f == 2 && r <= 16)) rpi = (int)f;

@@ -64,26 +64,41 @@ int check_rank(int32_t r, const char* fn) {
 // Kernel path: 0 = automatic, 1 = per-token (BGMV), 2 = segment tiles (SGMV).
 std::atomic<int> g_path{0};
 
-// Automatic choice, from timings of both kernel families on decode batches
-// (H = 4096, 4 adapters, MI355X): the per-token shrink wins up to about 512
-// tokens at rank 16 -- each token gets a workgroup of its own, while tiles
-// would need the H-sum split across workgroups and a second launch -- but the
-// per-token expand only for the smallest batches, because there a 64-token
-// tile shares one staged weight block and the per-token kernel re-reads it.
-// Larger ranks favour the tiles for both ops.
-constexpr int32_t kBgmvShrinkMaxTokens = 512;
-constexpr int32_t kBgmvExpandMaxTokens = 512;
-constexpr int32_t kBgmvAutoMaxRank = 16;
-
+// Automatic choice between the kernel families, from timings of both on
+// decode-sized batches (T = 16 .. 512, H = 4096 and 16384, r = 16 .. 64, 4
+// adapters, MI355X).
+//
+// Shrink: the per-token kernel needs one launch and no partial sums, but
+// re-reads the adapter's A (and, with several rank blocks, x) from L2 for
+// every token; the tiles read A once per 64-token tile but split the H-sum
+// over workgroups and add a second launch.  Fitted costs (microseconds):
+//   per-token  3 + (bytes read by its workgroups) / 22e6
+//   tiles      7 + H / 1600 + T H / 1.6e6
+// and the cheaper one is taken (at most 512 tokens for the per-token kernel).
+//
+// Expand: the per-token kernel streams a token's whole B_l, so it wins only
+// while the batch is small and the rank low (r <= 16 up to T n = 4M output
+// elements, r <= 32 up to 1M); a 64-token tile shares one staged weight block.
 enum class Op { kShrink, kExpand };
 
-bool use_bgmv(Op op, int32_t T, int32_t r) {
+bool use_bgmv(Op op, int32_t T, int32_t r, int64_t width, bool vec) {
   const int mode = g_path.load(std::memory_order_relaxed);
   if (r > lora::kBgmvMaxRank) return false;
   if (mode == 1) return true;
   if (mode == 2) return false;
-  if (r > kBgmvAutoMaxRank) return false;
-  return T <= (op == Op::kShrink ? kBgmvShrinkMaxTokens : kBgmvExpandMaxTokens);
+  if (T > 512) return false;
+  if (op == Op::kShrink) {
+    const int rt = lora::bgmv_shrink_ranks(T, r);
+    const double bytes = (double)T * ((r + rt - 1) / rt) * (rt + 1) * (double)width * 2.0;
+    const double t_token = 3.0 + bytes / 22e6;
+    const double t_tile = 7.0 + (double)width / 1600.0 + (double)T * (double)width / 1.6e6;
+    return t_token < t_tile;
+  }
+  if (!vec) return r <= 16;
+  const int64_t elems = (int64_t)T * width;
+  if (r <= 16) return elems <= ((int64_t)4 << 20);
+  if (r <= 32) return elems <= ((int64_t)1 << 20);
+  return false;
 }
 
 lora::SegView view(const lora_segments* seg) {
@@ -134,7 +149,7 @@ int lora_shrink(const void* x, int64_t ldx, const void* A, int32_t H, int32_t r,
     return fail(LORA_ERR_UNSUPPORTED, "%s: the per-token path takes r <= %d", fn, lora::kBgmvMaxRank);
   const bool vec = (H % 8 == 0) && (ldx % 8 == 0) && aligned16(x) && aligned16(A) &&
                    (ldv % 4 == 0) && aligned16(v);
-  if (use_bgmv(Op::kShrink, T, r)) {
+  if (use_bgmv(Op::kShrink, T, r, H, vec)) {
     hipError_t err = lora::launch_bgmv_shrink(view(seg), static_cast<const uint16_t*>(x), ldx,
                                               static_cast<const uint16_t*>(A), H, r, v, ldv, dtype,
                                               vec, static_cast<hipStream_t>(stream));
@@ -199,7 +214,9 @@ int lora_expand_slice(const float* v, int64_t ldv, int64_t v_slice_stride, const
     vec = vec && aligned16(B[s]) && (col_off[s] % 8 == 0) && (n_s[s] % 8 == 0);
   if (g_path.load(std::memory_order_relaxed) == 1 && r > lora::kBgmvMaxRank)
     return fail(LORA_ERR_UNSUPPORTED, "%s: the per-token path takes r <= %d", fn, lora::kBgmvMaxRank);
-  if (use_bgmv(Op::kExpand, T, r)) {
+  int64_t ncols = 0;
+  for (int s = 0; s < num_slices; ++s) ncols += n_s[s];
+  if (use_bgmv(Op::kExpand, T, r, ncols, vec)) {
     hipError_t err = lora::launch_bgmv_expand(view(seg), v, ldv, v_slice_stride, desc, num_slices, r,
                                               static_cast<uint16_t*>(y), ldy, add_inputs ? 1 : 0,
                                               dtype, vec, static_cast<hipStream_t>(stream));

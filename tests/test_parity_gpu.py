@@ -472,7 +472,12 @@ PLAN_VARIANTS = [
     ({"LORA_BGMV_RPI": "1", "LORA_BGMV_CB": "1"}, "bgmv", "bf16", 37, 1024, 16, 4, [[3072, 1024, 1024]]),
     ({"LORA_BGMV_CB": "2"}, "bgmv", "bf16", 5, 1024, 32, 3, [[8192]]),
     ({}, "bgmv", "f16", 3, 1024, 64, 2, [[16384, 512]]),
-    ({}, "bgmv", "bf16", 600, 1024, 16, 5, [[14336, 14336]]),
+    ({"LORA_BGMV_RPI": "2"}, "bgmv", "bf16", 600, 1024, 16, 5, [[14336, 14336]]),
+    # per-token shrink: ranks per workgroup
+    ({"LORA_BGMV_SHRINK_RT": "4"}, "bgmv", "f16", 40, 2048, 16, 3, [[1024]]),
+    ({"LORA_BGMV_SHRINK_RT": "8"}, "bgmv", "bf16", 300, 1024, 40, 5, [[512]]),
+    ({"LORA_BGMV_SHRINK_RT": "16"}, "bgmv", "f16", 7, 4096, 64, 3, [[512]]),
+    ({}, "bgmv", "bf16", 11, 1000, 24, 3, [[1000]]),
 ]
 
 
