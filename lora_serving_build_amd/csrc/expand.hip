@@ -395,11 +395,15 @@ hipError_t launch_expand(const SegView& seg, const float* v, int64_t ldv, int64_
   const int64_t mt_max = seg.T > 0 ? (seg.T + tt - 1) / tt + (seg.L < seg.T ? seg.L : seg.T) : 0;
   int64_t chunks = 0;
   for (int q = 0; q < num_slices; ++q) chunks += (slices[q].n + kExpandCols - 1) / kExpandCols;
-  // Chunks per run: long runs amortise an item's set-up and keep each y row
-  // streaming, but leave a few items per resident workgroup.
+  // Chunks per run: long runs amortise an item's set-up (its token list, v
+  // and the first y and weights, about two memory trips) and keep each y row
+  // streaming, but leave a few items per resident workgroup.  2 to 8 chunks,
+  // about 4096 items: measured best on the 2048-token, mixed-rank and
+  // 8192-token workloads (a run of one chunk spends about two thirds of its
+  // time in the set-up).
   int64_t cpr = mt_max * chunks / 4096;
-  if (cpr > 16) cpr = 16;
-  if (cpr < 1) cpr = 1;
+  if (cpr > 8) cpr = 8;
+  if (cpr < 2) cpr = 2;
   if (const char* e = getenv("LORA_EXPAND_CPR")) {
     const long f = atol(e);
     if (f >= 1) cpr = f;
