@@ -249,12 +249,23 @@ constexpr int log2_of() {
   return N <= 1 ? 0 : 1 + log2_of<N / 2>();
 }
 
-// XCD-aware renumbering: workgroups are dealt round-robin to the 8 XCDs, so
-// for a grid that is a multiple of 8 this maps consecutive logical ids onto
-// one XCD (and its L2).
-__device__ __forceinline__ int xcd_logical_id(int wg, int grid) {
-  if ((grid & 7) != 0) return wg;
-  return (wg & 7) * (grid >> 3) + (wg >> 3);
+// Work items of a persistent grid, dealt to the 8 XCDs in contiguous,
+// balanced blocks.  Workgroups are dispatched round-robin over the XCDs, so
+// XCD x runs workgroups x, x + 8, ...; it takes items [x per, (x + 1) per)
+// with per = ceil(n_items / 8).  Consecutive items then share one L2, and
+// every XCD gets an equal share even when the grid, sized on the host from an
+// upper bound on the items, has more workgroups than there are items.  A grid
+// that is not a multiple of 8 walks the items in plain order.
+struct XcdItems {
+  int first, stride, end;
+};
+
+__device__ __forceinline__ XcdItems xcd_items(int wg, int grid, int n_items) {
+  if ((grid & 7) != 0) return XcdItems{wg, grid, n_items};
+  const int per = (n_items + 7) >> 3;
+  const int begin = (wg & 7) * per;
+  const int end = min(begin + per, n_items);
+  return XcdItems{begin + (wg >> 3), grid >> 3, end};
 }
 
 }  // namespace lora

@@ -98,7 +98,8 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
   const int n_items = tiles * a.ks;
   const int grid = gridDim.x;
 
-  for (int item = xcd_logical_id(blockIdx.x, grid); item < n_items; item += grid) {
+  const XcdItems mine = xcd_items(blockIdx.x, grid, n_items);
+  for (int item = mine.first; item < mine.end; item += mine.stride) {
     // Consecutive items share the chunk of H and walk the tiles of a segment,
     // so neighbouring workgroups of an XCD read the same A_l block.
     const int ksi = item / tiles;
