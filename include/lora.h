@@ -92,6 +92,13 @@ typedef struct lora_segments {
   int32_t *seg_lora;           /* [L]                                           */
   int32_t *seg_start;          /* [L + 1]                                       */
   int32_t *counts;             /* [4]                                           */
+  const int32_t *lora_rank;    /* [L] optional (NULL = every adapter has rank r):
+                                * live rank of each adapter, read by the segment
+                                * (SGMV) kernels, which then skip A rows and B rank
+                                * pieces at or beyond it; those must hold zeros
+                                * (the issue's rank padding), since the per-token
+                                * kernels read the padded weights as they are.
+                                * Values are clamped to [0, r].                   */
 } lora_segments;
 
 /* Builds the segment metadata of seg->token_lora into the other four

@@ -49,6 +49,7 @@ class _CSegments(ctypes.Structure):
         ("seg_lora", ctypes.c_void_p),
         ("seg_start", ctypes.c_void_p),
         ("counts", ctypes.c_void_p),
+        ("lora_rank", ctypes.c_void_p),
     ]
 
 
@@ -129,9 +130,12 @@ class Segments:
     """Segment metadata buffers of one batch (device tensors) and the C
     struct that points at them."""
 
-    def __init__(self, token_lora: torch.Tensor, num_loras: int):
+    def __init__(self, token_lora: torch.Tensor, num_loras: int, lora_rank: torch.Tensor | None = None):
         if token_lora.dtype != torch.int32 or token_lora.dim() != 1 or not token_lora.is_cuda:
             raise ValueError("token_lora must be a 1-D int32 CUDA tensor")
+        if lora_rank is not None and (lora_rank.dtype != torch.int32 or lora_rank.shape != (int(num_loras),)
+                                      or not lora_rank.is_cuda or not lora_rank.is_contiguous()):
+            raise ValueError("lora_rank must be a contiguous int32 CUDA tensor of num_loras entries")
         token_lora = token_lora.contiguous()
         dev = token_lora.device
         T = token_lora.shape[0]
@@ -141,9 +145,10 @@ class Segments:
         self.seg_lora = torch.empty(self.num_loras, dtype=torch.int32, device=dev)
         self.seg_start = torch.empty(self.num_loras + 1, dtype=torch.int32, device=dev)
         self.counts = torch.empty(4, dtype=torch.int32, device=dev)
+        self.lora_rank = lora_rank
         self.c = _CSegments(T, self.num_loras, token_lora.data_ptr(), self.sorted_token.data_ptr(),
                             self.seg_lora.data_ptr(), self.seg_start.data_ptr(),
-                            self.counts.data_ptr())
+                            self.counts.data_ptr(), lora_rank.data_ptr() if lora_rank is not None else None)
 
     @property
     def num_tokens(self) -> int:
@@ -158,10 +163,11 @@ class Segments:
 
 
 def lora_build_segments(token_lora: torch.Tensor, num_loras: int,
-                        seg: Segments | None = None) -> Segments:
-    """Groups the batch's tokens by adapter id (see include/lora.h)."""
+                        seg: Segments | None = None, lora_rank: torch.Tensor | None = None) -> Segments:
+    """Groups the batch's tokens by adapter id (see include/lora.h).  lora_rank
+    (optional, [L] int32): live rank of each adapter, for the segment kernels."""
     if seg is None:
-        seg = Segments(token_lora, num_loras)
+        seg = Segments(token_lora, num_loras, lora_rank)
     _check(lib().lora_build_segments(seg.ref(), _stream(seg.device)))
     return seg
 

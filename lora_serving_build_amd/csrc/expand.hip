@@ -53,8 +53,8 @@ struct ExpandLds {
   static constexpr int BP = RK + 8;              // 16-bit elements per LDS weight row
   static constexpr int NB = NKS <= 4 ? 2 : 1;    // weight buffers
   static constexpr size_t weight_bytes = (size_t)NB * kExpandCols * BP * 2;
-  // weights, then the tile table (3 (L + 1) ints) and scan scratch
-  static size_t bytes(int L) { return weight_bytes + 4 * (3 * ((size_t)L + 1) + 8); }
+  // weights, then the tile table and scan scratch
+  static size_t bytes(int L) { return weight_bytes + 4 * ((size_t)tile_table_ints(L) + 8); }
 };
 
 // Column offset (inside a 32-column pair of op tiles) of the 8 columns a lane
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* s_b = reinterpret_cast<uint16_t*>(smem);
   int32_t* s_table = reinterpret_cast<int32_t*>(smem + Lds::weight_bytes);
-  int32_t* s_scan = s_table + 3 * (a.seg.L + 1);
+  int32_t* s_scan = s_table + tile_table_ints(a.seg.L);
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
   const int g = lane >> 4;  // lane group
   const int pc = pair_col(g);
 
-  const TileTable table = build_tile_table<kExpandThreads>(a.seg, TT, s_table, s_scan);
+  const TileTable table = build_tile_table<kExpandThreads>(a.seg, TT, a.r, s_table, s_scan);
   const int mtiles = table.tiles;
   const int nruns = a.run_start[a.num_slices];
   const int n_items = mtiles * nruns;
@@ -110,10 +110,15 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
     const bool ok = tile_range_lds(table, a.seg.T, a.seg.L, TT, mt, &p0, &p_end, &l);
     const uint16_t* Bl = a.slices[q].B + (int64_t)l * nq * a.r;
     uint16_t* ybase = a.y + a.slices[q].col_off;
+    // The adapter's live rank: weight pieces and v groups at or beyond it
+    // are zero and are not read (their pieces read the row's first one,
+    // which is loaded anyway), and their matrix ops are skipped.
+    const int rank_l = ok ? table.rank[l] : 0;
 
     // Weight chunk loader: piece p = tid + 256 i is row p / PPR, columns
     // 8 (p % PPR) .. +8 of the chunk's B_l^T rows.  Rows past the slice read
-    // the last row (their outputs are dropped); ranks >= r read zero.
+    // the last row (their outputs are dropped); ranks >= the live rank read
+    // zero.
     u32x4 rb[BL];
     auto gload_b = [&](int c) {
 #pragma unroll
@@ -125,19 +130,18 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
         n = n < nq ? n : nq - 1;
         if constexpr (VEC) {
           // r % 8 == 0: a piece is whole or past r.  The load is unconditional
-          // (clamped into the row) so the compiler can count loads in flight
-          // exactly; pieces past r are zeroed only when r < RK, in a uniform
-          // branch.
-          const int cs = col < a.r ? col : a.r - 8;
+          // (pieces at or past the live rank read the row's first piece) so
+          // the compiler can count loads in flight exactly.
+          const int cs = col < rank_l ? col : 0;
           rb[i] = *reinterpret_cast<const u32x4*>(Bl + (int64_t)n * a.r + cs);
         } else {
-          rb[i] = load8_16<false>(Bl + (int64_t)n * a.r + col, a.r - col);
+          rb[i] = load8_16<false>(Bl + (int64_t)n * a.r + col, rank_l - col);
         }
       }
     };
-    // Pieces past r (vector path) are zeroed here, when the chunk is written
-    // to LDS, not next to their loads: a select next to a load would make the
-    // wave wait for it at once.
+    // Pieces at or past the live rank are zeroed here, when the chunk is
+    // written to LDS, not next to their loads: a select next to a load would
+    // make the wave wait for it at once.
     auto swrite_b = [&](int buf) {
 #pragma unroll
       for (int i = 0; i < BL; ++i) {
@@ -145,7 +149,7 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
         const int row = p / PPR;
         const int col = (p - row * PPR) * 8;
         u32x4 w = rb[i];
-        if (VEC && col >= a.r) w = u32x4{0u, 0u, 0u, 0u};
+        if (col >= rank_l) w = u32x4{0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4*>(&s_b[(buf * kExpandCols + row) * BP + col]) = w;
       }
     };
@@ -222,7 +226,7 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
 #pragma unroll
         for (int st = 0; st < NV; ++st) {
           const int rk = kPack ? st * 32 + g * 8 : st * 16 + (g & 1) * 8;
-          const bool keep = tok_ok[b] && (VEC ? rk + 8 <= a.r : true);
+          const bool keep = tok_ok[b] && rk < rank_l && (VEC ? rk + 8 <= a.r : true);
           const float vv[8] = {vraw[b][st][0].x, vraw[b][st][0].y, vraw[b][st][0].z, vraw[b][st][0].w,
                                vraw[b][st][1].x, vraw[b][st][1].y, vraw[b][st][1].z, vraw[b][st][1].w};
           uint32_t h4[4], l4[4];
@@ -286,6 +290,7 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
           if constexpr (kPack) {
 #pragma unroll
             for (int st = 0; st < NKS / 2; ++st) {
+              if (32 * st >= rank_l) continue;  // ranks past the live rank are zero
 #pragma unroll
               for (int qq = 0; qq < NQ / 2; ++qq) {
                 const int row = (h * (NQ / 2) + qq) * 16 + m;

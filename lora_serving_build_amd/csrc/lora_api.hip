@@ -108,6 +108,7 @@ lora::SegView view(const lora_segments* seg) {
   s.seg_lora = seg->seg_lora;
   s.seg_start = seg->seg_start;
   s.counts = seg->counts;
+  s.lora_rank = seg->lora_rank;
   s.T = seg->num_tokens;
   s.L = seg->num_loras;
   return s;

@@ -27,6 +27,7 @@ struct SegView {
   const int32_t* seg_lora;
   const int32_t* seg_start;
   const int32_t* counts;
+  const int32_t* lora_rank;  // [L] live rank per adapter, or nullptr
   int32_t T;
   int32_t L;
 };

@@ -55,8 +55,8 @@ struct ShrinkArgs {
 template <int NJT>
 struct ShrinkLds {
   static constexpr size_t a_bytes = (size_t)2 * 16 * NJT * kSkPitch * 2;
-  // A blocks, then the tile table (3 (L + 1) ints) and scan scratch
-  static size_t bytes(int L) { return a_bytes + 4 * (3 * ((size_t)L + 1) + 8); }
+  // A blocks, then the tile table and scan scratch
+  static size_t bytes(int L) { return a_bytes + 4 * ((size_t)tile_table_ints(L) + 8); }
 };
 
 // Stores four consecutive j values of one row (j0 = first), clipped at r.
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* s_a = reinterpret_cast<uint16_t*>(smem);    // [2][RP * kSkPitch]
   int32_t* s_table = reinterpret_cast<int32_t*>(smem + ShrinkLds<NJT>::a_bytes);
-  int32_t* s_scan = s_table + 3 * (a.seg.L + 1);
+  int32_t* s_scan = s_table + tile_table_ints(a.seg.L);
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
   const int lrow = tid >> 4;
   const int lcol = (tid & 15) * 8;
 
-  const TileTable table = build_tile_table<kShrinkThreads>(a.seg, kSkTile, s_table, s_scan);
+  const TileTable table = build_tile_table<kShrinkThreads>(a.seg, kSkTile, a.r, s_table, s_scan);
   const int tiles = table.tiles;
   const int n_items = tiles * a.ks;
   const int grid = gridDim.x;
@@ -114,14 +114,18 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
     const bool tok_ok = t >= 0;
     const bool wave_live = ok && p0 + wave * 16 < p_end;
     // A missing token reads row 0 (its output column is dropped).  Rows
-    // j >= r of A read row 0 (output rows dropped).
+    // at or beyond the adapter's live rank (and the padding of r to 16 NJT)
+    // read row 0 -- lines this block loads anyway, so they cost no HBM
+    // traffic -- and are zeroed when written to LDS.
     const uint16_t* xrow = a.x + (int64_t)(tok_ok ? t : 0) * a.ldx;
     const uint16_t* Al = a.A + (int64_t)l * a.r * a.H;
+    const int rank_l = ok ? table.rank[l] : 0;
+    const int njt_live = (rank_l + 15) / 16;
     const uint16_t* asrc[AL];
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
       const int j = lrow + 16 * i;
-      asrc[i] = Al + (int64_t)(j < a.r ? j : 0) * a.H;
+      asrc[i] = Al + (int64_t)(j < rank_l ? j : 0) * a.H;
     }
 
     u32x4 ra[AL];
@@ -143,7 +147,7 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
 #pragma unroll
       for (int i = 0; i < AL; ++i) {
         u32x4 w = ra[i];
-        if (!(ok && off < kend)) w = u32x4{0u, 0u, 0u, 0u};
+        if (!(ok && off < kend) || lrow + 16 * i >= rank_l) w = u32x4{0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4*>(&s_a[(buf * RP + lrow + 16 * i) * kSkPitch + lcol]) = w;
       }
     };
@@ -185,8 +189,10 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
           const u32x4 xop = (kb + 32 * kk + 8 * g < kend) ? xcur[kk] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
           for (int jt = 0; jt < NJT; ++jt) {
-            const u32x4 aop = *reinterpret_cast<const u32x4*>(as + jt * 16 * kSkPitch + 32 * kk);
-            acc[jt] = mfma16x16x32<DT>(aop, xop, acc[jt]);
+            if (jt < njt_live) {  // rank tiles past the live rank stay zero
+              const u32x4 aop = *reinterpret_cast<const u32x4*>(as + jt * 16 * kSkPitch + 32 * kk);
+              acc[jt] = mfma16x16x32<DT>(aop, xop, acc[jt]);
+            }
           }
         }
       }

@@ -76,29 +76,39 @@ __device__ __forceinline__ bool tile_range(const SegView& seg, int tile_tokens,
 
 // LDS copy of everything a tile lookup needs, so that mapping a work item to
 // its tokens costs no global round trip: tile_start[0..S], seg_start[0..S],
-// seg_lora[0..S).  Each array holds L + 1 ints.
+// seg_lora[0..S) and rank[0..L) (the live rank of each adapter, r when the
+// metadata gives none).  Each array holds L + 1 ints.
 struct TileTable {
   int32_t* tile_start;
   int32_t* seg_start;
   int32_t* seg_lora;
+  int32_t* rank;
   int S;
   int tiles;
 };
 
+// LDS ints a TileTable of L adapters occupies.
+__host__ __device__ constexpr int64_t tile_table_ints(int64_t L) { return 4 * (L + 1); }
+
 // Fills a TileTable from the metadata (same clamping as build_tile_prefix).
 // Every thread of the block must call it.
 template <int NT>
-__device__ TileTable build_tile_table(const SegView& seg, int tile_tokens, int32_t* lds,
+__device__ TileTable build_tile_table(const SegView& seg, int tile_tokens, int r, int32_t* lds,
                                       int32_t* scratch) {
   TileTable tt;
   tt.tile_start = lds;
   tt.seg_start = lds + seg.L + 1;
   tt.seg_lora = lds + 2 * (seg.L + 1);
+  tt.rank = lds + 3 * (seg.L + 1);
   // All L + 1 entries are copied (they exist whatever S is), so these loads
   // go out together with the load of S instead of one round trip after it.
   int S = seg.counts[0];
   for (int s = threadIdx.x; s <= seg.L; s += NT) tt.seg_start[s] = seg.seg_start[s];
   for (int s = threadIdx.x; s < seg.L; s += NT) tt.seg_lora[s] = seg.seg_lora[s];
+  for (int s = threadIdx.x; s < seg.L; s += NT) {
+    const int k = seg.lora_rank ? seg.lora_rank[s] : r;
+    tt.rank[s] = k < 0 ? 0 : (k > r ? r : k);
+  }
   S = S < 0 ? 0 : (S > seg.L ? seg.L : S);
   __syncthreads();
   const int per = (S + NT - 1) / NT;

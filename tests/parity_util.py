@@ -61,10 +61,13 @@ class DeviceWorkload:
         self.ys = [dev_bits(o.y0, w.dtype).clone() for o in w.outputs]
         self.v = sentinel_v(w.T, w.r, ldv)
 
-    def run(self, add: bool | None = None):
+    def run(self, add: bool | None = None, lora_rank: np.ndarray | None = None):
+        """build -> shrink -> expand of every output; lora_rank (optional):
+        the per-adapter live ranks handed to the segment kernels."""
         w = self.w
         add = w.add if add is None else add
-        seg = lsb.lora_build_segments(self.ids, w.L)
+        rk = torch.from_numpy(np.ascontiguousarray(lora_rank, np.int32)).cuda() if lora_rank is not None else None
+        seg = lsb.lora_build_segments(self.ids, w.L, lora_rank=rk)
         lsb.lora_shrink(self.x, self.A, seg, self.v)
         for o, Bs, y in zip(w.outputs, self.Bs, self.ys):
             if len(o.slices) == 1 and o.slices[0].col_off == 0:

@@ -513,6 +513,44 @@ def test_plan_variants(force_path, monkeypatch, env, path, dtype, T, H, r, L, sl
     check_outside_slices(dw)
 
 
+RANK_CASES = [
+    # (dtype, T, H, r, L, slices, ranks_from, integer)
+    ("bf16", 500, 1024, 128, 16, [[1024, 256, 256], [2048]], [8, 16, 32, 64, 128], False),
+    ("f16", 300, 2048, 64, 7, [[1536]], [8, 24, 40, 64], False),       # ranks off the 16 / 32 grid
+    ("bf16", 200, 512, 32, 5, [[512, 128]], [8, 16, 32], True),
+    ("f16", 130, 1001, 16, 3, [[1001]], [8, 16], False),               # unaligned: element-wise loads
+]
+
+
+@pytest.mark.parametrize("dtype,T,H,r,L,slices,ranks_from,integer", RANK_CASES)
+def test_live_ranks(force_path, dtype, T, H, r, L, slices, ranks_from, integer):
+    """Per-adapter live ranks (zero-padded adapters, the issue's mixed-rank
+    batch): the segment kernels skip the padding and give the same values as
+    without the ranks, within the tolerance of the oracle; ranks above r are
+    clamped to r."""
+    _announce(f"live ranks {dtype} T={T} H={H} r={r} L={L} slices={slices} ranks={ranks_from}")
+    force_path(lsb.PATH_SGMV)
+    w = W.make("ranks", dtype, T, H, r, L, slices, seed=T + r, seq_len=(1, 40), neg_frac=0.1,
+               ranks_from=ranks_from, integer=integer)
+    plain = DeviceWorkload(w)
+    plain.run()
+    ranked = DeviceWorkload(w)
+    ranked.run(lora_rank=w.ranks)
+    rv, ry, ryi = compare_with_oracle(ranked)
+    assert rv <= 1 and ry <= 1 and ryi <= 1
+    check_neg_rows(ranked)
+    check_outside_slices(ranked)
+    act = np.nonzero(w.active)[0]
+    # Skipped steps only drop additions of exact zeros: values agree exactly
+    # (a zero may differ in sign).
+    assert np.array_equal(ranked.v.cpu().numpy()[act], plain.v.cpu().numpy()[act])
+    for y_r, y_p in zip(ranked.ys, plain.ys):
+        assert np.array_equal(decode(host_bits(y_r), w.dtype), decode(host_bits(y_p), w.dtype))
+    big = DeviceWorkload(w)
+    big.run(lora_rank=np.full(L, 10 * r, np.int32))
+    assert np.array_equal(big.v.cpu().numpy()[act], plain.v.cpu().numpy()[act])
+
+
 def test_bgmv_and_sgmv_agree(force_path):
     """The per-token and the segment kernels on the same batch agree with each
     other within the tolerance (punica issue: BGMV is a subset of SGMV)."""
