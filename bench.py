@@ -285,13 +285,19 @@ def summarize_profiles(args):
 SWEEP_POINTS = (  # (kind, tokens, hidden, rank): the micro-benchmark grid, thinned
     [(k, T, H, r) for k in ("bgmv", "sgmv") for T in (16, 256, 2048, 8192)
      for H in (4096, 16384) for r in (16, 64)]
-    + [("sgmv", 65536, 16384, 16)])  # the review thread's bs 8192 x seq 8 example
+    + [("sgmv", 65536, 16384, 16)]   # the review thread's bs 8192 x seq 8 example
+    # one adapter for every token (the TPU PR's unmasked single-adapter case):
+    # torch.mm of the same shapes (hipBLASLt) is timed beside it
+    + [("single", T, H, r) for T in (256, 2048, 8192) for H in (4096, 16384) for r in (16, 64)]
+    # LoRA on the logits layer (TPU PR): expand r -> vocabulary, 128256 columns
+    + [("logits", T, 4096, 16) for T in (16, 256, 2048)])
 
 
 def sweep(args):
     """Shrink and expand alone on the micro-benchmark sweep shapes: 4 adapters,
     ids sorted, one token per sequence (bgmv) or eight (sgmv), expand r -> H
-    with add_inputs.  Ids come from the shared generator; the tensors are drawn
+    with add_inputs; then one adapter for every token beside torch.mm of the
+    same shapes, and the logits layer (expand r -> 128256 columns).  Ids come from the shared generator; the tensors are drawn
     on the GPU (seeded) because host generation of the large points takes
     longer than timing them.  One JSON line per point and op."""
     import torch
@@ -301,10 +307,12 @@ def sweep(args):
     dt = torch.float16
     gen = torch.Generator(device="cuda")
     for kind, T, H, r in SWEEP_POINTS:
-        L = 4
-        ids_w = W.sweep_point(kind, T, 8, 8, L=L)  # same id draw as the full-size point
+        L = 1 if kind == "single" else 4
+        n = 128256 if kind == "logits" else H
+        ids_w = W.sweep_point("bgmv" if kind == "logits" else ("sgmv" if kind == "single" else kind),
+                              T, 8, 8, L=L)  # same id draw as the full-size point
         ids = torch.from_numpy(ids_w.ids).cuda()
-        per_set = (T * H * 2) * 2 + L * r * H * 2 * 2 + T * r * 4
+        per_set = T * H * 2 + T * n * 2 + L * r * H * 2 + L * r * n * 2 + T * r * 4
         P = max(2, min(64, int(math.ceil(args.pool_gib * 2**30 / per_set))))
         gen.manual_seed(T * 131 + H * 7 + r)
         sets = []
@@ -312,8 +320,8 @@ def sweep(args):
             sets.append(dict(
                 x=torch.randn(T, H, generator=gen, device="cuda").to(dt),
                 A=(torch.randn(L, r, H, generator=gen, device="cuda") / math.sqrt(H)).to(dt),
-                B=(torch.randn(L, H, r, generator=gen, device="cuda") / math.sqrt(r)).to(dt),
-                y=torch.randn(T, H, generator=gen, device="cuda").to(dt),
+                B=(torch.randn(L, n, r, generator=gen, device="cuda") / math.sqrt(r)).to(dt),
+                y=torch.randn(T, n, generator=gen, device="cuda").to(dt),
                 v=torch.zeros(T, r, device="cuda"),
                 seg=lsb.lora_build_segments(ids, L)))
         need = lsb.lora_shrink_workspace_bytes(T, L, H, r)
@@ -321,16 +329,46 @@ def sweep(args):
         torch.cuda.synchronize()
         K = min(P, 20) if T * H < 2**27 else 8
         shrink_b = T * H * 2 + L * r * H * 2 + T * r * 4
-        expand_b = T * r * 4 + L * r * H * 2 + 2 * T * H * 2
+        expand_b = T * r * 4 + L * r * n * 2 + 2 * T * n * 2
+        ref = {}
+        if kind == "single":
+            # The same products as one dense GEMM each (fp16 in, fp16 out):
+            # x . A0^T and y + v16 . B0^T, with the transposed weights made
+            # contiguous beforehand.
+            for s in sets:
+                s["At"] = s["A"][0].t().contiguous()
+                s["Bt"] = s["B"][0].t().contiguous()
+                s["v16"] = torch.zeros(T, r, dtype=dt, device="cuda")
+                s["vo"] = torch.empty(T, r, dtype=dt, device="cuda")
+            # The GEMM library does not allow stream capture here, so these are
+            # timed eagerly: K calls over the pool between two events, after
+            # one untimed pass (launch overhead is included).
+            mm = {"shrink": lambda s: torch.mm(s["x"], s["At"], out=s["vo"]),
+                  "expand": lambda s: s["y"].addmm_(s["v16"], s["Bt"])}
+            for op, fn in mm.items():
+                for i in range(K):
+                    fn(sets[i % P])
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for i in range(K):
+                    fn(sets[i % P])
+                e1.record()
+                torch.cuda.synchronize()
+                ref[op] = e0.elapsed_time(e1) / K * 1e3
         for op, fn, nb in (
                 ("shrink", lambda s: lsb.lora_shrink(s["x"], s["A"], s["seg"], s["v"], workspace=ws), shrink_b),
                 ("expand", lambda s: lsb.lora_expand(s["v"], s["B"], s["seg"], s["y"], True), expand_b)):
             us = graph_time(torch, fn, sets, 0, K) / K * 1e3
             gbs = nb / (us * 1e-6) / 1e9
-            print(json.dumps({"sweep": kind, "tokens": T, "hidden": H, "rank": r, "num_loras": L,
-                              "op": op, "us": round(us, 2), "GB_s": round(gbs, 1),
-                              "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                              "algorithmic_MiB": round(nb / 2**20, 2), "pool_sets": P}), flush=True)
+            rec = {"sweep": kind, "tokens": T, "hidden": H, "out_cols": n, "rank": r, "num_loras": L,
+                   "op": op, "us": round(us, 2), "GB_s": round(gbs, 1),
+                   "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                   "algorithmic_MiB": round(nb / 2**20, 2), "pool_sets": P}
+            if op in ref:
+                rec["torch_mm_us_eager"] = round(ref[op], 2)
+            print(json.dumps(rec), flush=True)
         del sets, ws
         torch.cuda.empty_cache()
 

@@ -94,8 +94,7 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
   const int n_items = mtiles * nruns;
   const int grid = gridDim.x;
 
-  const XcdItems mine = xcd_items(blockIdx.x, grid, n_items);
-  for (int item = mine.first; item < mine.end; item += mine.stride) {
+  for (int item = xcd_first_item(blockIdx.x, grid, n_items); item < n_items; item += grid) {
     // Consecutive items walk the token tiles under one run of columns, so
     // the weight run is reused from the L2 of one XCD.
     const int cr = item / mtiles;

@@ -98,8 +98,7 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
   const int n_items = tiles * a.ks;
   const int grid = gridDim.x;
 
-  const XcdItems mine = xcd_items(blockIdx.x, grid, n_items);
-  for (int item = mine.first; item < mine.end; item += mine.stride) {
+  for (int item = xcd_first_item(blockIdx.x, grid, n_items); item < n_items; item += grid) {
     // Consecutive items share the chunk of H and walk the tiles of a segment,
     // so neighbouring workgroups of an XCD read the same A_l block.
     const int ksi = item / tiles;
@@ -116,11 +115,11 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
     // A missing token reads row 0 (its output column is dropped).  Rows
     // at or beyond the adapter's live rank (and the padding of r to 16 NJT)
     // read row 0 -- lines this block loads anyway, so they cost no HBM
-    // traffic -- and are zeroed when written to LDS.
+    // traffic -- and are zeroed when written to LDS.  (Their matrix ops still
+    // run on the zeros: skipping them cost 7% on full-rank batches.)
     const uint16_t* xrow = a.x + (int64_t)(tok_ok ? t : 0) * a.ldx;
     const uint16_t* Al = a.A + (int64_t)l * a.r * a.H;
     const int rank_l = ok ? table.rank[l] : 0;
-    const int njt_live = (rank_l + 15) / 16;
     const uint16_t* asrc[AL];
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
@@ -189,10 +188,8 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
           const u32x4 xop = (kb + 32 * kk + 8 * g < kend) ? xcur[kk] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
           for (int jt = 0; jt < NJT; ++jt) {
-            if (jt < njt_live) {  // rank tiles past the live rank stay zero
-              const u32x4 aop = *reinterpret_cast<const u32x4*>(as + jt * 16 * kSkPitch + 32 * kk);
-              acc[jt] = mfma16x16x32<DT>(aop, xop, acc[jt]);
-            }
+            const u32x4 aop = *reinterpret_cast<const u32x4*>(as + jt * 16 * kSkPitch + 32 * kk);
+            acc[jt] = mfma16x16x32<DT>(aop, xop, acc[jt]);
           }
         }
       }

@@ -551,6 +551,34 @@ def test_live_ranks(force_path, dtype, T, H, r, L, slices, ranks_from, integer):
     assert np.array_equal(big.v.cpu().numpy()[act], plain.v.cpu().numpy()[act])
 
 
+@pytest.mark.parametrize("path", ["auto", "bgmv"])
+def test_logits_vocabulary_expand(force_path, path):
+    """LoRA on the logits layer (TPU PR): expand r -> a 128256-column
+    vocabulary, on both kernel families."""
+    _announce(f"logits expand path={path}")
+    if path == "bgmv":
+        force_path(lsb.PATH_BGMV)
+    w = W.make("logits", "bf16", 48, 512, 16, 4, [[128256]], seed=128, seq_len=(1, 4), neg_frac=0.1)
+    dw = DeviceWorkload(w)
+    dw.run()
+    rv, ry, ryi = compare_with_oracle(dw)
+    assert rv <= 1 and ry <= 1 and ryi <= 1
+    check_neg_rows(dw)
+
+
+def test_single_adapter_batch(force_path):
+    """One adapter for every token (the unmasked single-adapter case): one
+    segment covering the batch, on both kernel families."""
+    _announce("single adapter")
+    w = W.make("single", "f16", 700, 2048, 32, 1, [[3072]], seed=11, seq_len=(1, 30))
+    for mode in (lsb.PATH_BGMV, lsb.PATH_SGMV):
+        force_path(mode)
+        dw = DeviceWorkload(w)
+        dw.run()
+        rv, ry, ryi = compare_with_oracle(dw)
+        assert rv <= 1 and ry <= 1 and ryi <= 1
+
+
 def test_bgmv_and_sgmv_agree(force_path):
     """The per-token and the segment kernels on the same batch agree with each
     other within the tolerance (punica issue: BGMV is a subset of SGMV)."""
