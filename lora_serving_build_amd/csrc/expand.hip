@@ -388,18 +388,21 @@ hipError_t launch_expand(const SegView& seg, const float* v, int64_t ldv, int64_
   a.ldy = ldy;
   a.add = add;
   const int nks = r <= 16 ? 1 : r <= 32 ? 2 : r <= 64 ? 4 : 8;
-  // 64-token tiles measured faster than 128-token ones on the named
-  // workloads; the two-block form (r <= 64) stays selectable for tuning.
-  int tb = 1;
+  int64_t chunks = 0;
+  for (int q = 0; q < num_slices; ++q) chunks += (slices[q].n + kExpandCols - 1) / kExpandCols;
+  // 128-token tiles (two 16-token blocks per wave) halve the weight reads per
+  // y byte but give fewer, larger items.  Measured on MI355X: 3% faster on
+  // the 8192-token layer's gate_up call (57344 tile-chunks), slower when a
+  // call has few items (2048-token prefill: 640).  Taken from 16384
+  // tile-chunks up, for r <= 64.
+  int tb = (nks <= 4 && max_token_tiles(seg.T, seg.L, 2 * kTileTokens) * chunks >= 16384) ? 2 : 1;
   if (const char* e = getenv("LORA_EXPAND_TB")) {
     const long f = atol(e);
     if (f == 1 || f == 2) tb = (int)f;
   }
   if (nks == 8) tb = 1;
   const int64_t tt = (int64_t)kTileTokens * tb;
-  const int64_t mt_max = seg.T > 0 ? (seg.T + tt - 1) / tt + (seg.L < seg.T ? seg.L : seg.T) : 0;
-  int64_t chunks = 0;
-  for (int q = 0; q < num_slices; ++q) chunks += (slices[q].n + kExpandCols - 1) / kExpandCols;
+  const int64_t mt_max = max_token_tiles(seg.T, seg.L, tt);
   // Chunks per run: long runs amortise an item's set-up (its token list, v
   // and the first y and weights, about two memory trips) and keep each y row
   // streaming, but leave a few items per resident workgroup.  2 to 8 chunks,

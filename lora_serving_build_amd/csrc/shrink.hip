@@ -291,7 +291,7 @@ ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r) {
   p.mw = kSkTile / 16;
   p.jg = 1;
   p.kw = 1;
-  const int64_t tiles = T > 0 ? (T + kSkTile - 1) / kSkTile + (L < T ? L : T) : 0;
+  const int64_t tiles = max_token_tiles(T, L, kSkTile);
   p.max_tiles = (int32_t)tiles;
   // Split H across workgroups until there are about four items per CU (the
   // resident limit up to r = 64), keeping at least four blocks per chunk;

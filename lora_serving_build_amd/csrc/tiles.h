@@ -87,6 +87,12 @@ struct TileTable {
   int tiles;
 };
 
+// Tiles of tile_tokens tokens that T tokens over at most L segments can make:
+// one partial tile per segment at most.
+__host__ __device__ inline int64_t max_token_tiles(int64_t T, int64_t L, int64_t tile_tokens) {
+  return T > 0 ? (T + tile_tokens - 1) / tile_tokens + (L < T ? L : T) : 0;
+}
+
 // LDS ints a TileTable of L adapters occupies.
 __host__ __device__ constexpr int64_t tile_table_ints(int64_t L) { return 4 * (L + 1); }
 
