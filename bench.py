@@ -412,6 +412,7 @@ def main():
     ap.add_argument("--pool-gib", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--no-context", action="store_true", help="skip the torch streaming-rate context")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="also run one plain copy of 256 MiB (calibrates FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--summarize-profiles", action="store_true",
@@ -531,6 +532,31 @@ def main():
                 "value": round(live_bytes / (ms_live * 1e-3) / 1e9, 2)}
         log(f"live ranks: {ms_live * 1e3:.2f} us/step ({live['speedup']}x)")
 
+    # Context for the roofline fraction: what plain torch streaming kernels
+    # reach on this GPU (a copy and an in-place add over 512 MiB each, twice
+    # the Infinity Cache), timed eagerly over 10 calls between two events.
+    hbm_context = None
+    if not args.no_context:
+        src = torch.ones((512 << 20) // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        rates = {}
+        for name, fn in (("copy", lambda: dst.copy_(src)), ("rmw", lambda: src.add_(1))):
+            fn()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            rates[name] = round(2 * (512 << 20) * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+        del src, dst
+        torch.cuda.empty_cache()
+        hbm_context = {"copy_GB_s": rates["copy"], "rmw_GB_s": rates["rmw"],
+                       "how": "torch copy_ and in-place add_ over 512 MiB int32, read + write bytes"}
+        log(f"torch streaming context: copy {rates['copy']} GB/s, rmw {rates['rmw']} GB/s")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
@@ -563,6 +589,7 @@ def main():
         "cpu_baseline": cpu,
         "parity_ratio": worst,
         "live_ranks": live,
+        "hbm_context": hbm_context,
     }
     print(json.dumps(out), flush=True)
 
