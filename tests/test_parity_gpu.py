@@ -579,6 +579,31 @@ def test_single_adapter_batch(force_path):
         assert rv <= 1 and ry <= 1 and ryi <= 1
 
 
+MAX_CASES = [
+    # (dtype, T, H, r, L, slices, seq_len, path): the limits of the boundary
+    ("bf16", 3000, 256, 128, 2048, [[256]], (1, 3), "sgmv"),            # max adapters at max rank
+    ("f16", 2500, 512, 64, 2048, [[512]], (1, 3), "bgmv"),              # max adapters, per-token path
+    ("bf16", 600, 512, 32, 9, [[64, 32, 96, 8, 40, 16, 24, 200]], (1, 20), "auto"),  # 8 slices
+]
+
+
+@pytest.mark.parametrize("dtype,T,H,r,L,slices,seq_len,path", MAX_CASES)
+def test_boundary_limits(force_path, dtype, T, H, r, L, slices, seq_len, path):
+    """The largest adapter count (its tile table fills most of the LDS left
+    beside the weights), the largest rank and the most slices the header
+    allows."""
+    _announce(f"limits {dtype} T={T} H={H} r={r} L={L} slices={len(slices[0])} path={path}")
+    if path != "auto":
+        force_path(lsb.PATH_SGMV if path == "sgmv" else lsb.PATH_BGMV)
+    w = W.make("limits", dtype, T, H, r, L, slices, seed=L + r, seq_len=seq_len, neg_frac=0.05)
+    dw = DeviceWorkload(w)
+    dw.run()
+    rv, ry, ryi = compare_with_oracle(dw)
+    assert rv <= 1 and ry <= 1 and ryi <= 1
+    check_neg_rows(dw)
+    check_outside_slices(dw)
+
+
 def test_bgmv_and_sgmv_agree(force_path):
     """The per-token and the segment kernels on the same batch agree with each
     other within the tolerance (punica issue: BGMV is a subset of SGMV)."""
