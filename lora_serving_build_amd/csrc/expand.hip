@@ -18,10 +18,11 @@
 // op tiles 2p and 2p + 1 leaves every lane with 8 consecutive columns of its
 // token (row g: columns 32 p + {0, 16, 8, 24}[g] .. +8), so y is read and
 // written straight from registers, 16 bytes per lane (16 rows x 64 bytes per
-// instruction) -- the bulk of the traffic, with no staging tile.  The next
-// chunk's y is loaded during the current chunk; y is rounded once, to nearest
-// even.  LDS stays small enough for four workgroups per CU, which keeps about
-// 64 KB of y in flight per CU.
+// instruction) -- the bulk of the traffic, with no staging tile.  A chunk's y
+// goes out with the next chunk's weights, before the chunk's matrix ops (the
+// first chunk's with v, in the item's set-up); y is rounded once, to nearest
+// even.  LDS and registers leave room for four workgroups per CU up to
+// r = 32, three at r = 64 and two at r = 128 or with 128-token tiles.
 #include "lora_device.h"
 #include "lora_kernels.h"
 #include "tiles.h"

@@ -130,7 +130,7 @@ int lora_build_segments(const lora_segments* seg, void* stream) {
 size_t lora_shrink_workspace_bytes(int32_t T, int32_t L, int32_t H, int32_t r) {
   if (T <= 0 || L < 1 || H < 1 || r < 1 || r > LORA_MAX_RANK) return 0;
   const lora::ShrinkPlan p = lora::plan_shrink(T, L, H, r);
-  return p.partial_bytes + p.counter_bytes;
+  return p.partial_bytes;
 }
 
 int lora_shrink(const void* x, int64_t ldx, const void* A, int32_t H, int32_t r,
@@ -157,7 +157,7 @@ int lora_shrink(const void* x, int64_t ldx, const void* A, int32_t H, int32_t r,
     return hip_status(err, fn);
   }
   const lora::ShrinkPlan plan = lora::plan_shrink(T, seg->num_loras, H, r);
-  const size_t need = plan.partial_bytes + plan.counter_bytes;
+  const size_t need = plan.partial_bytes;
   if (need > 0) {
     if (!workspace || workspace_bytes < need)
       return fail(LORA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,

@@ -37,15 +37,13 @@ hipError_t launch_build_segments(const int32_t* token_lora, int32_t T, int32_t L
                                  int32_t* seg_start, int32_t* counts, hipStream_t s);
 
 struct ShrinkPlan {
-  int32_t mw, jg, kw;   // waves per workgroup: token groups x rank groups x H slices
-  int32_t jtw;          // 16-row tiles of r per wave (1 or 2)
+  int32_t jtw;          // 16-row tiles of r per wave (1, 2, 4 or 8)
   int32_t rp;           // rank padded to the rank groups
   int32_t ksplit;       // number of H chunks split across workgroups
   int32_t kchunk;       // H elements per chunk (multiple of kShrinkKStep)
   int32_t max_tiles;    // upper bound on token tiles
   int32_t grid;         // persistent workgroups
   size_t partial_bytes; // workspace for per-chunk partial rows (ksplit > 1)
-  size_t counter_bytes; // unused (0)
 };
 
 ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r);

@@ -288,9 +288,6 @@ ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r) {
   const int njt0 = (r + 15) / 16;
   p.jtw = njt0 <= 1 ? 1 : njt0 <= 2 ? 2 : njt0 <= 4 ? 4 : 8;  // rank tiles (template)
   p.rp = 16 * p.jtw;
-  p.mw = kSkTile / 16;
-  p.jg = 1;
-  p.kw = 1;
   const int64_t tiles = max_token_tiles(T, L, kSkTile);
   p.max_tiles = (int32_t)tiles;
   // Split H across workgroups until there are about four items per CU (the
@@ -310,7 +307,6 @@ ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r) {
   p.ksplit = (int32_t)ks;
   p.kchunk = (int32_t)chunk;
   p.partial_bytes = ks > 1 ? (size_t)(ks * (int64_t)T * p.rp * 4) : 0;
-  p.counter_bytes = 0;
   int64_t items = tiles * ks;
   // Persistent workgroups: as many as are resident at once (LDS and register
   // bound: four per CU up to r = 64, two beyond).

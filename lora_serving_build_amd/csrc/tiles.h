@@ -1,46 +1,17 @@
 // Token tiles over segments, shared by the segment (SGMV) kernels.
 //
-// A segment of len tokens is cut into ceil(len / kTileTokens) token tiles.
-// Each workgroup rebuilds the prefix of tile counts over the S segments in LDS
-// (S <= L <= 2048: a few KB read from L2) and maps a tile index to its segment
-// with a binary search.  The host never learns S or the segment lengths, so
-// launch geometry stays independent of the data.
+// A segment of len tokens is cut into ceil(len / tile_tokens) token tiles.
+// Each workgroup copies the segment metadata into an LDS table, rebuilds the
+// prefix of tile counts over the S segments there (S <= L <= 2048: a few KB
+// read from L2) and maps a tile index to its segment with a binary search.
+// The host never learns S or the segment lengths, so launch geometry stays
+// independent of the data.
 #pragma once
 
 #include "lora_device.h"
 #include "lora_kernels.h"
 
 namespace lora {
-
-// Fills tile_start[0..S] (tile_start[S] = total) and returns the number of
-// token tiles of `tile_tokens` tokens.  S is clamped to [0, L] and lengths to
-// >= 0, so malformed metadata can only shrink the work.  Every thread of the
-// block must call it.
-template <int NT>
-__device__ int build_tile_prefix(const SegView& seg, int tile_tokens, int32_t* tile_start,
-                                 int32_t* scratch, int* S_out) {
-  int S = seg.counts[0];
-  S = S < 0 ? 0 : (S > seg.L ? seg.L : S);
-  const int per = (S + NT - 1) / NT;
-  const int lo = min((int)threadIdx.x * per, S);
-  const int hi = min(lo + per, S);
-  int mine = 0;
-  for (int s = lo; s < hi; ++s) {
-    const int len = seg.seg_start[s + 1] - seg.seg_start[s];
-    mine += len > 0 ? (len + tile_tokens - 1) / tile_tokens : 0;
-  }
-  int total;
-  int run = block_exclusive_sum<NT>(mine, scratch, &total);
-  for (int s = lo; s < hi; ++s) {
-    tile_start[s] = run;
-    const int len = seg.seg_start[s + 1] - seg.seg_start[s];
-    run += len > 0 ? (len + tile_tokens - 1) / tile_tokens : 0;
-  }
-  if (threadIdx.x == 0) tile_start[S] = total;
-  __syncthreads();
-  *S_out = S;
-  return total;
-}
 
 // Segment that owns token tile `tile` (tile < tile_start[S]).
 __device__ __forceinline__ int tile_segment(const int32_t* tile_start, int S, int tile) {
@@ -53,25 +24,6 @@ __device__ __forceinline__ int tile_segment(const int32_t* tile_start, int S, in
       hi = mid - 1;
   }
   return lo;
-}
-
-// The token range [p0, p_end) of sorted positions that tile `tile` covers,
-// and its adapter.  Returns false if the metadata is inconsistent (the tile is
-// then skipped rather than read out of bounds).
-__device__ __forceinline__ bool tile_range(const SegView& seg, int tile_tokens,
-                                           const int32_t* tile_start, int S, int tile, int* p0,
-                                           int* p_end, int* lora_id) {
-  const int s = tile_segment(tile_start, S, tile);
-  const int start = seg.seg_start[s];
-  const int end = seg.seg_start[s + 1];
-  const int b = start + (tile - tile_start[s]) * tile_tokens;
-  const int e = min(b + tile_tokens, end);
-  const int l = seg.seg_lora[s];
-  if (b < 0 || e > seg.T || b >= e || l < 0 || l >= seg.L) return false;
-  *p0 = b;
-  *p_end = e;
-  *lora_id = l;
-  return true;
 }
 
 // LDS copy of everything a tile lookup needs, so that mapping a work item to
