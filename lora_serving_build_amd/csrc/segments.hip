@@ -5,8 +5,10 @@
 // contiguous block of tokens [w * span, (w + 1) * span), walked in chunks of
 // 64 (lane i takes token chunk_start + i), and keeps its keys in registers
 // (key = adapter id, or L for "no adapter"):
-//   1. each wave counts its keys into its own LDS row cnt[w][key]: lanes with
-//      equal keys are grouped with ballots and one lane adds the group size;
+//   1. each wave counts its keys into its own LDS row cnt[w][key] -- up to
+//      128 keys, into two registers per lane instead (lane k holds keys k
+//      and k + 64) -- : lanes with equal keys are grouped with ballots and
+//      one lane adds the group size;
 //   2. one block scan over the keys gives every key its start; each row entry
 //      then becomes the first position of that wave's tokens of that key
 //      (start + the key's tokens in earlier waves); segments, tails and the
