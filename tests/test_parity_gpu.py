@@ -604,6 +604,34 @@ def test_boundary_limits(force_path, dtype, T, H, r, L, slices, seq_len, path):
     check_outside_slices(dw)
 
 
+THRESHOLD_CASES = [
+    # (dtype, T, H, r, slices): shapes on both sides of the automatic path
+    # choice (at most 512 tokens for the per-token kernels; the expand's
+    # T n <= 4M at r <= 16 and <= 1M at r <= 32; the shrink's fitted costs)
+    ("f16", 512, 1024, 16, [[8192]]),
+    ("f16", 513, 1024, 16, [[8192]]),
+    ("bf16", 256, 2048, 16, [[16384]]),
+    ("bf16", 256, 2048, 16, [[16392]]),
+    ("f16", 128, 4096, 32, [[8192]]),
+    ("f16", 128, 4096, 32, [[8200]]),
+    ("bf16", 64, 16384, 64, [[1024]]),
+    ("bf16", 300, 8192, 64, [[1024]]),
+]
+
+
+@pytest.mark.parametrize("dtype,T,H,r,slices", THRESHOLD_CASES)
+def test_automatic_path_thresholds(dtype, T, H, r, slices):
+    """The automatic choice between the kernel families gives the oracle's
+    result on both sides of each of its thresholds."""
+    _announce(f"auto path {dtype} T={T} H={H} r={r} n={slices}")
+    w = W.make("auto", dtype, T, H, r, 4, slices, seed=T + H + r, seq_len=1, neg_frac=0.05)
+    dw = DeviceWorkload(w)
+    dw.run()
+    rv, ry, ryi = compare_with_oracle(dw)
+    assert rv <= 1 and ry <= 1 and ryi <= 1
+    check_neg_rows(dw)
+
+
 def test_bgmv_and_sgmv_agree(force_path):
     """The per-token and the segment kernels on the same batch agree with each
     other within the tolerance (punica issue: BGMV is a subset of SGMV)."""
