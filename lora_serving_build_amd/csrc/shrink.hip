@@ -226,25 +226,36 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
 }
 
 // v[t, :r] = sum over the ks chunks of the partial rows, in chunk order.
+// Every load of a row -- the active count, its token, eight partial rows at a
+// time -- goes out before any of them is checked, so a reduction of up to
+// eight chunks is one memory trip; positions past the active tokens (whose
+// partial rows were never written) and ranks past r are dropped at the store.
 template <bool VEC>
 __global__ __launch_bounds__(256) void shrink_reduce_kernel(SegView seg, const float* partial,
                                                             int32_t ks, int32_t rp, int32_t r,
                                                             float* v, int64_t ldv) {
-  int ta = seg.counts[1];
-  ta = ta < 0 ? 0 : (ta > seg.T ? seg.T : ta);
   const int per_row = rp / 4;
-  const int64_t n = (int64_t)ta * per_row;
+  const int64_t n = (int64_t)seg.T * per_row;
   for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < n;
        o += (int64_t)gridDim.x * blockDim.x) {
     const int p = (int)(o / per_row);
     const int j0 = (int)(o - (int64_t)p * per_row) * 4;
-    if (j0 >= r) continue;
+    int ta = seg.counts[1];
     const int t = seg.sorted_token[p];
-    if (t < 0 || t >= seg.T) continue;
     f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int q = 0; q < ks; ++q)
-      sum += *reinterpret_cast<const f32x4*>(partial + ((int64_t)q * seg.T + p) * rp + j0);
-    store4<VEC>(v + (int64_t)t * ldv + j0, j0, r, sum);
+    for (int q0 = 0; q0 < ks; q0 += 8) {
+      f32x4 part[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int q = q0 + u < ks ? q0 + u : ks - 1;
+        part[u] = *reinterpret_cast<const f32x4*>(partial + ((int64_t)q * seg.T + p) * rp + j0);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (q0 + u < ks) sum += part[u];
+    }
+    ta = ta < 0 ? 0 : (ta > seg.T ? seg.T : ta);
+    if (p < ta && j0 < r && t >= 0 && t < seg.T) store4<VEC>(v + (int64_t)t * ldv + j0, j0, r, sum);
   }
 }
 
