@@ -142,14 +142,31 @@ __device__ __forceinline__ void load8_f32(const float* __restrict__ p, int limit
 }
 
 // ---------------------------------------------------------------- scans
-// Inclusive prefix sum across the 64 lanes of a wave.
+// Inclusive prefix sum across the 64 lanes of a wave, in six DPP moves with
+// no LDS round trip: shifts right by 1, 2, 4 and 8 lanes inside each row of
+// 16 build the row sums, then the last lane of row 0 is added into row 1 and
+// that of row 2 into row 3 (row_bcast:15), and lane 31 into rows 2 and 3
+// (row_bcast:31).  A lane whose source lies outside its row, or whose row is
+// masked off, adds the tied old value, 0.
 __device__ __forceinline__ int wave_inclusive_sum(int x) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    int y = __shfl_up(x, d, kWave);
-    if (lane >= d) x += y;
-  }
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
+// Running maximum across the lanes of a wave for values >= 0 (same moves as
+// wave_inclusive_sum; 0 is the identity).  Lane 63 holds the wave maximum.
+__device__ __forceinline__ int wave_inclusive_max(int x) {
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false));
   return x;
 }
 

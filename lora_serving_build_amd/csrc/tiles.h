@@ -48,7 +48,7 @@ __host__ __device__ inline int64_t max_token_tiles(int64_t T, int64_t L, int64_t
 // LDS ints a TileTable of L adapters occupies.
 __host__ __device__ constexpr int64_t tile_table_ints(int64_t L) { return 4 * (L + 1); }
 
-// Fills a TileTable from the metadata (same clamping as build_tile_prefix).
+// Fills a TileTable from the metadata (S clamped to [0, L]).
 // Every thread of the block must call it.
 template <int NT>
 __device__ TileTable build_tile_table(const SegView& seg, int tile_tokens, int r, int32_t* lds,

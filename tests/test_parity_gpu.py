@@ -63,7 +63,12 @@ META_CASES = [(0, 1, "uniform"), (1, 1, "uniform"), (1, 4, "neg"), (7, 3, "unifo
               (64, 4, "uniform"), (257, 4, "neg"), (1000, 64, "bad"), (513, 1, "uniform"),
               (300, 16, "allneg"), (129, 5, "one"), (2048, 200, "bad"), (5000, 2048, "neg"),
               (20000, 7, "uniform"), (3000, 3, "sorted"), (8192, 64, "bad"), (8193, 64, "bad"),
-              (40000, 300, "bad"), (9000, 1500, "bad")]
+              (40000, 300, "bad"), (9000, 1500, "bad"),
+              # key widths at powers of two, every lane of a chunk on its own key,
+              # the register-reload threshold of the 16-wave form, the largest L
+              (256, 63, "uniform"), (256, 64, "cyclic"), (640, 64, "cyclic"), (4096, 1023, "neg"),
+              (4096, 1024, "bad"), (32768, 64, "bad"), (32769, 1024, "neg"), (65536, 2048, "bad"),
+              (1, 2048, "neg"), (100, 2048, "one"), (2049, 2048, "cyclic")]
 
 
 @pytest.mark.parametrize("T,L,kind", META_CASES)
@@ -84,6 +89,8 @@ def test_segments_bit_exact(T, L, kind):
         ids[:] = L - 1
     elif kind == "sorted":
         ids.sort()
+    elif kind == "cyclic":
+        ids = (np.arange(T) % L).astype(np.int32)
     seg = lsb.lora_build_segments(torch.from_numpy(ids).cuda(), L)
     torch.cuda.synchronize()
     got = seg_host(seg)
