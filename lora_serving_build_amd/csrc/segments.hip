@@ -63,7 +63,7 @@ __global__ __launch_bounds__(NW * kWave) void build_segments_kernel(
   // LDS: cnt[NW][L + 1], first counts, then per-wave positions.
   extern __shared__ int32_t cnt[];
   __shared__ int4 s_scan[NW];
-  __shared__ int32_t s_bad[NW], s_none[NW];
+  __shared__ int2 s_wave[NW];  // per wave: ids outside [-1, L), tokens without an adapter
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -112,8 +112,9 @@ __global__ __launch_bounds__(NW * kWave) void build_segments_kernel(
   for (int cb = 0; cb < nch; cb += KR) {
     if (cb > 0) load_keys(cb, true);
     const int cend = min(KR, nch - cb);
-#pragma unroll 1
-    for (int c = 0; c < cend; ++c) {
+#pragma unroll
+    for (int c = 0; c < KR; ++c) {
+      if (c >= cend) break;
       const int key = keys[c];
       const uint64_t live = __ballot(key >= 0);
       if (live == 0) continue;
@@ -123,73 +124,80 @@ __global__ __launch_bounds__(NW * kWave) void build_segments_kernel(
     }
   }
   nbad = __builtin_amdgcn_readlane(wave_inclusive_sum(nbad), kWave - 1);
-  if (lane == 0) {
-    s_bad[wave] = nbad;
-    s_none[wave] = none;
-  }
+  if (lane == 0) s_wave[wave] = make_int2(nbad, none);
   __syncthreads();
 
   // ---- 2. scan over keys: starts, per-wave bases, segments, tails, counts
-  int bad = 0, t_active = T;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    bad += s_bad[w];
-    t_active -= s_none[w];
-  }
-  const int per = (nkeys + (NW * kWave) - 1) / (NW * kWave);
+  // Only the KW waves that own keys take part (one wave up to 64 keys); the
+  // others wait at the barriers, so the scan's instructions are not issued
+  // by every wave of a SIMD.  KW and per are uniform.
+  const int KW = min(NW, (nkeys + kWave - 1) / kWave);
+  const int per = (nkeys + (KW * kWave) - 1) / (KW * kWave);
   const int k_lo = min(tid * per, nkeys);
   const int k_hi = min(k_lo + per, nkeys);
-  int my_tokens = 0, my_segs = 0, my_long = 0;
-  for (int k = k_lo; k < k_hi; ++k) {
-    int c = 0;
+  int my_tokens = 0, my_segs = 0;
+  if (wave < KW) {
+    int my_long = 0;
+    for (int k = k_lo; k < k_hi; ++k) {
+      int c = 0;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) c += cnt[w * nkeys + k];
-    my_tokens += c;
-    if (k < L && c > 0) {
-      ++my_segs;
-      my_long = max(my_long, c);
+      for (int w = 0; w < NW; ++w) c += cnt[w * nkeys + k];  // independent reads, issued together
+      my_tokens += c;
+      if (k < L && c > 0) {
+        ++my_segs;
+        my_long = max(my_long, c);
+      }
     }
+    // Block scan of (tokens, segments) and maximum of the segment lengths.
+    const int inc_t = wave_inclusive_sum(my_tokens);
+    const int inc_s = wave_inclusive_sum(my_segs);
+    const int max_l = wave_inclusive_max(my_long);
+    if (lane == kWave - 1) s_scan[wave] = make_int4(inc_t, inc_s, max_l, 0);
+    my_tokens = inc_t - my_tokens;  // now exclusive, inside the wave
+    my_segs = inc_s - my_segs;
   }
-  // Block scan of (tokens, segments) and maximum of the segment lengths.
-  const int inc_t = wave_inclusive_sum(my_tokens);
-  const int inc_s = wave_inclusive_sum(my_segs);
-  const int max_l = wave_inclusive_max(my_long);
-  if (lane == kWave - 1) s_scan[wave] = make_int4(inc_t, inc_s, max_l, 0);
   __syncthreads();
-  int tok_before = inc_t - my_tokens, seg_before = inc_s - my_segs, S = 0, longest = 0;
+  if (wave < KW) {
+    // Per-wave records are combined across lanes (lane w takes wave w's).
+    const int2 qw = lane < NW ? s_wave[lane] : make_int2(0, 0);
+    const int bad = __builtin_amdgcn_readlane(wave_inclusive_sum(qw.x), kWave - 1);
+    const int t_active = T - __builtin_amdgcn_readlane(wave_inclusive_sum(qw.y), kWave - 1);
+    const int4 q = lane < KW ? s_scan[lane] : make_int4(0, 0, 0, 0);
+    const int qt = wave_inclusive_sum(q.x);
+    const int qs = wave_inclusive_sum(q.y);
+    const int S = __builtin_amdgcn_readlane(qs, kWave - 1);
+    const int longest = __builtin_amdgcn_readlane(wave_inclusive_max(q.z), kWave - 1);
+    // Tokens and segments of the key waves before this one.
+    int tok_before = __builtin_amdgcn_readlane(qt - q.x, wave) + my_tokens;
+    int seg_before = __builtin_amdgcn_readlane(qs - q.y, wave) + my_segs;
+    for (int k = k_lo; k < k_hi; ++k) {
+      // All of the key's row entries are read before any is rewritten, so the
+      // reads go out together instead of one round trip per wave.
+      int cw[NW];
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const int4 q = s_scan[w];
-    if (w < wave) {
-      tok_before += q.x;
-      seg_before += q.y;
-    }
-    S += q.y;
-    longest = max(longest, q.z);
-  }
-  for (int k = k_lo; k < k_hi; ++k) {
-    int b = tok_before;
+      for (int w = 0; w < NW; ++w) cw[w] = cnt[w * nkeys + k];
+      int b = tok_before;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const int c = cnt[w * nkeys + k];
-      cnt[w * nkeys + k] = b;
-      b += c;
+      for (int w = 0; w < NW; ++w) {
+        cnt[w * nkeys + k] = b;
+        b += cw[w];
+      }
+      const int c = b - tok_before;
+      if (k < L && c > 0 && seg_before < L) {
+        seg_lora[seg_before] = k;
+        seg_start[seg_before] = tok_before;
+        ++seg_before;
+      }
+      tok_before = b;
     }
-    const int c = b - tok_before;
-    if (k < L && c > 0 && seg_before < L) {
-      seg_lora[seg_before] = k;
-      seg_start[seg_before] = tok_before;
-      ++seg_before;
+    for (int s = S + tid; s < L; s += (KW * kWave)) seg_lora[s] = -1;
+    for (int s = S + tid; s <= L; s += (KW * kWave)) seg_start[s] = t_active;
+    if (tid == 0) {
+      counts[0] = S;
+      counts[1] = t_active;
+      counts[2] = longest;
+      counts[3] = bad;
     }
-    tok_before = b;
-  }
-  for (int s = S + tid; s < L; s += (NW * kWave)) seg_lora[s] = -1;
-  for (int s = S + tid; s <= L; s += (NW * kWave)) seg_start[s] = t_active;
-  if (tid == 0) {
-    counts[0] = S;
-    counts[1] = t_active;
-    counts[2] = longest;
-    counts[3] = bad;
   }
   __syncthreads();
 
@@ -197,8 +205,9 @@ __global__ __launch_bounds__(NW * kWave) void build_segments_kernel(
   for (int cb = 0; cb < nch; cb += KR) {
     if (!in_regs) load_keys(cb, false);
     const int cend = min(KR, nch - cb);
-#pragma unroll 1
-    for (int c = 0; c < cend; ++c) {
+#pragma unroll
+    for (int c = 0; c < KR; ++c) {
+      if (c >= cend) break;
       const int key = keys[c];
       const uint64_t live = __ballot(key >= 0);
       if (live == 0) continue;
