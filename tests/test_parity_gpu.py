@@ -485,7 +485,7 @@ PLAN_VARIANTS = [
     ({"LORA_BGMV_SHRINK_RT": "8"}, "bgmv", "bf16", 300, 1024, 40, 5, [[512]]),
     ({"LORA_BGMV_SHRINK_RT": "16"}, "bgmv", "f16", 7, 4096, 64, 3, [[512]]),
     ({}, "bgmv", "bf16", 11, 1000, 24, 3, [[1000]]),
-    # per-token shrink over long rows: the two-stage pipeline, ragged ends
+    # per-token shrink over long rows (several trips per rank block), ragged ends
     ({"LORA_BGMV_SHRINK_RT": "16"}, "bgmv", "bf16", 40, 20000, 16, 3, [[512]]),
     ({"LORA_BGMV_SHRINK_RT": "8"}, "bgmv", "f16", 30, 17000, 16, 3, [[512]]),
     ({"LORA_BGMV_SHRINK_RT": "4"}, "bgmv", "bf16", 20, 40000, 16, 2, [[256]]),
