@@ -135,9 +135,9 @@ __global__ __launch_bounds__(NW * kWave) void build_segments_kernel(
   const int per = (nkeys + (KW * kWave) - 1) / (KW * kWave);
   const int k_lo = min(tid * per, nkeys);
   const int k_hi = min(k_lo + per, nkeys);
-  int my_tokens = 0, my_segs = 0;
+  int my_tokens = 0, my_segs = 0, my_long = 0;
+  int wave_segs = 0, wave_long = 0;  // totals of this wave (lane 63)
   if (wave < KW) {
-    int my_long = 0;
     for (int k = k_lo; k < k_hi; ++k) {
       int c = 0;
 #pragma unroll
@@ -152,24 +152,32 @@ __global__ __launch_bounds__(NW * kWave) void build_segments_kernel(
     const int inc_t = wave_inclusive_sum(my_tokens);
     const int inc_s = wave_inclusive_sum(my_segs);
     const int max_l = wave_inclusive_max(my_long);
-    if (lane == kWave - 1) s_scan[wave] = make_int4(inc_t, inc_s, max_l, 0);
+    if (KW > 1 && lane == kWave - 1) s_scan[wave] = make_int4(inc_t, inc_s, max_l, 0);
+    wave_segs = __builtin_amdgcn_readlane(inc_s, kWave - 1);
+    wave_long = __builtin_amdgcn_readlane(max_l, kWave - 1);
     my_tokens = inc_t - my_tokens;  // now exclusive, inside the wave
     my_segs = inc_s - my_segs;
   }
-  __syncthreads();
+  // One key wave (up to 64 keys) needs no exchange between waves.  KW is
+  // uniform, so every wave takes the same side of this barrier.
+  if (KW > 1) __syncthreads();
   if (wave < KW) {
     // Per-wave records are combined across lanes (lane w takes wave w's).
     const int2 qw = lane < NW ? s_wave[lane] : make_int2(0, 0);
     const int bad = __builtin_amdgcn_readlane(wave_inclusive_sum(qw.x), kWave - 1);
     const int t_active = T - __builtin_amdgcn_readlane(wave_inclusive_sum(qw.y), kWave - 1);
-    const int4 q = lane < KW ? s_scan[lane] : make_int4(0, 0, 0, 0);
-    const int qt = wave_inclusive_sum(q.x);
-    const int qs = wave_inclusive_sum(q.y);
-    const int S = __builtin_amdgcn_readlane(qs, kWave - 1);
-    const int longest = __builtin_amdgcn_readlane(wave_inclusive_max(q.z), kWave - 1);
-    // Tokens and segments of the key waves before this one.
-    int tok_before = __builtin_amdgcn_readlane(qt - q.x, wave) + my_tokens;
-    int seg_before = __builtin_amdgcn_readlane(qs - q.y, wave) + my_segs;
+    int S = wave_segs, longest = wave_long;
+    int tok_before = my_tokens, seg_before = my_segs;
+    if (KW > 1) {
+      const int4 q = lane < KW ? s_scan[lane] : make_int4(0, 0, 0, 0);
+      const int qt = wave_inclusive_sum(q.x);
+      const int qs = wave_inclusive_sum(q.y);
+      S = __builtin_amdgcn_readlane(qs, kWave - 1);
+      longest = __builtin_amdgcn_readlane(wave_inclusive_max(q.z), kWave - 1);
+      // Tokens and segments of the key waves before this one.
+      tok_before += __builtin_amdgcn_readlane(qt - q.x, wave);
+      seg_before += __builtin_amdgcn_readlane(qs - q.y, wave);
+    }
     for (int k = k_lo; k < k_hi; ++k) {
       // All of the key's row entries are read before any is rewritten, so the
       // reads go out together instead of one round trip per wave.
