@@ -207,6 +207,49 @@ def op_of(kernel_name):
     return None
 
 
+COUNTER_SET = ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "SQ_INSTS_MFMA",
+               "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+
+
+def summarize_counters(args, name, out_dir):
+    """Per-kernel LDS and matrix-core counters of one --pmc pass (summed over
+    dispatches): the share of LDS cycles lost to bank conflicts, and
+    matrix-core busy cycles per CU and active GPU cycle (256 CUs)."""
+    import csv
+    import collections
+    tot = collections.defaultdict(lambda: collections.defaultdict(float))
+    calls = collections.defaultdict(set)
+    for r in csv.DictReader(open(args.counters)):
+        kn = r["Kernel_Name"]
+        if op_of(kn) is None:
+            continue
+        short = kn.replace("void ", "").replace("lora::(anonymous namespace)::", "").split("(")[0]
+        tot[short][r["Counter_Name"]] += float(r["Counter_Value"])
+        calls[short].add(r.get("Dispatch_Id", r.get("Correlation_Id", "")))
+    lines = [f"# rocprofv3 LDS and matrix-core counters: {name}", "",
+             "command (from the repository root, on one MI355X):",
+             f"  rocprofv3 --pmc {' '.join(COUNTER_SET)} -d <dir> -o run --output-format csv -- "
+             f"python bench.py --config {args.config} --no-cpu-baseline --no-context",
+             "",
+             "Sums over all dispatches of each kernel.  LDS conflict share = SQ_LDS_BANK_CONFLICT / "
+             "SQ_LDS_IDX_ACTIVE (cycles).  Matrix-core busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+             "(GRBM_GUI_ACTIVE x 256 CUs).", "",
+             "| kernel | dispatches | LDS instructions | LDS conflict share | MFMA instructions | "
+             "matrix-core busy |", "|---|---|---|---|---|---|"]
+    for k in sorted(tot):
+        c = tot[k]
+        lds_active = c.get("SQ_LDS_IDX_ACTIVE", 0.0)
+        conflict = c.get("SQ_LDS_BANK_CONFLICT", 0.0) / lds_active if lds_active else 0.0
+        gui = c.get("GRBM_GUI_ACTIVE", 0.0)
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (gui * 256) if gui else 0.0
+        lines.append(f"| {k} | {len(calls[k])} | {c.get('SQ_INSTS_LDS', 0.0):.3g} | {100 * conflict:.2f}% | "
+                     f"{c.get('SQ_INSTS_MFMA', 0.0):.3g} | {100 * busy:.2f}% |")
+    path = os.path.join(out_dir, f"counters_{name}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("wrote", path)
+
+
 def summarize_profiles(args):
     """Turns rocprofv3 CSV output of this script into the short summaries kept
     under profiles/: a kernel-trace table, and per-op HBM traffic from the
@@ -249,6 +292,8 @@ def summarize_profiles(args):
     with open(os.path.join(out_dir, f"trace_{name}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("wrote", os.path.join(out_dir, f"trace_{name}.md"))
+    if args.counters:
+        summarize_counters(args, name, out_dir)
     if not (args.fetch and args.write):
         return
 
@@ -439,6 +484,7 @@ def main():
     ap.add_argument("--trace")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
+    ap.add_argument("--counters", help="CSV of a --pmc pass over the LDS / matrix-core counter set")
     args = ap.parse_args()
     if args.summarize_profiles:
         summarize_profiles(args)

@@ -11,9 +11,8 @@
 //    in two register sets that the loop alternates (no copy waits for a load);
 //  - A_l is shared by the four waves: its block (r rows x 256 B, 16 lanes per
 //    row) is loaded cooperatively one block ahead and written to a
-//    double-buffered LDS tile (row pitch padded to 272 B, which spreads the 16
-//    rows of an operand read over all banks), so A_l is read from L2 once per
-//    64 tokens.
+//    double-buffered LDS tile (row pitch 288 B, see kSkPitch), so A_l is read
+//    from L2 once per 64 tokens.
 // Loads are unconditional (addresses clamped into the chunk): values past the
 // end of the chunk are zeroed where they are used, so the compiler can count
 // the loads in flight exactly.  LDS holds only A and the tile table, which
@@ -34,7 +33,13 @@ namespace {
 constexpr int kShrinkThreads = 256;
 constexpr int kSkTile = 64;              // tokens per tile (4 waves x 16)
 constexpr int kSkKB = kShrinkKStep;      // H elements per block
-constexpr int kSkPitch = kSkKB + 8;      // 16-bit elements per LDS row of A
+// 16-bit elements per LDS row of A.  A 16-byte LDS read is served for 16
+// lanes at a time, lanes 0-7 with 16-23 (and so on); here those are rows 0-7
+// of the operand at two 16-byte columns.  A row stride that is an odd
+// multiple of 8 dwords (mod 64 banks) puts those 16 pieces on distinct banks:
+// 72 dwords.  Measured with SQ_LDS_BANK_CONFLICT on MI355X: 0 % of LDS cycles,
+// against 34-39 % for a 68-dword stride.
+constexpr int kSkPitch = kSkKB + 16;
 constexpr int kSkChunks = kSkKB / 8;     // 16-byte pieces per row and block
 
 struct ShrinkArgs {
