@@ -316,7 +316,11 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_expand_fast_kernel(BgExpandAr
   constexpr int KB = K < 16 ? K : 16;        // loads per batch (register bound)
   constexpr int CPI = kWave / G;             // columns per load instruction
   constexpr int NW = kBgThreads / kWave;
-  __shared__ __align__(16) float s_out[NW][RPI * kRoundCols];
+  // Column c of the staged sums sits at c + 4 (c / 128): each lane reads its
+  // 8 columns at 8 lane, and 16-byte LDS reads serve lanes 0-7 with 16-23,
+  // whose columns lie 128 apart -- the same banks without the 4-float shift.
+  constexpr int kSoRow = kRoundCols + kRoundCols / 32;
+  __shared__ __align__(16) float s_out[NW][RPI * kSoRow];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int part = lane & (G - 1);
@@ -385,7 +389,10 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_expand_fast_kernel(BgExpandAr
               if constexpr (G >= 2) p = p + lane_xor<0>(p, lane);
               if constexpr (G >= 4) p = p + lane_xor<1>(p, lane);
               if constexpr (G >= 8) p = p + lane_xor<2>(p, lane);
-              if (part == 0) so[u * kRoundCols + (kb + k) * CPI + (lane >> LG)] = p;
+              if (part == 0) {
+                const int c = (kb + k) * CPI + (lane >> LG);  // a run of CPI columns in one 128
+                so[u * kSoRow + c + ((c >> 7) << 2)] = p;
+              }
             }
           }
         }
@@ -396,8 +403,9 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_expand_fast_kernel(BgExpandAr
 #pragma unroll
         for (int u = 0; u < RPI; ++u) {
           const int c0 = (R0 + u) * kRoundCols + lane * 8;
-          const f32x4 o0 = *reinterpret_cast<const f32x4*>(so + u * kRoundCols + lane * 8);
-          const f32x4 o1 = *reinterpret_cast<const f32x4*>(so + u * kRoundCols + lane * 8 + 4);
+          const float* sr = so + u * kSoRow + lane * 8 + ((lane >> 4) << 2);
+          const f32x4 o0 = *reinterpret_cast<const f32x4*>(sr);
+          const f32x4 o1 = *reinterpret_cast<const f32x4*>(sr + 4);
           float out[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
           if (c0 < nq) bg_store_cols<DT, true>(yrow, nq, c0, a.add, yv[u], out);
         }
