@@ -34,8 +34,12 @@ namespace {
 constexpr size_t kSegMaxLds = 64 * 1024;  // bytes of per-wave rows a launch may take
 
 // Lanes of the wave whose key equals this lane's, for keys in [0, 2^nbits);
-// `live` is the ballot of the lanes that hold a key at all.
+// `live` is the ballot of the lanes that hold a key at all.  A chunk whose
+// live lanes all hold one key (the common case inside long sequences) is one
+// group, found with one compare.
 __device__ __forceinline__ uint64_t key_group(int key, uint64_t live, int nbits) {
+  const int k0 = __builtin_amdgcn_readlane(key, (int)__builtin_ctzll(live));
+  if (__ballot(key == k0) == live) return live;  // uniform
   uint64_t m = live;
   for (int i = 0; i < nbits; ++i) {
     const bool bit = (key >> i) & 1;
