@@ -534,14 +534,17 @@ RANK_CASES = [
 ]
 
 
+@pytest.mark.parametrize("path", ["sgmv", "bgmv"])
 @pytest.mark.parametrize("dtype,T,H,r,L,slices,ranks_from,integer", RANK_CASES)
-def test_live_ranks(force_path, dtype, T, H, r, L, slices, ranks_from, integer):
+def test_live_ranks(force_path, path, dtype, T, H, r, L, slices, ranks_from, integer):
     """Per-adapter live ranks (zero-padded adapters, the issue's mixed-rank
-    batch): the segment kernels skip the padding and give the same values as
-    without the ranks, within the tolerance of the oracle; ranks above r are
-    clamped to r."""
-    _announce(f"live ranks {dtype} T={T} H={H} r={r} L={L} slices={slices} ranks={ranks_from}")
-    force_path(lsb.PATH_SGMV)
+    batch): the segment kernels skip the padding, the per-token kernels read
+    the zero padding as it is; both give the same values as without the
+    ranks, within the tolerance of the oracle; ranks above r are clamped to r."""
+    if path == "bgmv" and r > 64:
+        pytest.skip("the per-token kernels take r <= 64")
+    _announce(f"live ranks {path} {dtype} T={T} H={H} r={r} L={L} slices={slices} ranks={ranks_from}")
+    force_path(lsb.PATH_SGMV if path == "sgmv" else lsb.PATH_BGMV)
     w = W.make("ranks", dtype, T, H, r, L, slices, seed=T + r, seq_len=(1, 40), neg_frac=0.1,
                ranks_from=ranks_from, integer=integer)
     plain = DeviceWorkload(w)
@@ -561,6 +564,69 @@ def test_live_ranks(force_path, dtype, T, H, r, L, slices, ranks_from, integer):
     big = DeviceWorkload(w)
     big.run(lora_rank=np.full(L, 10 * r, np.int32))
     assert np.array_equal(big.v.cpu().numpy()[act], plain.v.cpu().numpy()[act])
+
+
+GRAPH_CASES = [
+    # dtype, T, H, r, L, slices, seq_len, ranks_from: the per-token decode path;
+    # the tile path with the H split (workspace and reduce kernel); live ranks
+    ("f16", 256, 4096, 16, 4, [[4096]], 1, None),
+    ("bf16", 700, 2048, 32, 7, [[512, 256, 256]], (1, 40), None),
+    ("bf16", 500, 1024, 128, 16, [[1024, 256, 256], [2048]], (1, 40), [8, 16, 32, 64, 128]),
+]
+
+
+@pytest.mark.parametrize("dtype,T,H,r,L,slices,seq_len,ranks_from", GRAPH_CASES)
+def test_graph_replays_match_eager(dtype, T, H, r, L, slices, seq_len, ranks_from):
+    """One step (build, shrink, every expand) captured in a HIP graph and
+    replayed three times, with eager work between the replays (y reset to y0,
+    v and the metadata buffers overwritten): every replay gives the eager
+    step's bits."""
+    _announce(f"graph replays {dtype} T={T} H={H} r={r} L={L} slices={slices}")
+    w = W.make("graph", dtype, T, H, r, L, slices, seed=T + 3 * r, seq_len=seq_len, neg_frac=0.1,
+               ranks_from=ranks_from)
+    rk = None if w.ranks is None else torch.from_numpy(np.ascontiguousarray(w.ranks, np.int32)).cuda()
+    eager = DeviceWorkload(w)
+    seg_e = eager.run(lora_rank=None if rk is None else w.ranks)
+    meta_e = seg_host(seg_e)
+    act = np.nonzero(w.active)[0]
+    v_e = eager.v.cpu().numpy()
+
+    g_w = DeviceWorkload(w)
+    y0 = [y.clone() for y in g_w.ys]
+    v0 = g_w.v.clone()
+    seg = lsb.Segments(g_w.ids, w.L, rk)
+    need = lsb.lora_shrink_workspace_bytes(w.T, w.L, w.H, w.r)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
+
+    def step():
+        lsb.lora_build_segments(g_w.ids, w.L, seg=seg)
+        lsb.lora_shrink(g_w.x, g_w.A, seg, g_w.v, workspace=ws)
+        for o, Bs, y in zip(w.outputs, g_w.Bs, g_w.ys):
+            if len(o.slices) == 1 and o.slices[0].col_off == 0:
+                lsb.lora_expand(g_w.v, Bs[0], seg, y, w.add)
+            else:
+                lsb.lora_expand_slice(g_w.v, Bs, [q.col_off for q in o.slices], seg, y, w.add)
+
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        for y, y_init in zip(g_w.ys, y0):
+            y.copy_(y_init)
+        g_w.v.copy_(v0)
+        seg.sorted_token.fill_(-5)
+        seg.seg_lora.fill_(-5)
+        seg.seg_start.fill_(-5)
+        seg.counts.fill_(-5)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a_, b_ in zip(seg_host(seg), meta_e):
+            assert np.array_equal(a_, b_)
+        assert np.array_equal(g_w.v.cpu().numpy()[act].view(np.uint32), v_e[act].view(np.uint32))
+        for y_g, y_e in zip(g_w.ys, eager.ys):
+            assert np.array_equal(host_bits(y_g), host_bits(y_e))
 
 
 @pytest.mark.parametrize("path", ["auto", "bgmv"])
