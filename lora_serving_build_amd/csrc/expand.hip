@@ -158,12 +158,27 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
         *reinterpret_cast<u32x4*>(&s_b[(buf * kExpandCols + row) * BP + col]) = w;
       }
     };
-    // The first chunk's weights depend only on the adapter: issue them before
-    // the token list arrives.
-    if (ok && c_beg < c_end) gload_b(c_beg);
-
     // Wave w takes tokens [16 TB w, 16 TB (w + 1)) of the tile, block b the
-    // 16 tokens from 16 (TB w + b); every lane reads its own token id.
+    // 16 tokens from 16 (TB w + b); every lane reads its own token id.  The
+    // id loads go out first (unconditionally, at positions clamped into the
+    // batch), then the first chunk's weights, which depend only on the
+    // adapter: loads complete in issue order, so the wait for the ids does not
+    // include the weight block (32 KB per workgroup at r = 128), which stays
+    // in flight behind them.
+    int traw[TB];
+#pragma unroll
+    for (int b = 0; b < TB; ++b) {
+      int pos = p0 + 16 * (TB * wave + b) + m;
+      pos = pos < 0 ? 0 : (pos < a.seg.T ? pos : a.seg.T - 1);
+      traw[b] = a.seg.sorted_token[pos];
+    }
+    // Unconditional (an invalid tile reads adapter 0's clamped rows and drops
+    // them): a load on only some paths would make the compiler's wait for
+    // the ids include it.
+    gload_b(c_beg);
+    // Nothing that uses an id may be scheduled above these loads.
+    __builtin_amdgcn_sched_barrier(0);
+
     bool blk_live[TB], tok_ok[TB];
     int tok[TB];
     uint16_t* yrow[TB];
@@ -171,7 +186,7 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
     for (int b = 0; b < TB; ++b) {
       const int pos = p0 + 16 * (TB * wave + b) + m;
       blk_live[b] = ok && p0 + 16 * (TB * wave + b) < p_end;
-      int t = (ok && pos < p_end) ? a.seg.sorted_token[pos] : -1;
+      int t = (ok && pos < p_end) ? traw[b] : -1;
       t = (t >= 0 && t < a.seg.T) ? t : -1;
       tok[b] = t;
       tok_ok[b] = blk_live[b] && t >= 0;
