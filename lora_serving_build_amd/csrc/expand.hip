@@ -220,6 +220,11 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
     // r, operand 2 p holds hi and 2 p + 1 lo of ranks 32 p .. +32, so one
     // weight operand read from LDS feeds two products.
     u32x4 bop[TB][NKS];
+    // y of the first chunk depends only on the tokens: it goes out right
+    // behind v (a scheduling barrier keeps it there), so the wait for v does
+    // not hold it back and it is in flight through v's conversion and the
+    // first barrier.
+    u32x4 yfirst[TB][NP];
     {
       constexpr int NV = kPack ? NKS / 2 : NKS;  // 8-rank groups per lane
       f32x4 vraw[TB][NV][2];
@@ -241,6 +246,8 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
           }
         }
       }
+      gload_y(c_beg, yfirst);  // unconditional: addresses are clamped, c_beg < c_end
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int b = 0; b < TB; ++b) {
 #pragma unroll
@@ -271,10 +278,6 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
       }
     }
 
-    // y of the first chunk depends only on the tokens: it goes out here,
-    // with v, instead of one barrier later.
-    u32x4 yfirst[TB][NP];
-    if (c_beg < c_end) gload_y(c_beg, yfirst);
     if (ok && c_beg < c_end) swrite_b(0);
     __syncthreads();
     // One chunk: the next chunk's weights and this chunk's y go out first,
