@@ -423,12 +423,16 @@ int bg_grid(int32_t T) {
 
 }  // namespace
 
-int bgmv_shrink_ranks(int64_t T, int32_t r) {
-  // Measured on MI355X (4 adapters, H = 1024 .. 16384): the best choice is
-  // the largest block that still gives 256 workgroups; fewer ranks per
-  // workgroup re-read x from L2 more often for no gain in parallelism.
+int bgmv_shrink_ranks(int64_t T, int32_t r, int32_t H) {
+  // Measured on MI355X (4 adapters, H = 1024 .. 16384, inputs in HBM): the
+  // best choice is the largest block that still gives 256 workgroups --
+  // fewer ranks per workgroup re-read x from L2 more often for no gain in
+  // parallelism -- except on rows of 12288 elements and more, where a
+  // workgroup's row takes several latency-bound trips and 512 workgroups (two
+  // per CU) pay: 256 tokens x 16384 at r = 16 went from 13.0 to 11.6 us.
+  const int64_t want = H >= 12288 ? 512 : 256;
   int rt = 16;
-  while (rt > 4 && (rt / 2 >= r || T * ((r + rt - 1) / rt) < 256)) rt /= 2;
+  while (rt > 4 && (rt / 2 >= r || T * ((r + rt - 1) / rt) < want)) rt /= 2;
   if (const char* e = getenv("LORA_BGMV_SHRINK_RT")) {
     const long f = atol(e);
     if (f == 4 || f == 8 || f == 16) rt = (int)f;
@@ -441,7 +445,7 @@ hipError_t launch_bgmv_shrink(const SegView& seg, const uint16_t* x, int64_t ldx
                               hipStream_t s) {
   BgShrinkArgs a{seg, x, ldx, A, H, r, v, ldv, 1};
   const int64_t T = seg.T > 0 ? seg.T : 1;
-  const int rt = bgmv_shrink_ranks(T, r);
+  const int rt = bgmv_shrink_ranks(T, r, H);
   a.jb = (r + rt - 1) / rt;
   int64_t grid = T * a.jb;
   if (grid > 8192) grid = 8192;

@@ -88,7 +88,7 @@ bool use_bgmv(Op op, int32_t T, int32_t r, int64_t width, bool vec) {
   if (mode == 2) return false;
   if (T > 512) return false;
   if (op == Op::kShrink) {
-    const int rt = lora::bgmv_shrink_ranks(T, r);
+    const int rt = lora::bgmv_shrink_ranks(T, r, (int32_t)width);
     const double bytes = (double)T * ((r + rt - 1) / rt) * (rt + 1) * (double)width * 2.0;
     const double t_token = 3.0 + bytes / 22e6;
     const double t_tile = 7.0 + (double)width / 1600.0 + (double)T * (double)width / 1.6e6;

@@ -62,8 +62,9 @@ struct ExpandSliceDesc {
 constexpr int kBgmvMaxRank = 64;
 
 // Ranks per workgroup of the per-token shrink (4, 8 or 16) for T tokens at
-// rank r: the largest that still gives 256 workgroups, 4 if none does.
-int bgmv_shrink_ranks(int64_t T, int32_t r);
+// rank r over rows of H: the largest that still gives 256 workgroups (512
+// for H >= 12288), 4 if none does.
+int bgmv_shrink_ranks(int64_t T, int32_t r, int32_t H);
 
 hipError_t launch_bgmv_shrink(const SegView& seg, const uint16_t* x, int64_t ldx, const uint16_t* A,
                               int32_t H, int32_t r, float* v, int64_t ldv, int dtype, bool vec,
