@@ -204,6 +204,9 @@ EDGE_CASES = [
     ("f16", 4099, 256, 32, 300, [[256]], (1, 3), 0.05, "zipf"),     # many short segments
     ("bf16", 2000, 16384, 16, 4, [[1024]], 8, 0.0, "uniform"),      # widest H of the sweep
     ("f16", 260, 1024, 48, 6, [[40, 24, 8, 128]], (1, 50), 0.3, "uniform"),
+    ("f16", 33, 1, 1, 2, [[1]], 1, 0.1, "uniform"),                  # H = r = n = 1
+    ("bf16", 17, 8, 1, 3, [[8, 1]], (1, 5), 0.0, "uniform"),         # rank 1, a one-column slice
+    ("f16", 1, 4096, 64, 2048, [[4096]], 1, 0.0, "uniform"),        # one token, the most adapters
 ]
 
 
