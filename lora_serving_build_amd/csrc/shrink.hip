@@ -306,12 +306,26 @@ ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r) {
   p.rp = 16 * p.jtw;
   const int64_t tiles = max_token_tiles(T, L, kSkTile);
   p.max_tiles = (int32_t)tiles;
-  // Split H across workgroups until there are about four items per CU (the
-  // resident limit up to r = 64), keeping at least four blocks per chunk;
-  // measured on the named workloads, the extra partial-row traffic costs
-  // less than idle CUs.
+  // Persistent workgroups: as many as are resident at once (LDS and register
+  // bound: four per CU up to r = 64, two beyond).
+  int64_t per_cu = (int64_t)(160 * 1024 / shrink_lds_bytes(p.jtw, L));
+  const int64_t reg_cu = p.jtw <= 4 ? 4 : 2;
+  per_cu = per_cu < 1 ? 1 : (per_cu > reg_cu ? reg_cu : per_cu);
+  const int64_t resident = 256 * per_cu;
+  // Split H across workgroups so that the items fill one round of resident
+  // workgroups, with at least four blocks per chunk: the extra partial-row
+  // traffic costs less than idle CUs.  Rounding the chunk count up leaves
+  // some items for a second round.  A few of them cost little, but more
+  // than 2% of a round leave most CUs idle while they run, and then the
+  // count is rounded down.  Measured on MI355X (upper-bound tile counts):
+  //   8192-token layer, 192 tiles: 6 chunks 56.5 us, 5 chunks 52.5 us;
+  //   8192 x 4096 at r = 128, 132 tiles (512 resident): 4 -> 46 us, 3 -> 40 us;
+  //   16384 x 4096 at r = 16, 260 tiles: 4 -> 37.8 us, 3 -> 40.5 us.
   int64_t ks = 1;
-  if (tiles > 0 && tiles < 1024) ks = (1024 + tiles - 1) / tiles;
+  if (tiles > 0 && tiles < resident) {
+    ks = (resident + tiles - 1) / tiles;
+    if (tiles * ks - resident > resident / 50) ks = resident / tiles;
+  }
   int64_t ks_max = H / (4 * kSkKB);
   if (ks_max < 1) ks_max = 1;
   if (ks > ks_max) ks = ks_max;
@@ -324,12 +338,7 @@ ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r) {
   p.kchunk = (int32_t)chunk;
   p.partial_bytes = ks > 1 ? (size_t)(ks * (int64_t)T * p.rp * 4) : 0;
   int64_t items = tiles * ks;
-  // Persistent workgroups: as many as are resident at once (LDS and register
-  // bound: four per CU up to r = 64, two beyond).
-  int64_t per_cu = (int64_t)(160 * 1024 / shrink_lds_bytes(p.jtw, L));
-  const int64_t reg_cu = p.jtw <= 4 ? 4 : 2;
-  per_cu = per_cu < 1 ? 1 : (per_cu > reg_cu ? reg_cu : per_cu);
-  int64_t grid = items < 256 * per_cu ? items : 256 * per_cu;
+  int64_t grid = items < resident ? items : resident;
   grid = (grid + 7) / 8 * 8;
   if (grid < 8) grid = 8;
   p.grid = (int32_t)grid;
