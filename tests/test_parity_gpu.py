@@ -224,6 +224,51 @@ def test_edge_shapes(dtype, T, H, r, L, slices, sl, neg, dist):
     check_outside_slices(dw)
 
 
+def _random_cases(n=24, seed=2024):
+    """Seeded random shapes: odd and aligned H, r and slice widths, one to
+    four slices, mixed segment lengths, -1 tokens, every path choice."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dtype = ("f16", "bf16")[i % 2]
+        T = int(np.exp(rng.uniform(0, np.log(1200)))) if i % 3 == 0 else int(rng.integers(64, 1201))
+        H = int(rng.integers(1, 3000))
+        if rng.random() < 0.6:
+            H = max(8, H // 8 * 8)
+        r = int(rng.choice([8, 16, 32, 64, 128])) if rng.random() < 0.5 else int(rng.integers(1, 129))
+        L = int(rng.integers(1, 41))
+        widths = []
+        for _ in range(int(rng.integers(1, 5))):
+            wd = int(rng.integers(1, 1500))
+            widths.append(max(8, wd // 8 * 8) if rng.random() < 0.6 else wd)
+        while T * max(H, sum(widths)) > 3_000_000:
+            T = max(1, T // 2)
+        sl = (1, int(rng.integers(1, 200)))
+        neg = float(rng.choice([0.0, 0.1, 0.3]))
+        dist = ("uniform", "zipf")[int(rng.integers(0, 2))]
+        path = ("auto", "bgmv", "sgmv")[int(rng.integers(0, 3))]
+        if path == "bgmv" and r > 64:
+            path = "sgmv"
+        cases.append((i, dtype, T, H, r, L, widths, sl, neg, dist, path))
+    return cases
+
+
+@pytest.mark.parametrize("i,dtype,T,H,r,L,widths,sl,neg,dist,path", _random_cases())
+def test_random_shapes(force_path, i, dtype, T, H, r, L, widths, sl, neg, dist, path):
+    _announce(f"random {i}: {dtype} T={T} H={H} r={r} L={L} slices={widths} seq={sl} neg={neg} "
+              f"{dist} path={path}")
+    force_path({"auto": lsb.PATH_AUTO, "bgmv": lsb.PATH_BGMV, "sgmv": lsb.PATH_SGMV}[path])
+    w = W.make("rand", dtype, T, H, r, L, [widths], seed=1000 + i, seq_len=sl, neg_frac=neg,
+               id_dist=dist)
+    dw = DeviceWorkload(w)
+    dw.run()
+    rv, ry, ryi = compare_with_oracle(dw)
+    print(f"  tolerance ratios: v {rv:.3g}  y {ry:.3g}  y(isolated) {ryi:.3g}")
+    assert rv <= 1 and ry <= 1 and ryi <= 1
+    check_neg_rows(dw)
+    check_outside_slices(dw)
+
+
 def test_empty_and_all_negative_batches():
     _announce("empty and all -1 batches")
     for T, neg in ((0, 0.0), (50, 1.0)):
