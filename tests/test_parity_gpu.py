@@ -269,6 +269,37 @@ def test_random_shapes(force_path, i, dtype, T, H, r, L, widths, sl, neg, dist, 
     check_outside_slices(dw)
 
 
+LARGE_RANDOM = [
+    # dtype, T, H, r, L, slices, seq_len, neg_frac, id_dist: multi-round shrink splits and
+    # multi-item expands at sizes the oracle checks on sampled rows
+    ("bf16", 6000, 8192, 64, 48, [[4096, 1024, 1024]], (1, 400), 0.05, "zipf"),
+    ("f16", 8192, 4096, 128, 4, [[5000]], (1, 64), 0.0, "uniform"),
+    ("bf16", 3000, 5000, 100, 20, [[2048, 1000]], (1, 300), 0.1, "uniform"),
+    ("f16", 4096, 4096, 16, 64, [[4096], [3000, 1000]], (1, 16), 0.2, "zipf"),
+]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("dtype,T,H,r,L,slices,sl,neg,dist", LARGE_RANDOM)
+def test_large_shapes_sampled(dtype, T, H, r, L, slices, sl, neg, dist):
+    _announce(f"large {dtype} T={T} H={H} r={r} L={L} slices={slices} seq={sl} neg={neg} {dist}")
+    w = W.make("large", dtype, T, H, r, L, slices, seed=T + H + r, seq_len=sl, neg_frac=neg,
+               id_dist=dist)
+    dw = DeviceWorkload(w)
+    seg = dw.run()
+    st, _, ss, cn = seg_host(seg)
+    S = cn[0]
+    bounds = np.unique(np.concatenate([st[ss[:S]], st[np.maximum(ss[1:S + 1] - 1, 0)]]))
+    act = np.nonzero(w.active)[0]
+    rng = np.random.default_rng(T)
+    rows = np.unique(np.concatenate([bounds, rng.choice(act, 128, replace=False)])).astype(np.int32)
+    rv, ry, ryi = compare_with_oracle(dw, rows=rows)
+    print(f"  rows {rows.size}; tolerance ratios: v {rv:.3g}  y {ry:.3g}  y(isolated) {ryi:.3g}")
+    assert rv <= 1 and ry <= 1 and ryi <= 1
+    check_neg_rows(dw)
+    check_outside_slices(dw)
+
+
 def test_empty_and_all_negative_batches():
     _announce("empty and all -1 batches")
     for T, neg in ((0, 0.0), (50, 1.0)):
