@@ -333,11 +333,12 @@ def summarize_profiles(args):
                           "write_kib": round(write.get(op, 0.0), 1),
                           "algorithmic_bytes": alg,
                           "source_hash": source_hash(KERNEL_SOURCES[op])}
+    pool = f" --pool-gib {args.pool_gib:g}" if args.pool_gib != 1.0 else ""
     rec["commands"] = [
         f"rocprofv3 --pmc FETCH_SIZE -d <dir> -o run --output-format csv -- python bench.py "
-        f"--config {args.config} --no-cpu-baseline --traffic-probe",
+        f"--config {args.config} --no-cpu-baseline --traffic-probe{pool}",
         f"rocprofv3 --pmc WRITE_SIZE -d <dir> -o run --output-format csv -- python bench.py "
-        f"--config {args.config} --no-cpu-baseline --traffic-probe"]
+        f"--config {args.config} --no-cpu-baseline --traffic-probe{pool}"]
     path = os.path.join(out_dir, f"traffic_{name}.json")
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
