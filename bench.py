@@ -41,34 +41,81 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def _set_layout(w):
+    """(key, element bytes, shape) of every device tensor of one argument set,
+    in allocation order."""
+    items = [("ids", 4, (w.T,)), ("x", 2, (w.T, w.H)), ("A", 2, (w.L, w.r, w.H))]
+    for oi, o in enumerate(w.outputs):
+        for si, q in enumerate(o.slices):
+            items.append((f"B{oi}.{si}", 2, (w.L, q.n, w.r)))
+    for oi, o in enumerate(w.outputs):
+        items.append((f"y{oi}", 2, (w.T, o.ldy)))
+    items.append(("v", 4, (w.T, w.r)))
+    return items
+
+
+def _host_bits(w, key):
+    import numpy as np
+    if key == "ids":
+        return np.ascontiguousarray(w.ids, np.int32)
+    if key == "x":
+        return w.x
+    if key == "A":
+        return w.A
+    if key == "v":
+        return np.zeros((w.T, w.r), np.float32)
+    if key[0] == "B":
+        oi, si = map(int, key[1:].split("."))
+        return w.outputs[oi].slices[si].B
+    return w.outputs[int(key[1:])].y0
+
+
 class ArgSet:
-    """One set of device buffers for one step."""
+    """One step's device buffers: views into a pool allocation."""
 
-    def __init__(self, w, torch, lsb, src=None):
+    def __init__(self, w, torch, lsb, flat, base, layout, offs):
         tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
-        import numpy as np
-
-        def dev(bits):
-            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(tdt)
-
-        if src is None:
-            self.ids = torch.from_numpy(w.ids).cuda()
-            self.x = dev(w.x)
-            self.A = dev(w.A)
-            self.Bs = [[dev(s.B) for s in o.slices] for o in w.outputs]
-            self.ys = [dev(o.y0) for o in w.outputs]
-        else:
-            self.ids = src.ids.clone()
-            self.x = src.x.clone()
-            self.A = src.A.clone()
-            self.Bs = [[b.clone() for b in bl] for bl in src.Bs]
-            self.ys = [y.clone() for y in src.ys]
-        self.v = torch.zeros(w.T, w.r, dtype=torch.float32, device="cuda")
+        t = {}
+        for (key, eb, shape), off in zip(layout, offs):
+            n = math.prod(shape)
+            view = flat[base + off: base + off + n * eb]
+            dt = torch.int32 if key == "ids" else (torch.float32 if key == "v" else tdt)
+            t[key] = view.view(dt).view(shape)
+        self.ids, self.x, self.A, self.v = t["ids"], t["x"], t["A"], t["v"]
+        self.Bs = [[t[f"B{oi}.{si}"] for si in range(len(o.slices))] for oi, o in enumerate(w.outputs)]
+        self.ys = [t[f"y{oi}"] for oi in range(len(w.outputs))]
         self.seg = lsb.Segments(self.ids, w.L)
 
-    def nbytes(self):
-        t = [self.ids, self.x, self.A, self.v] + [b for bl in self.Bs for b in bl] + self.ys
-        return sum(x.numel() * x.element_size() for x in t)
+
+def set_bytes(w):
+    return sum(((math.prod(shape) * eb + 255) // 256) * 256 for _, eb, shape in _set_layout(w))
+
+
+def make_pool(w, torch, lsb, P):
+    """P argument sets of the workload, carved from one device allocation.
+    Set 0 is copied from the host tensor by tensor; the others are filled by
+    doubling copies of the sets already filled, so the pool costs about
+    log2(P) + a few copy dispatches whatever its size (thousands of small
+    per-tensor copies under a counter profiler are avoided)."""
+    import numpy as np
+    layout = _set_layout(w)
+    offs, off = [], 0
+    for _, eb, shape in layout:
+        offs.append(off)
+        off += ((math.prod(shape) * eb + 255) // 256) * 256
+    S = max(off, 256)
+    flat = torch.empty(P * S, dtype=torch.uint8, device="cuda")
+    for (key, eb, shape), o in zip(layout, offs):
+        nb = math.prod(shape) * eb
+        if nb:
+            src = torch.from_numpy(np.ascontiguousarray(_host_bits(w, key)).reshape(-1).view(np.uint8))
+            flat[o:o + nb].copy_(src)
+    k = 1
+    while k < P:
+        m = min(k, P - k)
+        flat[k * S:(k + m) * S].copy_(flat[0:m * S])
+        k += m
+    return [ArgSet(w, torch, lsb, flat, i * S, layout, offs) for i in range(P)]
 
 
 def op_build(w, lsb, s, ws):
@@ -79,12 +126,17 @@ def op_shrink(w, lsb, s, ws):
     lsb.lora_shrink(s.x, s.A, s.seg, s.v, workspace=ws)
 
 
+def op_expand_output(w, lsb, s, oi):
+    o = w.outputs[oi]
+    if len(o.slices) == 1 and o.slices[0].col_off == 0:
+        lsb.lora_expand(s.v, s.Bs[oi][0], s.seg, s.ys[oi], w.add)
+    else:
+        lsb.lora_expand_slice(s.v, s.Bs[oi], [q.col_off for q in o.slices], s.seg, s.ys[oi], w.add)
+
+
 def op_expand(w, lsb, s, ws):
-    for o, Bs, y in zip(w.outputs, s.Bs, s.ys):
-        if len(o.slices) == 1 and o.slices[0].col_off == 0:
-            lsb.lora_expand(s.v, Bs[0], s.seg, y, w.add)
-        else:
-            lsb.lora_expand_slice(s.v, Bs, [q.col_off for q in o.slices], s.seg, y, w.add)
+    for oi in range(len(w.outputs)):
+        op_expand_output(w, lsb, s, oi)
 
 
 def step(w, lsb, s, ws):
@@ -132,64 +184,117 @@ def graph_time(torch, fn, sets, first, count, evict=True):
     return ms
 
 
+def tol_ratio(got, ref):
+    """max |got - ref| / (1e-2 (1 + |ref|)) over all elements; <= 1 passes.
+    Any NaN in the errors (a NaN or infinite output where the oracle is
+    finite, or the reverse) makes the ratio infinite."""
+    import numpy as np
+    if got.size == 0:
+        return 0.0
+    err = np.abs(got - ref) / (1e-2 * (1.0 + np.abs(ref)))
+    if np.isnan(err).any():
+        return float("inf")
+    return float(err.max())
+
+
 def parity_check(w, torch, lsb, ws):
-    """Checks one fresh step against the oracle before anything is timed."""
+    """Checks one fresh step against the oracle before anything is timed:
+    metadata bit for bit, every active row of v and of every output in full
+    (streamed through the oracle in row blocks, so no fp64 copy of a whole
+    output is held), and rows without an adapter untouched."""
     import numpy as np
     import oracle
     import workloads as W
-    s = ArgSet(w, torch, lsb)
+    s = make_pool(w, torch, lsb, 1)[0]
     step(w, lsb, s, ws)
     torch.cuda.synchronize()
+    meta = (s.seg.sorted_token[:w.T].cpu().numpy(), s.seg.seg_lora.cpu().numpy(),
+            s.seg.seg_start.cpu().numpy(), s.seg.counts.cpu().numpy())
+    for g_, r_ in zip(meta, oracle.build_segments(w.ids, w.L)):
+        if not np.array_equal(g_, r_):
+            return float("inf")
     act = np.nonzero(w.active)[0].astype(np.int32)
+    inact = np.nonzero(~w.active)[0]
     v_ref = oracle.shrink(w.dtype, w.x, w.A, w.ids, rows=act)
     vg = s.v.cpu().numpy().astype(np.float64)[act]
-    worst = float(np.max(np.abs(vg - v_ref) / (1e-2 * (1 + np.abs(v_ref))))) if act.size else 0.0
+    worst = tol_ratio(vg, v_ref)
     v_full = np.zeros((w.T, w.r))
     v_full[act] = v_ref
     for o, y in zip(w.outputs, s.ys):
         cols = np.concatenate([np.arange(q.col_off, q.col_off + q.n) for q in o.slices])
-        ref = oracle.expand_slice(w.dtype, v_full, [q.B for q in o.slices], [q.col_off for q in o.slices],
-                                  w.ids, o.y0, w.add, rows=act)
-        yb = y.view(torch.int16).cpu().numpy().view(np.uint16)[act][:, cols]
-        got = W.bits_to_f32(yb, w.dtype).astype(np.float64)
-        if act.size:
-            worst = max(worst, float(np.max(np.abs(got - ref) / (1e-2 * (1 + np.abs(ref))))))
+        block = max(1, (32 << 20) // o.ldy)
+        for b in range(0, act.size, block):
+            rows = act[b:b + block]
+            ref = oracle.expand_slice(w.dtype, v_full, [q.B for q in o.slices],
+                                      [q.col_off for q in o.slices], w.ids, o.y0, w.add, rows=rows)
+            yb = y.index_select(0, torch.from_numpy(rows).long().cuda()).view(torch.int16)
+            got = W.bits_to_f32(yb.cpu().numpy().view(np.uint16)[:, cols], w.dtype).astype(np.float64)
+            worst = max(worst, tol_ratio(got, ref))
+        if inact.size:
+            yb = y.index_select(0, torch.from_numpy(inact).long().cuda()).view(torch.int16)
+            if not np.array_equal(yb.cpu().numpy().view(np.uint16), o.y0[inact]):
+                return float("inf")
+    del s
+    torch.cuda.empty_cache()
     return worst
+
+
+def run_oracle_step(w):
+    """The whole workload through the oracle: metadata, shrink, every expand."""
+    import numpy as np
+    import oracle
+    oracle.build_segments(w.ids, w.L)
+    v = np.nan_to_num(oracle.shrink(w.dtype, w.x, w.A, w.ids))
+    for o in w.outputs:
+        oracle.expand_slice(w.dtype, v, [q.B for q in o.slices], [q.col_off for q in o.slices],
+                            w.ids, o.y0, w.add)
+
+
+def _time_oracle(w, target_s, max_s):
+    t0 = time.perf_counter()
+    run_oracle_step(w)
+    t1 = time.perf_counter() - t0
+    reps = 1 if t1 >= target_s else max(1, min(100000, int(math.ceil(target_s / max(t1, 1e-6)))))
+    reps = min(reps, max(1, int(max_s / max(t1, 1e-6))))
+    t0 = time.perf_counter()
+    for _ in range(reps - 1):
+        run_oracle_step(w)
+    el = time.perf_counter() - t0 + t1
+    return reps, el
 
 
 def cpu_baseline(w, step_bytes):
     """The fp64 oracle (as it is) on the host cores, over the same workload,
-    repeated to about 10 s of CPU work."""
-    import numpy as np
+    repeated to about 12 s of CPU work; then, on one thread, the three
+    smallest named workloads (about 1.5 s each)."""
     import oracle
-
-    def run():
-        oracle.build_segments(w.ids, w.L)
-        v = oracle.shrink(w.dtype, w.x, w.A, w.ids)
-        v = np.nan_to_num(v)
-        for o in w.outputs:
-            oracle.expand_slice(w.dtype, v, [q.B for q in o.slices], [q.col_off for q in o.slices],
-                                w.ids, o.y0, w.add)
-
-    t0 = time.perf_counter()
-    run()
-    t1 = time.perf_counter() - t0
-    reps = max(1, min(100000, int(math.ceil(12.0 / max(t1, 1e-6)))))
-    if t1 > 30.0:
-        reps = 1
-    t0 = time.perf_counter()
-    for _ in range(reps - 1):
-        run()
-    el = time.perf_counter() - t0 + (t1 if reps >= 1 else 0.0)
-    return {
+    import workloads as W
+    reps, el = _time_oracle(w, 12.0, 30.0)
+    out = {
         "value": round(step_bytes * reps / el / 1e9, 4),
         "unit": "GB/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": f"the whole workload (metadata, shrink, expand of every output) run {reps}x "
-                  f"in {el:.1f} s, OpenMP over tokens",
+        "sample": f"the whole workload (metadata, shrink, expand of every output, every row) run "
+                  f"{reps}x in {el:.1f} s, OpenMP over tokens",
         "tokens_per_s": round(w.T * reps / el, 2),
+        "host_cpus": os.cpu_count(),
+        "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS"),
     }
+    single = {}
+    prev = oracle.set_num_threads(1)
+    try:
+        for k in (1, 2, 3):
+            wk = W.config(k)
+            r1, e1 = _time_oracle(wk, 1.5, 5.0)
+            b = wk.shrink_bytes() + wk.expand_bytes()
+            single[wk.name] = {"GB_s": round(b * r1 / e1 / 1e9, 4),
+                               "tokens_per_s": round(wk.T * r1 / e1, 1), "runs": r1,
+                               "seconds": round(e1, 2)}
+    finally:
+        oracle.set_num_threads(prev)
+    out["one_thread"] = single
+    return out
 
 
 OP_KERNELS = {  # kernel-name fragments of each op (rocprofv3 names)
@@ -204,6 +309,43 @@ def op_of(kernel_name):
     for op, frags in OP_KERNELS.items():
         if any(f in kernel_name for f in frags):
             return op
+    return None
+
+
+def short_name(kn):
+    return kn.replace("void ", "").replace("lora::(anonymous namespace)::", "").split("(")[0]
+
+
+def assign_units(rows, n_outputs):
+    """Unit of every library dispatch of a --profile run, in dispatch order:
+    each step is build, shrink (one or two kernels), then one expand call per
+    output, so the k-th expand dispatch after a build belongs to output k.
+    Returns [(unit, row)]; other kernels (the copy probe, torch's fills) are
+    returned with unit None."""
+    out = []
+    k = 0
+    for r in sorted(rows, key=lambda r: int(r.get("Dispatch_Id") or r.get("Correlation_Id") or 0)):
+        op = op_of(r["Kernel_Name"])
+        if op == "build":
+            k = 0
+            out.append(("build", r))
+        elif op == "shrink":
+            out.append(("shrink", r))
+        elif op == "expand":
+            out.append((f"expand[{k}]" if n_outputs > 1 else "expand", r))
+            k += 1
+        else:
+            out.append((None, r))
+    return out
+
+
+def unit_bytes(w, unit):
+    if unit == "shrink":
+        return w.shrink_bytes()
+    if unit == "expand":
+        return w.expand_bytes()
+    if unit.startswith("expand["):
+        return w.output_bytes(w.outputs[int(unit[7:-1])])
     return None
 
 
@@ -223,13 +365,13 @@ def summarize_counters(args, name, out_dir):
         kn = r["Kernel_Name"]
         if op_of(kn) is None:
             continue
-        short = kn.replace("void ", "").replace("lora::(anonymous namespace)::", "").split("(")[0]
+        short = short_name(kn)
         tot[short][r["Counter_Name"]] += float(r["Counter_Value"])
         calls[short].add(r.get("Dispatch_Id", r.get("Correlation_Id", "")))
     lines = [f"# rocprofv3 LDS and matrix-core counters: {name}", "",
              "command (from the repository root, on one MI355X):",
              f"  rocprofv3 --pmc {' '.join(COUNTER_SET)} -d <dir> -o run --output-format csv -- "
-             f"python bench.py --config {args.config} --no-cpu-baseline --no-context",
+             f"python bench.py --config {args.config} --profile",
              "",
              "Sums over all dispatches of each kernel.  LDS conflict share = SQ_LDS_BANK_CONFLICT / "
              "SQ_LDS_IDX_ACTIVE (cycles).  Matrix-core busy = SQ_VALU_MFMA_BUSY_CYCLES / "
@@ -251,73 +393,83 @@ def summarize_counters(args, name, out_dir):
 
 
 def summarize_profiles(args):
-    """Turns rocprofv3 CSV output of this script into the short summaries kept
-    under profiles/: a kernel-trace table, and per-op HBM traffic from the
-    FETCH_SIZE / WRITE_SIZE runs scaled by a copy of known size."""
+    """Turns rocprofv3 CSV output of `bench.py --profile` into the short
+    summaries kept under profiles/: a kernel-trace table (per kernel, and per
+    call of the step: build, shrink, each expand), and per-call HBM traffic from
+    the FETCH_SIZE / WRITE_SIZE runs scaled by a copy of known size."""
     import csv
     import collections
+    import statistics
     import workloads as W
     w = W.config(args.config)
     name = w.name
+    nout = len(w.outputs)
     out_dir = os.path.join(ROOT, "profiles")
     os.makedirs(out_dir, exist_ok=True)
-    lines = [f"# rocprofv3 kernel trace: {name}", "",
-             "command (from the repository root, on one MI355X):",
-             f"  rocprofv3 --kernel-trace --stats -d <dir> -o run --output-format csv -- "
-             f"python bench.py --config {args.config} --no-cpu-baseline",
-             "", "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
-    stats = list(csv.DictReader(open(args.trace)))
-    op_avg = {}
-    for r in stats:
-        kn = r["Name"]
-        op = op_of(kn)
-        if op is None and "copy" not in kn.lower():
-            continue
-        short = kn.replace("void ", "").replace("lora::(anonymous namespace)::", "").split("(")[0]
-        lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | "
-                     f"{float(r['MinNs'])/1e3:.2f} | {float(r['MaxNs'])/1e3:.2f} |")
-        if op:
-            op_avg.setdefault(op, []).append((kn, float(r["AverageNs"]) / 1e3, int(r["Calls"])))
-    steps = sum(c for _, _, c in op_avg.get("build", [])) or 1
-    lines += ["", f"Per op and step ({steps} steps traced; every kernel of the op counted, "
-              "algorithmic bytes of the op):"]
-    nbytes = {"shrink": w.shrink_bytes(), "expand": w.expand_bytes()}
-    for op, rows in sorted(op_avg.items()):
-        per_step = sum(a * c for _, a, c in rows) / steps
-        line = f"- {op}: {per_step:.2f} us per step"
-        if op in nbytes:
-            line += (f"; {nbytes[op] / 2**20:.3f} MiB -> "
-                     f"{nbytes[op] / (per_step * 1e-6) / 1e9:.1f} GB/s")
-        lines.append(line)
-    with open(os.path.join(out_dir, f"trace_{name}.md"), "w") as f:
-        f.write("\n".join(lines) + "\n")
-    print("wrote", os.path.join(out_dir, f"trace_{name}.md"))
+    pool = f" --pool-gib {args.pool_gib:g}" if args.pool_gib != 1.0 else ""
+    if args.trace:
+        lines = [f"# rocprofv3 kernel trace: {name}", "",
+                 "command (from the repository root, on one MI355X):",
+                 f"  rocprofv3 --kernel-trace --stats -d <dir> -o run --output-format csv -- "
+                 f"python bench.py --config {args.config} --profile{pool}",
+                 "",
+                 "Every launch of the run: the parity step, the warm-up steps and both replays of "
+                 "the K-step graph (inputs in HBM for the replays).  Durations are each kernel's "
+                 "own (end - start).", "",
+                 "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+        rows = list(csv.DictReader(open(args.trace)))
+        per_kernel = collections.defaultdict(list)
+        per_unit = collections.defaultdict(list)
+        steps = 0
+        for unit, r in assign_units(rows, nout):
+            d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            if unit is None and "copy" not in r["Kernel_Name"].lower():
+                continue
+            per_kernel[short_name(r["Kernel_Name"])].append(d)
+            if unit:
+                per_unit[unit].append(d)
+                steps += unit == "build"
+        for k in sorted(per_kernel):
+            v = per_kernel[k]
+            lines.append(f"| {k} | {len(v)} | {statistics.fmean(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+        lines += ["", f"Per call of the step ({steps} steps traced; a call's kernels summed; "
+                  "algorithmic bytes of the call; fraction of the 8 TB/s HBM peak):", "",
+                  "| call | us per step | algorithmic MiB | GB/s | of 8 TB/s |", "|---|---|---|---|---|"]
+        for unit in sorted(per_unit):
+            per_step = sum(per_unit[unit]) / max(1, steps)
+            nb = unit_bytes(w, unit)
+            if nb:
+                gbs = nb / (per_step * 1e-6) / 1e9
+                lines.append(f"| {unit} | {per_step:.2f} | {nb / 2**20:.3f} | {gbs:.1f} | "
+                             f"{gbs / HBM_PEAK_GBS:.4f} |")
+            else:
+                lines.append(f"| {unit} | {per_step:.2f} | | | |")
+        path = os.path.join(out_dir, f"trace_{name}.md")
+        with open(path, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print("wrote", path)
     if args.counters:
         summarize_counters(args, name, out_dir)
     if not (args.fetch and args.write):
         return
 
-    def per_op(path, counter):
-        rows = list(csv.DictReader(open(path)))
+    def per_unit(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
         tot = collections.defaultdict(float)
         steps = 0
         copy_vals = []
-        for r in rows:
-            if r["Counter_Name"] != counter:
-                continue
-            kn = r["Kernel_Name"]
+        for unit, r in assign_units(rows, nout):
             val = float(r["Counter_Value"])  # KiB per dispatch
-            op = op_of(kn)
-            if op == "build":
+            if unit == "build":
                 steps += 1
-            if op:
-                tot[op] += val
-            elif "neg_kernel" in kn:
+            if unit:
+                tot[unit] += val
+            elif "neg_kernel" in r["Kernel_Name"]:
                 copy_vals.append(val)
         return {k: v / max(1, steps) for k, v in tot.items()}, copy_vals, steps
 
-    fetch, fcopy, steps = per_op(args.fetch, "FETCH_SIZE")
-    write, wcopy, _ = per_op(args.write, "WRITE_SIZE")
+    fetch, fcopy, steps = per_unit(args.fetch, "FETCH_SIZE")
+    write, wcopy, _ = per_unit(args.write, "WRITE_SIZE")
     if not fcopy or not wcopy:
         raise SystemExit("no copy probe dispatch found: run the --pmc passes with --traffic-probe")
     f_fetch = max(fcopy) * 1024 / COPY_PROBE_BYTES
@@ -326,19 +478,20 @@ def summarize_profiles(args):
            "copy_probe_bytes": COPY_PROBE_BYTES,
            "fetch_scale": round(f_fetch, 4), "write_scale": round(f_write, 4),
            "ops": {}}
-    for op in sorted(set(fetch) | set(write)):
-        b = fetch.get(op, 0.0) * 1024 / f_fetch + write.get(op, 0.0) * 1024 / f_write
-        alg = {"shrink": w.shrink_bytes(), "expand": w.expand_bytes()}.get(op)
-        rec["ops"][op] = {"bytes_per_call": int(b), "fetch_kib": round(fetch.get(op, 0.0), 1),
-                          "write_kib": round(write.get(op, 0.0), 1),
-                          "algorithmic_bytes": alg,
-                          "source_hash": source_hash(KERNEL_SOURCES[op])}
-    pool = f" --pool-gib {args.pool_gib:g}" if args.pool_gib != 1.0 else ""
+    for unit in sorted(set(fetch) | set(write)):
+        b = fetch.get(unit, 0.0) * 1024 / f_fetch + write.get(unit, 0.0) * 1024 / f_write
+        alg = unit_bytes(w, unit)
+        fam = "build" if unit == "build" else ("shrink" if unit == "shrink" else "expand")
+        rec["ops"][unit] = {"bytes_per_call": int(b), "fetch_kib": round(fetch.get(unit, 0.0), 1),
+                            "write_kib": round(write.get(unit, 0.0), 1),
+                            "algorithmic_bytes": alg,
+                            "ratio": round(b / alg, 3) if alg else None,
+                            "source_hash": source_hash(KERNEL_SOURCES[fam])}
     rec["commands"] = [
         f"rocprofv3 --pmc FETCH_SIZE -d <dir> -o run --output-format csv -- python bench.py "
-        f"--config {args.config} --no-cpu-baseline --traffic-probe{pool}",
+        f"--config {args.config} --profile --traffic-probe{pool}",
         f"rocprofv3 --pmc WRITE_SIZE -d <dir> -o run --output-format csv -- python bench.py "
-        f"--config {args.config} --no-cpu-baseline --traffic-probe{pool}"]
+        f"--config {args.config} --profile --traffic-probe{pool}"]
     path = os.path.join(out_dir, f"traffic_{name}.json")
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
@@ -444,17 +597,18 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(op, workload_name, src_hash, launches):
-    """HBM bytes per launch of an op from the committed rocprofv3 counter
-    summary, if the op's kernel sources have not changed since it was taken."""
+def measured_traffic(unit, workload_name, src_hash):
+    """HBM bytes of one call (build, shrink, expand or expand[k]) from the
+    committed rocprofv3 counter summary, if the kernel sources of its op have
+    not changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        rec = json.load(f).get("ops", {}).get(op)
+        rec = json.load(f).get("ops", {}).get(unit)
     if not rec or rec.get("source_hash") != src_hash:
         return None
-    return rec["bytes_per_call"] // launches
+    return rec["bytes_per_call"]
 
 
 _COMMON = ["lora_serving_build_amd/csrc/lora_device.h", "lora_serving_build_amd/csrc/tiles.h",
@@ -466,64 +620,29 @@ KERNEL_SOURCES = {
 }
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, help="named workload 1..5 (default 2)")
-    ap.add_argument("--pool-gib", type=float, default=1.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-check", action="store_true")
-    ap.add_argument("--no-context", action="store_true", help="skip the torch streaming-rate context")
-    ap.add_argument("--traffic-probe", action="store_true",
-                    help="also run one plain copy of 256 MiB (calibrates FETCH_SIZE / WRITE_SIZE)")
-    ap.add_argument("--summarize-profiles", action="store_true",
-                    help="write profiles/ summaries from rocprofv3 CSVs (--trace, --fetch, --write)")
-    ap.add_argument("--sweep", action="store_true",
-                    help="time shrink and expand alone on the micro-benchmark sweep shapes")
-    ap.add_argument("--trace")
-    ap.add_argument("--fetch")
-    ap.add_argument("--write")
-    ap.add_argument("--counters", help="CSV of a --pmc pass over the LDS / matrix-core counter set")
-    args = ap.parse_args()
-    if args.summarize_profiles:
-        summarize_profiles(args)
-        return
-    if args.sweep:
-        sweep(args)
-        return
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the multi-LoRA path here has no multi-GPU mode "
-              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
-        sys.exit(2)
+def _output_label(o):
+    return "+".join(str(q.n) for q in o.slices)
 
-    import torch
-    import lora_serving_build_amd as lsb
-    import workloads as W
 
-    lsb.lib()
-    torch.cuda.set_device(0)
-    log(f"generating workload {args.config}")
-    w = W.config(args.config)
+def measure(w, args, torch, lsb, check=True):
+    """Times one workload: the K-step graph, then every op and every expand
+    call alone.  Returns the fields of the JSON line that depend on it."""
     need = lsb.lora_shrink_workspace_bytes(w.T, w.L, w.H, w.r)
     ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda") if need else None
 
     worst = None
-    if not args.no_check:
-        log("parity check of one fresh step against the oracle")
+    if check:
+        log(f"{w.name}: parity check of one fresh step against the oracle (every row)")
         worst = parity_check(w, torch, lsb, ws)
         log(f"worst tolerance ratio {worst:.3g}")
         if not worst <= 1.0:
-            print(json.dumps({"error": "parity check failed", "ratio": worst}))
+            print(json.dumps({"error": "parity check failed", "workload": w.name, "ratio": worst}))
             sys.exit(1)
 
-    base = ArgSet(w, torch, lsb)
-    per_set = base.nbytes()
+    per_set = set_bytes(w)
     P = max(2, int(math.ceil(args.pool_gib * 2**30 / per_set)))
     log(f"argument pool: {P} sets of {per_set / 2**20:.1f} MiB")
-    sets = [base] + [ArgSet(w, torch, lsb, src=base) for _ in range(P - 1)]
+    sets = make_pool(w, torch, lsb, P)
     torch.cuda.synchronize()
 
     fstep = lambda s: step(w, lsb, s, ws)
@@ -535,42 +654,63 @@ def main():
     log(f"timing {K} steps in one graph")
     ms = graph_time(torch, fstep, sets, args.warmup, K)
     ms_per_step = ms / K
+    res = {"ms_per_step": ms_per_step, "pool_sets": P, "parity_ratio": worst}
+    if args.profile:
+        # Profiler runs: the steps only, so that every dispatch belongs to a
+        # step in order (build, shrink, one expand per output).
+        if args.traffic_probe:
+            # A plain streaming kernel of known size (reads and writes 256 MiB
+            # once each): the yardstick for the FETCH_SIZE / WRITE_SIZE counters.
+            src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.int32, device="cuda")
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            torch.neg(src, out=dst)
+            torch.cuda.synchronize()
+            del src, dst
+        return res, sets
 
-    shrink_b = w.shrink_bytes()
-    expand_b = w.expand_bytes()
-    step_bytes = shrink_b + expand_b
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-
-    # Per-op timing: each op alone, K launches over the pool in one graph.
+    # Each op alone, K launches over the pool in one graph; every expand
+    # call (one per output) also alone.
+    units = [("build", lambda s: op_build(w, lsb, s, ws), 8 * w.T + 8 * (w.L + 1) + 16, 0, 1),
+             ("shrink", lambda s: op_shrink(w, lsb, s, ws), w.shrink_bytes(), w.shrink_flops(), 1),
+             ("expand", lambda s: op_expand(w, lsb, s, ws), w.expand_bytes(), w.expand_flops(),
+              len(w.outputs))]
+    if len(w.outputs) > 1:
+        for oi, o in enumerate(w.outputs):
+            n = sum(q.n for q in o.slices)
+            units.append((f"expand[{oi}]", lambda s, oi=oi: op_expand_output(w, lsb, s, oi),
+                          w.output_bytes(o), 2 * w.T_a * w.r * n, 1))
     ops = {}
-    for name, fn, nbytes, flops in (
-            ("build", op_build, 8 * w.T + 8 * (w.L + 1) + 16, 0),
-            ("shrink", op_shrink, shrink_b, w.shrink_flops()),
-            ("expand", op_expand, expand_b, w.expand_flops())):
-        t = graph_time(torch, lambda s, fn=fn: fn(w, lsb, s, ws), sets, args.warmup + K, K) / K
-        launches = 1 if name != "expand" else len(w.outputs)
+    first = args.warmup + K
+    for name, fn, nbytes, flops, launches in units:
+        t = graph_time(torch, fn, sets, first, K) / K
         ops[name] = {"us_per_op": round(t * 1e3, 3), "launches": launches, "bytes": nbytes,
                      "GB_s": round(nbytes / (t * 1e-3) / 1e9, 1),
                      "TFLOP_s": round(flops / (t * 1e-3) / 1e12, 2)}
+        if name.startswith("expand["):
+            ops[name]["slices"] = _output_label(w.outputs[int(name[7:-1])])
         log(f"{name}: {t * 1e3:.2f} us/op, {ops[name]['GB_s']} GB/s, {ops[name]['TFLOP_s']} TFLOP/s")
-    if args.traffic_probe:
-        # A plain streaming kernel of known size (reads and writes 256 MiB
-        # once each): the yardstick for the FETCH_SIZE / WRITE_SIZE counters.
-        src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.int32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
-    dom = max(("shrink", "expand"), key=lambda k: ops[k]["us_per_op"])
-    src_hash = source_hash(KERNEL_SOURCES[dom])
-    traffic = measured_traffic(dom, w.name, src_hash, ops[dom]["launches"])
+        first += K
+
+    # The roofline names one call, the longest single launch: the shrink, or
+    # one expand call (with several outputs, each is timed alone above).
+    cands = ["shrink"] + ([k for k in ops if k.startswith("expand[")] if len(w.outputs) > 1 else ["expand"])
+    dom = max(cands, key=lambda k: ops[k]["us_per_op"])
+    op_family = "shrink" if dom == "shrink" else "expand"
+    src_hash = source_hash(KERNEL_SOURCES[op_family])
+    traffic = measured_traffic(dom, w.name, src_hash)
     achieved = ops[dom]["bytes"] / (ops[dom]["us_per_op"] * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "bytes_per_launch": ops[dom]["bytes"] // ops[dom]["launches"],
-                "us_per_launch": round(ops[dom]["us_per_op"] / ops[dom]["launches"], 3),
-                "source_hash": src_hash}
+    desc = {"shrink": "lora_shrink (segment tiles; with an H split, plus its reduce kernel)"
+            if w.T > 512 else "lora_shrink", "expand": "lora_expand"}
+    if dom.startswith("expand["):
+        kdesc = f"lora_expand_slice into output {dom[7:-1]} (slices {ops[dom]['slices']})"
+    else:
+        kdesc = desc[dom]
+    roofline = {"bound": "hbm", "kernel": kdesc, "op": dom, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "bytes_per_launch": ops[dom]["bytes"],
+                "us_per_launch": ops[dom]["us_per_op"], "source_hash": src_hash}
+    res.update(ops=ops, roofline=roofline)
 
     # Mixed-rank workloads: the same step with each adapter's live rank handed
     # to the segment kernels (they then skip the zero padding).  Bytes count
@@ -595,6 +735,83 @@ def main():
                 "bytes_live_ranks": live_bytes,
                 "value": round(live_bytes / (ms_live * 1e-3) / 1e9, 2)}
         log(f"live ranks: {ms_live * 1e3:.2f} us/step ({live['speedup']}x)")
+    res["live_ranks"] = live
+    return res, sets
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=5,
+                    help="named workload 1..5 (default 5, the largest: the 8192-token 70B layer)")
+    ap.add_argument("--also", default="2",
+                    help="comma-separated named workloads also timed, reported under "
+                         "'other_workloads' (default 2, the 256-token decode; '' for none)")
+    ap.add_argument("--pool-gib", type=float, default=1.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--no-context", action="store_true", help="skip the torch streaming-rate context")
+    ap.add_argument("--profile", action="store_true",
+                    help="profiler run: warm-up and the timed steps only, no per-op graphs, no "
+                         "other workloads, no context, no CPU baseline")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="with --profile: also run one plain copy of 256 MiB (calibrates "
+                         "FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--summarize-profiles", action="store_true",
+                    help="write profiles/ summaries from rocprofv3 CSVs (--trace, --fetch, --write)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time shrink and expand alone on the micro-benchmark sweep shapes")
+    ap.add_argument("--trace", help="kernel_trace.csv of a --kernel-trace run")
+    ap.add_argument("--stats", help="kernel_stats.csv of the same run")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--counters", help="CSV of a --pmc pass over the LDS / matrix-core counter set")
+    args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args)
+        return
+    if args.sweep:
+        sweep(args)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the multi-LoRA path here has no multi-GPU mode "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import lora_serving_build_amd as lsb
+    import workloads as W
+
+    lsb.lib()
+    torch.cuda.set_device(0)
+    log(f"generating workload {args.config}")
+    w = W.config(args.config)
+    res, sets = measure(w, args, torch, lsb, check=not args.no_check)
+    del sets
+    torch.cuda.empty_cache()
+    ms_per_step = res["ms_per_step"]
+    step_bytes = w.shrink_bytes() + w.expand_bytes()
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    if args.profile:
+        log(f"{w.name}: {ms_per_step * 1e3:.2f} us/step")
+        return
+
+    others = {}
+    for k in [int(c) for c in args.also.split(",") if c.strip()]:
+        if k == args.config:
+            continue
+        wk = W.config(k)
+        rk, sk = measure(wk, args, torch, lsb, check=not args.no_check)
+        del sk
+        torch.cuda.empty_cache()
+        bk = wk.shrink_bytes() + wk.expand_bytes()
+        others[wk.name] = {"value": round(bk / (rk["ms_per_step"] * 1e-3) / 1e9, 2), "unit": "GB/s",
+                           "ms_per_step": round(rk["ms_per_step"], 6), "ops": rk["ops"],
+                           "roofline": rk["roofline"], "parity_ratio": rk["parity_ratio"],
+                           "pool_sets": rk["pool_sets"]}
 
     # Context for the roofline fraction: what plain torch streaming kernels
     # reach on this GPU (a copy and an in-place add over 512 MiB each, twice
@@ -632,7 +849,7 @@ def main():
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True,
@@ -643,16 +860,17 @@ def main():
         "config": {"workload": w.name, "tokens": w.T, "active_tokens": w.T_a, "hidden": w.H,
                    "rank": w.r, "num_loras": w.L, "distinct_loras": w.distinct,
                    "outputs": [[q.n for q in o.slices] for o in w.outputs], "add_inputs": w.add,
-                   "pool_sets": P, "parallelism": "none"},
+                   "pool_sets": res["pool_sets"], "parallelism": "none"},
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
         "mfma_frac": round(flops / (ms_per_step * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype], 5),
         "tokens_per_s": round(w.T / (ms_per_step * 1e-3), 1),
-        "ops": ops,
-        "roofline": roofline,
+        "ops": res["ops"],
+        "roofline": res["roofline"],
         "cpu_baseline": cpu,
-        "parity_ratio": worst,
-        "live_ranks": live,
+        "parity_ratio": res["parity_ratio"],
+        "live_ranks": res["live_ranks"],
+        "other_workloads": others,
         "hbm_context": hbm_context,
     }
     print(json.dumps(out), flush=True)

@@ -43,8 +43,12 @@
  *
  * Precision.  Products are accumulated in fp32.  expand rounds once, to
  * nearest even, when it writes y.  Inside expand the fp32 v is split into a
- * high and a low fp16/bf16 part so that the matrix cores see v to about 16
- * significant bits; with fp16 data, |v| must stay below 65504.
+ * high and a low 16-bit part, hi = round(v) and lo = round(v - hi), so that
+ * the matrix cores see v to about 16 significant bits (bf16) or 22 (fp16).
+ * With fp16 data each token's v is first multiplied by a power of two that
+ * brings its largest |v| into [2^13, 2^14), and the fp32 products are
+ * multiplied back before y is added: any finite fp32 v is accepted, also
+ * beyond the fp16 range.
  */
 #ifndef LORA_MI355X_H
 #define LORA_MI355X_H
@@ -82,12 +86,14 @@ extern "C" {
  *   seg_start[L+1]   first position in sorted_token of segment s; entries
  *                    S..L hold T_a (the number of active tokens)
  *   counts[4]        {S, T_a, longest segment, number of ids outside [-1, L)}
- * Callers that already hold grouped batches may fill these buffers
- * themselves, as long as they respect exactly these invariants. */
+ * Callers that already hold grouped batches may fill these buffers (and the
+ * three fields that lora_build_segments sets) themselves, as long as they
+ * respect exactly these invariants. */
 typedef struct lora_segments {
-  int32_t num_tokens;          /* T >= 0                                       */
-  int32_t num_loras;           /* L in [1, LORA_MAX_LORAS]                      */
-  const int32_t *token_lora;   /* [T] adapter id of each token, -1 = none       */
+  int32_t num_tokens;          /* T >= 0 (set by lora_build_segments)            */
+  int32_t num_loras;           /* L in [1, LORA_MAX_LORAS] (set by the build)     */
+  const int32_t *token_lora;   /* [T] adapter id of each token, -1 = none (set by
+                                * the build to the pointer it was given)         */
   int32_t *sorted_token;       /* [T]                                           */
   int32_t *seg_lora;           /* [L]                                           */
   int32_t *seg_start;          /* [L + 1]                                       */
@@ -101,13 +107,30 @@ typedef struct lora_segments {
                                 * Values are clamped to [0, r].                   */
 } lora_segments;
 
-/* Builds the segment metadata of seg->token_lora into the other four
- * buffers of *seg (one kernel, one workgroup).  The grouping follows the
- * punica issue's SGMV segments; the order inside a segment is ascending token
- * index, so the result is unique.  T = 0 and all-(-1) batches are valid.
+/* Device scratch bytes lora_build_segments needs for T tokens and L
+ * adapters.  The builder is one workgroup whose histogram, scans and scatter
+ * cursors live in LDS, so this is 0 for every T and L in range; callers that
+ * size a workspace from it stay correct if that changes. */
+size_t lora_segments_workspace_bytes(int32_t T, int32_t L);
+
+/* Builds the segment metadata of one batch (punica issue: SGMV segments of
+ * tokens that share an adapter; TPU PR summary: tokens without an adapter
+ * are skipped) with one kernel of one workgroup.
+ *   token_lora  [T] device, adapter id per token; -1 = no adapter; ids outside
+ *               [-1, L) are treated as -1 and counted in counts[3]
+ *   seg         host struct whose four output pointers (sorted_token,
+ *               seg_lora, seg_start, counts) the caller has set to device
+ *               buffers of the sizes above; the call sets num_tokens = T,
+ *               num_loras = L and token_lora, and leaves lora_rank alone
+ *   workspace   device scratch of lora_segments_workspace_bytes(T, L) bytes
+ *               (may be NULL when that is 0)
+ * The order inside a segment is ascending token index, so the result is
+ * unique.  T = 0 and all-(-1) batches are valid.
  * Errors: LORA_ERR_INVALID_ARG for a NULL seg or buffer (with T > 0) or
- * T < 0; LORA_ERR_UNSUPPORTED for L outside [1, LORA_MAX_LORAS]. */
-int lora_build_segments(const lora_segments *seg, void *stream);
+ * T < 0; LORA_ERR_UNSUPPORTED for L outside [1, LORA_MAX_LORAS];
+ * LORA_ERR_WORKSPACE; LORA_ERR_HIP. */
+int lora_build_segments(const int32_t *token_lora, int32_t T, int32_t L, lora_segments *seg,
+                        void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace bytes that lora_shrink needs for T tokens, L adapters, hidden
  * size H and rank r (0 if it needs none).  Only batches with too few token
@@ -170,6 +193,14 @@ int lora_expand_slice(const float *v, int64_t ldv, int64_t v_slice_stride,
  * 2 = always segment tiles.  Process-wide, meant for tests and measurement.
  * Returns the previous mode, or LORA_ERR_INVALID_ARG for an unknown mode. */
 int lora_set_path(int mode);
+
+/* Re-reads the launch-plan overrides (LORA_SHRINK_KSPLIT, LORA_EXPAND_TB,
+ * LORA_EXPAND_CPR, LORA_BGMV_SHRINK_RT, LORA_BGMV_RPI, LORA_BGMV_CB) from the
+ * environment.  They are read once when the library is loaded; this is for
+ * tests and measurement that change them within one process, and must not
+ * run concurrently with other calls.  Every plan they select computes the
+ * same result. */
+void lora_reload_tuning(void);
 
 /* Message describing the last non-OK status returned on this thread. */
 const char *lora_last_error(void);

@@ -4,8 +4,9 @@ Argument marshalling only: every step of the path runs in the library's HIP
 kernels.  PyTorch provides device memory and the current stream.  The entry
 points carry the C-ABI names of ``include/lora.h``:
 
-    lora_build_segments, lora_shrink, lora_expand, lora_expand_slice,
-    lora_shrink_workspace_bytes, lora_set_path, lora_last_error
+    lora_segments_workspace_bytes, lora_build_segments, lora_shrink,
+    lora_expand, lora_expand_slice, lora_shrink_workspace_bytes,
+    lora_set_path, lora_reload_tuning, lora_last_error
 
 If the shared library has not been built (``python -m
 lora_serving_build_amd.build``), every entry point raises: there is no
@@ -21,7 +22,8 @@ import torch
 
 __all__ = [
     "LoraError", "Segments", "lib", "lora_build_segments", "lora_shrink", "lora_expand",
-    "lora_expand_slice", "lora_shrink_workspace_bytes", "lora_last_error", "lora_set_path",
+    "lora_expand_slice", "lora_shrink_workspace_bytes", "lora_segments_workspace_bytes",
+    "lora_last_error", "lora_set_path", "lora_reload_tuning",
     "PATH_AUTO", "PATH_BGMV", "PATH_SGMV", "LORA_F16", "LORA_BF16", "LORA_MAX_RANK", "LORA_MAX_LORAS",
     "LORA_MAX_SLICES", "library_path",
 ]
@@ -71,7 +73,11 @@ def lib() -> ctypes.CDLL:
             L = ctypes.CDLL(library_path)
             p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
             seg_p = ctypes.POINTER(_CSegments)
-            L.lora_build_segments.argtypes = [seg_p, p]
+            L.lora_segments_workspace_bytes.argtypes = [i32, i32]
+            L.lora_segments_workspace_bytes.restype = sz
+            L.lora_build_segments.argtypes = [p, i32, i32, seg_p, p, sz, p]
+            L.lora_reload_tuning.argtypes = []
+            L.lora_reload_tuning.restype = None
             L.lora_shrink_workspace_bytes.argtypes = [i32, i32, i32, i32]
             L.lora_shrink_workspace_bytes.restype = sz
             L.lora_shrink.argtypes = [p, i64, p, i32, i32, seg_p, p, i64, p, sz, ctypes.c_int, p]
@@ -97,6 +103,12 @@ def lora_set_path(mode: int) -> int:
     if rc < 0:
         raise LoraError(rc, lora_last_error())
     return rc
+
+
+def lora_reload_tuning() -> None:
+    """Re-reads the launch-plan override variables from the environment
+    (tests and measurement only)."""
+    lib().lora_reload_tuning()
 
 
 def lora_last_error() -> str:
@@ -162,13 +174,27 @@ class Segments:
         return ctypes.byref(self.c)
 
 
+def lora_segments_workspace_bytes(T: int, L: int) -> int:
+    return int(lib().lora_segments_workspace_bytes(int(T), int(L)))
+
+
 def lora_build_segments(token_lora: torch.Tensor, num_loras: int,
                         seg: Segments | None = None, lora_rank: torch.Tensor | None = None) -> Segments:
     """Groups the batch's tokens by adapter id (see include/lora.h).  lora_rank
-    (optional, [L] int32): live rank of each adapter, for the segment kernels."""
+    (optional, [L] int32): live rank of each adapter, for the segment kernels.
+    With seg given, its buffers are reused (seg must have been made for this
+    token_lora tensor and num_loras)."""
     if seg is None:
         seg = Segments(token_lora, num_loras, lora_rank)
-    _check(lib().lora_build_segments(seg.ref(), _stream(seg.device)))
+    elif seg.token_lora.data_ptr() != token_lora.data_ptr() or seg.num_loras != int(num_loras):
+        raise ValueError("seg was made for another token_lora tensor or adapter count")
+    T = seg.num_tokens
+    need = lora_segments_workspace_bytes(T, seg.num_loras)
+    ws = _workspace(seg.device, need)
+    ws_ptr = ctypes.c_void_p(ws.data_ptr()) if ws is not None else None
+    ws_bytes = ws.numel() if ws is not None else 0
+    _check(lib().lora_build_segments(ctypes.c_void_p(seg.token_lora.data_ptr()), T, seg.num_loras,
+                                     seg.ref(), ws_ptr, ws_bytes, _stream(seg.device)))
     return seg
 
 

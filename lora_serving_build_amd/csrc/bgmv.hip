@@ -267,12 +267,20 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_expand_kernel(BgExpandArgs a)
       const int nq = a.slices[q].n;
       const uint16_t* Bl = a.slices[q].B + (int64_t)l * nq * a.r;
       uint16_t* yrow = a.y + (int64_t)t * a.ldy + a.slices[q].col_off;
-      // hi / lo 16-bit pairs of v (ranks >= r are zero).
+      // hi / lo 16-bit pairs of v (ranks >= r are zero), after the binary16
+      // prescale of the token's v (f16_prescale; none for bfloat16).
+      float vv[RT];
+      float vmax = 0.f;
+#pragma unroll
+      for (int k = 0; k < RT; ++k) {
+        vv[k] = k < a.r ? vrow[k] : 0.f;
+        vmax = fmaxf(vmax, fabsf(vv[k]));
+      }
+      float down = 1.f, up = 1.f;
+      if constexpr (DT == 0) f16_prescale(vmax, &down, &up);
       uint32_t vhi[RT / 2], vlo[RT / 2];
 #pragma unroll
-      for (int k = 0; k < RT / 2; ++k)
-        split_hilo<DT>(2 * k < a.r ? vrow[2 * k] : 0.f, 2 * k + 1 < a.r ? vrow[2 * k + 1] : 0.f,
-                       &vhi[k], &vlo[k]);
+      for (int k = 0; k < RT / 2; ++k) split_hilo<DT>(vv[2 * k] * down, vv[2 * k + 1] * down, &vhi[k], &vlo[k]);
       // Up to two column blocks per trip; their y loads are issued first.
       for (int c0 = tid * 8; c0 < nq; c0 += UNR * BLK) {
         u32x4 yv[UNR];
@@ -285,8 +293,13 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_expand_kernel(BgExpandArgs a)
         float out[UNR][8];
 #pragma unroll
         for (int u = 0; u < UNR; ++u)
-          if (c0 + u * BLK < nq)
+          if (c0 + u * BLK < nq) {
             bg_expand_cols<DT, VEC, RT / 8>(Bl, nq, a.r, c0 + u * BLK, vhi, vlo, out[u]);
+            if constexpr (DT == 0) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) out[u][e] *= up;
+            }
+          }
 #pragma unroll
         for (int u = 0; u < UNR; ++u)
           if (c0 + u * BLK < nq) bg_store_cols<DT, VEC>(yrow, nq, c0 + u * BLK, a.add, yv[u], out[u]);
@@ -366,6 +379,19 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_expand_fast_kernel(BgExpandAr
         // the opaque moves keep the split of v from being hoisted above them.
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("" : "+v"(va), "+v"(vb));
+        // Binary16 prescale of the token's v (f16_prescale): the G lanes of
+        // a column group hold the whole row, so their maximum is the row's.
+        float down = 1.f, up = 1.f;
+        if constexpr (DT == 0) {
+          float vmax = fmaxf(fmaxf(fmaxf(fabsf(va.x), fabsf(va.y)), fmaxf(fabsf(va.z), fabsf(va.w))),
+                             fmaxf(fmaxf(fabsf(vb.x), fabsf(vb.y)), fmaxf(fabsf(vb.z), fabsf(vb.w))));
+          if constexpr (G >= 2) vmax = fmaxf(vmax, lane_xor<0>(vmax, lane));
+          if constexpr (G >= 4) vmax = fmaxf(vmax, lane_xor<1>(vmax, lane));
+          if constexpr (G >= 8) vmax = fmaxf(vmax, lane_xor<2>(vmax, lane));
+          f16_prescale(vmax, &down, &up);
+          va *= down;
+          vb *= down;
+        }
         uint32_t vh[4], vl[4];
         split_hilo<DT>(va.x, va.y, &vh[0], &vl[0]);
         split_hilo<DT>(va.z, va.w, &vh[1], &vl[1]);
@@ -391,7 +417,7 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_expand_fast_kernel(BgExpandAr
               if constexpr (G >= 8) p = p + lane_xor<2>(p, lane);
               if (part == 0) {
                 const int c = (kb + k) * CPI + (lane >> LG);  // a run of CPI columns in one 128
-                so[u * kSoRow + c + ((c >> 7) << 2)] = p;
+                so[u * kSoRow + c + ((c >> 7) << 2)] = DT == 0 ? p * up : p;
               }
             }
           }
@@ -433,10 +459,8 @@ int bgmv_shrink_ranks(int64_t T, int32_t r, int32_t H) {
   const int64_t want = H >= 12288 ? 512 : 256;
   int rt = 16;
   while (rt > 4 && (rt / 2 >= r || T * ((r + rt - 1) / rt) < want)) rt /= 2;
-  if (const char* e = getenv("LORA_BGMV_SHRINK_RT")) {
-    const long f = atol(e);
-    if (f == 4 || f == 8 || f == 16) rt = (int)f;
-  }
+  const int f = tuning().bgmv_shrink_rt;
+  if (f == 4 || f == 8 || f == 16) rt = f;
   return rt;
 }
 
@@ -492,15 +516,11 @@ hipError_t launch_bgmv_expand(const SegView& seg, const float* v, int64_t ldv, i
     }
     const int64_t T = seg.T > 0 ? seg.T : 1;
     int rpi = 1;
-    if (const char* e = getenv("LORA_BGMV_RPI")) {
-      const long f = atol(e);
-      if (f == 1 || (f == 2 && r <= 16)) rpi = (int)f;
-    }
+    const int f_rpi = tuning().bgmv_rpi;
+    if (f_rpi == 1 || (f_rpi == 2 && r <= 16)) rpi = f_rpi;
     int64_t cb = (rounds + (int64_t)nw * rpi - 1) / ((int64_t)nw * rpi);
-    if (const char* e = getenv("LORA_BGMV_CB")) {
-      const long f = atol(e);
-      if (f >= 1 && f < cb) cb = f;
-    }
+    const int f_cb = tuning().bgmv_cb;
+    if (f_cb >= 1 && f_cb < cb) cb = f_cb;
     a.cb = (int32_t)cb;
     int64_t grid = T * cb;
     if (grid > 8192) grid = 8192;

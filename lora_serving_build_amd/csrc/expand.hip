@@ -225,6 +225,9 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
     // not hold it back and it is in flight through v's conversion and the
     // first barrier.
     u32x4 yfirst[TB][NP];
+    // Per token: 2^k of the binary16 prescale (1 for bfloat16, whose range is
+    // fp32's), applied to the fp32 products before y is added.
+    float vscale[TB];
     {
       constexpr int NV = kPack ? NKS / 2 : NKS;  // 8-rank groups per lane
       f32x4 vraw[TB][NV][2];
@@ -250,16 +253,31 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int b = 0; b < TB; ++b) {
+        float vk[NV][8];
+        float vmax = 0.f;
 #pragma unroll
         for (int st = 0; st < NV; ++st) {
           const int rk = kPack ? st * 32 + g * 8 : st * 16 + (g & 1) * 8;
           const bool keep = tok_ok[b] && rk < rank_l && (VEC ? rk + 8 <= a.r : true);
           const float vv[8] = {vraw[b][st][0].x, vraw[b][st][0].y, vraw[b][st][0].z, vraw[b][st][0].w,
                                vraw[b][st][1].x, vraw[b][st][1].y, vraw[b][st][1].z, vraw[b][st][1].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            vk[st][e] = keep ? vv[e] : 0.f;
+            vmax = fmaxf(vmax, fabsf(vk[st][e]));
+          }
+        }
+        // The four lane groups of row position m together hold every rank of
+        // token m (groups 2 and 3 repeat 0 and 1 for r <= 16).
+        float down = 1.f;
+        vscale[b] = 1.f;
+        if constexpr (DT == 0) f16_prescale(max_over_lane_groups(vmax), &down, &vscale[b]);
+#pragma unroll
+        for (int st = 0; st < NV; ++st) {
           uint32_t h4[4], l4[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float f0 = keep ? vv[2 * e] : 0.f, f1 = keep ? vv[2 * e + 1] : 0.f;
+            const float f0 = vk[st][2 * e] * down, f1 = vk[st][2 * e + 1] * down;
             const uint32_t hi = cvt_pack2<DT>(f0, f1);
             float h0, h1;
             unpack2<DT>(hi, &h0, &h1);
@@ -348,6 +366,10 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
                 out[e] = __uint_as_float(sw[0]);
                 out[4 + e] = __uint_as_float(sw[1]);
               }
+              if constexpr (DT == 0) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) out[e] *= vscale[b];
+              }
               const int col = c * kExpandCols + 32 * p + pc;
               const int cvalid = nq - col;
               if (cvalid <= 0) continue;
@@ -420,10 +442,7 @@ hipError_t launch_expand(const SegView& seg, const float* v, int64_t ldv, int64_
   // call has few items (2048-token prefill: 640).  Taken from 16384
   // tile-chunks up, for r <= 64.
   int tb = (nks <= 4 && max_token_tiles(seg.T, seg.L, 2 * kTileTokens) * chunks >= 16384) ? 2 : 1;
-  if (const char* e = getenv("LORA_EXPAND_TB")) {
-    const long f = atol(e);
-    if (f == 1 || f == 2) tb = (int)f;
-  }
+  if (tuning().expand_tb == 1 || tuning().expand_tb == 2) tb = tuning().expand_tb;
   if (nks == 8) tb = 1;
   const int64_t tt = (int64_t)kTileTokens * tb;
   const int64_t mt_max = max_token_tiles(seg.T, seg.L, tt);
@@ -436,10 +455,7 @@ hipError_t launch_expand(const SegView& seg, const float* v, int64_t ldv, int64_
   int64_t cpr = mt_max * chunks / 4096;
   if (cpr > 8) cpr = 8;
   if (cpr < 2) cpr = 2;
-  if (const char* e = getenv("LORA_EXPAND_CPR")) {
-    const long f = atol(e);
-    if (f >= 1) cpr = f;
-  }
+  if (tuning().expand_cpr >= 1) cpr = tuning().expand_cpr;
   a.cpr = (int32_t)cpr;
   int32_t runs = 0;
   for (int q = 0; q < num_slices; ++q) {

@@ -3,6 +3,7 @@
 // copies between host and device or synchronises.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -101,6 +102,27 @@ bool use_bgmv(Op op, int32_t T, int32_t r, int64_t width, bool vec) {
   return false;
 }
 
+int read_env_int(const char* name) {
+  const char* e = getenv(name);
+  if (!e) return 0;
+  const long v = atol(e);
+  return v > 0 && v < (1 << 20) ? (int)v : 0;
+}
+
+lora::Tuning read_tuning() {
+  lora::Tuning t;
+  t.shrink_ksplit = read_env_int("LORA_SHRINK_KSPLIT");
+  t.expand_tb = read_env_int("LORA_EXPAND_TB");
+  t.expand_cpr = read_env_int("LORA_EXPAND_CPR");
+  t.bgmv_shrink_rt = read_env_int("LORA_BGMV_SHRINK_RT");
+  t.bgmv_rpi = read_env_int("LORA_BGMV_RPI");
+  t.bgmv_cb = read_env_int("LORA_BGMV_CB");
+  return t;
+}
+
+// Read once, when the library is loaded.
+lora::Tuning g_tuning = read_tuning();
+
 lora::SegView view(const lora_segments* seg) {
   lora::SegView s;
   s.token_lora = seg->token_lora;
@@ -116,10 +138,36 @@ lora::SegView view(const lora_segments* seg) {
 
 }  // namespace
 
+namespace lora {
+const Tuning& tuning() { return g_tuning; }
+void reload_tuning() { g_tuning = read_tuning(); }
+}  // namespace lora
+
 extern "C" {
 
-int lora_build_segments(const lora_segments* seg, void* stream) {
+size_t lora_segments_workspace_bytes(int32_t T, int32_t L) {
+  // The builder is one workgroup whose histogram, scans and scatter cursors
+  // all live in LDS: it needs no device scratch for any T and L in range.
+  (void)T;
+  (void)L;
+  return 0;
+}
+
+int lora_build_segments(const int32_t* token_lora, int32_t T, int32_t L, lora_segments* seg,
+                        void* workspace, size_t workspace_bytes, void* stream) {
   static const char* fn = "lora_build_segments";
+  if (!seg) return fail(LORA_ERR_INVALID_ARG, "%s: seg is NULL", fn);
+  if (T < 0) return fail(LORA_ERR_INVALID_ARG, "%s: num_tokens %d < 0", fn, T);
+  if (L < 1 || L > LORA_MAX_LORAS)
+    return fail(LORA_ERR_UNSUPPORTED, "%s: num_loras %d outside [1, %d]", fn, L, LORA_MAX_LORAS);
+  if (T > 0 && !token_lora) return fail(LORA_ERR_INVALID_ARG, "%s: token buffers must not be NULL", fn);
+  const size_t need = lora_segments_workspace_bytes(T, L);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(LORA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace ? workspace_bytes : (size_t)0);
+  seg->num_tokens = T;
+  seg->num_loras = L;
+  seg->token_lora = token_lora;
   if (int e = check_segments(seg, fn)) return e;
   hipError_t err = lora::launch_build_segments(seg->token_lora, seg->num_tokens, seg->num_loras,
                                                seg->sorted_token, seg->seg_lora, seg->seg_start,
@@ -250,6 +298,8 @@ int lora_set_path(int mode) {
     return fail(LORA_ERR_INVALID_ARG, "lora_set_path: mode %d is not 0, 1 or 2", mode);
   return g_path.exchange(mode);
 }
+
+void lora_reload_tuning(void) { lora::reload_tuning(); }
 
 const char* lora_last_error(void) { return g_error; }
 

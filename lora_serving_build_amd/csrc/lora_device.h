@@ -70,6 +70,34 @@ __device__ __forceinline__ void unpack2(uint32_t d, float* lo, float* hi) {
   }
 }
 
+// ---------------------------------------------------------------- binary16 range of v
+// expand feeds the fp32 v to 16-bit products as hi = round16(v) plus
+// lo = round16(v - hi).  In binary16 a |v| of 65520 or more would round to
+// infinity, and values below 2^-14 lose bits to subnormals.  A power of two
+// 2^-k taken per token moves the token's largest |v| into [2^13, 2^14) before
+// the split, and the fp32 product is multiplied by 2^k afterwards: both are
+// exact, so the result is the unscaled one wherever that one is in range.
+// k = 0 for a zero, fp32-subnormal or non-finite maximum; |k| <= 100 keeps
+// both factors normal fp32 numbers.
+__device__ __forceinline__ void f16_prescale(float maxabs, float* down, float* up) {
+  const uint32_t e = (__float_as_uint(maxabs) >> 23) & 0xffu;
+  int k = (e == 0u || e == 255u) ? 0 : (int)e - 127 - 13;
+  k = k < -100 ? -100 : (k > 100 ? 100 : k);
+  *down = __uint_as_float((uint32_t)(127 - k) << 23);
+  *up = __uint_as_float((uint32_t)(127 + k) << 23);
+}
+
+// Maximum of x over the four lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four
+// lane groups of one row position), with the gfx950 lane-swap instructions:
+// called with both operands equal, each returns the lane's own value and that
+// of its partner row.  Every lane of the wave must be active.
+__device__ __forceinline__ float max_over_lane_groups(float x) {
+  auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+
 // ---------------------------------------------------------------- matrix core
 // D(16x16, fp32) += A(16x32) * B(32x16) with 8 elements of A and B per lane.
 // Whatever the hardware's internal k numbering, slot (lane / 16, element e) of

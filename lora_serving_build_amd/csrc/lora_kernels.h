@@ -21,6 +21,22 @@ constexpr int kExpandCols = 128;
 // H elements one shrink K-step covers (4 lane groups x 32 elements).
 constexpr int kShrinkKStep = 128;
 
+// Launch-plan overrides for tests and measurement, read from the
+// environment once when the library is loaded (and again on
+// lora_reload_tuning): LORA_SHRINK_KSPLIT, LORA_EXPAND_TB, LORA_EXPAND_CPR,
+// LORA_BGMV_SHRINK_RT, LORA_BGMV_RPI, LORA_BGMV_CB.  0 = not set: the
+// launchers' own choice.
+struct Tuning {
+  int shrink_ksplit;
+  int expand_tb;
+  int expand_cpr;
+  int bgmv_shrink_rt;
+  int bgmv_rpi;
+  int bgmv_cb;
+};
+const Tuning& tuning();
+void reload_tuning();
+
 struct SegView {
   const int32_t* token_lora;
   const int32_t* sorted_token;

@@ -290,13 +290,6 @@ hipError_t launch_typed(const ShrinkArgs& args, int njt, int grid, hipStream_t s
   return hipGetLastError();
 }
 
-int env_int(const char* name, int dflt) {
-  const char* e = getenv(name);
-  if (!e) return dflt;
-  const long v = atol(e);
-  return v > 0 ? (int)v : dflt;
-}
-
 }  // namespace
 
 ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r) {
@@ -330,7 +323,7 @@ ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r) {
   if (ks_max < 1) ks_max = 1;
   if (ks > ks_max) ks = ks_max;
   if (ks < 1) ks = 1;
-  ks = env_int("LORA_SHRINK_KSPLIT", (int)ks);
+  if (tuning().shrink_ksplit > 0) ks = tuning().shrink_ksplit;
   int64_t chunk = (H + ks - 1) / ks;
   chunk = (chunk + kSkKB - 1) / kSkKB * kSkKB;
   ks = (H + chunk - 1) / chunk;

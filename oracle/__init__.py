@@ -47,7 +47,9 @@ def build(force: bool = True) -> str:
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        stale = (_LIB.endswith("liblora_oracle.so") and os.path.exists(_LIB)
+                 and os.path.getmtime(_LIB) < os.path.getmtime(_SRC))
+        if not os.path.exists(_LIB) or stale:
             build(force=True)
         L = ctypes.CDLL(_LIB)
         i32, i64, p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
@@ -56,6 +58,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
         L.oracle_decode_bf16.restype = ctypes.c_double
         L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        L.oracle_set_num_threads.restype = ctypes.c_int
         L.oracle_build_segments.argtypes = [p, i32, i32, p, p, p, p]
         L.oracle_shrink.argtypes = [ctypes.c_int, p, i64, p, i32, i32, p, i32,
                                     i32, p, i32, p]
@@ -80,6 +84,12 @@ def _c(a, dtype):
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> int:
+    """Sets the oracle's OpenMP thread count; returns the previous one.
+    Results do not depend on it (every row's sum order is fixed)."""
+    return int(lib().oracle_set_num_threads(int(n)))
 
 
 def decode(bits: np.ndarray, dtype) -> np.ndarray:

@@ -91,6 +91,19 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads of the loops below (n < 1 leaves the setting alone); returns the
+ * previous count.  Every row's sum order is fixed, so results do not depend
+ * on it: it only changes how long a call takes. */
+int oracle_set_num_threads(int n) {
+  int prev = oracle_num_threads();
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+  return prev;
+}
+
 static int active_id(int32_t id, int32_t L) { return id >= 0 && id < L; }
 
 /* ---- segment metadata -------------------------------------------------

@@ -26,11 +26,23 @@ def declared_functions():
     return sorted(names)
 
 
+# The boundary's calls: the four operations, the metadata workspace query and
+# the error message, plus this library's shrink workspace query, path switch
+# and tuning reload.
+BOUNDARY = ("lora_segments_workspace_bytes", "lora_build_segments", "lora_shrink", "lora_expand",
+            "lora_expand_slice", "lora_last_error", "lora_shrink_workspace_bytes", "lora_set_path",
+            "lora_reload_tuning")
+
+
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for f in ("lora_build_segments", "lora_shrink", "lora_expand", "lora_expand_slice",
-              "lora_shrink_workspace_bytes", "lora_last_error"):
+    for f in BOUNDARY:
         assert f in names
+
+
+def test_binding_carries_the_boundary_names():
+    for f in BOUNDARY:
+        assert callable(getattr(lsb, f)), f
 
 
 @pytest.mark.parametrize("name", declared_functions())
@@ -51,14 +63,36 @@ def _expect(rc, code, text):
 
 def test_build_segments_validation():
     lib = lsb.lib()
-    _expect(lib.lora_build_segments(None, None), lsb.LORA_ERR_INVALID_ARG, "seg is NULL")
-    s = _seg(T=-1)
-    _expect(lib.lora_build_segments(ctypes.byref(s), None), lsb.LORA_ERR_INVALID_ARG, "num_tokens")
+    s = _seg()
+    sp = ctypes.byref(s)
+    _expect(lib.lora_build_segments(FAKE, 16, 4, None, None, 0, None), lsb.LORA_ERR_INVALID_ARG,
+            "seg is NULL")
+    _expect(lib.lora_build_segments(FAKE, -1, 4, sp, None, 0, None), lsb.LORA_ERR_INVALID_ARG,
+            "num_tokens")
     for L in (0, lsb.LORA_MAX_LORAS + 1):
-        s = _seg(L=L)
-        _expect(lib.lora_build_segments(ctypes.byref(s), None), lsb.LORA_ERR_UNSUPPORTED, "num_loras")
-    s = _seg(token=False)
-    _expect(lib.lora_build_segments(ctypes.byref(s), None), lsb.LORA_ERR_INVALID_ARG, "token buffers")
+        _expect(lib.lora_build_segments(FAKE, 16, L, sp, None, 0, None), lsb.LORA_ERR_UNSUPPORTED,
+                "num_loras")
+    _expect(lib.lora_build_segments(None, 16, 4, sp, None, 0, None), lsb.LORA_ERR_INVALID_ARG,
+            "token buffers")
+    s2 = lsb._CSegments(0, 0, None, None, FAKE.value, FAKE.value, FAKE.value)
+    _expect(lib.lora_build_segments(FAKE, 16, 4, ctypes.byref(s2), None, 0, None),
+            lsb.LORA_ERR_INVALID_ARG, "token buffers")
+
+
+def test_build_segments_fills_the_struct():
+    """The call records T, L and the id pointer in the struct before it
+    checks the output buffers (a missing one here, so nothing is launched)."""
+    lib = lsb.lib()
+    s = lsb._CSegments(99, 99, None, FAKE.value, None, FAKE.value, FAKE.value)
+    _expect(lib.lora_build_segments(FAKE, 5, 7, ctypes.byref(s), None, 0, None),
+            lsb.LORA_ERR_INVALID_ARG, "segment buffers")
+    assert (s.num_tokens, s.num_loras, s.token_lora) == (5, 7, FAKE.value)
+
+
+@pytest.mark.parametrize("T,L", [(0, 1), (16, 4), (8192, 64), (65536, 2048)])
+def test_segments_workspace_bytes(T, L):
+    # The one-workgroup builder keeps its scratch in LDS.
+    assert lsb.lora_segments_workspace_bytes(T, L) == 0
 
 
 def test_shrink_validation():

@@ -26,3 +26,32 @@ def test_launcher_world_size_is_refused():
     r = _run(env={"WORLD_SIZE": "4"})
     assert r.returncode == 2
     assert "WORLD_SIZE 4" in r.stderr
+
+
+def test_tolerance_ratio_fails_on_nan():
+    """The benchmark's pre-timing check: a NaN or an infinity where the
+    oracle is finite fails it (a plain max() would skip a NaN)."""
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    import bench
+    ref = np.array([1.0, 2.0, 3.0])
+    assert bench.tol_ratio(ref + 0.001, ref) <= 1
+    assert bench.tol_ratio(np.array([1.0, np.nan, 3.0]), ref) == float("inf")
+    assert bench.tol_ratio(np.array([1.0, np.inf, 3.0]), ref) == float("inf")
+    assert bench.tol_ratio(np.array([1.0, 2.5, 3.0]), ref) > 1
+
+
+def test_profile_dispatches_are_assigned_to_calls():
+    """rocprofv3 rows of a --profile run are attributed to the calls of a
+    step by dispatch order: build, shrink (one or two kernels), then one
+    expand per output."""
+    sys.path.insert(0, ROOT)
+    import bench
+    names = ["build_segments_kernel", "shrink_kernel", "shrink_reduce_kernel", "expand_kernel<1>",
+             "expand_kernel<2>", "at::neg_kernel", "build_segments_kernel", "bgmv_shrink_kernel",
+             "expand_kernel<1>", "expand_kernel<2>"]
+    rows = [{"Dispatch_Id": str(i + 1), "Kernel_Name": n} for i, n in enumerate(names)]
+    units = [u for u, _ in bench.assign_units(list(reversed(rows)), 2)]
+    assert units == ["build", "shrink", "shrink", "expand[0]", "expand[1]", None,
+                     "build", "shrink", "expand[0]", "expand[1]"]
+    assert [u for u, _ in bench.assign_units(rows[:4], 1)] == ["build", "shrink", "shrink", "expand"]

@@ -131,13 +131,16 @@ class Workload:
         e = 2
         return self.T_a * self.H * e + self.distinct * self.r * self.H * e + self.T_a * self.r * 4
 
-    def expand_bytes(self) -> int:
+    def output_bytes(self, o: "Output") -> int:
+        """Algorithmic bytes of the one expand / expand_slice call that writes
+        output o: v read, the present adapters' weights, y read (add) and
+        written."""
         e = 2
-        tot = 0
-        for o in self.outputs:
-            n = sum(s.n for s in o.slices)
-            tot += self.T_a * self.r * 4 + self.distinct * self.r * n * e + (2 if self.add else 1) * self.T_a * n * e
-        return tot
+        n = sum(s.n for s in o.slices)
+        return self.T_a * self.r * 4 + self.distinct * self.r * n * e + (2 if self.add else 1) * self.T_a * n * e
+
+    def expand_bytes(self) -> int:
+        return sum(self.output_bytes(o) for o in self.outputs)
 
     def shrink_flops(self) -> int:
         return 2 * self.T_a * self.H * self.r
