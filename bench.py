@@ -498,36 +498,78 @@ def summarize_profiles(args):
     print("wrote", path)
 
 
-SWEEP_POINTS = (  # (kind, tokens, hidden, rank): the micro-benchmark grid, thinned
-    [(k, T, H, r) for k in ("bgmv", "sgmv") for T in (16, 256, 2048, 8192)
-     for H in (4096, 16384) for r in (16, 64)]
-    + [("sgmv", 65536, 16384, 16)]   # the review thread's bs 8192 x seq 8 example
-    # one adapter for every token (the TPU PR's unmasked single-adapter case):
-    # torch.mm of the same shapes (hipBLASLt) is timed beside it
-    + [("single", T, H, r) for T in (256, 2048, 8192) for H in (4096, 16384) for r in (16, 64)]
-    # LoRA on the logits layer (TPU PR): expand r -> vocabulary, 128256 columns
-    + [("logits", T, 4096, 16) for T in (16, 256, 2048)])
+def golden_shapes():
+    """The problem shapes the micro-benchmark PR prints (tests/golden/
+    microbench_shapes.txt): its console table's SGMV expand and the review
+    thread's bs 8192 x seq 8 example."""
+    out = []
+    with open(os.path.join(ROOT, "tests", "golden", "microbench_shapes.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                src, bs, sl, m, k, n, L, srt, ns = line.split()
+                out.append(dict(source=src, bs=int(bs), sl=int(sl), m=int(m), rank=int(k), n=int(n),
+                                num_loras=int(L), sort=bool(int(srt)), num_slices=int(ns)))
+    return out
+
+
+SWEEP_TOKENS = (16, 128, 256, 512, 1024, 2048, 8192)
+SWEEP_HIDDEN = (1024, 2048, 4096, 8192, 16384)
+SWEEP_RANKS = (8, 16, 32, 64, 128)
+
+
+def sweep_points(grid="full"):
+    """(kind, tokens, hidden, rank, out_cols, adapters, seq_len, add) of the
+    sweep.  kind bgmv / sgmv: the micro-benchmark PR's grid (batches,
+    hidden sizes, 4 adapters, sorted by id; one token per sequence or eight)
+    widened to ranks 8-128; single: one adapter for every token, beside
+    torch.mm of the same shapes; logits: expand r -> 128256 columns; golden:
+    the shapes the PR prints (expand with add_inputs off, as its table)."""
+    pts = []
+    if grid == "full":
+        for kind in ("bgmv", "sgmv"):
+            for T in SWEEP_TOKENS:
+                for H in SWEEP_HIDDEN:
+                    for r in SWEEP_RANKS:
+                        pts.append((kind, T, H, r, H, 4, 1 if kind == "bgmv" else 8, True))
+    else:
+        for kind in ("bgmv", "sgmv"):
+            for T in (16, 256, 2048, 8192):
+                for H in (4096, 16384):
+                    for r in (16, 64):
+                        pts.append((kind, T, H, r, H, 4, 1 if kind == "bgmv" else 8, True))
+    pts += [("single", T, H, r, H, 1, 8, True) for T in (256, 2048, 8192) for H in (4096, 16384)
+            for r in (16, 64)]
+    pts += [("logits", T, 4096, 16, 128256, 4, 1, True) for T in (16, 256, 2048)]
+    for g in golden_shapes():
+        pts.append((f"golden:{g['source']}", g["m"], g["n"], g["rank"], g["n"], g["num_loras"], g["sl"],
+                    g["source"] != "console_table"))
+    return pts
 
 
 def sweep(args):
-    """Shrink and expand alone on the micro-benchmark sweep shapes: 4 adapters,
-    ids sorted, one token per sequence (bgmv) or eight (sgmv), expand r -> H
-    with add_inputs; then one adapter for every token beside torch.mm of the
-    same shapes, and the logits layer (expand r -> 128256 columns).  Ids come from the shared generator; the tensors are drawn
-    on the GPU (seeded) because host generation of the large points takes
-    longer than timing them.  One JSON line per point and op."""
+    """Shrink and expand alone on the sweep shapes (fp16).  Before a point is
+    timed, one set of its inputs runs build -> shrink -> expand and a sample
+    of rows (the first and last of every segment, plus random ones) is
+    checked against the oracle; a point that fails is reported and not
+    timed.  Ids come from the shared generator; the tensors are drawn on the
+    GPU (seeded), because host generation of the large points takes longer
+    than timing them.  One JSON line per point and op."""
+    import numpy as np
     import torch
     import lora_serving_build_amd as lsb
+    import oracle
     import workloads as W
     torch.cuda.set_device(0)
     dt = torch.float16
     gen = torch.Generator(device="cuda")
-    for kind, T, H, r in SWEEP_POINTS:
-        L = 1 if kind == "single" else 4
-        n = 128256 if kind == "logits" else H
-        ids_w = W.sweep_point("bgmv" if kind == "logits" else ("sgmv" if kind == "single" else kind),
-                              T, 8, 8, L=L)  # same id draw as the full-size point
-        ids = torch.from_numpy(ids_w.ids).cuda()
+    for kind, T, H, r, n, L, sl, add in sweep_points(args.sweep_grid):
+        base_kind = "sgmv" if kind in ("single",) or kind.startswith("golden") else \
+            ("bgmv" if kind == "logits" else kind)
+        ids_w = W.make(f"{kind}_T{T}", "f16", T, 8, 8, L, [[8]], seed=7, seq_len=sl, sort_by_id=True) \
+            if kind.startswith("golden") or kind == "single" else \
+            W.sweep_point(base_kind, T, 8, 8, L=L)  # the same id draw at every size
+        ids_np = ids_w.ids
+        ids = torch.from_numpy(ids_np).cuda()
         per_set = T * H * 2 + T * n * 2 + L * r * H * 2 + L * r * n * 2 + T * r * 4
         P = max(2, min(64, int(math.ceil(args.pool_gib * 2**30 / per_set))))
         gen.manual_seed(T * 131 + H * 7 + r)
@@ -543,9 +585,45 @@ def sweep(args):
         need = lsb.lora_shrink_workspace_bytes(T, L, H, r)
         ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
         torch.cuda.synchronize()
+        head = {"sweep": kind, "tokens": T, "hidden": H, "out_cols": n, "rank": r, "num_loras": L,
+                "seq_len": sl, "add_inputs": add}
+
+        # Correctness first: one step on set 0 (y on a copy), sampled rows
+        # against the oracle.
+        s0 = sets[0]
+        y_chk = s0["y"].clone()
+        lsb.lora_build_segments(ids, L, seg=s0["seg"])
+        lsb.lora_shrink(s0["x"], s0["A"], s0["seg"], s0["v"], workspace=ws)
+        lsb.lora_expand(s0["v"], s0["B"], s0["seg"], y_chk, add)
+        torch.cuda.synchronize()
+        st = s0["seg"].sorted_token[:T].cpu().numpy()
+        ss = s0["seg"].seg_start.cpu().numpy()
+        S = int(s0["seg"].counts[0].item())
+        rng = np.random.default_rng(T + H + r)
+        rows = np.unique(np.concatenate([st[ss[:S]], st[np.maximum(ss[1:S + 1] - 1, 0)],
+                                         rng.integers(0, T, 16)])).astype(np.int64)
+        ri = torch.from_numpy(rows).cuda()
+        bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+        x_s = bits(s0["x"].index_select(0, ri))
+        y0_s = bits(s0["y"].index_select(0, ri))
+        ids_s = ids_np[rows]
+        v_ref = oracle.shrink("f16", x_s, bits(s0["A"]), ids_s)
+        y_ref = oracle.expand("f16", v_ref, bits(s0["B"]), ids_s, y0_s, 0, add)
+        v_got = s0["v"].index_select(0, ri).cpu().numpy().astype(np.float64)
+        y_got = y_chk.index_select(0, ri).float().cpu().numpy().astype(np.float64)
+        ratio = max(tol_ratio(v_got, v_ref), tol_ratio(y_got, y_ref))
+        head["parity_rows"] = int(rows.size)
+        head["parity_ratio"] = round(ratio, 4)
+        del y_chk
+        if not ratio <= 1.0:
+            print(json.dumps(dict(head, error="parity check failed")), flush=True)
+            del sets, ws
+            torch.cuda.empty_cache()
+            continue
+
         K = min(P, 20) if T * H < 2**27 else 8
         shrink_b = T * H * 2 + L * r * H * 2 + T * r * 4
-        expand_b = T * r * 4 + L * r * n * 2 + 2 * T * n * 2
+        expand_b = T * r * 4 + L * r * n * 2 + (2 if add else 1) * T * n * 2
         ref = {}
         if kind == "single":
             # The same products as one dense GEMM each (fp16 in, fp16 out):
@@ -575,18 +653,56 @@ def sweep(args):
                 ref[op] = e0.elapsed_time(e1) / K * 1e3
         for op, fn, nb in (
                 ("shrink", lambda s: lsb.lora_shrink(s["x"], s["A"], s["seg"], s["v"], workspace=ws), shrink_b),
-                ("expand", lambda s: lsb.lora_expand(s["v"], s["B"], s["seg"], s["y"], True), expand_b)):
+                ("expand", lambda s: lsb.lora_expand(s["v"], s["B"], s["seg"], s["y"], add), expand_b)):
             us = graph_time(torch, fn, sets, 0, K) / K * 1e3
             gbs = nb / (us * 1e-6) / 1e9
-            rec = {"sweep": kind, "tokens": T, "hidden": H, "out_cols": n, "rank": r, "num_loras": L,
-                   "op": op, "us": round(us, 2), "GB_s": round(gbs, 1),
-                   "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                   "algorithmic_MiB": round(nb / 2**20, 2), "pool_sets": P}
+            rec = dict(head, op=op, us=round(us, 2), GB_s=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
+                       algorithmic_MiB=round(nb / 2**20, 2), pool_sets=P)
             if op in ref:
                 rec["torch_mm_us_eager"] = round(ref[op], 2)
             print(json.dumps(rec), flush=True)
         del sets, ws
         torch.cuda.empty_cache()
+
+
+def summarize_sweep(path):
+    """profiles/sweep_shrink_expand_f16.md from the JSON lines of a --sweep run."""
+    import collections
+    recs = [json.loads(l) for l in open(path) if l.startswith("{")]
+    by = collections.OrderedDict()
+    fails = []
+    for r in recs:
+        if "error" in r:
+            fails.append(r)
+            continue
+        key = (r["sweep"], r["tokens"], r["hidden"], r["out_cols"], r["rank"])
+        by.setdefault(key, {})[r["op"]] = r
+    lines = ["# Sweep: shrink and expand alone, fp16 (MI355X, one GPU)", "",
+             "command (from the repository root):",
+             "  python bench.py --sweep > sweep.jsonl; python bench.py --summarize-sweep sweep.jsonl", "",
+             "Each op timed alone: K launches over a pool of argument sets (>= 1 GiB, or 64 sets) "
+             "captured in one graph, inputs in HBM.  bgmv = one token per sequence, sgmv = eight, "
+             "4 adapters sorted by id, expand with add_inputs unless noted; single = one adapter "
+             "(torch.mm / addmm_ of the same shapes beside it, eager); logits = expand to 128256 "
+             "columns; golden = shapes the micro-benchmark PR prints.  Before timing, each point "
+             "checks sampled rows against the oracle (ratio <= 1 passes).  GB/s = algorithmic bytes "
+             "/ time; frac = of 8 TB/s.", "",
+             "| kind | T | H | n | r | parity | shrink us | GB/s | frac | expand us | GB/s | frac | torch.mm us | torch.addmm us |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for key, ops in by.items():
+        sh, ex = ops.get("shrink", {}), ops.get("expand", {})
+        any_ = sh or ex
+        lines.append(f"| {key[0]} | {key[1]} | {key[2]} | {key[3]} | {key[4]} | {any_.get('parity_ratio', '')} | "
+                     f"{sh.get('us', '')} | {sh.get('GB_s', '')} | {sh.get('hbm_frac', '')} | "
+                     f"{ex.get('us', '')} | {ex.get('GB_s', '')} | {ex.get('hbm_frac', '')} | "
+                     f"{sh.get('torch_mm_us_eager', '')} | {ex.get('torch_mm_us_eager', '')} |")
+    if fails:
+        lines += ["", "Points that failed the parity check (not timed):", ""]
+        lines += [f"- {json.dumps(f)}" for f in fails]
+    out = os.path.join(ROOT, "profiles", "sweep_shrink_expand_f16.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("wrote", out)
 
 
 def source_hash(paths):
@@ -763,6 +879,9 @@ def main():
                     help="write profiles/ summaries from rocprofv3 CSVs (--trace, --fetch, --write)")
     ap.add_argument("--sweep", action="store_true",
                     help="time shrink and expand alone on the micro-benchmark sweep shapes")
+    ap.add_argument("--sweep-grid", default="full", choices=("full", "thin"))
+    ap.add_argument("--summarize-sweep", metavar="JSONL",
+                    help="write profiles/sweep_shrink_expand_f16.md from a --sweep run's output")
     ap.add_argument("--trace", help="kernel_trace.csv of a --kernel-trace run")
     ap.add_argument("--stats", help="kernel_stats.csv of the same run")
     ap.add_argument("--fetch")
@@ -771,6 +890,9 @@ def main():
     args = ap.parse_args()
     if args.summarize_profiles:
         summarize_profiles(args)
+        return
+    if args.summarize_sweep:
+        summarize_sweep(args.summarize_sweep)
         return
     if args.sweep:
         sweep(args)
