@@ -159,6 +159,28 @@ int lora_shrink(const void *x, int64_t ldx, const void *A, int32_t H, int32_t r,
                 const lora_segments *seg, float *v, int64_t ldv, void *workspace,
                 size_t workspace_bytes, int dtype, void *stream);
 
+/* Size of the static device scratch of lora_shrink_noalloc (16 MiB per GPU). */
+#define LORA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* lora_shrink without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * kernels and results as lora_shrink; the partial rows of an H split go to a
+ * static device array of LORA_NOALLOC_SCRATCH_BYTES that each GPU holds from
+ * the library's load until the process ends (its address is looked up once
+ * per device, on the first call that needs it, with the stream's device
+ * current).  Every partial row is written before it is read, so nothing has
+ * to be cleared between calls; the array keeps the last call's contents.
+ * All calls on one GPU share the array: calls that overlap in time on one
+ * GPU (different streams, or host threads) race and must be serialised by
+ * the caller; calls on one stream are ordered and safe.
+ * Errors: those of lora_shrink; LORA_ERR_UNSUPPORTED when the call's split
+ * needs more than LORA_NOALLOC_SCRATCH_BYTES (lora_shrink_workspace_bytes
+ * gives the need) -- reported before anything is launched; LORA_ERR_INVALID_ARG
+ * when the stream belongs to a device other than the current one. */
+int lora_shrink_noalloc(const void *x, int64_t ldx, const void *A, int32_t H, int32_t r,
+                        const lora_segments *seg, float *v, int64_t ldv, int dtype, void *stream);
+
 /* Expand (micro-benchmark PR: bgmv_expand / sgmv_expand, add_inputs):
  *   y[t, c] = (add_inputs ? y[t, c] : 0) + sum_{j<r} v[t, j] * B_l[j, c],  c < n
  * for every active token; rows of tokens without an adapter and columns

@@ -23,7 +23,8 @@ import torch
 __all__ = [
     "LoraError", "Segments", "lib", "lora_build_segments", "lora_shrink", "lora_expand",
     "lora_expand_slice", "lora_shrink_workspace_bytes", "lora_segments_workspace_bytes",
-    "lora_last_error", "lora_set_path", "lora_reload_tuning",
+    "lora_last_error", "lora_set_path", "lora_reload_tuning", "lora_shrink_noalloc",
+    "LORA_NOALLOC_SCRATCH_BYTES",
     "PATH_AUTO", "PATH_BGMV", "PATH_SGMV", "LORA_F16", "LORA_BF16", "LORA_MAX_RANK", "LORA_MAX_LORAS",
     "LORA_MAX_SLICES", "library_path",
 ]
@@ -34,6 +35,7 @@ library_path = os.path.join(_HERE, "liblora_mi355x.so")
 LORA_OK, LORA_ERR_INVALID_ARG, LORA_ERR_UNSUPPORTED, LORA_ERR_WORKSPACE, LORA_ERR_HIP = 0, -1, -2, -3, -4
 LORA_F16, LORA_BF16 = 0, 1
 LORA_MAX_RANK, LORA_MAX_LORAS, LORA_MAX_SLICES = 128, 2048, 8
+LORA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class LoraError(RuntimeError):
@@ -81,13 +83,15 @@ def lib() -> ctypes.CDLL:
             L.lora_shrink_workspace_bytes.argtypes = [i32, i32, i32, i32]
             L.lora_shrink_workspace_bytes.restype = sz
             L.lora_shrink.argtypes = [p, i64, p, i32, i32, seg_p, p, i64, p, sz, ctypes.c_int, p]
+            L.lora_shrink_noalloc.argtypes = [p, i64, p, i32, i32, seg_p, p, i64, ctypes.c_int, p]
             L.lora_expand.argtypes = [p, i64, p, i32, i32, seg_p, p, i64, ctypes.c_int, ctypes.c_int, p]
             L.lora_expand_slice.argtypes = [p, i64, i64, p, p, p, i32, i32, seg_p, p, i64,
                                             ctypes.c_int, ctypes.c_int, p]
             L.lora_last_error.restype = ctypes.c_char_p
             L.lora_set_path.argtypes = [ctypes.c_int]
             L.lora_set_path.restype = ctypes.c_int
-            for f in ("lora_build_segments", "lora_shrink", "lora_expand", "lora_expand_slice"):
+            for f in ("lora_build_segments", "lora_shrink", "lora_shrink_noalloc", "lora_expand",
+                      "lora_expand_slice"):
                 getattr(L, f).restype = ctypes.c_int
             _lib = L
     return _lib
@@ -240,6 +244,26 @@ def lora_shrink(x: torch.Tensor, A: torch.Tensor, seg: Segments, v: torch.Tensor
     _check(lib().lora_shrink(ctypes.c_void_p(x.data_ptr()), ldx, ctypes.c_void_p(A.data_ptr()), H, r,
                              seg.ref(), ctypes.c_void_p(v.data_ptr()), ldv, ws_ptr, ws_bytes,
                              _dtype_code(x.dtype), _stream(x.device)))
+    return v
+
+
+def lora_shrink_noalloc(x: torch.Tensor, A: torch.Tensor, seg: Segments, v: torch.Tensor) -> torch.Tensor:
+    """lora_shrink whose H-split partial rows go to the library's static
+    device scratch: no workspace, no allocation (see include/lora.h)."""
+    if A.dim() != 3 or not A.is_contiguous():
+        raise ValueError("A must be a contiguous [L][r][H] tensor")
+    L, r, H = A.shape
+    if L != seg.num_loras:
+        raise ValueError(f"A holds {L} adapters, segments were built for {seg.num_loras}")
+    if v.dtype != torch.float32:
+        raise TypeError("v must be float32")
+    if x.dtype != A.dtype:
+        raise TypeError("x and A must share a dtype")
+    ldx = _row_major(x, "x")
+    ldv = _row_major(v, "v")
+    _check(lib().lora_shrink_noalloc(ctypes.c_void_p(x.data_ptr()), ldx, ctypes.c_void_p(A.data_ptr()), H, r,
+                                     seg.ref(), ctypes.c_void_p(v.data_ptr()), ldv, _dtype_code(x.dtype),
+                                     _stream(x.device)))
     return v
 
 

@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "lora.h"
 #include "lora_kernels.h"
@@ -143,6 +144,96 @@ const Tuning& tuning() { return g_tuning; }
 void reload_tuning() { g_tuning = read_tuning(); }
 }  // namespace lora
 
+// Scratch of lora_shrink_noalloc: the partial rows of the shrink's H split.
+// Each GPU the library runs on holds its own copy from module load until the
+// process ends.  Host code never uses this name as an address: the device
+// address of the current GPU's copy comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[LORA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of scratch on the GPU that runs `stream` (which must be the
+// current device), looked up once per device.
+int scratch_address(const char* fn, void* stream, void** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(LORA_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (stream) {
+    hipDevice_t sd = 0;
+    e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sd);
+    if (e != hipSuccess) return fail(LORA_ERR_HIP, "%s: hipStreamGetDevice: %s", fn, hipGetErrorString(e));
+    if ((int)sd != cur)
+      return fail(LORA_ERR_INVALID_ARG, "%s: the stream belongs to device %d but device %d is current", fn,
+                  (int)sd, cur);
+  }
+  if (cur < 0 || cur >= kMaxDevices)
+    return fail(LORA_ERR_UNSUPPORTED, "%s: device %d beyond the %d devices supported", fn, cur, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[cur]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(LORA_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(e));
+    g_scratch_ptr[cur] = p;
+  }
+  *out = g_scratch_ptr[cur];
+  return LORA_OK;
+}
+
+// lora_shrink and lora_shrink_noalloc.  With use_scratch, the H-split
+// partial rows go to this device's static scratch instead of a workspace.
+int shrink_call(const char* fn, const void* x, int64_t ldx, const void* A, int32_t H, int32_t r,
+                const lora_segments* seg, float* v, int64_t ldv, void* workspace, size_t workspace_bytes,
+                bool use_scratch, int dtype, void* stream) {
+  if (int e = check_dtype(dtype, fn)) return e;
+  if (int e = check_segments(seg, fn)) return e;
+  if (int e = check_rank(r, fn)) return e;
+  if (H < 1) return fail(LORA_ERR_INVALID_ARG, "%s: H %d < 1", fn, H);
+  if (ldx < H) return fail(LORA_ERR_INVALID_ARG, "%s: ldx %lld < H %d", fn, (long long)ldx, H);
+  if (ldv < r) return fail(LORA_ERR_INVALID_ARG, "%s: ldv %lld < r %d", fn, (long long)ldv, r);
+  const int32_t T = seg->num_tokens;
+  if (T == 0) return ok();
+  if (!x || !A || !v) return fail(LORA_ERR_INVALID_ARG, "%s: x, A and v must not be NULL", fn);
+  if (g_path.load(std::memory_order_relaxed) == 1 && r > lora::kBgmvMaxRank)
+    return fail(LORA_ERR_UNSUPPORTED, "%s: the per-token path takes r <= %d", fn, lora::kBgmvMaxRank);
+  const bool vec = (H % 8 == 0) && (ldx % 8 == 0) && aligned16(x) && aligned16(A) &&
+                   (ldv % 4 == 0) && aligned16(v);
+  if (use_bgmv(Op::kShrink, T, r, H, vec)) {
+    hipError_t err = lora::launch_bgmv_shrink(view(seg), static_cast<const uint16_t*>(x), ldx,
+                                              static_cast<const uint16_t*>(A), H, r, v, ldv, dtype,
+                                              vec, static_cast<hipStream_t>(stream));
+    return hip_status(err, fn);
+  }
+  const lora::ShrinkPlan plan = lora::plan_shrink(T, seg->num_loras, H, r);
+  const size_t need = plan.partial_bytes;
+  if (use_scratch && need > 0) {
+    if (need > (size_t)LORA_NOALLOC_SCRATCH_BYTES)
+      return fail(LORA_ERR_UNSUPPORTED,
+                  "%s: this shrink needs %zu bytes of scratch, more than the %zu of the static scratch "
+                  "(LORA_NOALLOC_SCRATCH_BYTES); use lora_shrink with a workspace",
+                  fn, need, (size_t)LORA_NOALLOC_SCRATCH_BYTES);
+    if (int e = scratch_address(fn, stream, &workspace)) return e;
+    workspace_bytes = LORA_NOALLOC_SCRATCH_BYTES;
+  }
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(LORA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace))
+      return fail(LORA_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned", fn);
+  }
+  hipError_t err = lora::launch_shrink(view(seg), static_cast<const uint16_t*>(x), ldx,
+                                       static_cast<const uint16_t*>(A), H, r, v, ldv, workspace,
+                                       plan, dtype, vec, static_cast<hipStream_t>(stream));
+  return hip_status(err, fn);
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t lora_segments_workspace_bytes(int32_t T, int32_t L) {
@@ -184,39 +275,14 @@ size_t lora_shrink_workspace_bytes(int32_t T, int32_t L, int32_t H, int32_t r) {
 int lora_shrink(const void* x, int64_t ldx, const void* A, int32_t H, int32_t r,
                 const lora_segments* seg, float* v, int64_t ldv, void* workspace,
                 size_t workspace_bytes, int dtype, void* stream) {
-  static const char* fn = "lora_shrink";
-  if (int e = check_dtype(dtype, fn)) return e;
-  if (int e = check_segments(seg, fn)) return e;
-  if (int e = check_rank(r, fn)) return e;
-  if (H < 1) return fail(LORA_ERR_INVALID_ARG, "%s: H %d < 1", fn, H);
-  if (ldx < H) return fail(LORA_ERR_INVALID_ARG, "%s: ldx %lld < H %d", fn, (long long)ldx, H);
-  if (ldv < r) return fail(LORA_ERR_INVALID_ARG, "%s: ldv %lld < r %d", fn, (long long)ldv, r);
-  const int32_t T = seg->num_tokens;
-  if (T == 0) return ok();
-  if (!x || !A || !v) return fail(LORA_ERR_INVALID_ARG, "%s: x, A and v must not be NULL", fn);
-  if (g_path.load(std::memory_order_relaxed) == 1 && r > lora::kBgmvMaxRank)
-    return fail(LORA_ERR_UNSUPPORTED, "%s: the per-token path takes r <= %d", fn, lora::kBgmvMaxRank);
-  const bool vec = (H % 8 == 0) && (ldx % 8 == 0) && aligned16(x) && aligned16(A) &&
-                   (ldv % 4 == 0) && aligned16(v);
-  if (use_bgmv(Op::kShrink, T, r, H, vec)) {
-    hipError_t err = lora::launch_bgmv_shrink(view(seg), static_cast<const uint16_t*>(x), ldx,
-                                              static_cast<const uint16_t*>(A), H, r, v, ldv, dtype,
-                                              vec, static_cast<hipStream_t>(stream));
-    return hip_status(err, fn);
-  }
-  const lora::ShrinkPlan plan = lora::plan_shrink(T, seg->num_loras, H, r);
-  const size_t need = plan.partial_bytes;
-  if (need > 0) {
-    if (!workspace || workspace_bytes < need)
-      return fail(LORA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
-                  workspace ? workspace_bytes : (size_t)0);
-    if (!aligned16(workspace))
-      return fail(LORA_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned", fn);
-  }
-  hipError_t err = lora::launch_shrink(view(seg), static_cast<const uint16_t*>(x), ldx,
-                                       static_cast<const uint16_t*>(A), H, r, v, ldv, workspace,
-                                       plan, dtype, vec, static_cast<hipStream_t>(stream));
-  return hip_status(err, fn);
+  return shrink_call("lora_shrink", x, ldx, A, H, r, seg, v, ldv, workspace, workspace_bytes, false,
+                     dtype, stream);
+}
+
+int lora_shrink_noalloc(const void* x, int64_t ldx, const void* A, int32_t H, int32_t r,
+                        const lora_segments* seg, float* v, int64_t ldv, int dtype, void* stream) {
+  return shrink_call("lora_shrink_noalloc", x, ldx, A, H, r, seg, v, ldv, nullptr, 0, true, dtype,
+                     stream);
 }
 
 int lora_expand_slice(const float* v, int64_t ldv, int64_t v_slice_stride, const void* const* B,

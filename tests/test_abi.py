@@ -212,3 +212,23 @@ def test_forced_bgmv_rejects_large_rank_before_launch():
         _expect(rc, lsb.LORA_ERR_UNSUPPORTED, "per-token path")
     finally:
         lib.lora_set_path(prev)
+
+
+def test_noalloc_shrink_rejects_splits_beyond_its_scratch():
+    """lora_shrink_noalloc refuses, before anything is launched or looked up
+    on a device, a shrink whose H split needs more than the static scratch."""
+    lib = lsb.lib()
+    T, L, H, r = 16392, 4, 8192, 64
+    assert lsb.lora_shrink_workspace_bytes(T, L, H, r) > lsb.LORA_NOALLOC_SCRATCH_BYTES
+    s = _seg(T=T, L=L)
+    prev = lib.lora_set_path(2)
+    try:
+        rc = lib.lora_shrink_noalloc(FAKE, H, FAKE, H, r, ctypes.byref(s), FAKE, r, 0, None)
+        _expect(rc, lsb.LORA_ERR_UNSUPPORTED, "static scratch")
+        _expect(lib.lora_shrink_noalloc(FAKE, H, FAKE, H, r, ctypes.byref(s), FAKE, r, 7, None),
+                lsb.LORA_ERR_INVALID_ARG, "dtype")
+        _expect(lib.lora_shrink_noalloc(FAKE, H - 8, FAKE, H, r, ctypes.byref(s), FAKE, r, 0, None),
+                lsb.LORA_ERR_INVALID_ARG, "ldx")
+    finally:
+        lib.lora_set_path(prev)
+    assert lsb.lora_last_error().startswith("lora_shrink_noalloc:")
