@@ -51,6 +51,9 @@ def _set_layout(w):
     for oi, o in enumerate(w.outputs):
         items.append((f"y{oi}", 2, (w.T, o.ldy)))
     items.append(("v", 4, (w.T, w.r)))
+    # segment metadata: built once on set 0, then copied with everything else
+    items += [("meta.st", 4, (max(w.T, 1),)), ("meta.sl", 4, (w.L,)), ("meta.ss", 4, (w.L + 1,)),
+              ("meta.cn", 4, (4,))]
     return items
 
 
@@ -64,6 +67,8 @@ def _host_bits(w, key):
         return w.A
     if key == "v":
         return np.zeros((w.T, w.r), np.float32)
+    if key.startswith("meta."):
+        return None
     if key[0] == "B":
         oi, si = map(int, key[1:].split("."))
         return w.outputs[oi].slices[si].B
@@ -79,12 +84,14 @@ class ArgSet:
         for (key, eb, shape), off in zip(layout, offs):
             n = math.prod(shape)
             view = flat[base + off: base + off + n * eb]
-            dt = torch.int32 if key == "ids" else (torch.float32 if key == "v" else tdt)
+            dt = torch.int32 if (key == "ids" or key.startswith("meta.")) else (
+                torch.float32 if key == "v" else tdt)
             t[key] = view.view(dt).view(shape)
         self.ids, self.x, self.A, self.v = t["ids"], t["x"], t["A"], t["v"]
         self.Bs = [[t[f"B{oi}.{si}"] for si in range(len(o.slices))] for oi, o in enumerate(w.outputs)]
         self.ys = [t[f"y{oi}"] for oi in range(len(w.outputs))]
-        self.seg = lsb.Segments(self.ids, w.L)
+        self.seg = lsb.Segments(self.ids, w.L,
+                                buffers=(t["meta.st"], t["meta.sl"], t["meta.ss"], t["meta.cn"]))
 
 
 def set_bytes(w):
@@ -107,15 +114,20 @@ def make_pool(w, torch, lsb, P):
     flat = torch.empty(P * S, dtype=torch.uint8, device="cuda")
     for (key, eb, shape), o in zip(layout, offs):
         nb = math.prod(shape) * eb
-        if nb:
-            src = torch.from_numpy(np.ascontiguousarray(_host_bits(w, key)).reshape(-1).view(np.uint8))
+        bits = _host_bits(w, key)
+        if nb and bits is not None:
+            src = torch.from_numpy(np.ascontiguousarray(bits).reshape(-1).view(np.uint8))
             flat[o:o + nb].copy_(src)
+    first = ArgSet(w, torch, lsb, flat, 0, layout, offs)
+    # Every set carries valid metadata before anything is timed (a call timed
+    # alone, without the build, reads the set's metadata as it stands).
+    lsb.lora_build_segments(first.ids, w.L, seg=first.seg)
     k = 1
     while k < P:
         m = min(k, P - k)
         flat[k * S:(k + m) * S].copy_(flat[0:m * S])
         k += m
-    return [ArgSet(w, torch, lsb, flat, i * S, layout, offs) for i in range(P)]
+    return [first] + [ArgSet(w, torch, lsb, flat, i * S, layout, offs) for i in range(1, P)]
 
 
 def op_build(w, lsb, s, ws):
@@ -562,7 +574,10 @@ def sweep(args):
     torch.cuda.set_device(0)
     dt = torch.float16
     gen = torch.Generator(device="cuda")
+    kinds = [k for k in args.sweep_kinds.split(",") if k] if args.sweep_kinds else None
     for kind, T, H, r, n, L, sl, add in sweep_points(args.sweep_grid):
+        if kinds and not any(kind.startswith(k) for k in kinds):
+            continue
         base_kind = "sgmv" if kind in ("single",) or kind.startswith("golden") else \
             ("bgmv" if kind == "logits" else kind)
         ids_w = W.make(f"{kind}_T{T}", "f16", T, 8, 8, L, [[8]], seed=7, seq_len=sl, sort_by_id=True) \
@@ -587,14 +602,23 @@ def sweep(args):
         torch.cuda.synchronize()
         head = {"sweep": kind, "tokens": T, "hidden": H, "out_cols": n, "rank": r, "num_loras": L,
                 "seq_len": sl, "add_inputs": add}
+        if kind == "single":
+            # The single-adapter entry points: no metadata, token index = row.
+            f_shrink = lambda s: lsb.lora_shrink_single(s["x"], s["A"][0], s["v"], workspace=ws)
+            f_expand = lambda s, y=None: lsb.lora_expand_single(s["v"], s["B"][0], s["y"] if y is None else y,
+                                                                add)
+        else:
+            f_shrink = lambda s: lsb.lora_shrink(s["x"], s["A"], s["seg"], s["v"], workspace=ws)
+            f_expand = lambda s, y=None: lsb.lora_expand(s["v"], s["B"], s["seg"], s["y"] if y is None else y,
+                                                         add)
 
         # Correctness first: one step on set 0 (y on a copy), sampled rows
         # against the oracle.
         s0 = sets[0]
         y_chk = s0["y"].clone()
         lsb.lora_build_segments(ids, L, seg=s0["seg"])
-        lsb.lora_shrink(s0["x"], s0["A"], s0["seg"], s0["v"], workspace=ws)
-        lsb.lora_expand(s0["v"], s0["B"], s0["seg"], y_chk, add)
+        f_shrink(s0)
+        f_expand(s0, y_chk)
         torch.cuda.synchronize()
         st = s0["seg"].sorted_token[:T].cpu().numpy()
         ss = s0["seg"].seg_start.cpu().numpy()
@@ -651,9 +675,7 @@ def sweep(args):
                 e1.record()
                 torch.cuda.synchronize()
                 ref[op] = e0.elapsed_time(e1) / K * 1e3
-        for op, fn, nb in (
-                ("shrink", lambda s: lsb.lora_shrink(s["x"], s["A"], s["seg"], s["v"], workspace=ws), shrink_b),
-                ("expand", lambda s: lsb.lora_expand(s["v"], s["B"], s["seg"], s["y"], add), expand_b)):
+        for op, fn, nb in (("shrink", f_shrink, shrink_b), ("expand", f_expand, expand_b)):
             us = graph_time(torch, fn, sets, 0, K) / K * 1e3
             gbs = nb / (us * 1e-6) / 1e9
             rec = dict(head, op=op, us=round(us, 2), GB_s=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
@@ -755,8 +777,13 @@ def measure(w, args, torch, lsb, check=True):
             print(json.dumps({"error": "parity check failed", "workload": w.name, "ratio": worst}))
             sys.exit(1)
 
+    # Enough sets that every call timed alone cycles >= pool_gib of its own
+    # operands (a shrink alone touches only x and A: with too few sets they
+    # would stay in the 256 MB Infinity Cache), within 24 GiB of HBM.
     per_set = set_bytes(w)
-    P = max(2, int(math.ceil(args.pool_gib * 2**30 / per_set)))
+    op_min = min([w.shrink_bytes()] + [w.output_bytes(o) for o in w.outputs])
+    P = max(2, int(math.ceil(args.pool_gib * 2**30 / max(1, op_min))))
+    P = max(2, min(P, int((24 << 30) // per_set)))
     log(f"argument pool: {P} sets of {per_set / 2**20:.1f} MiB")
     sets = make_pool(w, torch, lsb, P)
     torch.cuda.synchronize()
@@ -880,6 +907,8 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="time shrink and expand alone on the micro-benchmark sweep shapes")
     ap.add_argument("--sweep-grid", default="full", choices=("full", "thin"))
+    ap.add_argument("--sweep-kinds", default="",
+                    help="comma-separated sweep kinds to run (bgmv, sgmv, single, logits, golden)")
     ap.add_argument("--summarize-sweep", metavar="JSONL",
                     help="write profiles/sweep_shrink_expand_f16.md from a --sweep run's output")
     ap.add_argument("--trace", help="kernel_trace.csv of a --kernel-trace run")

@@ -205,6 +205,28 @@ int lora_expand_slice(const float *v, int64_t ldv, int64_t v_slice_stride,
                       int32_t num_slices, int32_t r, const lora_segments *seg, void *y,
                       int64_t ldy, int add_inputs, int dtype, void *stream);
 
+/* Single-adapter forms (TPU PR summary: the masking is removed when only one
+ * adapter is in use; micro-benchmark PR review thread: with few adapters the
+ * kernels should match torch.mm).  Every token t in [0, T) uses the one
+ * adapter, so no segment metadata exists and none is read: token index =
+ * row, as in a plain dense product.  Same results as the segment forms with
+ * every id 0 and L = 1; same validation, except that T >= 0 replaces the
+ * metadata checks.
+ *   A  [r][H] device (the adapter's H x r matrix stored transposed)
+ *   B  [n][r] device, per slice (the adapter's r x n matrix stored transposed)
+ * lora_shrink_single needs a workspace of lora_shrink_single_workspace_bytes
+ * (T, H, r) bytes (0 when its H-sum is not split). */
+size_t lora_shrink_single_workspace_bytes(int32_t T, int32_t H, int32_t r);
+int lora_shrink_single(const void *x, int64_t ldx, const void *A, int32_t H, int32_t r, int32_t T,
+                       float *v, int64_t ldv, void *workspace, size_t workspace_bytes, int dtype,
+                       void *stream);
+int lora_expand_single(const float *v, int64_t ldv, const void *B, int32_t r, int32_t n, int32_t T,
+                       void *y, int64_t ldy, int add_inputs, int dtype, void *stream);
+int lora_expand_slice_single(const float *v, int64_t ldv, int64_t v_slice_stride,
+                             const void *const *B, const int32_t *n_s, const int64_t *col_off,
+                             int32_t num_slices, int32_t r, int32_t T, void *y, int64_t ldy,
+                             int add_inputs, int dtype, void *stream);
+
 /* Kernel path (punica issue: BGMV, one adapter per input, is a strict subset
  * of SGMV, segments of inputs sharing an adapter; both compute the same
  * result).  0 = automatic: batches of at most 512 tokens may take the

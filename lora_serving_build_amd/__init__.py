@@ -6,7 +6,9 @@ points carry the C-ABI names of ``include/lora.h``:
 
     lora_segments_workspace_bytes, lora_build_segments, lora_shrink,
     lora_expand, lora_expand_slice, lora_shrink_workspace_bytes,
-    lora_set_path, lora_reload_tuning, lora_last_error
+    lora_set_path, lora_reload_tuning, lora_last_error, lora_shrink_noalloc,
+    and the single-adapter forms lora_shrink_single, lora_expand_single,
+    lora_expand_slice_single, lora_shrink_single_workspace_bytes
 
 If the shared library has not been built (``python -m
 lora_serving_build_amd.build``), every entry point raises: there is no
@@ -24,7 +26,8 @@ __all__ = [
     "LoraError", "Segments", "lib", "lora_build_segments", "lora_shrink", "lora_expand",
     "lora_expand_slice", "lora_shrink_workspace_bytes", "lora_segments_workspace_bytes",
     "lora_last_error", "lora_set_path", "lora_reload_tuning", "lora_shrink_noalloc",
-    "LORA_NOALLOC_SCRATCH_BYTES",
+    "LORA_NOALLOC_SCRATCH_BYTES", "lora_shrink_single", "lora_shrink_single_workspace_bytes",
+    "lora_expand_single", "lora_expand_slice_single",
     "PATH_AUTO", "PATH_BGMV", "PATH_SGMV", "LORA_F16", "LORA_BF16", "LORA_MAX_RANK", "LORA_MAX_LORAS",
     "LORA_MAX_SLICES", "library_path",
 ]
@@ -84,6 +87,12 @@ def lib() -> ctypes.CDLL:
             L.lora_shrink_workspace_bytes.restype = sz
             L.lora_shrink.argtypes = [p, i64, p, i32, i32, seg_p, p, i64, p, sz, ctypes.c_int, p]
             L.lora_shrink_noalloc.argtypes = [p, i64, p, i32, i32, seg_p, p, i64, ctypes.c_int, p]
+            L.lora_shrink_single_workspace_bytes.argtypes = [i32, i32, i32]
+            L.lora_shrink_single_workspace_bytes.restype = sz
+            L.lora_shrink_single.argtypes = [p, i64, p, i32, i32, i32, p, i64, p, sz, ctypes.c_int, p]
+            L.lora_expand_single.argtypes = [p, i64, p, i32, i32, i32, p, i64, ctypes.c_int, ctypes.c_int, p]
+            L.lora_expand_slice_single.argtypes = [p, i64, i64, p, p, p, i32, i32, i32, p, i64,
+                                                   ctypes.c_int, ctypes.c_int, p]
             L.lora_expand.argtypes = [p, i64, p, i32, i32, seg_p, p, i64, ctypes.c_int, ctypes.c_int, p]
             L.lora_expand_slice.argtypes = [p, i64, i64, p, p, p, i32, i32, seg_p, p, i64,
                                             ctypes.c_int, ctypes.c_int, p]
@@ -91,7 +100,8 @@ def lib() -> ctypes.CDLL:
             L.lora_set_path.argtypes = [ctypes.c_int]
             L.lora_set_path.restype = ctypes.c_int
             for f in ("lora_build_segments", "lora_shrink", "lora_shrink_noalloc", "lora_expand",
-                      "lora_expand_slice"):
+                      "lora_expand_slice", "lora_shrink_single", "lora_expand_single",
+                      "lora_expand_slice_single"):
                 getattr(L, f).restype = ctypes.c_int
             _lib = L
     return _lib
@@ -146,7 +156,10 @@ class Segments:
     """Segment metadata buffers of one batch (device tensors) and the C
     struct that points at them."""
 
-    def __init__(self, token_lora: torch.Tensor, num_loras: int, lora_rank: torch.Tensor | None = None):
+    def __init__(self, token_lora: torch.Tensor, num_loras: int, lora_rank: torch.Tensor | None = None,
+                 buffers=None):
+        """buffers (optional): the four int32 device tensors (sorted_token [>= T],
+        seg_lora [L], seg_start [L + 1], counts [4]) to use instead of new ones."""
         if token_lora.dtype != torch.int32 or token_lora.dim() != 1 or not token_lora.is_cuda:
             raise ValueError("token_lora must be a 1-D int32 CUDA tensor")
         if lora_rank is not None and (lora_rank.dtype != torch.int32 or lora_rank.shape != (int(num_loras),)
@@ -157,10 +170,18 @@ class Segments:
         T = token_lora.shape[0]
         self.token_lora = token_lora
         self.num_loras = int(num_loras)
-        self.sorted_token = torch.empty(max(T, 1), dtype=torch.int32, device=dev)
-        self.seg_lora = torch.empty(self.num_loras, dtype=torch.int32, device=dev)
-        self.seg_start = torch.empty(self.num_loras + 1, dtype=torch.int32, device=dev)
-        self.counts = torch.empty(4, dtype=torch.int32, device=dev)
+        if buffers is None:
+            self.sorted_token = torch.empty(max(T, 1), dtype=torch.int32, device=dev)
+            self.seg_lora = torch.empty(self.num_loras, dtype=torch.int32, device=dev)
+            self.seg_start = torch.empty(self.num_loras + 1, dtype=torch.int32, device=dev)
+            self.counts = torch.empty(4, dtype=torch.int32, device=dev)
+        else:
+            st, sl, ss, cn = buffers
+            for t, n in ((st, max(T, 1)), (sl, self.num_loras), (ss, self.num_loras + 1), (cn, 4)):
+                if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() < n or t.device != dev:
+                    raise ValueError("metadata buffers must be contiguous int32 tensors on the ids' device, "
+                                     "of at least T, L, L + 1 and 4 elements")
+            self.sorted_token, self.seg_lora, self.seg_start, self.counts = st, sl, ss, cn
         self.lora_rank = lora_rank
         self.c = _CSegments(T, self.num_loras, token_lora.data_ptr(), self.sorted_token.data_ptr(),
                             self.seg_lora.data_ptr(), self.seg_start.data_ptr(),
@@ -312,4 +333,82 @@ def lora_expand_slice(v: torch.Tensor, Bs, col_offs, seg: Segments, y: torch.Ten
     _check(lib().lora_expand_slice(ctypes.c_void_p(v.data_ptr()), ldv, int(v_slice_stride), ptrs, n_s,
                                    offs, ns, r, seg.ref(), ctypes.c_void_p(y.data_ptr()), ldy,
                                    int(bool(add_inputs)), _dtype_code(y.dtype), _stream(y.device)))
+    return y
+
+
+# ---------------------------------------------------------------- one adapter
+def _weight2d(W: torch.Tensor, name: str):
+    if W.dim() == 3 and W.shape[0] == 1:
+        W = W[0]
+    if W.dim() != 2 or not W.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 2-D tensor (or [1][..][..])")
+    return W
+
+
+def lora_shrink_single_workspace_bytes(T: int, H: int, r: int) -> int:
+    return int(lib().lora_shrink_single_workspace_bytes(T, H, r))
+
+
+def lora_shrink_single(x: torch.Tensor, A: torch.Tensor, v: torch.Tensor,
+                       workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """v[t, :r] = x[t, :H] . A for every row t of x, one adapter, no metadata
+    (A is [r][H])."""
+    A = _weight2d(A, "A")
+    r, H = A.shape
+    T = x.shape[0]
+    if v.dtype != torch.float32 or v.shape[0] < T:
+        raise TypeError("v must be float32 with at least as many rows as x")
+    if x.dtype != A.dtype:
+        raise TypeError("x and A must share a dtype")
+    ldx = _row_major(x, "x")
+    ldv = _row_major(v, "v")
+    need = lora_shrink_single_workspace_bytes(T, H, r)
+    if workspace is None:
+        workspace = _workspace(x.device, need)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().lora_shrink_single(ctypes.c_void_p(x.data_ptr()), ldx, ctypes.c_void_p(A.data_ptr()), H, r,
+                                    T, ctypes.c_void_p(v.data_ptr()), ldv, ws_ptr, ws_bytes,
+                                    _dtype_code(x.dtype), _stream(x.device)))
+    return v
+
+
+def lora_expand_single(v: torch.Tensor, B: torch.Tensor, y: torch.Tensor,
+                       add_inputs: bool = True) -> torch.Tensor:
+    """y[t, :n] (+)= v[t, :r] . B for every row t of y, one adapter, no
+    metadata (B is [n][r])."""
+    B = _weight2d(B, "B")
+    n, r = B.shape
+    T = y.shape[0]
+    if v.dtype != torch.float32 or y.dtype != B.dtype or v.shape[0] < T:
+        raise TypeError("v must be float32 with at least as many rows as y, and y must share B's dtype")
+    ldv = _row_major(v, "v")
+    ldy = _row_major(y, "y")
+    _check(lib().lora_expand_single(ctypes.c_void_p(v.data_ptr()), ldv, ctypes.c_void_p(B.data_ptr()), r, n,
+                                    T, ctypes.c_void_p(y.data_ptr()), ldy, int(bool(add_inputs)),
+                                    _dtype_code(y.dtype), _stream(y.device)))
+    return y
+
+
+def lora_expand_slice_single(v: torch.Tensor, Bs, col_offs, y: torch.Tensor, add_inputs: bool = True,
+                             v_slice_stride: int = 0) -> torch.Tensor:
+    """expand_slice for one adapter and no metadata (each B is [n_s][r])."""
+    Bs = [_weight2d(b, "B") for b in Bs]
+    ns = len(Bs)
+    if ns != len(col_offs):
+        raise ValueError("one column offset per slice")
+    r = Bs[0].shape[1]
+    if any(b.shape[1] != r or b.dtype != y.dtype for b in Bs):
+        raise ValueError("all slices must share the rank and y's dtype")
+    T = y.shape[0]
+    if v.dtype != torch.float32 or v.shape[0] < T:
+        raise TypeError("v must be float32 with at least as many rows as y")
+    ldv = _row_major(v, "v")
+    ldy = _row_major(y, "y")
+    ptrs = (ctypes.c_void_p * ns)(*[b.data_ptr() for b in Bs])
+    n_s = (ctypes.c_int32 * ns)(*[b.shape[0] for b in Bs])
+    offs = (ctypes.c_int64 * ns)(*[int(o) for o in col_offs])
+    _check(lib().lora_expand_slice_single(ctypes.c_void_p(v.data_ptr()), ldv, int(v_slice_stride), ptrs, n_s,
+                                          offs, ns, r, T, ctypes.c_void_p(y.data_ptr()), ldy,
+                                          int(bool(add_inputs)), _dtype_code(y.dtype), _stream(y.device)))
     return y

@@ -72,6 +72,7 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 // constant address space: a scalar load, counted apart from the vector loads
 // in flight, so waiting for the id does not wait for them.
 __device__ __forceinline__ int token_adapter(const SegView& seg, int t) {
+  if (seg.dense) return 0;  // the single-adapter form: no ids to read
   typedef const __attribute__((address_space(4))) int32_t* const_ptr;
   const int l = __builtin_amdgcn_readfirstlane(*(const_ptr)(uintptr_t)(seg.token_lora + t));
   return (l >= 0 && l < seg.L) ? l : -1;

@@ -71,7 +71,9 @@ __device__ __forceinline__ int pair_col(int g) { return 8 * (((g & 1) << 1) | (g
 // (tile = 64 TB tokens; two blocks share every weight operand read from LDS
 // and halve the weight traffic per token).  VEC: 16-byte aligned rows, r and
 // the slice offsets multiples of 8, ldy a multiple of 8.
-template <int DT, bool VEC, int NKS, int TB>
+// DENSE: one adapter (0) for every token, token index = position (the
+// single-adapter form): no metadata is read.
+template <int DT, bool VEC, int NKS, int TB, bool DENSE>
 __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <= 2 ? 4 : 3)) void expand_kernel(ExpandArgs a) {
   using Lds = ExpandLds<NKS>;
   constexpr int BP = Lds::BP;
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
   const int g = lane >> 4;  // lane group
   const int pc = pair_col(g);
 
-  const TileTable table = build_tile_table<kExpandThreads>(a.seg, TT, a.r, s_table, s_scan);
+  const TileTable table = build_tile_table<kExpandThreads, DENSE>(a.seg, TT, a.r, s_table, s_scan);
   const int mtiles = table.tiles;
   const int nruns = a.run_start[a.num_slices];
   const int n_items = mtiles * nruns;
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
     for (int b = 0; b < TB; ++b) {
       int pos = p0 + 16 * (TB * wave + b) + m;
       pos = pos < 0 ? 0 : (pos < a.seg.T ? pos : a.seg.T - 1);
-      traw[b] = a.seg.sorted_token[pos];
+      traw[b] = DENSE ? pos : a.seg.sorted_token[pos];
     }
     // Unconditional (an invalid tile reads adapter 0's clamped rows and drops
     // them): a load on only some paths would make the compiler's wait for
@@ -437,24 +439,38 @@ hipError_t launch_expand(const SegView& seg, const float* v, int64_t ldv, int64_
   int64_t chunks = 0;
   for (int q = 0; q < num_slices; ++q) chunks += (slices[q].n + kExpandCols - 1) / kExpandCols;
   // 128-token tiles (two 16-token blocks per wave) halve the weight reads per
-  // y byte but give fewer, larger items.  Measured on MI355X: 3% faster on
-  // the 8192-token layer's gate_up call (57344 tile-chunks), slower when a
-  // call has few items (2048-token prefill: 640).  Taken from 16384
-  // tile-chunks up, for r <= 64.
-  int tb = (nks <= 4 && max_token_tiles(seg.T, seg.L, 2 * kTileTokens) * chunks >= 16384) ? 2 : 1;
+  // y byte and double each wave's y loads in flight, but give fewer, larger
+  // items (two workgroups per CU instead of three or four).  Measured on
+  // MI355X, each call alone with inputs in HBM (64-token tiles against
+  // 128-token tiles with runs of 4 chunks):
+  //   8192 x 16384, r = 16 / 32 / 64:   119.7 / 121.3 / 138.8 us -> 115.3 / 118.5 / 123.1
+  //   8192 x 4096,  r = 16 / 64:         32.6 / 40.7 us -> 33.0 / 36.0
+  //   8192-token layer, qkv slices:      95.5 us -> 92.1
+  //   2048 x 16384 / 2048 x 4096, r = 64: 40.5 / 13.2 us -> 41.7 / 19.1
+  // so they are taken from 64 tiles of 128 tokens and 2048 tile-chunks up,
+  // for r <= 64 (r = 128 keeps 64-token tiles for its registers).
+  const int64_t mt128 = max_token_tiles(seg.T, seg.L, 2 * kTileTokens);
+  int tb = (nks <= 4 && mt128 >= 64 && mt128 * chunks >= 2048) ? 2 : 1;
   if (tuning().expand_tb == 1 || tuning().expand_tb == 2) tb = tuning().expand_tb;
   if (nks == 8) tb = 1;
   const int64_t tt = (int64_t)kTileTokens * tb;
   const int64_t mt_max = max_token_tiles(seg.T, seg.L, tt);
   // Chunks per run: long runs amortise an item's set-up (its token list, v
   // and the first y and weights, about two memory trips) and keep each y row
-  // streaming, but leave a few items per resident workgroup.  2 to 8 chunks,
-  // about 4096 items: measured best on the 2048-token, mixed-rank and
-  // 8192-token workloads (a run of one chunk spends about two thirds of its
-  // time in the set-up).
-  int64_t cpr = mt_max * chunks / 4096;
-  if (cpr > 8) cpr = 8;
-  if (cpr < 2) cpr = 2;
+  // streaming, but leave a few items per resident workgroup.  64-token
+  // tiles: 2 to 8 chunks, about 4096 items -- measured best on the 2048-token
+  // and mixed-rank workloads (a run of one chunk spends about two thirds of
+  // its time in the set-up).  128-token tiles: 4 chunks, 8 from 32768
+  // tile-chunks up (the 8192-token layer's gate_up call: 445.6 us at 8, 450.7
+  // at 4).  Runs of 3 or 6 chunks, which leave ragged runs at the slice ends,
+  // measured 7-30% slower than 2, 4 or 8 on every shape above.
+  int64_t cpr;
+  if (tb == 2) {
+    cpr = mt_max * chunks >= 32768 ? 8 : 4;
+  } else {
+    const int64_t want = mt_max * chunks / 4096;
+    cpr = want >= 8 ? 8 : (want >= 4 ? 4 : 2);
+  }
   if (tuning().expand_cpr >= 1) cpr = tuning().expand_cpr;
   a.cpr = (int32_t)cpr;
   int32_t runs = 0;
@@ -477,26 +493,33 @@ hipError_t launch_expand(const SegView& seg, const float* v, int64_t ldv, int64_
   int64_t grid = items < 256 * per_cu ? items : 256 * per_cu;
   grid = (grid + 7) / 8 * 8;
   if (grid < 8) grid = 8;
-#define LORA_EXPAND_LAUNCH(DT_, VEC_, TB_)                                                           \
+#define LORA_EXPAND_LAUNCH(DT_, VEC_, TB_, DN_)                                                      \
   switch (nks) {                                                                                    \
-    case 1: hipLaunchKernelGGL((expand_kernel<DT_, VEC_, 1, TB_>), dim3(grid), dim3(kExpandThreads), lds, s, a); break; \
-    case 2: hipLaunchKernelGGL((expand_kernel<DT_, VEC_, 2, TB_>), dim3(grid), dim3(kExpandThreads), lds, s, a); break; \
-    case 4: hipLaunchKernelGGL((expand_kernel<DT_, VEC_, 4, TB_>), dim3(grid), dim3(kExpandThreads), lds, s, a); break; \
-    default: hipLaunchKernelGGL((expand_kernel<DT_, VEC_, 8, 1>), dim3(grid), dim3(kExpandThreads), lds, s, a); break; \
+    case 1: hipLaunchKernelGGL((expand_kernel<DT_, VEC_, 1, TB_, DN_>), dim3(grid), dim3(kExpandThreads), lds, s, a); break; \
+    case 2: hipLaunchKernelGGL((expand_kernel<DT_, VEC_, 2, TB_, DN_>), dim3(grid), dim3(kExpandThreads), lds, s, a); break; \
+    case 4: hipLaunchKernelGGL((expand_kernel<DT_, VEC_, 4, TB_, DN_>), dim3(grid), dim3(kExpandThreads), lds, s, a); break; \
+    default: hipLaunchKernelGGL((expand_kernel<DT_, VEC_, 8, 1, DN_>), dim3(grid), dim3(kExpandThreads), lds, s, a); break; \
   }
-  if (tb == 2) {
-    if (dtype == 0) {
-      if (vec) { LORA_EXPAND_LAUNCH(0, true, 2) } else { LORA_EXPAND_LAUNCH(0, false, 2) }
-    } else {
-      if (vec) { LORA_EXPAND_LAUNCH(1, true, 2) } else { LORA_EXPAND_LAUNCH(1, false, 2) }
-    }
+#define LORA_EXPAND_TYPED(DN_)                                                                       \
+  if (tb == 2) {                                                                                    \
+    if (dtype == 0) {                                                                               \
+      if (vec) { LORA_EXPAND_LAUNCH(0, true, 2, DN_) } else { LORA_EXPAND_LAUNCH(0, false, 2, DN_) } \
+    } else {                                                                                        \
+      if (vec) { LORA_EXPAND_LAUNCH(1, true, 2, DN_) } else { LORA_EXPAND_LAUNCH(1, false, 2, DN_) } \
+    }                                                                                               \
+  } else {                                                                                          \
+    if (dtype == 0) {                                                                               \
+      if (vec) { LORA_EXPAND_LAUNCH(0, true, 1, DN_) } else { LORA_EXPAND_LAUNCH(0, false, 1, DN_) } \
+    } else {                                                                                        \
+      if (vec) { LORA_EXPAND_LAUNCH(1, true, 1, DN_) } else { LORA_EXPAND_LAUNCH(1, false, 1, DN_) } \
+    }                                                                                               \
+  }
+  if (seg.dense) {
+    LORA_EXPAND_TYPED(true)
   } else {
-    if (dtype == 0) {
-      if (vec) { LORA_EXPAND_LAUNCH(0, true, 1) } else { LORA_EXPAND_LAUNCH(0, false, 1) }
-    } else {
-      if (vec) { LORA_EXPAND_LAUNCH(1, true, 1) } else { LORA_EXPAND_LAUNCH(1, false, 1) }
-    }
+    LORA_EXPAND_TYPED(false)
   }
+#undef LORA_EXPAND_TYPED
 #undef LORA_EXPAND_LAUNCH
   return hipGetLastError();
 }

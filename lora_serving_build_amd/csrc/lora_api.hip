@@ -134,6 +134,7 @@ lora::SegView view(const lora_segments* seg) {
   s.lora_rank = seg->lora_rank;
   s.T = seg->num_tokens;
   s.L = seg->num_loras;
+  s.dense = 0;
   return s;
 }
 
@@ -184,18 +185,18 @@ int scratch_address(const char* fn, void* stream, void** out) {
   return LORA_OK;
 }
 
-// lora_shrink and lora_shrink_noalloc.  With use_scratch, the H-split
+// lora_shrink, lora_shrink_noalloc and lora_shrink_single, after their
+// batch description (sv) has been checked.  With use_scratch, the H-split
 // partial rows go to this device's static scratch instead of a workspace.
-int shrink_call(const char* fn, const void* x, int64_t ldx, const void* A, int32_t H, int32_t r,
-                const lora_segments* seg, float* v, int64_t ldv, void* workspace, size_t workspace_bytes,
+int shrink_core(const char* fn, const void* x, int64_t ldx, const void* A, int32_t H, int32_t r,
+                const lora::SegView& sv, float* v, int64_t ldv, void* workspace, size_t workspace_bytes,
                 bool use_scratch, int dtype, void* stream) {
   if (int e = check_dtype(dtype, fn)) return e;
-  if (int e = check_segments(seg, fn)) return e;
   if (int e = check_rank(r, fn)) return e;
   if (H < 1) return fail(LORA_ERR_INVALID_ARG, "%s: H %d < 1", fn, H);
   if (ldx < H) return fail(LORA_ERR_INVALID_ARG, "%s: ldx %lld < H %d", fn, (long long)ldx, H);
   if (ldv < r) return fail(LORA_ERR_INVALID_ARG, "%s: ldv %lld < r %d", fn, (long long)ldv, r);
-  const int32_t T = seg->num_tokens;
+  const int32_t T = sv.T;
   if (T == 0) return ok();
   if (!x || !A || !v) return fail(LORA_ERR_INVALID_ARG, "%s: x, A and v must not be NULL", fn);
   if (g_path.load(std::memory_order_relaxed) == 1 && r > lora::kBgmvMaxRank)
@@ -203,12 +204,12 @@ int shrink_call(const char* fn, const void* x, int64_t ldx, const void* A, int32
   const bool vec = (H % 8 == 0) && (ldx % 8 == 0) && aligned16(x) && aligned16(A) &&
                    (ldv % 4 == 0) && aligned16(v);
   if (use_bgmv(Op::kShrink, T, r, H, vec)) {
-    hipError_t err = lora::launch_bgmv_shrink(view(seg), static_cast<const uint16_t*>(x), ldx,
+    hipError_t err = lora::launch_bgmv_shrink(sv, static_cast<const uint16_t*>(x), ldx,
                                               static_cast<const uint16_t*>(A), H, r, v, ldv, dtype,
                                               vec, static_cast<hipStream_t>(stream));
     return hip_status(err, fn);
   }
-  const lora::ShrinkPlan plan = lora::plan_shrink(T, seg->num_loras, H, r);
+  const lora::ShrinkPlan plan = lora::plan_shrink(T, sv.L, H, r);
   const size_t need = plan.partial_bytes;
   if (use_scratch && need > 0) {
     if (need > (size_t)LORA_NOALLOC_SCRATCH_BYTES)
@@ -226,10 +227,27 @@ int shrink_call(const char* fn, const void* x, int64_t ldx, const void* A, int32
     if (!aligned16(workspace))
       return fail(LORA_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned", fn);
   }
-  hipError_t err = lora::launch_shrink(view(seg), static_cast<const uint16_t*>(x), ldx,
+  hipError_t err = lora::launch_shrink(sv, static_cast<const uint16_t*>(x), ldx,
                                        static_cast<const uint16_t*>(A), H, r, v, ldv, workspace,
                                        plan, dtype, vec, static_cast<hipStream_t>(stream));
   return hip_status(err, fn);
+}
+
+int shrink_call(const char* fn, const void* x, int64_t ldx, const void* A, int32_t H, int32_t r,
+                const lora_segments* seg, float* v, int64_t ldv, void* workspace, size_t workspace_bytes,
+                bool use_scratch, int dtype, void* stream) {
+  if (int e = check_segments(seg, fn)) return e;
+  return shrink_core(fn, x, ldx, A, H, r, view(seg), v, ldv, workspace, workspace_bytes, use_scratch,
+                     dtype, stream);
+}
+
+// The batch of the single-adapter entry points: T tokens, all on adapter 0.
+lora::SegView dense_view(int32_t T) {
+  lora::SegView s{};
+  s.T = T;
+  s.L = 1;
+  s.dense = 1;
+  return s;
 }
 
 }  // namespace
@@ -285,13 +303,16 @@ int lora_shrink_noalloc(const void* x, int64_t ldx, const void* A, int32_t H, in
                      stream);
 }
 
-int lora_expand_slice(const float* v, int64_t ldv, int64_t v_slice_stride, const void* const* B,
-                      const int32_t* n_s, const int64_t* col_off, int32_t num_slices, int32_t r,
-                      const lora_segments* seg, void* y, int64_t ldy, int add_inputs, int dtype,
-                      void* stream) {
-  static const char* fn = "lora_expand_slice";
+}  // extern "C"
+
+namespace {
+
+// lora_expand_slice and lora_expand_slice_single after their batch
+// description (sv) has been checked.
+int expand_core(const char* fn, const float* v, int64_t ldv, int64_t v_slice_stride, const void* const* B,
+                const int32_t* n_s, const int64_t* col_off, int32_t num_slices, int32_t r,
+                const lora::SegView& sv, void* y, int64_t ldy, int add_inputs, int dtype, void* stream) {
   if (int e = check_dtype(dtype, fn)) return e;
-  if (int e = check_segments(seg, fn)) return e;
   if (int e = check_rank(r, fn)) return e;
   if (num_slices < 1 || num_slices > LORA_MAX_SLICES)
     return fail(LORA_ERR_UNSUPPORTED, "%s: num_slices %d outside [1, %d]", fn, num_slices,
@@ -320,7 +341,7 @@ int lora_expand_slice(const float* v, int64_t ldv, int64_t v_slice_stride, const
     if (col_off[a] + n_s[a] > col_off[b])
       return fail(LORA_ERR_INVALID_ARG, "%s: slices %d and %d overlap", fn, a, b);
   }
-  const int32_t T = seg->num_tokens;
+  const int32_t T = sv.T;
   if (T == 0) return ok();
   if (!v || !y) return fail(LORA_ERR_INVALID_ARG, "%s: v and y must not be NULL", fn);
   bool vec = (r % 8 == 0) && (ldv % 4 == 0) && (v_slice_stride % 4 == 0) && aligned16(v) &&
@@ -332,15 +353,65 @@ int lora_expand_slice(const float* v, int64_t ldv, int64_t v_slice_stride, const
   int64_t ncols = 0;
   for (int s = 0; s < num_slices; ++s) ncols += n_s[s];
   if (use_bgmv(Op::kExpand, T, r, ncols, vec)) {
-    hipError_t err = lora::launch_bgmv_expand(view(seg), v, ldv, v_slice_stride, desc, num_slices, r,
+    hipError_t err = lora::launch_bgmv_expand(sv, v, ldv, v_slice_stride, desc, num_slices, r,
                                               static_cast<uint16_t*>(y), ldy, add_inputs ? 1 : 0,
                                               dtype, vec, static_cast<hipStream_t>(stream));
     return hip_status(err, fn);
   }
-  hipError_t err = lora::launch_expand(view(seg), v, ldv, v_slice_stride, desc, num_slices, r,
+  hipError_t err = lora::launch_expand(sv, v, ldv, v_slice_stride, desc, num_slices, r,
                                        static_cast<uint16_t*>(y), ldy, add_inputs ? 1 : 0, dtype,
                                        vec, static_cast<hipStream_t>(stream));
   return hip_status(err, fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int lora_expand_slice(const float* v, int64_t ldv, int64_t v_slice_stride, const void* const* B,
+                      const int32_t* n_s, const int64_t* col_off, int32_t num_slices, int32_t r,
+                      const lora_segments* seg, void* y, int64_t ldy, int add_inputs, int dtype,
+                      void* stream) {
+  static const char* fn = "lora_expand_slice";
+  if (int e = check_segments(seg, fn)) return e;
+  return expand_core(fn, v, ldv, v_slice_stride, B, n_s, col_off, num_slices, r, view(seg), y, ldy,
+                     add_inputs, dtype, stream);
+}
+
+int lora_expand_slice_single(const float* v, int64_t ldv, int64_t v_slice_stride, const void* const* B,
+                             const int32_t* n_s, const int64_t* col_off, int32_t num_slices, int32_t r,
+                             int32_t T, void* y, int64_t ldy, int add_inputs, int dtype, void* stream) {
+  static const char* fn = "lora_expand_slice_single";
+  if (T < 0) return fail(LORA_ERR_INVALID_ARG, "%s: T %d < 0", fn, T);
+  return expand_core(fn, v, ldv, v_slice_stride, B, n_s, col_off, num_slices, r, dense_view(T), y, ldy,
+                     add_inputs, dtype, stream);
+}
+
+int lora_expand_single(const float* v, int64_t ldv, const void* B, int32_t r, int32_t n, int32_t T,
+                       void* y, int64_t ldy, int add_inputs, int dtype, void* stream) {
+  const void* Bs[1] = {B};
+  const int32_t ns[1] = {n};
+  const int64_t off[1] = {0};
+  int rc = lora_expand_slice_single(v, ldv, 0, Bs, ns, off, 1, r, T, y, ldy, add_inputs, dtype, stream);
+  if (rc != LORA_OK) {
+    char tmp[512];
+    snprintf(tmp, sizeof tmp, "lora_expand_single: %s", g_error);
+    snprintf(g_error, sizeof g_error, "%s", tmp);
+  }
+  return rc;
+}
+
+size_t lora_shrink_single_workspace_bytes(int32_t T, int32_t H, int32_t r) {
+  return lora_shrink_workspace_bytes(T, 1, H, r);
+}
+
+int lora_shrink_single(const void* x, int64_t ldx, const void* A, int32_t H, int32_t r, int32_t T,
+                       float* v, int64_t ldv, void* workspace, size_t workspace_bytes, int dtype,
+                       void* stream) {
+  static const char* fn = "lora_shrink_single";
+  if (T < 0) return fail(LORA_ERR_INVALID_ARG, "%s: T %d < 0", fn, T);
+  return shrink_core(fn, x, ldx, A, H, r, dense_view(T), v, ldv, workspace, workspace_bytes, false, dtype,
+                     stream);
 }
 
 int lora_expand(const float* v, int64_t ldv, const void* B, int32_t r, int32_t n,

@@ -46,6 +46,9 @@ struct SegView {
   const int32_t* lora_rank;  // [L] live rank per adapter, or nullptr
   int32_t T;
   int32_t L;
+  // 1: the single-adapter form -- every token uses adapter 0 and token index
+  // = position; no metadata pointer is read (they may be null).
+  int32_t dense;
 };
 
 hipError_t launch_build_segments(const int32_t* token_lora, int32_t T, int32_t L,

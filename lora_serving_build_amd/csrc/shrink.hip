@@ -79,7 +79,9 @@ __device__ __forceinline__ void store4(float* p, int j0, int r, f32x4 val) {
 
 // NJT = 16-row tiles of r (r <= 16 * NJT).  VEC: 16-byte aligned rows with H
 // and ldx multiples of 8 (otherwise element-wise loads).
-template <int DT, bool VEC, int NJT>
+// DENSE: one adapter (0) for every token, token index = position (the
+// single-adapter form): no metadata is read.
+template <int DT, bool VEC, int NJT, bool DENSE>
 __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kernel(ShrinkArgs a) {
   constexpr int RP = 16 * NJT;
   constexpr int AL = RP * kSkChunks / kShrinkThreads;  // A pieces per thread per block (NJT)
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
   const int lrow = tid >> 4;
   const int lcol = (tid & 15) * 8;
 
-  const TileTable table = build_tile_table<kShrinkThreads>(a.seg, kSkTile, a.r, s_table, s_scan);
+  const TileTable table = build_tile_table<kShrinkThreads, DENSE>(a.seg, kSkTile, a.r, s_table, s_scan);
   const int tiles = table.tiles;
   const int n_items = tiles * a.ks;
   const int grid = gridDim.x;
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
     const int kbeg = ksi * a.kchunk;
     const int kend = min(a.H, kbeg + a.kchunk);
     const int pos = p0 + wave * 16 + m;
-    int t = (ok && pos < p_end) ? a.seg.sorted_token[pos] : -1;
+    int t = (ok && pos < p_end) ? (DENSE ? pos : a.seg.sorted_token[pos]) : -1;
     t = (t >= 0 && t < a.seg.T) ? t : -1;
     const bool tok_ok = t >= 0;
     const bool wave_live = ok && p0 + wave * 16 < p_end;
@@ -172,18 +174,33 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
 #pragma unroll
     for (int jt = 0; jt < NJT; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int nblk = kend > kbeg ? (kend - kbeg + kSkKB - 1) / kSkKB : 0;
+    // The blocks of the chunk are walked in a rotated order that starts at
+    // block (tile mod nblk).  The concurrent items otherwise read x at the
+    // same few offsets inside their rows, and when the row pitch is a
+    // multiple of the HBM interleave those offsets fall on the same few
+    // channels: measured on MI355X (8192 tokens x 8192, r = 64), chunks that
+    // start at multiples of 4 KB in the 16 KB rows (4 or 8 chunks) ran
+    // 15-20% slower than 3, 5 or 7 chunks.  Block s of the walk is block
+    // (s + rot) mod nblk; positions past the walk map to kend (clamped loads
+    // whose data is dropped).
+    const int rot = nblk > 0 ? tile % nblk : 0;
+    auto kb_of = [&](int step) {
+      if (step >= nblk) return kend;
+      const int blk = step + rot < nblk ? step + rot : step + rot - nblk;
+      return kbeg + blk * kSkKB;
+    };
 
     // One block: the next block's A and x go out first, then the ops of this
     // one from LDS (A) and registers (x).
     auto block = [&](int b, u32x4* xcur, u32x4* xnext) {
       const int buf = b & 1;
-      const int kb = kbeg + b * kSkKB;
+      const int kb = kb_of(b);
       const bool has_next = b + 1 < nblk;
       // Issued on every block (the last one reads clamped addresses and drops
       // the data): a load that only some paths issue would make the compiler
       // assume none and wait for everything before the ops below.
-      gload_a(kb + kSkKB);
-      gload_x(kb + kSkKB, xnext);
+      gload_a(kb_of(b + 1));
+      gload_x(kb_of(b + 1), xnext);
       __builtin_amdgcn_sched_barrier(0);
       if (wave_live) {
         const uint16_t* as = &s_a[(buf * RP + m) * kSkPitch + 8 * g];
@@ -198,15 +215,15 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
           }
         }
       }
-      if (has_next) swrite_a(buf ^ 1, kb + kSkKB);
+      if (has_next) swrite_a(buf ^ 1, kb_of(b + 1));
       __syncthreads();
     };
 
     u32x4 xa[KS], xb[KS];
     if (nblk > 0) {
-      gload_a(kbeg);
-      gload_x(kbeg, xa);
-      swrite_a(0, kbeg);
+      gload_a(kb_of(0));
+      gload_x(kb_of(0), xa);
+      swrite_a(0, kb_of(0));
     }
     __syncthreads();
     for (int b = 0; b < nblk; b += 2) {
@@ -245,8 +262,8 @@ __global__ __launch_bounds__(256) void shrink_reduce_kernel(SegView seg, const f
        o += (int64_t)gridDim.x * blockDim.x) {
     const int p = (int)(o / per_row);
     const int j0 = (int)(o - (int64_t)p * per_row) * 4;
-    int ta = seg.counts[1];
-    const int t = seg.sorted_token[p];
+    int ta = seg.dense ? seg.T : seg.counts[1];
+    const int t = seg.dense ? p : seg.sorted_token[p];
     f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int q0 = 0; q0 < ks; q0 += 8) {
       f32x4 part[8];
@@ -270,24 +287,30 @@ size_t shrink_lds_bytes(int njt, int L) {
          : njt == 4 ? ShrinkLds<4>::bytes(L) : ShrinkLds<8>::bytes(L);
 }
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool DENSE>
 hipError_t launch_typed(const ShrinkArgs& args, int njt, int grid, hipStream_t s) {
   const size_t lds = shrink_lds_bytes(njt, args.seg.L);
   switch (njt) {
     case 1:
-      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 1>), dim3(grid), dim3(kShrinkThreads), lds, s, args);
+      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 1, DENSE>), dim3(grid), dim3(kShrinkThreads), lds, s, args);
       break;
     case 2:
-      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 2>), dim3(grid), dim3(kShrinkThreads), lds, s, args);
+      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 2, DENSE>), dim3(grid), dim3(kShrinkThreads), lds, s, args);
       break;
     case 4:
-      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 4>), dim3(grid), dim3(kShrinkThreads), lds, s, args);
+      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 4, DENSE>), dim3(grid), dim3(kShrinkThreads), lds, s, args);
       break;
     default:
-      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 8>), dim3(grid), dim3(kShrinkThreads), lds, s, args);
+      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 8, DENSE>), dim3(grid), dim3(kShrinkThreads), lds, s, args);
       break;
   }
   return hipGetLastError();
+}
+
+template <int DT, bool VEC>
+hipError_t launch_dense(const ShrinkArgs& args, int njt, int grid, hipStream_t s) {
+  return args.seg.dense ? launch_typed<DT, VEC, true>(args, njt, grid, s)
+                        : launch_typed<DT, VEC, false>(args, njt, grid, s);
 }
 
 }  // namespace
@@ -356,9 +379,9 @@ hipError_t launch_shrink(const SegView& seg, const uint16_t* x, int64_t ldx, con
   a.rp = plan.rp;
   hipError_t e;
   if (dtype == 0)
-    e = vec ? launch_typed<0, true>(a, plan.jtw, plan.grid, s) : launch_typed<0, false>(a, plan.jtw, plan.grid, s);
+    e = vec ? launch_dense<0, true>(a, plan.jtw, plan.grid, s) : launch_dense<0, false>(a, plan.jtw, plan.grid, s);
   else
-    e = vec ? launch_typed<1, true>(a, plan.jtw, plan.grid, s) : launch_typed<1, false>(a, plan.jtw, plan.grid, s);
+    e = vec ? launch_dense<1, true>(a, plan.jtw, plan.grid, s) : launch_dense<1, false>(a, plan.jtw, plan.grid, s);
   if (e != hipSuccess || plan.ksplit == 1) return e;
   int64_t blocks = ((int64_t)seg.T * (plan.rp / 4) + 255) / 256;
   if (blocks > 1024) blocks = 1024;

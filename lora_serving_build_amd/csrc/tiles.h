@@ -48,9 +48,11 @@ __host__ __device__ inline int64_t max_token_tiles(int64_t T, int64_t L, int64_t
 // LDS ints a TileTable of L adapters occupies.
 __host__ __device__ constexpr int64_t tile_table_ints(int64_t L) { return 4 * (L + 1); }
 
-// Fills a TileTable from the metadata (S clamped to [0, L]).
+// Fills a TileTable from the metadata (S clamped to [0, L]).  DENSE: the
+// single-adapter form, one segment of all T tokens on adapter 0 at its full
+// rank, written without reading any metadata.
 // Every thread of the block must call it.
-template <int NT>
+template <int NT, bool DENSE = false>
 __device__ TileTable build_tile_table(const SegView& seg, int tile_tokens, int r, int32_t* lds,
                                       int32_t* scratch) {
   TileTable tt;
@@ -58,6 +60,21 @@ __device__ TileTable build_tile_table(const SegView& seg, int tile_tokens, int r
   tt.seg_start = lds + seg.L + 1;
   tt.seg_lora = lds + 2 * (seg.L + 1);
   tt.rank = lds + 3 * (seg.L + 1);
+  if constexpr (DENSE) {
+    const int tiles = seg.T > 0 ? (seg.T + tile_tokens - 1) / tile_tokens : 0;
+    if (threadIdx.x == 0) {
+      tt.tile_start[0] = 0;
+      tt.tile_start[1] = tiles;
+      tt.seg_start[0] = 0;
+      tt.seg_start[1] = seg.T;
+      tt.seg_lora[0] = 0;
+      tt.rank[0] = r;
+    }
+    __syncthreads();
+    tt.S = 1;
+    tt.tiles = tiles;
+    return tt;
+  }
   // All L + 1 entries are copied (they exist whatever S is), so these loads
   // go out together with the load of S instead of one round trip after it.
   int S = seg.counts[0];
@@ -87,7 +104,12 @@ __device__ TileTable build_tile_table(const SegView& seg, int tile_tokens, int r
   if (threadIdx.x == 0) tt.tile_start[S] = total;
   __syncthreads();
   tt.S = S;
-  tt.tiles = total;
+  // Metadata that breaks its invariants (the caller may fill it) can claim
+  // more tiles than T tokens make; the walk never goes past what a valid
+  // batch can hold, so such a call costs no more than a valid one.  Tiles
+  // past the claimed segments' tokens are refused by tile_range_lds.
+  const int64_t cap = max_token_tiles(seg.T, seg.L, tile_tokens);
+  tt.tiles = total < 0 ? 0 : (total > cap ? (int)cap : total);
   return tt;
 }
 

@@ -232,3 +232,32 @@ def test_noalloc_shrink_rejects_splits_beyond_its_scratch():
     finally:
         lib.lora_set_path(prev)
     assert lsb.lora_last_error().startswith("lora_shrink_noalloc:")
+
+
+def test_single_adapter_validation():
+    """The single-adapter entry points: T < 0 and the usual argument errors
+    are refused before anything is launched."""
+    lib = lsb.lib()
+    _expect(lib.lora_shrink_single(FAKE, 64, FAKE, 64, 16, -1, FAKE, 16, None, 0, 0, None),
+            lsb.LORA_ERR_INVALID_ARG, "T -1")
+    _expect(lib.lora_shrink_single(FAKE, 63, FAKE, 64, 16, 8, FAKE, 16, None, 0, 0, None),
+            lsb.LORA_ERR_INVALID_ARG, "ldx")
+    _expect(lib.lora_shrink_single(FAKE, 64, FAKE, 64, 200, 8, FAKE, 200, None, 0, 0, None),
+            lsb.LORA_ERR_UNSUPPORTED, "rank")
+    need = lsb.lora_shrink_single_workspace_bytes(256, 4096, 16)
+    assert need == lsb.lora_shrink_workspace_bytes(256, 1, 4096, 16)
+    prev = lib.lora_set_path(2)
+    try:
+        _expect(lib.lora_shrink_single(FAKE, 4096, FAKE, 4096, 16, 256, FAKE, 16, FAKE, need - 1, 0, None),
+                lsb.LORA_ERR_WORKSPACE, "workspace")
+    finally:
+        lib.lora_set_path(prev)
+    assert lib.lora_shrink_single(FAKE, 64, FAKE, 64, 16, 0, FAKE, 16, None, 0, 0, None) == lsb.LORA_OK
+    _expect(lib.lora_expand_single(FAKE, 16, FAKE, 16, 64, -2, FAKE, 64, 1, 0, None),
+            lsb.LORA_ERR_INVALID_ARG, "T -2")
+    assert lsb.lora_last_error().startswith("lora_expand_single:")
+    B = (ctypes.c_void_p * 2)(FAKE.value, FAKE.value)
+    n = (ctypes.c_int32 * 2)(32, 32)
+    o = (ctypes.c_int64 * 2)(0, 16)
+    _expect(lib.lora_expand_slice_single(FAKE, 16, 0, B, n, o, 2, 16, 8, FAKE, 64, 1, 0, None),
+            lsb.LORA_ERR_INVALID_ARG, "overlap")

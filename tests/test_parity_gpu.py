@@ -616,6 +616,11 @@ PLAN_VARIANTS = [
     ({"LORA_SHRINK_KSPLIT": "1"}, "sgmv", "bf16", 300, 2048, 32, 7, [[512, 256, 256]]),
     ({"LORA_SHRINK_KSPLIT": "2"}, "sgmv", "f16", 300, 2048, 32, 7, [[512, 256, 256]]),
     ({"LORA_SHRINK_KSPLIT": "5"}, "sgmv", "bf16", 500, 4096, 64, 9, [[1024]]),
+    # the rotated block walk with even and odd chunk counts, ragged chunk ends
+    ({"LORA_SHRINK_KSPLIT": "4"}, "sgmv", "bf16", 500, 4096, 64, 9, [[1024]]),
+    ({"LORA_SHRINK_KSPLIT": "1"}, "sgmv", "f16", 300, 1408, 16, 5, [[256]]),
+    ({"LORA_SHRINK_KSPLIT": "3"}, "sgmv", "bf16", 300, 2000, 40, 5, [[256]]),
+    ({"LORA_SHRINK_KSPLIT": "2"}, "sgmv", "bf16", 260, 1152, 128, 4, [[128]]),
     ({"LORA_EXPAND_TB": "2"}, "sgmv", "bf16", 700, 1024, 64, 5, [[2048, 512]]),
     ({"LORA_EXPAND_TB": "2"}, "sgmv", "f16", 300, 1024, 16, 3, [[1000]]),
     ({"LORA_EXPAND_TB": "2"}, "sgmv", "bf16", 300, 512, 128, 3, [[384]]),
@@ -884,3 +889,68 @@ def test_forced_bgmv_rejects_large_rank(force_path):
     with pytest.raises(lsb.LoraError) as e:
         dw.run()
     assert e.value.code == lsb.LORA_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- one adapter, no metadata
+SINGLE_CASES = [
+    # dtype, T, H, r, slices, path, integer
+    ("f16", 1, 64, 16, [64], "auto", False),
+    ("bf16", 63, 2049, 20, [300], "auto", False),            # element-wise path
+    ("f16", 700, 4096, 32, [4096, 1024], "sgmv", False),
+    ("bf16", 700, 4096, 32, [4096, 1024], "bgmv", False),
+    ("bf16", 300, 4096, 16, [4096], "auto", False),           # per-token kernels by the automatic choice
+    ("bf16", 4099, 1024, 64, [2048], "auto", False),          # ragged last tile, 128-token expand tiles
+    ("f16", 8192, 4096, 128, [1024, 512], "auto", False),     # rank 128, split H
+    ("bf16", 1500, 2048, 24, [512, 64, 104], "sgmv", True),   # integer inputs: exact
+]
+
+
+@pytest.mark.parametrize("dtype,T,H,r,widths,path,integer", SINGLE_CASES)
+def test_single_adapter_forms(force_path, dtype, T, H, r, widths, path, integer):
+    """The single-adapter entry points (no metadata, token index = row)
+    against the oracle, and bit for bit against the segment entry points run
+    on the same batch with every id 0 (same kernels, same tiles)."""
+    _announce(f"single-adapter forms {dtype} T={T} H={H} r={r} slices={widths} path={path}")
+    force_path({"auto": lsb.PATH_AUTO, "bgmv": lsb.PATH_BGMV, "sgmv": lsb.PATH_SGMV}[path])
+    w = W.make("single", dtype, T, H, r, 1, [widths], seed=T + H + r, seq_len=(1, 40), integer=integer)
+    assert (w.ids == 0).all()
+    seg_w = DeviceWorkload(w)
+    seg_w.run()
+    x = dev_bits(w.x, dtype)
+    A = dev_bits(w.A, dtype)
+    o = w.outputs[0]
+    Bs = [dev_bits(q.B, dtype) for q in o.slices]
+    v = sentinel_v(T, r)
+    lsb.lora_shrink_single(x, A, v)
+    y = dev_bits(o.y0, dtype)
+    if len(widths) == 1:
+        lsb.lora_expand_single(v, Bs[0], y, True)
+    else:
+        lsb.lora_expand_slice_single(v, Bs, [q.col_off for q in o.slices], y, True)
+    torch.cuda.synchronize()
+    assert np.array_equal(v.cpu().numpy().view(np.uint32), seg_w.v.cpu().numpy().view(np.uint32))
+    assert np.array_equal(host_bits(y), host_bits(seg_w.ys[0]))
+    v_or = oracle.shrink(dtype, w.x, w.A, w.ids)
+    cols = _slice_cols(o)
+    if integer:
+        assert np.array_equal(v.cpu().numpy().astype(np.float64), v_or)
+        ref = oracle.expand_slice(dtype, v_or, [q.B for q in o.slices], [q.col_off for q in o.slices],
+                                  w.ids, o.y0, True)
+        assert np.array_equal(host_bits(y)[:, cols], W.f32_to_bits(ref.astype(np.float32), dtype))
+    else:
+        assert tol_ratio(v.cpu().numpy().astype(np.float64), v_or) <= 1
+        ref = oracle.expand_slice(dtype, v_or, [q.B for q in o.slices], [q.col_off for q in o.slices],
+                                  w.ids, o.y0, True)
+        assert tol_ratio(decode(host_bits(y), dtype)[:, cols], ref) <= 1
+
+
+def test_single_adapter_empty_batch():
+    """T = 0 launches nothing and touches nothing."""
+    _announce("single-adapter forms, T = 0")
+    x = torch.empty(0, 256, dtype=torch.float16, device="cuda")
+    A = torch.zeros(16, 256, dtype=torch.float16, device="cuda")
+    v = torch.empty(0, 16, device="cuda")
+    lsb.lora_shrink_single(x, A, v)
+    y = torch.empty(0, 64, dtype=torch.float16, device="cuda")
+    lsb.lora_expand_single(v, torch.zeros(64, 16, dtype=torch.float16, device="cuda"), y)
+    torch.cuda.synchronize()
