@@ -21,8 +21,11 @@
 //   r = 8, 16, 32, 64 reads the weight block front to back, 1 KB per wave
 //   instruction; the general kernel covers every other shape with the same
 //   arithmetic.
+#include <algorithm>
+
 #include "lora_device.h"
 #include "lora_kernels.h"
+#include "tiles.h"
 
 namespace lora {
 
@@ -54,6 +57,10 @@ struct BgExpandArgs {
   int64_t ldy;
   int32_t add;
   int32_t cb;  // column blocks per token (aligned kernel)
+  // 0: every token of the batch, by token index.  k >= 1: only the tokens of
+  // segments of at most k tokens (the decode requests of a mixed batch),
+  // found from the segment metadata; the tile kernel takes the others.
+  int32_t short_max;
 };
 
 template <int DT>
@@ -76,6 +83,34 @@ __device__ __forceinline__ int token_adapter(const SegView& seg, int t) {
   typedef const __attribute__((address_space(4))) int32_t* const_ptr;
   const int l = __builtin_amdgcn_readfirstlane(*(const_ptr)(uintptr_t)(seg.token_lora + t));
   return (l >= 0 && l < seg.L) ? l : -1;
+}
+
+// Number of tokens a per-token expand walks, and its short-segment table
+// when it takes short segments only (every thread must call it).
+__device__ __forceinline__ int bg_expand_tokens(const BgExpandArgs& a, ShortTable* st, int32_t* lds) {
+  if (a.short_max <= 0) return a.seg.T;
+  *st = build_short_table<kBgThreads>(a.seg, a.short_max, lds, lds + short_table_ints(a.seg.L));
+  return st->count;
+}
+
+// Token and adapter of item k: token k itself (adapter from token_lora), or
+// the k-th short-segment token (adapter from the segment).  false: nothing
+// to do (no adapter, or invalid metadata).  The results are uniform.
+__device__ __forceinline__ bool bg_expand_token(const BgExpandArgs& a, const ShortTable& st, int k, int* t,
+                                                int* l) {
+  if (a.short_max <= 0) {
+    *t = k;
+    *l = token_adapter(a.seg, k);
+    return *l >= 0;
+  }
+  int p = 0, lora_id = -1;
+  if (!short_token(st, a.seg.T, a.seg.L, k, &p, &lora_id)) return false;
+  typedef const __attribute__((address_space(4))) int32_t* const_ptr;
+  const int tok = __builtin_amdgcn_readfirstlane(*(const_ptr)(uintptr_t)(a.seg.sorted_token + p));
+  if (tok < 0 || tok >= a.seg.T) return false;
+  *t = tok;
+  *l = lora_id;
+  return true;
 }
 
 // Work item = (token, block of RT ranks): a small batch is spread over
@@ -259,10 +294,13 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_expand_kernel(BgExpandArgs a)
   constexpr int BLK = kBgThreads * 8;
   constexpr int UNR = RT <= 16 ? 2 : 1;  // column blocks per trip (register bound)
   const int tid = threadIdx.x;
+  extern __shared__ int32_t s_tab[];  // short-segment table (short_max > 0)
+  ShortTable st{};
+  const int ntok = bg_expand_tokens(a, &st, s_tab);
 
-  for (int t = blockIdx.x; t < a.seg.T; t += gridDim.x) {
-    const int l = token_adapter(a.seg, t);
-    if (l < 0) continue;  // uniform: the row of y stays as it is
+  for (int k = blockIdx.x; k < ntok; k += gridDim.x) {
+    int t = 0, l = -1;
+    if (!bg_expand_token(a, st, k, &t, &l)) continue;  // uniform: the row of y stays as it is
     for (int q = 0; q < a.num_slices; ++q) {
       const float* vrow = a.v + (int64_t)t * a.ldv + (int64_t)q * a.v_slice_stride;
       const int nq = a.slices[q].n;
@@ -339,11 +377,18 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_expand_fast_kernel(BgExpandAr
   const int wave = threadIdx.x / kWave;
   const int part = lane & (G - 1);
   float* so = s_out[wave];
+  extern __shared__ int32_t s_tab[];  // short-segment table (short_max > 0)
+  ShortTable st{};
+  const int ntok = bg_expand_tokens(a, &st, s_tab);
 
-  const int items = a.seg.T * a.cb;
+  const int items = ntok * a.cb;
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
-    const int t = it / a.cb;
-    const int cb = it - t * a.cb;
+    const int k = it / a.cb;
+    const int cb = it - k * a.cb;
+    // With every token, the adapter id is loaded (scalar) while y and v are
+    // in flight; short-segment tokens know theirs from the table.
+    int t = k, l_short = -1;
+    if (a.short_max > 0 && !bg_expand_token(a, st, k, &t, &l_short)) continue;
     for (int q = 0; q < a.num_slices; ++q) {
       const int nq = a.slices[q].n;
       const float* vrow = a.v + (int64_t)t * a.ldv + (int64_t)q * a.v_slice_stride + part * 8;
@@ -352,7 +397,7 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_expand_fast_kernel(BgExpandAr
         // y and v do not depend on the adapter: they are in flight while the
         // (scalar) adapter id arrives, and only the id is waited for before
         // the weight loads go out.
-        const int l = token_adapter(a.seg, t);
+        const int l = a.short_max > 0 ? l_short : token_adapter(a.seg, t);
         u32x4 yv[RPI];
 #pragma unroll
         for (int u = 0; u < RPI; ++u) {
@@ -492,8 +537,16 @@ hipError_t launch_bgmv_shrink(const SegView& seg, const uint16_t* x, int64_t ldx
 
 hipError_t launch_bgmv_expand(const SegView& seg, const float* v, int64_t ldv, int64_t v_slice_stride,
                               const ExpandSliceDesc* slices, int32_t num_slices, int32_t r,
-                              uint16_t* y, int64_t ldy, int add, int dtype, bool vec, hipStream_t s) {
+                              uint16_t* y, int64_t ldy, int add, int dtype, bool vec, hipStream_t s,
+                              int short_max) {
   BgExpandArgs a{};
+  a.short_max = short_max > 0 ? short_max : 0;
+  // Tokens walked: every token, or at most min(S, T) * short_max of short
+  // segments (S <= L); the table of short segments lives in LDS.
+  const int64_t T_walk = a.short_max > 0
+                             ? std::min<int64_t>(seg.T, (int64_t)std::min(seg.L, seg.T) * a.short_max)
+                             : seg.T;
+  const size_t lds = a.short_max > 0 ? 4 * (size_t)(short_table_ints(seg.L) + kBgThreads / kWave + 1) : 0;
   a.seg = seg;
   a.v = v;
   a.ldv = ldv;
@@ -515,7 +568,7 @@ hipError_t launch_bgmv_expand(const SegView& seg, const float* v, int64_t ldv, i
       const int64_t rq = (slices[q].n + kRoundCols - 1) / kRoundCols;
       rounds = rq > rounds ? rq : rounds;
     }
-    const int64_t T = seg.T > 0 ? seg.T : 1;
+    const int64_t T = T_walk > 0 ? T_walk : 1;
     int rpi = 1;
     const int f_rpi = tuning().bgmv_rpi;
     if (f_rpi == 1 || (f_rpi == 2 && r <= 16)) rpi = f_rpi;
@@ -528,28 +581,28 @@ hipError_t launch_bgmv_expand(const SegView& seg, const float* v, int64_t ldv, i
 #define LORA_BG_FAST(DT_)                                                                            \
   switch (r) {                                                                                      \
     case 8:                                                                                         \
-      if (rpi == 2) hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 1, 2>), dim3(grid), dim3(kBgThreads), 0, s, a); \
-      else hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 1, 1>), dim3(grid), dim3(kBgThreads), 0, s, a); \
+      if (rpi == 2) hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 1, 2>), dim3(grid), dim3(kBgThreads), lds, s, a); \
+      else hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 1, 1>), dim3(grid), dim3(kBgThreads), lds, s, a); \
       break;                                                                                        \
     case 16:                                                                                        \
-      if (rpi == 2) hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 2, 2>), dim3(grid), dim3(kBgThreads), 0, s, a); \
-      else hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 2, 1>), dim3(grid), dim3(kBgThreads), 0, s, a); \
+      if (rpi == 2) hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 2, 2>), dim3(grid), dim3(kBgThreads), lds, s, a); \
+      else hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 2, 1>), dim3(grid), dim3(kBgThreads), lds, s, a); \
       break;                                                                                        \
-    case 32: hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 4, 1>), dim3(grid), dim3(kBgThreads), 0, s, a); break; \
-    default: hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 8, 1>), dim3(grid), dim3(kBgThreads), 0, s, a); break; \
+    case 32: hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 4, 1>), dim3(grid), dim3(kBgThreads), lds, s, a); break; \
+    default: hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 8, 1>), dim3(grid), dim3(kBgThreads), lds, s, a); break; \
   }
     if (dtype == 0) { LORA_BG_FAST(0) } else { LORA_BG_FAST(1) }
 #undef LORA_BG_FAST
     return hipGetLastError();
   }
-  const int grid = bg_grid(seg.T);
+  const int grid = bg_grid((int32_t)T_walk);
 #define LORA_BG_EXPAND(DT_, VEC_)                                                                     \
   if (r <= 16)                                                                                       \
-    hipLaunchKernelGGL((bgmv_expand_kernel<DT_, VEC_, 16>), dim3(grid), dim3(kBgThreads), 0, s, a);  \
+    hipLaunchKernelGGL((bgmv_expand_kernel<DT_, VEC_, 16>), dim3(grid), dim3(kBgThreads), lds, s, a);  \
   else if (r <= 32)                                                                                  \
-    hipLaunchKernelGGL((bgmv_expand_kernel<DT_, VEC_, 32>), dim3(grid), dim3(kBgThreads), 0, s, a);  \
+    hipLaunchKernelGGL((bgmv_expand_kernel<DT_, VEC_, 32>), dim3(grid), dim3(kBgThreads), lds, s, a);  \
   else                                                                                               \
-    hipLaunchKernelGGL((bgmv_expand_kernel<DT_, VEC_, 64>), dim3(grid), dim3(kBgThreads), 0, s, a);
+    hipLaunchKernelGGL((bgmv_expand_kernel<DT_, VEC_, 64>), dim3(grid), dim3(kBgThreads), lds, s, a);
   if (dtype == 0) {
     if (vec) { LORA_BG_EXPAND(0, true) } else { LORA_BG_EXPAND(0, false) }
   } else {

@@ -46,6 +46,7 @@ struct ExpandArgs {
   uint16_t* y;
   int64_t ldy;
   int32_t add;
+  int32_t min_seg_len;  // segments with fewer tokens are left to another kernel
 };
 
 template <int NKS>
@@ -96,7 +97,8 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
   const int g = lane >> 4;  // lane group
   const int pc = pair_col(g);
 
-  const TileTable table = build_tile_table<kExpandThreads, DENSE>(a.seg, TT, a.r, s_table, s_scan);
+  const TileTable table =
+      build_tile_table<kExpandThreads, DENSE>(a.seg, TT, a.r, s_table, s_scan, a.min_seg_len);
   const int mtiles = table.tiles;
   const int nruns = a.run_start[a.num_slices];
   const int n_items = mtiles * nruns;
@@ -424,8 +426,10 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
 
 hipError_t launch_expand(const SegView& seg, const float* v, int64_t ldv, int64_t v_slice_stride,
                          const ExpandSliceDesc* slices, int32_t num_slices, int32_t r,
-                         uint16_t* y, int64_t ldy, int add, int dtype, bool vec, hipStream_t s) {
+                         uint16_t* y, int64_t ldy, int add, int dtype, bool vec, hipStream_t s,
+                         int min_seg_len) {
   ExpandArgs a{};
+  a.min_seg_len = min_seg_len > 1 ? min_seg_len : 1;
   a.seg = seg;
   a.v = v;
   a.ldv = ldv;

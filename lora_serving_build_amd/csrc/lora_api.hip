@@ -358,9 +358,27 @@ int expand_core(const char* fn, const float* v, int64_t ldv, int64_t v_slice_str
                                               dtype, vec, static_cast<hipStream_t>(stream));
     return hip_status(err, fn);
   }
+  // Per-segment choice on the device (punica issue: BGMV for inputs with
+  // their own adapter, SGMV for segments sharing one): in a batch that mixes
+  // prefill segments with one-token (decode) segments, the tile kernel takes
+  // the segments of two tokens and more and the per-token kernel takes the
+  // one-token segments, each finding its own from the metadata.  Measured on
+  // MI355X (7168 prefill tokens over 16 adapters plus 1024 decode tokens with
+  // an adapter each, H = n = 4096): tiles alone 174 us (r = 16) and 219 us
+  // (r = 64), tiles on the prefill + per-token on the decode tokens 81 and
+  // 158 us.  Segments of 2 to 7 tokens measured faster on tiles at r = 64, so
+  // only one-token segments move.  The second launch costs a few
+  // microseconds when it finds nothing, so it is made only when the batch can
+  // hold many one-token segments: at least 256 adapters.
+  const bool split = g_path.load(std::memory_order_relaxed) == 0 && !sv.dense && sv.L >= 256 &&
+                     r <= lora::kBgmvMaxRank;
   hipError_t err = lora::launch_expand(sv, v, ldv, v_slice_stride, desc, num_slices, r,
                                        static_cast<uint16_t*>(y), ldy, add_inputs ? 1 : 0, dtype,
-                                       vec, static_cast<hipStream_t>(stream));
+                                       vec, static_cast<hipStream_t>(stream), split ? 2 : 1);
+  if (err == hipSuccess && split)
+    err = lora::launch_bgmv_expand(sv, v, ldv, v_slice_stride, desc, num_slices, r,
+                                   static_cast<uint16_t*>(y), ldy, add_inputs ? 1 : 0, dtype, vec,
+                                   static_cast<hipStream_t>(stream), 1);
   return hip_status(err, fn);
 }
 

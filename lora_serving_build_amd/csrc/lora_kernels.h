@@ -89,12 +89,17 @@ hipError_t launch_bgmv_shrink(const SegView& seg, const uint16_t* x, int64_t ldx
                               int32_t H, int32_t r, float* v, int64_t ldv, int dtype, bool vec,
                               hipStream_t s);
 
+// short_max = 0: every token; k >= 1: only the tokens of segments of at most
+// k tokens (found from the segment metadata).
 hipError_t launch_bgmv_expand(const SegView& seg, const float* v, int64_t ldv, int64_t v_slice_stride,
                               const ExpandSliceDesc* slices, int32_t num_slices, int32_t r,
-                              uint16_t* y, int64_t ldy, int add, int dtype, bool vec, hipStream_t s);
+                              uint16_t* y, int64_t ldy, int add, int dtype, bool vec, hipStream_t s,
+                              int short_max = 0);
 
+// min_seg_len: segments with fewer tokens are left to another kernel.
 hipError_t launch_expand(const SegView& seg, const float* v, int64_t ldv, int64_t v_slice_stride,
                          const ExpandSliceDesc* slices, int32_t num_slices, int32_t r,
-                         uint16_t* y, int64_t ldy, int add, int dtype, bool vec, hipStream_t s);
+                         uint16_t* y, int64_t ldy, int add, int dtype, bool vec, hipStream_t s,
+                         int min_seg_len = 1);
 
 }  // namespace lora

@@ -54,7 +54,7 @@ __host__ __device__ constexpr int64_t tile_table_ints(int64_t L) { return 4 * (L
 // Every thread of the block must call it.
 template <int NT, bool DENSE = false>
 __device__ TileTable build_tile_table(const SegView& seg, int tile_tokens, int r, int32_t* lds,
-                                      int32_t* scratch) {
+                                      int32_t* scratch, int min_len = 1) {
   TileTable tt;
   tt.tile_start = lds;
   tt.seg_start = lds + seg.L + 1;
@@ -89,17 +89,18 @@ __device__ TileTable build_tile_table(const SegView& seg, int tile_tokens, int r
   const int per = (S + NT - 1) / NT;
   const int lo = min((int)threadIdx.x * per, S);
   const int hi = min(lo + per, S);
-  int mine = 0;
-  for (int s = lo; s < hi; ++s) {
+  // Segments shorter than min_len get no tiles (another kernel takes them).
+  auto seg_tiles = [&](int s) {
     const int len = tt.seg_start[s + 1] - tt.seg_start[s];
-    mine += len > 0 ? (len + tile_tokens - 1) / tile_tokens : 0;
-  }
+    return (len > 0 && len >= min_len) ? (len + tile_tokens - 1) / tile_tokens : 0;
+  };
+  int mine = 0;
+  for (int s = lo; s < hi; ++s) mine += seg_tiles(s);
   int total;
   int run = block_exclusive_sum<NT>(mine, scratch, &total);
   for (int s = lo; s < hi; ++s) {
     tt.tile_start[s] = run;
-    const int len = tt.seg_start[s + 1] - tt.seg_start[s];
-    run += len > 0 ? (len + tile_tokens - 1) / tile_tokens : 0;
+    run += seg_tiles(s);
   }
   if (threadIdx.x == 0) tt.tile_start[S] = total;
   __syncthreads();
@@ -111,6 +112,71 @@ __device__ TileTable build_tile_table(const SegView& seg, int tile_tokens, int r
   const int64_t cap = max_token_tiles(seg.T, seg.L, tile_tokens);
   tt.tiles = total < 0 ? 0 : (total > cap ? (int)cap : total);
   return tt;
+}
+
+// Tokens of the short segments (1 .. max_len tokens: the decode requests of
+// a batch that mixes decode and prefill), numbered 0 .. count - 1 in sorted
+// order, for a per-token kernel that takes only those.  LDS copy of
+// seg_start[0..S] and seg_lora[0..S) with the prefix of short lengths,
+// 3 (L + 1) ints in all (scratch: NT / 64 + 1 more).
+struct ShortTable {
+  int32_t* start;      // [S + 1] first short-token number of segment s
+  int32_t* seg_start;
+  int32_t* seg_lora;
+  int S;
+  int count;
+};
+
+__host__ __device__ constexpr int64_t short_table_ints(int64_t L) { return 3 * (L + 1); }
+
+// Every thread of the block must call it.
+template <int NT>
+__device__ ShortTable build_short_table(const SegView& seg, int max_len, int32_t* lds, int32_t* scratch) {
+  ShortTable st;
+  st.start = lds;
+  st.seg_start = lds + seg.L + 1;
+  st.seg_lora = lds + 2 * (seg.L + 1);
+  int S = seg.counts[0];
+  for (int s = threadIdx.x; s <= seg.L; s += NT) st.seg_start[s] = seg.seg_start[s];
+  for (int s = threadIdx.x; s < seg.L; s += NT) st.seg_lora[s] = seg.seg_lora[s];
+  S = S < 0 ? 0 : (S > seg.L ? seg.L : S);
+  __syncthreads();
+  auto short_len = [&](int s) {
+    const int len = st.seg_start[s + 1] - st.seg_start[s];
+    return (len >= 1 && len <= max_len) ? len : 0;
+  };
+  const int per = (S + NT - 1) / NT;
+  const int lo = min((int)threadIdx.x * per, S);
+  const int hi = min(lo + per, S);
+  int mine = 0;
+  for (int s = lo; s < hi; ++s) mine += short_len(s);
+  int total;
+  int run = block_exclusive_sum<NT>(mine, scratch, &total);
+  for (int s = lo; s < hi; ++s) {
+    st.start[s] = run;
+    run += short_len(s);
+  }
+  if (threadIdx.x == 0) st.start[S] = total;
+  __syncthreads();
+  st.S = S;
+  // As for the tiles: invalid metadata never claims more than T tokens.
+  st.count = total < 0 ? 0 : (total > seg.T ? seg.T : total);
+  return st;
+}
+
+// Sorted position and adapter of short token k (k < st.count); false when
+// the metadata does not hold one.
+__device__ __forceinline__ bool short_token(const ShortTable& st, int T, int L, int k, int* pos,
+                                            int* lora_id) {
+  if (st.S <= 0) return false;
+  const int s = tile_segment(st.start, st.S, k);
+  if (k < st.start[s] || k >= st.start[s + 1]) return false;
+  const int p = st.seg_start[s] + (k - st.start[s]);
+  const int l = st.seg_lora[s];
+  if (p < 0 || p >= T || l < 0 || l >= L) return false;
+  *pos = p;
+  *lora_id = l;
+  return true;
 }
 
 // tile_range on a TileTable (LDS only).

@@ -954,3 +954,86 @@ def test_single_adapter_empty_batch():
     y = torch.empty(0, 64, dtype=torch.float16, device="cuda")
     lsb.lora_expand_single(v, torch.zeros(64, 16, dtype=torch.float16, device="cuda"), y)
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- decode + prefill mixes
+MIXED_CASES = [
+    # dtype, n_prefill, prefill_loras, n_decode, L, H, r, slices, integer: batches
+    # of >= 256 adapters, where the expand sends one-token segments to the
+    # per-token kernel and the rest to the tile kernel
+    ("bf16", 2000, 16, 700, 1024, 1024, 16, [[1024]], False),
+    ("f16", 1500, 8, 600, 700, 2048, 64, [[512, 256]], False),
+    ("bf16", 1200, 12, 400, 512, 512, 24, [[300]], False),        # per-token general kernel
+    ("bf16", 900, 4, 300, 400, 1024, 32, [[512], [256, 256]], True),
+    ("f16", 0, 1, 800, 1024, 512, 16, [[1024]], False),          # decode only, above 512 tokens
+    ("bf16", 3000, 16, 300, 320, 1024, 128, [[512]], False),      # rank 128: tiles for every segment
+]
+
+
+@pytest.mark.parametrize("dtype,n_pre,pre_l,n_dec,L,H,r,slices,integer", MIXED_CASES)
+def test_decode_prefill_mix(dtype, n_pre, pre_l, n_dec, L, H, r, slices, integer):
+    """Mixed batches through the automatic path: every row against the
+    oracle (integer inputs: bit for bit), untouched rows and columns kept."""
+    _announce(f"decode+prefill mix {dtype} prefill={n_pre}/{pre_l} decode={n_dec} L={L} H={H} r={r} "
+              f"slices={slices} integer={integer}")
+    w = W.make_mixed("mix", dtype, n_pre, pre_l, n_dec, L, H, r, slices, seed=n_pre + n_dec + r,
+                     neg_frac=0.05, integer=integer)
+    dw = DeviceWorkload(w)
+    seg = dw.run()
+    for g, ref in zip(seg_host(seg), oracle.build_segments(w.ids, w.L)):
+        assert np.array_equal(g, ref)
+    if integer:
+        act = np.nonzero(w.active)[0]
+        v_or = oracle.shrink(w.dtype, w.x, w.A, w.ids)
+        assert np.array_equal(dw.v.cpu().numpy()[act].astype(np.float64), v_or[act])
+        for o, y in zip(w.outputs, dw.ys):
+            ref = oracle.expand_slice(w.dtype, np.nan_to_num(v_or), [s.B for s in o.slices],
+                                      [s.col_off for s in o.slices], w.ids, o.y0, w.add)
+            ref_bits = W.f32_to_bits(ref.astype(np.float32), dtype) if dtype == "bf16" else \
+                ref.astype(np.float16).view(np.uint16)
+            assert np.array_equal(host_bits(y)[:, _slice_cols(o)][act], ref_bits[act])
+    else:
+        rv, ry, ryi = compare_all_rows(dw)
+        print(f"  tolerance ratios: v {rv:.3g}  y {ry:.3g}  y(isolated) {ryi:.3g}")
+        assert rv <= 1 and ry <= 1 and ryi <= 1
+    check_neg_rows(dw)
+    check_outside_slices(dw)
+
+
+def test_decode_prefill_mix_graph_replays():
+    """The split expand (tile launch + per-token launch) captured in a HIP
+    graph: three replays with the metadata and outputs overwritten between
+    them give the eager step's bits."""
+    _announce("decode+prefill mix, graph replays")
+    w = W.make_mixed("mixg", "bf16", 1500, 8, 500, 600, 1024, 16, [[1024, 512]], seed=77, neg_frac=0.05)
+    eager = DeviceWorkload(w)
+    eager.run()
+    g_w = DeviceWorkload(w)
+    y0 = [y.clone() for y in g_w.ys]
+    v0 = g_w.v.clone()
+    seg = lsb.Segments(g_w.ids, w.L)
+    ws = torch.zeros(max(lsb.lora_shrink_workspace_bytes(w.T, w.L, w.H, w.r), 256), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        lsb.lora_build_segments(g_w.ids, w.L, seg=seg)
+        lsb.lora_shrink(g_w.x, g_w.A, seg, g_w.v, workspace=ws)
+        o = w.outputs[0]
+        lsb.lora_expand_slice(g_w.v, g_w.Bs[0], [q.col_off for q in o.slices], seg, g_w.ys[0], w.add)
+
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    act = np.nonzero(w.active)[0]
+    for _ in range(3):
+        g_w.ys[0].copy_(y0[0])
+        g_w.v.copy_(v0)
+        for b in (seg.sorted_token, seg.seg_lora, seg.seg_start, seg.counts):
+            b.fill_(-5)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(g_w.v.cpu().numpy()[act].view(np.uint32),
+                              eager.v.cpu().numpy()[act].view(np.uint32))
+        assert np.array_equal(host_bits(g_w.ys[0]), host_bits(eager.ys[0]))

@@ -61,3 +61,21 @@ def test_zipf_popularity():
     freq = np.bincount(seq_ids, minlength=64) / seq_ids.size
     p = W.zipf_probs(64, 1.1)
     assert abs(freq[0] - p[0]) < 0.02 and freq[0] > freq[1] > freq[4] > freq[40]
+
+
+def test_mixed_batch_structure():
+    """make_mixed: prefill sequences on the first adapters, one-token decode
+    requests each on an adapter of its own, shuffled; x and weights are
+    make()'s."""
+    w = W.make_mixed("m", "bf16", 500, 4, 100, 200, 64, 8, [[32]], seed=3, neg_frac=0.0)
+    assert w.T == 600 and w.ids.shape == (600,)
+    ids = w.ids
+    pre = ids[ids < 4]
+    dec = ids[ids >= 4]
+    assert pre.size == 500 and dec.size == 100
+    assert np.unique(dec).size == 100                      # each decode adapter used once
+    assert sum(w.seq_lens) == 600
+    ref = W.make("m", "bf16", 600, 64, 8, 200, [[32]], seed=3)
+    assert np.array_equal(ref.x, w.x) and np.array_equal(ref.A, w.A)
+    first_dec = int(np.argmax(ids >= 4))
+    assert 0 < first_dec < 600 or ids[0] >= 4               # decode tokens are not all at the end

@@ -293,3 +293,30 @@ def sweep_point(kind: str, T: int, H: int, r: int, L: int = 4, seed: int = 7,
     sl = 1 if kind == "bgmv" else 8
     return make(f"{kind}_T{T}_H{H}_r{r}_L{L}", dtype, T, H, r, L, [[H]], seed=seed,
                 seq_len=sl, sort_by_id=True)
+
+
+def make_mixed(name: str, dtype: str, n_prefill: int, prefill_loras: int, n_decode: int, L: int,
+               H: int, r: int, slices_per_output: list[list[int]], *, seed: int, max_len: int = 64,
+               neg_frac: float = 0.0, integer: bool = False) -> Workload:
+    """A batch that mixes prefill and decode: prefill sequences of U{1..max_len}
+    tokens (n_prefill in all) on adapters drawn uniformly from the first
+    prefill_loras, and n_decode one-token requests whose adapters are drawn
+    without replacement from the other L - prefill_loras (each is a segment of
+    one token).  Sequences in shuffled order; a fraction of whole sequences
+    take id -1.  x, weights and y0 are those of make() with the same seed."""
+    if n_decode > L - prefill_loras:
+        raise ValueError("each decode token needs an adapter of its own")
+    T = n_prefill + n_decode
+    w = make(name, dtype, T, H, r, L, slices_per_output, seed=seed, integer=integer)
+    rng = np.random.Generator(np.random.PCG64(seed + 7919))
+    lens = seq_lengths(rng, n_prefill, max_len) if n_prefill else []
+    seq_ids = rng.integers(0, prefill_loras, size=len(lens)) if lens else np.zeros(0, np.int64)
+    dec_ids = prefill_loras + rng.permutation(L - prefill_loras)[:n_decode]
+    seqs = [(int(n), int(i)) for n, i in zip(lens, seq_ids)] + [(1, int(d)) for d in dec_ids]
+    order = rng.permutation(len(seqs))
+    neg = rng.random(len(seqs)) < neg_frac
+    ids = np.concatenate([np.full(seqs[k][0], -1 if neg[k] else seqs[k][1], np.int32) for k in order])
+    assert ids.shape[0] == T
+    w.ids = ids.astype(np.int32)
+    w.seq_lens = [seqs[k][0] for k in order]
+    return w
