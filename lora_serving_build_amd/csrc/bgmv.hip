@@ -18,7 +18,7 @@
 // expand: the token's v is split into hi + lo 16-bit parts; each output
 //   column is the balanced pairwise sum of per-8-rank group dot products (see
 //   group_dot), rounded once when added to y.  The aligned kernel for
-//   r = 8, 16, 32, 64 reads the weight block front to back, 1 KB per wave
+//   r = 8, 16, 32, 64, 128 reads the weight block front to back, 1 KB per wave
 //   instruction; the general kernel covers every other shape with the same
 //   arithmetic.
 #include <algorithm>
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_expand_kernel(BgExpandArgs a)
   }
 }
 
-// Per-token expand for r = 8 G (G = 1, 2, 4, 8) on aligned data.  A token's
+// Per-token expand for r = 8 G (G = 1, 2, 4, 8, 16) on aligned data.  A token's
 // weight block B_l is read front to back: load k of lane i takes 16-byte chunk
 // 64 k + i of the current stretch, so each wave instruction reads 1 KB of
 // consecutive memory.  Chunk c holds ranks 8 (c % G) .. +8 of column c / G;
@@ -363,7 +363,7 @@ constexpr int kRoundCols = kWave * 8;
 
 template <int DT, int G, int RPI>
 __global__ __launch_bounds__(kBgThreads) void bgmv_expand_fast_kernel(BgExpandArgs a) {
-  constexpr int LG = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
+  constexpr int LG = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : G == 8 ? 3 : 4;
   constexpr int K = 8 * G;                   // weight loads per lane and round
   constexpr int KB = K < 16 ? K : 16;        // loads per batch (register bound)
   constexpr int CPI = kWave / G;             // columns per load instruction
@@ -434,6 +434,7 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_expand_fast_kernel(BgExpandAr
           if constexpr (G >= 2) vmax = fmaxf(vmax, lane_xor<0>(vmax, lane));
           if constexpr (G >= 4) vmax = fmaxf(vmax, lane_xor<1>(vmax, lane));
           if constexpr (G >= 8) vmax = fmaxf(vmax, lane_xor<2>(vmax, lane));
+          if constexpr (G >= 16) vmax = fmaxf(vmax, lane_xor<3>(vmax, lane));
           f16_prescale(vmax, &down, &up);
           va *= down;
           vb *= down;
@@ -461,6 +462,7 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_expand_fast_kernel(BgExpandAr
               if constexpr (G >= 2) p = p + lane_xor<0>(p, lane);
               if constexpr (G >= 4) p = p + lane_xor<1>(p, lane);
               if constexpr (G >= 8) p = p + lane_xor<2>(p, lane);
+              if constexpr (G >= 16) p = p + lane_xor<3>(p, lane);
               if (part == 0) {
                 const int c = (kb + k) * CPI + (lane >> LG);  // a run of CPI columns in one 128
                 so[u * kSoRow + c + ((c >> 7) << 2)] = DT == 0 ? p * up : p;
@@ -557,7 +559,7 @@ hipError_t launch_bgmv_expand(const SegView& seg, const float* v, int64_t ldv, i
   a.y = y;
   a.ldy = ldy;
   a.add = add;
-  if (vec && (r == 8 || r == 16 || r == 32 || r == 64)) {
+  if (vec && (r == 8 || r == 16 || r == 32 || r == 64 || r == 128)) {
     // Rounds of 512 columns in the widest slice, and workgroups per token
     // that give each wave RPI rounds of it.  One round per wave (twice the
     // workgroups of two) measured faster on 16- and 256-token batches; two
@@ -589,7 +591,8 @@ hipError_t launch_bgmv_expand(const SegView& seg, const float* v, int64_t ldv, i
       else hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 2, 1>), dim3(grid), dim3(kBgThreads), lds, s, a); \
       break;                                                                                        \
     case 32: hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 4, 1>), dim3(grid), dim3(kBgThreads), lds, s, a); break; \
-    default: hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 8, 1>), dim3(grid), dim3(kBgThreads), lds, s, a); break; \
+    case 64: hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 8, 1>), dim3(grid), dim3(kBgThreads), lds, s, a); break; \
+    default: hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 16, 1>), dim3(grid), dim3(kBgThreads), lds, s, a); break; \
   }
     if (dtype == 0) { LORA_BG_FAST(0) } else { LORA_BG_FAST(1) }
 #undef LORA_BG_FAST

@@ -85,7 +85,7 @@ enum class Op { kShrink, kExpand };
 
 bool use_bgmv(Op op, int32_t T, int32_t r, int64_t width, bool vec) {
   const int mode = g_path.load(std::memory_order_relaxed);
-  if (r > lora::kBgmvMaxRank) return false;
+  if (!lora::bgmv_supports(op == Op::kExpand, r, vec)) return false;
   if (mode == 1) return true;
   if (mode == 2) return false;
   if (T > 512) return false;
@@ -199,8 +199,6 @@ int shrink_core(const char* fn, const void* x, int64_t ldx, const void* A, int32
   const int32_t T = sv.T;
   if (T == 0) return ok();
   if (!x || !A || !v) return fail(LORA_ERR_INVALID_ARG, "%s: x, A and v must not be NULL", fn);
-  if (g_path.load(std::memory_order_relaxed) == 1 && r > lora::kBgmvMaxRank)
-    return fail(LORA_ERR_UNSUPPORTED, "%s: the per-token path takes r <= %d", fn, lora::kBgmvMaxRank);
   const bool vec = (H % 8 == 0) && (ldx % 8 == 0) && aligned16(x) && aligned16(A) &&
                    (ldv % 4 == 0) && aligned16(v);
   if (use_bgmv(Op::kShrink, T, r, H, vec)) {
@@ -348,8 +346,10 @@ int expand_core(const char* fn, const float* v, int64_t ldv, int64_t v_slice_str
              (ldy % 8 == 0) && aligned16(y);
   for (int s = 0; s < num_slices; ++s)
     vec = vec && aligned16(B[s]) && (col_off[s] % 8 == 0) && (n_s[s] % 8 == 0);
-  if (g_path.load(std::memory_order_relaxed) == 1 && r > lora::kBgmvMaxRank)
-    return fail(LORA_ERR_UNSUPPORTED, "%s: the per-token path takes r <= %d", fn, lora::kBgmvMaxRank);
+  if (g_path.load(std::memory_order_relaxed) == 1 && !lora::bgmv_supports(true, r, vec))
+    return fail(LORA_ERR_UNSUPPORTED,
+                "%s: the per-token path takes r <= %d, or r = 128 with 16-byte aligned rows and sizes "
+                "that are multiples of 8", fn, lora::kBgmvMaxRank);
   int64_t ncols = 0;
   for (int s = 0; s < num_slices; ++s) ncols += n_s[s];
   if (use_bgmv(Op::kExpand, T, r, ncols, vec)) {
@@ -367,9 +367,11 @@ int expand_core(const char* fn, const float* v, int64_t ldv, int64_t v_slice_str
   // an adapter each, H = n = 4096): tiles alone 174 us (r = 16) and 219 us
   // (r = 64), tiles on the prefill + per-token on the decode tokens 81 and
   // 158 us.  Segments of 2 to 7 tokens measured faster on tiles at r = 64, so
-  // only one-token segments move.  The second launch costs a few
-  // microseconds when it finds nothing, so it is made only when the batch can
-  // hold many one-token segments: at least 256 adapters.
+  // only one-token segments move; at r = 128 the per-token expand is about
+  // twice as slow as the tiles on small batches (16-512 tokens: 15-20 us
+  // against 10-12), so the split stops at r = 64.  The second launch costs a
+  // few microseconds when it finds nothing, so it is made only when the batch
+  // can hold many one-token segments: at least 256 adapters.
   const bool split = g_path.load(std::memory_order_relaxed) == 0 && !sv.dense && sv.L >= 256 &&
                      r <= lora::kBgmvMaxRank;
   hipError_t err = lora::launch_expand(sv, v, ldv, v_slice_stride, desc, num_slices, r,

@@ -77,8 +77,12 @@ struct ExpandSliceDesc {
   int64_t col_off;
 };
 
-// Per-token (BGMV) kernels for decode-shaped batches; r <= kBgmvMaxRank.
+// Per-token (BGMV) kernels for decode-shaped batches.  The shrink takes any
+// r <= 128; the expand takes r <= 64, and r = 128 on aligned data.
 constexpr int kBgmvMaxRank = 64;
+inline bool bgmv_supports(bool expand, int32_t r, bool vec) {
+  return expand ? (r <= kBgmvMaxRank || (r == 128 && vec)) : r <= kMaxRank;
+}
 
 // Ranks per workgroup of the per-token shrink (4, 8 or 16) for T tokens at
 // rank r over rows of H: the largest that still gives 256 workgroups (512

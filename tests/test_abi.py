@@ -201,15 +201,20 @@ def test_set_path_validation():
 
 
 def test_forced_bgmv_rejects_large_rank_before_launch():
+    """Forced onto the per-token kernels, an expand rank they do not take
+    (above 64 and not an aligned 128) is refused before any launch; a rank
+    above 128 is refused by every entry point."""
     lib = lsb.lib()
     s = _seg()
     prev = lib.lora_set_path(1)
     try:
-        rc = lib.lora_shrink(FAKE, 4096, FAKE, 4096, 128, ctypes.byref(s), FAKE, 128, FAKE, 1 << 30, 0,
+        rc = lib.lora_shrink(FAKE, 4096, FAKE, 4096, 129, ctypes.byref(s), FAKE, 129, FAKE, 1 << 30, 0,
                              None)
+        _expect(rc, lsb.LORA_ERR_UNSUPPORTED, "rank")
+        rc = _slice_call(lib, ctypes.byref(s), [FAKE.value], [8], [0], r=100, ldy=64, ldv=100)
         _expect(rc, lsb.LORA_ERR_UNSUPPORTED, "per-token path")
-        rc = _slice_call(lib, ctypes.byref(s), [FAKE.value], [8], [0], r=128, ldy=64, ldv=128)
-        _expect(rc, lsb.LORA_ERR_UNSUPPORTED, "per-token path")
+        rc = _slice_call(lib, ctypes.byref(s), [FAKE.value], [12], [0], r=128, ldy=64, ldv=128)
+        _expect(rc, lsb.LORA_ERR_UNSUPPORTED, "per-token path")     # n % 8 != 0: not aligned
     finally:
         lib.lora_set_path(prev)
 

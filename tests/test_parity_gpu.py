@@ -257,7 +257,7 @@ def _random_cases(n=24, seed=2024):
         neg = float(rng.choice([0.0, 0.1, 0.3]))
         dist = ("uniform", "zipf")[int(rng.integers(0, 2))]
         path = ("auto", "bgmv", "sgmv")[int(rng.integers(0, 3))]
-        if path == "bgmv" and r > 64:
+        if path == "bgmv" and r > 64 and not (r == 128 and H % 8 == 0):
             path = "sgmv"
         cases.append((i, dtype, T, H, r, L, widths, sl, neg, dist, path))
     return cases
@@ -449,7 +449,7 @@ def test_rank_padding(r_true, r_pad, force_path):
     # Same v into both expands, on one kernel family at a time: identical bits.
     v_pad = torch.zeros(w.T, r_pad, device="cuda")
     v_pad[:, :r_true] = vs[0]
-    modes = [lsb.PATH_SGMV] + ([lsb.PATH_BGMV] if r_pad <= 64 else [])
+    modes = [lsb.PATH_SGMV] + ([lsb.PATH_BGMV] if (r_pad <= 64 or r_pad == 128) else [])
     for mode in modes:
         force_path(mode)
         ys = []
@@ -561,6 +561,8 @@ def force_path():
 
 PATH_CASES = [
     # dtype, T, H, r, L, slices, seq_len, neg_frac
+    ("bf16", 40, 2048, 128, 5, [[1024, 512]], (1, 4), 0.1),   # rank 128 (per-token: 16 lanes a column)
+    ("f16", 16, 1000, 128, 3, [[256]], 1, 0.0),               # rank 128, shrink on the element-wise path
     ("f16", 16, 1024, 16, 4, [[1024]], 1, 0.0),
     ("f16", 256, 4096, 16, 4, [[4096]], 1, 0.0),
     ("bf16", 300, 2048, 32, 7, [[512, 256, 256]], (1, 20), 0.1),
@@ -696,8 +698,8 @@ def test_live_ranks(force_path, path, dtype, T, H, r, L, slices, ranks_from, int
     batch): the segment kernels skip the padding, the per-token kernels read
     the zero padding as it is; both give the same values as without the
     ranks, within the tolerance of the oracle; ranks above r are clamped to r."""
-    if path == "bgmv" and r > 64:
-        pytest.skip("the per-token kernels take r <= 64")
+    if path == "bgmv" and r > 64 and r != 128:
+        pytest.skip("the per-token kernels take r <= 64 or 128")
     _announce(f"live ranks {path} {dtype} T={T} H={H} r={r} L={L} slices={slices} ranks={ranks_from}")
     force_path(lsb.PATH_SGMV if path == "sgmv" else lsb.PATH_BGMV)
     w = W.make("ranks", dtype, T, H, r, L, slices, seed=T + r, seq_len=(1, 40), neg_frac=0.1,
@@ -882,13 +884,16 @@ def test_bgmv_and_sgmv_agree(force_path):
     assert tol_ratio(outs[0][1][act], outs[1][1][act]) <= 1
 
 
-def test_forced_bgmv_rejects_large_rank(force_path):
+def test_forced_bgmv_rejects_unsupported_expand_rank(force_path):
+    """The per-token expand takes r <= 64, or 128 on aligned data: r = 100
+    forced onto it is refused (the per-token shrink takes it)."""
     force_path(lsb.PATH_BGMV)
-    w = W.make("big", "bf16", 32, 256, 128, 2, [[64]], seed=3)
+    w = W.make("big", "bf16", 32, 256, 100, 2, [[64]], seed=3)
     dw = DeviceWorkload(w)
     with pytest.raises(lsb.LoraError) as e:
         dw.run()
     assert e.value.code == lsb.LORA_ERR_UNSUPPORTED
+    assert "lora_expand" in str(e.value)
 
 
 # ---------------------------------------------------------------- one adapter, no metadata
