@@ -328,27 +328,51 @@ def short_name(kn):
     return kn.replace("void ", "").replace("lora::(anonymous namespace)::", "").split("(")[0]
 
 
-def assign_units(rows, n_outputs):
+def assign_units(rows, n_outputs, with_step=False):
     """Unit of every library dispatch of a --profile run, in dispatch order:
     each step is build, shrink (one or two kernels), then one expand call per
-    output, so the k-th expand dispatch after a build belongs to output k.
-    Returns [(unit, row)]; other kernels (the copy probe, torch's fills) are
-    returned with unit None."""
+    output (one or two kernels each: the tile launch, and the per-token launch
+    when the expand splits a decode + prefill mix), so the expand kernels after
+    a build are numbered by output in order.  Returns [(unit, row)], or
+    [(unit, step, row)] with with_step; other kernels (the copy probe, torch's
+    fills) get unit None.  A build not followed by a shrink (the argument
+    pool's one-time metadata) forms no step of its own."""
     out = []
     k = 0
+    step = -1
+    prev = None
     for r in sorted(rows, key=lambda r: int(r.get("Dispatch_Id") or r.get("Correlation_Id") or 0)):
-        op = op_of(r["Kernel_Name"])
+        kn = r["Kernel_Name"]
+        op = op_of(kn)
         if op == "build":
             k = 0
-            out.append(("build", r))
+            step += 1
+            unit = "build"
         elif op == "shrink":
-            out.append(("shrink", r))
+            unit = "shrink"
         elif op == "expand":
-            out.append((f"expand[{k}]" if n_outputs > 1 else "expand", r))
-            k += 1
+            # A per-token launch right after the tile launch of the same call.
+            if prev is not None and prev[0].startswith("expand") and "bgmv" in kn and "bgmv" not in prev[1]:
+                unit = prev[0]
+            else:
+                unit = f"expand[{k}]" if n_outputs > 1 else "expand"
+                k += 1
         else:
-            out.append((None, r))
+            unit = None
+        if unit:
+            prev = (unit, kn)
+        out.append((unit, step, r) if with_step else (unit, r))
     return out
+
+
+def steps_of(assigned):
+    """Per unit, the number of distinct steps it occurs in."""
+    import collections
+    seen = collections.defaultdict(set)
+    for unit, step, _ in assigned:
+        if unit:
+            seen[unit].add(step)
+    return {u: len(v) for u, v in seen.items()}
 
 
 def unit_bytes(w, unit):
@@ -432,23 +456,23 @@ def summarize_profiles(args):
         rows = list(csv.DictReader(open(args.trace)))
         per_kernel = collections.defaultdict(list)
         per_unit = collections.defaultdict(list)
-        steps = 0
-        for unit, r in assign_units(rows, nout):
+        assigned = assign_units(rows, nout, with_step=True)
+        nsteps = steps_of(assigned)
+        for unit, _, r in assigned:
             d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
             if unit is None and "copy" not in r["Kernel_Name"].lower():
                 continue
             per_kernel[short_name(r["Kernel_Name"])].append(d)
             if unit:
                 per_unit[unit].append(d)
-                steps += unit == "build"
         for k in sorted(per_kernel):
             v = per_kernel[k]
             lines.append(f"| {k} | {len(v)} | {statistics.fmean(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
-        lines += ["", f"Per call of the step ({steps} steps traced; a call's kernels summed; "
-                  "algorithmic bytes of the call; fraction of the 8 TB/s HBM peak):", "",
+        lines += ["", f"Per call of the step ({nsteps.get('shrink', 0)} steps traced; a call's kernels "
+                  "summed; algorithmic bytes of the call; fraction of the 8 TB/s HBM peak):", "",
                   "| call | us per step | algorithmic MiB | GB/s | of 8 TB/s |", "|---|---|---|---|---|"]
         for unit in sorted(per_unit):
-            per_step = sum(per_unit[unit]) / max(1, steps)
+            per_step = sum(per_unit[unit]) / max(1, nsteps.get(unit, 1))
             nb = unit_bytes(w, unit)
             if nb:
                 gbs = nb / (per_step * 1e-6) / 1e9
@@ -468,17 +492,17 @@ def summarize_profiles(args):
     def per_unit(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
         tot = collections.defaultdict(float)
-        steps = 0
         copy_vals = []
-        for unit, r in assign_units(rows, nout):
+        assigned = assign_units(rows, nout, with_step=True)
+        nsteps = steps_of(assigned)
+        for unit, _, r in assigned:
             val = float(r["Counter_Value"])  # KiB per dispatch
-            if unit == "build":
-                steps += 1
             if unit:
                 tot[unit] += val
             elif "neg_kernel" in r["Kernel_Name"]:
                 copy_vals.append(val)
-        return {k: v / max(1, steps) for k, v in tot.items()}, copy_vals, steps
+        return ({k: v / max(1, nsteps.get(k, 1)) for k, v in tot.items()}, copy_vals,
+                nsteps.get("shrink", 0))
 
     fetch, fcopy, steps = per_unit(args.fetch, "FETCH_SIZE")
     write, wcopy, _ = per_unit(args.write, "WRITE_SIZE")

@@ -55,3 +55,11 @@ def test_profile_dispatches_are_assigned_to_calls():
     assert units == ["build", "shrink", "shrink", "expand[0]", "expand[1]", None,
                      "build", "shrink", "expand[0]", "expand[1]"]
     assert [u for u, _ in bench.assign_units(rows[:4], 1)] == ["build", "shrink", "shrink", "expand"]
+    # the argument pool's one-time build forms no step; a split expand's
+    # per-token launch belongs to the call whose tile launch precedes it
+    names = ["build_segments_kernel", "build_segments_kernel", "shrink_kernel", "expand_kernel<1>",
+             "bgmv_expand_fast_kernel<1>", "expand_kernel<2>"]
+    rows = [{"Dispatch_Id": str(i + 1), "Kernel_Name": n} for i, n in enumerate(names)]
+    got = bench.assign_units(rows, 2, with_step=True)
+    assert [u for u, _, _ in got] == ["build", "build", "shrink", "expand[0]", "expand[0]", "expand[1]"]
+    assert bench.steps_of(got) == {"build": 2, "shrink": 1, "expand[0]": 1, "expand[1]": 1}
