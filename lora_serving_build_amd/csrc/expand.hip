@@ -494,6 +494,7 @@ hipError_t launch_expand(const SegView& seg, const float* v, int64_t ldv, int64_
   int64_t per_cu = (int64_t)(160 * 1024 / lds);
   const int64_t reg_cu = tb == 2 || nks == 8 ? 2 : (nks <= 2 ? 4 : 3);
   per_cu = per_cu < 1 ? 1 : (per_cu > reg_cu ? reg_cu : per_cu);
+  if (tuning().expand_wgs_per_cu >= 1 && tuning().expand_wgs_per_cu < per_cu) per_cu = tuning().expand_wgs_per_cu;
   int64_t grid = items < 256 * per_cu ? items : 256 * per_cu;
   grid = (grid + 7) / 8 * 8;
   if (grid < 8) grid = 8;
