@@ -451,10 +451,12 @@ hipError_t launch_expand(const SegView& seg, const float* v, int64_t ldv, int64_
   //   8192 x 4096,  r = 16 / 64:         32.6 / 40.7 us -> 33.0 / 36.0
   //   8192-token layer, qkv slices:      95.5 us -> 92.1
   //   2048 x 16384 / 2048 x 4096, r = 64: 40.5 / 13.2 us -> 41.7 / 19.1
+  //   2048 x 128256 (logits), r = 16:   266 us -> 228
   // so they are taken from 64 tiles of 128 tokens and 2048 tile-chunks up,
-  // for r <= 64 (r = 128 keeps 64-token tiles for its registers).
+  // or from 16384 tile-chunks up, for r <= 64 (r = 128 keeps 64-token tiles
+  // for its registers).
   const int64_t mt128 = max_token_tiles(seg.T, seg.L, 2 * kTileTokens);
-  int tb = (nks <= 4 && mt128 >= 64 && mt128 * chunks >= 2048) ? 2 : 1;
+  int tb = (nks <= 4 && ((mt128 >= 64 && mt128 * chunks >= 2048) || mt128 * chunks >= 16384)) ? 2 : 1;
   if (tuning().expand_tb == 1 || tuning().expand_tb == 2) tb = tuning().expand_tb;
   if (nks == 8) tb = 1;
   const int64_t tt = (int64_t)kTileTokens * tb;
