@@ -751,6 +751,165 @@ def summarize_sweep(path):
     print("wrote", out)
 
 
+def _graph_us(torch, fn, sets, K):
+    return graph_time(torch, fn, sets, 0, K) / K * 1e3
+
+
+def plan_sweep(args):
+    """The launch-plan measurements the design notes quote, each call alone
+    over a pool of argument sets far beyond the Infinity Cache (bf16 unless
+    noted; one JSON line per measurement):
+      shrink_split  -- the tile shrink over H-split counts 1..8 (LORA_SHRINK_KSPLIT)
+      expand_plan   -- the tile expand over token-tile size x run length
+                       (LORA_EXPAND_TB x LORA_EXPAND_CPR)
+      path          -- forced per-token, forced tile and automatic path, fp16,
+                       4 adapters, one token per sequence
+      mixed         -- decode + prefill mixes, and a prefill of a few adapters
+                       of a large pool: the automatic path (the per-segment
+                       split) against tiles only and per-token only
+    Inputs are drawn on the GPU (seeded); ids from the shared generator."""
+    import numpy as np
+    import torch
+    import lora_serving_build_amd as lsb
+    import workloads as W
+    torch.cuda.set_device(0)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3)
+    parts = [p for p in args.plans.split(",") if p]
+
+    def emit(**kw):
+        print(json.dumps(kw), flush=True)
+
+    def with_env(env):
+        for k in [k for k in os.environ if k.startswith("LORA_")]:
+            del os.environ[k]
+        os.environ.update(env)
+        lsb.lora_reload_tuning()
+
+    def ids_of(name):
+        if name == "llama3_70b_layer":
+            return W.make("p", "bf16", 8192, 8, 8, 64, [[8]], seed=1005, seq_len=(1, 512), id_dist="zipf",
+                          zipf_s=1.1, neg_frac=0.05).ids, 64
+        if name == "prefill_T2048":
+            return W.make("p", "bf16", 2048, 8, 8, 4, [[8]], seed=1003, seq_len=8, sort_by_id=True).ids, 4
+        T = int(name.split("_T")[1])
+        return W.sweep_point("sgmv", T, 8, 8, L=4).ids, 4
+
+    if "shrink_split" in parts:
+        for name, H, r in (("llama3_70b_layer", 8192, 64), ("seq8_T8192", 16384, 16), ("seq8_T8192", 16384, 64),
+                           ("prefill_T2048", 4096, 16)):
+            ids_np, L = ids_of(name)
+            T = ids_np.size
+            ids = torch.from_numpy(ids_np).cuda()
+            P = max(3, math.ceil(1.5 * 2**30 / (T * H * 2)))
+            sets = [dict(x=torch.randn(T, H, generator=gen, device="cuda").to(torch.bfloat16),
+                         A=(torch.randn(L, r, H, generator=gen, device="cuda") / math.sqrt(H)).to(torch.bfloat16),
+                         v=torch.zeros(T, r, device="cuda"), seg=lsb.lora_build_segments(ids, L))
+                    for _ in range(P)]
+            ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+            for ks in ("", "1", "2", "3", "4", "5", "6", "7", "8"):
+                with_env({"LORA_SHRINK_KSPLIT": ks} if ks else {})
+                need = lsb.lora_shrink_workspace_bytes(T, L, H, r)
+                us = _graph_us(torch, lambda s: lsb.lora_shrink(s["x"], s["A"], s["seg"], s["v"], workspace=ws),
+                               sets, 2 * P)
+                emit(plan="shrink_split", shape=name, H=H, r=r, ksplit=ks or "auto",
+                     workspace_MB=round(need / 1e6, 2), us=round(us, 2))
+            del sets, ws
+            torch.cuda.empty_cache()
+
+    if "expand_plan" in parts:
+        shapes = (("llama3_70b_layer", [8192, 1024, 1024], 64), ("llama3_70b_layer", [28672, 28672], 64),
+                  ("seq8_T8192", [16384], 16), ("seq8_T8192", [16384], 64), ("seq8_T8192", [4096], 64),
+                  ("seq8_T2048", [16384], 64), ("seq8_T2048", [4096], 64))
+        plans = ("", "1:2", "1:4", "2:2", "2:3", "2:4", "2:6", "2:8")
+        for name, widths, r in shapes:
+            ids_np, L = ids_of(name)
+            T = ids_np.size
+            n = sum(widths)
+            ids = torch.from_numpy(ids_np).cuda()
+            offs = [int(o) for o in np.cumsum([0] + widths[:-1])]
+            P = max(3, math.ceil(2.0 * 2**30 / (T * n * 2)))
+            sets = [dict(v=torch.randn(T, r, generator=gen, device="cuda"),
+                         Bs=[(torch.randn(L, wd, r, generator=gen, device="cuda") / 8).to(torch.bfloat16)
+                             for wd in widths],
+                         y=torch.randn(T, n, generator=gen, device="cuda").to(torch.bfloat16),
+                         seg=lsb.lora_build_segments(ids, L)) for _ in range(P)]
+            for plan in plans:
+                env = {}
+                if plan:
+                    tb, cpr = plan.split(":")
+                    env = {"LORA_EXPAND_TB": tb, "LORA_EXPAND_CPR": cpr}
+                with_env(env)
+                us = _graph_us(torch, lambda s: lsb.lora_expand_slice(s["v"], s["Bs"], offs, s["seg"], s["y"], True),
+                               sets, 3 * P)
+                emit(plan="expand_plan", shape=name, slices=widths, r=r, tile_blocks_cpr=plan or "auto",
+                     us=round(us, 2))
+            del sets
+            torch.cuda.empty_cache()
+    with_env({})
+
+    if "path" in parts:
+        L = 4
+        for T in (16, 64, 256, 512):
+            ids = torch.from_numpy(W.sweep_point("bgmv", T, 8, 8, L=L).ids).cuda()
+            for H in (1024, 4096, 16384):
+                for r in (32, 64, 128):
+                    P = max(4, min(64, math.ceil(2**30 / (T * H * 4 + L * r * H * 4))))
+                    sets = [dict(x=torch.randn(T, H, generator=gen, device="cuda").half(),
+                                 A=(torch.randn(L, r, H, generator=gen, device="cuda") / 64).half(),
+                                 B=(torch.randn(L, H, r, generator=gen, device="cuda") / 8).half(),
+                                 y=torch.randn(T, H, generator=gen, device="cuda").half(),
+                                 v=torch.randn(T, r, generator=gen, device="cuda"),
+                                 seg=lsb.lora_build_segments(ids, L)) for _ in range(P)]
+                    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+                    rec = {}
+                    for label, mode in (("per_token", lsb.PATH_BGMV), ("tiles", lsb.PATH_SGMV),
+                                        ("auto", lsb.PATH_AUTO)):
+                        lsb.lora_set_path(mode)
+                        rec["shrink_" + label] = round(_graph_us(
+                            torch, lambda s: lsb.lora_shrink(s["x"], s["A"], s["seg"], s["v"], workspace=ws),
+                            sets, 2 * P), 2)
+                        try:
+                            rec["expand_" + label] = round(_graph_us(
+                                torch, lambda s: lsb.lora_expand(s["v"], s["B"], s["seg"], s["y"], True),
+                                sets, 2 * P), 2)
+                        except lsb.LoraError:
+                            rec["expand_" + label] = None
+                    lsb.lora_set_path(lsb.PATH_AUTO)
+                    emit(plan="path", T=T, H=H, r=r, **rec)
+                    del sets, ws
+                    torch.cuda.empty_cache()
+
+    if "mixed" in parts:
+        H = n = 4096
+        for n_pre, pre_l, n_dec, L in ((7168, 16, 1024, 1040), (3072, 16, 1024, 1040), (7936, 16, 256, 300),
+                                       (4096, 8, 0, 1024)):
+            w = W.make_mixed("m", "bf16", n_pre, pre_l, n_dec, L, 8, 8, [[8]], seed=5)
+            ids = torch.from_numpy(w.ids).cuda()
+            T = w.T
+            for r in (16, 32, 64):
+                P = 6
+                sets = [dict(x=torch.randn(T, H, generator=gen, device="cuda").to(torch.bfloat16),
+                             A=(torch.randn(L, r, H, generator=gen, device="cuda") / 64).to(torch.bfloat16),
+                             B=(torch.randn(L, n, r, generator=gen, device="cuda") / 8).to(torch.bfloat16),
+                             y=torch.randn(T, n, generator=gen, device="cuda").to(torch.bfloat16),
+                             v=torch.randn(T, r, generator=gen, device="cuda"),
+                             seg=lsb.lora_build_segments(ids, L)) for _ in range(P)]
+                ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+                rec = {}
+                for label, mode in (("auto", lsb.PATH_AUTO), ("tiles", lsb.PATH_SGMV), ("per_token", lsb.PATH_BGMV)):
+                    lsb.lora_set_path(mode)
+                    rec["shrink_" + label] = round(_graph_us(
+                        torch, lambda s: lsb.lora_shrink(s["x"], s["A"], s["seg"], s["v"], workspace=ws),
+                        sets, 2 * P), 2)
+                    rec["expand_" + label] = round(_graph_us(
+                        torch, lambda s: lsb.lora_expand(s["v"], s["B"], s["seg"], s["y"], True), sets, 2 * P), 2)
+                lsb.lora_set_path(lsb.PATH_AUTO)
+                emit(plan="mixed", prefill=n_pre, prefill_loras=pre_l, decode=n_dec, L=L, H=H, r=r, **rec)
+                del sets, ws
+                torch.cuda.empty_cache()
+
+
 def source_hash(paths):
     h = hashlib.sha256()
     for p in paths:
@@ -933,6 +1092,8 @@ def main():
     ap.add_argument("--sweep-grid", default="full", choices=("full", "thin"))
     ap.add_argument("--sweep-kinds", default="",
                     help="comma-separated sweep kinds to run (bgmv, sgmv, single, logits, golden)")
+    ap.add_argument("--plans", default="",
+                    help="comma-separated launch-plan measurements: shrink_split, expand_plan, path, mixed")
     ap.add_argument("--summarize-sweep", metavar="JSONL",
                     help="write profiles/sweep_shrink_expand_f16.md from a --sweep run's output")
     ap.add_argument("--trace", help="kernel_trace.csv of a --kernel-trace run")
@@ -949,6 +1110,9 @@ def main():
         return
     if args.sweep:
         sweep(args)
+        return
+    if args.plans:
+        plan_sweep(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -135,7 +135,12 @@ int lora_build_segments(const int32_t *token_lora, int32_t T, int32_t L, lora_se
 /* Workspace bytes that lora_shrink needs for T tokens, L adapters, hidden
  * size H and rank r (0 if it needs none).  Only batches with too few token
  * tiles to occupy the GPU split the H-sum across workgroups; the workspace
- * then holds one fp32 partial row per token and H chunk. */
+ * then holds a 256-byte header (the split the kernel chose) and one fp32
+ * partial row per token and H chunk, for as many chunks as the fewest tiles
+ * of T tokens would take.  The host sees only an upper bound on the tiles
+ * (one partial tile per adapter of the pool); the kernel sets the split from
+ * the true count, so a batch that uses few adapters of a large pool still
+ * fills the GPU. */
 size_t lora_shrink_workspace_bytes(int32_t T, int32_t L, int32_t H, int32_t r);
 
 /* Shrink (micro-benchmark PR: bgmv_shrink / sgmv_shrink; TPU PR: the
@@ -165,7 +170,7 @@ int lora_shrink(const void *x, int64_t ldx, const void *A, int32_t H, int32_t r,
 /* lora_shrink without a workspace argument and without any allocation, for
  * callers that cannot allocate device memory: code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
- * kernels and results as lora_shrink; the partial rows of an H split go to a
+ * kernels as lora_shrink; the partial rows of an H split go to a
  * static device array of LORA_NOALLOC_SCRATCH_BYTES that each GPU holds from
  * the library's load until the process ends (its address is looked up once
  * per device, on the first call that needs it, with the stream's device
@@ -173,10 +178,13 @@ int lora_shrink(const void *x, int64_t ldx, const void *A, int32_t H, int32_t r,
  * to be cleared between calls; the array keeps the last call's contents.
  * All calls on one GPU share the array: calls that overlap in time on one
  * GPU (different streams, or host threads) race and must be serialised by
- * the caller; calls on one stream are ordered and safe.
- * Errors: those of lora_shrink; LORA_ERR_UNSUPPORTED when the call's split
- * needs more than LORA_NOALLOC_SCRATCH_BYTES (lora_shrink_workspace_bytes
- * gives the need) -- reported before anything is launched; LORA_ERR_INVALID_ARG
+ * the caller; calls on one stream are ordered and safe.  The results are
+ * lora_shrink's bits except where the kernel would split H into more chunks
+ * than the array holds: then it takes fewer, and v may differ in the last
+ * bits (fp32 sums in another grouping), within the same tolerance.
+ * Errors: those of lora_shrink; LORA_ERR_UNSUPPORTED when the split the host
+ * chooses from the tile bound needs more than LORA_NOALLOC_SCRATCH_BYTES --
+ * reported before anything is launched; LORA_ERR_INVALID_ARG
  * when the stream belongs to a device other than the current one. */
 int lora_shrink_noalloc(const void *x, int64_t ldx, const void *A, int32_t H, int32_t r,
                         const lora_segments *seg, float *v, int64_t ldv, int dtype, void *stream);

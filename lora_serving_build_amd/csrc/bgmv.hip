@@ -25,7 +25,6 @@
 
 #include "lora_device.h"
 #include "lora_kernels.h"
-#include "tiles.h"
 
 namespace lora {
 
@@ -43,6 +42,9 @@ struct BgShrinkArgs {
   float* v;
   int64_t ldv;
   int32_t jb;  // rank blocks per token
+  // 0: every token, by token index; k >= 1: only the tokens of segments of
+  // at most k tokens, from the segment metadata (as in BgExpandArgs).
+  int32_t short_max;
 };
 
 struct BgExpandArgs {
@@ -85,31 +87,63 @@ __device__ __forceinline__ int token_adapter(const SegView& seg, int t) {
   return (l >= 0 && l < seg.L) ? l : -1;
 }
 
-// Number of tokens a per-token expand walks, and its short-segment table
-// when it takes short segments only (every thread must call it).
-__device__ __forceinline__ int bg_expand_tokens(const BgExpandArgs& a, ShortTable* st, int32_t* lds) {
-  if (a.short_max <= 0) return a.seg.T;
-  *st = build_short_table<kBgThreads>(a.seg, a.short_max, lds, lds + short_table_ints(a.seg.L));
-  return st->count;
+// Items a per-token kernel walks: every token, or, when it takes only the
+// tokens of short segments (1 .. short_max tokens: the decode requests of a
+// batch that mixes decode and prefill), short_max items per segment slot
+// (S <= min(L, T) slots).  An item of a slot whose segment is longer, or past
+// the segment's tokens, finds nothing to do after one round of loads: no
+// workgroup needs a table of all segments.
+__device__ __forceinline__ int bg_items(const SegView& seg, int short_max) {
+  if (short_max <= 0) return seg.T;
+  return min(seg.L, seg.T) * short_max;
 }
 
-// Token and adapter of item k: token k itself (adapter from token_lora), or
-// the k-th short-segment token (adapter from the segment).  false: nothing
-// to do (no adapter, or invalid metadata).  The results are uniform.
-__device__ __forceinline__ bool bg_expand_token(const BgExpandArgs& a, const ShortTable& st, int k, int* t,
-                                                int* l) {
-  if (a.short_max <= 0) {
-    *t = k;
-    *l = token_adapter(a.seg, k);
-    return *l >= 0;
-  }
-  int p = 0, lora_id = -1;
-  if (!short_token(st, a.seg.T, a.seg.L, k, &p, &lora_id)) return false;
-  typedef const __attribute__((address_space(4))) int32_t* const_ptr;
-  const int tok = __builtin_amdgcn_readfirstlane(*(const_ptr)(uintptr_t)(a.seg.sorted_token + p));
-  if (tok < 0 || tok >= a.seg.T) return false;
+// Token and adapter of slot item k (k < bg_items): token k % short_max of
+// segment k / short_max, if that segment is short.  false: nothing to do (a
+// longer segment, a slot past S, or invalid metadata).  Per lane.
+__device__ __forceinline__ bool short_slot_token(const SegView& seg, int short_max, int k, int* t, int* l) {
+  const int s = k / short_max;  // < min(L, T): the loads below are in bounds
+  const int j = k - s * short_max;
+  const int S = seg.counts[0];
+  const int b = seg.seg_start[s];
+  const int e = seg.seg_start[s + 1];
+  const int lora_id = seg.seg_lora[s];
+  const int len = e - b;
+  if (s >= S || len < 1 || len > short_max || j >= len) return false;
+  const int p = b + j;
+  if (p < 0 || p >= seg.T || lora_id < 0 || lora_id >= seg.L) return false;
+  const int tok = seg.sorted_token[p];
+  if (tok < 0 || tok >= seg.T) return false;
   *t = tok;
   *l = lora_id;
+  return true;
+}
+
+// The short-segment checks of 64 items of a workgroup's walk, one per lane,
+// made in one round of loads and refreshed every 64 items: item n of the
+// walk is checked by lane n % 64 of the batch loaded at item n - n % 64.
+// Every wave loads the same batch, so the results are uniform.
+struct ShortBatch {
+  int t = 0;
+  int l = -1;
+  int ok = 0;
+};
+
+// For item `it`, the n-th of this workgroup's grid-stride walk over `items`
+// items of `per` items per slot: false if it has no work, else its token and
+// adapter.
+__device__ __forceinline__ bool short_item(const SegView& seg, int short_max, int per, int items, int it,
+                                           int n, ShortBatch& sb, int* t, int* l) {
+  const int i = n & (kWave - 1);
+  if (i == 0) {
+    const int mine = it + (int)(threadIdx.x & (kWave - 1)) * (int)gridDim.x;
+    sb.t = 0;
+    sb.l = -1;
+    sb.ok = mine < items && short_slot_token(seg, short_max, mine / per, &sb.t, &sb.l);
+  }
+  if (!__builtin_amdgcn_readlane(sb.ok, i)) return false;
+  *t = __builtin_amdgcn_readlane(sb.t, i);
+  *l = __builtin_amdgcn_readlane(sb.l, i);
   return true;
 }
 
@@ -117,8 +151,9 @@ __device__ __forceinline__ bool bg_expand_token(const BgExpandArgs& a, const Sho
 // T ceil(r / RT) workgroups, each of which reads the token's x row (again, from
 // L2, for every block after the first) and RT rows of A.  Lane i owns elements
 // 8 (i + 256 k) .. +8 of H; UNR blocks of 2048 elements are in flight per trip,
-// more when RT is small.
-template <int DT, bool VEC, int RT>
+// more when RT is small.  SH: the short segments' tokens only (a compile-time
+// variant, so the every-token kernels carry none of its code).
+template <int DT, bool VEC, int RT, bool SH>
 __global__ __launch_bounds__(kBgThreads) void bgmv_shrink_kernel(BgShrinkArgs a) {
   constexpr int BLK = kBgThreads * 8;
   constexpr int UNR = RT <= 4 ? 8 : RT <= 8 ? 4 : 2;  // blocks per trip (register bound)
@@ -126,11 +161,19 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_shrink_kernel(BgShrinkArgs a)
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int items = a.seg.T * a.jb;
-
-  for (int it = blockIdx.x; it < items; it += gridDim.x) {
-    const int t = it / a.jb;
-    const int j0 = (it - t * a.jb) * RT;
+  const int items = bg_items(a.seg, SH ? a.short_max : 0) * a.jb;
+  ShortBatch sb;
+  int n = 0;
+  for (int it = blockIdx.x; it < items; it += gridDim.x, ++n) {
+    const int k = it / a.jb;
+    const int j0 = (it - k * a.jb) * RT;
+    // With every token, the adapter id is loaded (scalar) while x is in
+    // flight; a short-segment token has its adapter from the segment.
+    int t = k, l_short = -1;
+    if constexpr (SH) {
+      if (!short_item(a.seg, a.short_max, a.jb, items, it, n, sb, &t, &l_short)) continue;
+    }
+    auto adapter = [&]() { return SH ? l_short : token_adapter(a.seg, t); };
     const uint16_t* xrow = a.x + (int64_t)t * a.ldx;
     float acc[RT];
 #pragma unroll
@@ -144,7 +187,7 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_shrink_kernel(BgShrinkArgs a)
         for (int u = 0; u < UNR; ++u)
           xv[u] = h0 + u * BLK < a.H ? *reinterpret_cast<const u32x4*>(xrow + h0 + u * BLK)
                                      : u32x4{0u, 0u, 0u, 0u};
-        l = token_adapter(a.seg, t);
+        l = adapter();
         if (l < 0) break;
         const uint16_t* Al = a.A + (int64_t)l * a.r * a.H;
 #pragma unroll
@@ -164,9 +207,9 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_shrink_kernel(BgShrinkArgs a)
           acc[j] = s;
         }
       }
-      if (a.H > 0) l = token_adapter(a.seg, t);
+      if (a.H > 0) l = adapter();
     } else {
-      l = token_adapter(a.seg, t);
+      l = adapter();
       if (l >= 0) {
         const uint16_t* Al = a.A + (int64_t)l * a.r * a.H;
         for (int h = tid; h < a.H; h += kBgThreads) {
@@ -288,19 +331,24 @@ __device__ __forceinline__ void bg_store_cols(uint16_t* yrow, int nq, int c0, in
 }
 
 // General per-token expand: any r <= RT, any alignment.  Lane i owns 8
-// consecutive output columns and reads their weight rows itself.
-template <int DT, bool VEC, int RT>
+// consecutive output columns and reads their weight rows itself.  SH as for
+// the shrink.
+template <int DT, bool VEC, int RT, bool SH>
 __global__ __launch_bounds__(kBgThreads) void bgmv_expand_kernel(BgExpandArgs a) {
   constexpr int BLK = kBgThreads * 8;
   constexpr int UNR = RT <= 16 ? 2 : 1;  // column blocks per trip (register bound)
   const int tid = threadIdx.x;
-  extern __shared__ int32_t s_tab[];  // short-segment table (short_max > 0)
-  ShortTable st{};
-  const int ntok = bg_expand_tokens(a, &st, s_tab);
-
-  for (int k = blockIdx.x; k < ntok; k += gridDim.x) {
-    int t = 0, l = -1;
-    if (!bg_expand_token(a, st, k, &t, &l)) continue;  // uniform: the row of y stays as it is
+  const int ntok = bg_items(a.seg, SH ? a.short_max : 0);
+  ShortBatch sb;
+  int n = 0;
+  for (int k = blockIdx.x; k < ntok; k += gridDim.x, ++n) {
+    int t = k, l = -1;
+    if constexpr (SH) {
+      if (!short_item(a.seg, a.short_max, 1, ntok, k, n, sb, &t, &l)) continue;
+    } else {
+      l = token_adapter(a.seg, t);
+    }
+    if (l < 0) continue;  // uniform: the row of y stays as it is
     for (int q = 0; q < a.num_slices; ++q) {
       const float* vrow = a.v + (int64_t)t * a.ldv + (int64_t)q * a.v_slice_stride;
       const int nq = a.slices[q].n;
@@ -361,7 +409,7 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_expand_kernel(BgExpandArgs a)
 // rounds whose index divided by 4 RPI is b modulo cb.
 constexpr int kRoundCols = kWave * 8;
 
-template <int DT, int G, int RPI>
+template <int DT, int G, int RPI, bool SH>
 __global__ __launch_bounds__(kBgThreads) void bgmv_expand_fast_kernel(BgExpandArgs a) {
   constexpr int LG = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : G == 8 ? 3 : 4;
   constexpr int K = 8 * G;                   // weight loads per lane and round
@@ -377,18 +425,18 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_expand_fast_kernel(BgExpandAr
   const int wave = threadIdx.x / kWave;
   const int part = lane & (G - 1);
   float* so = s_out[wave];
-  extern __shared__ int32_t s_tab[];  // short-segment table (short_max > 0)
-  ShortTable st{};
-  const int ntok = bg_expand_tokens(a, &st, s_tab);
-
-  const int items = ntok * a.cb;
-  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+  const int items = bg_items(a.seg, SH ? a.short_max : 0) * a.cb;
+  ShortBatch sb;
+  int n = 0;
+  for (int it = blockIdx.x; it < items; it += gridDim.x, ++n) {
     const int k = it / a.cb;
     const int cb = it - k * a.cb;
     // With every token, the adapter id is loaded (scalar) while y and v are
-    // in flight; short-segment tokens know theirs from the table.
+    // in flight; short-segment tokens have theirs from the segment.
     int t = k, l_short = -1;
-    if (a.short_max > 0 && !bg_expand_token(a, st, k, &t, &l_short)) continue;
+    if constexpr (SH) {
+      if (!short_item(a.seg, a.short_max, a.cb, items, it, n, sb, &t, &l_short)) continue;
+    }
     for (int q = 0; q < a.num_slices; ++q) {
       const int nq = a.slices[q].n;
       const float* vrow = a.v + (int64_t)t * a.ldv + (int64_t)q * a.v_slice_stride + part * 8;
@@ -397,7 +445,7 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_expand_fast_kernel(BgExpandAr
         // y and v do not depend on the adapter: they are in flight while the
         // (scalar) adapter id arrives, and only the id is waited for before
         // the weight loads go out.
-        const int l = a.short_max > 0 ? l_short : token_adapter(a.seg, t);
+        const int l = SH ? l_short : token_adapter(a.seg, t);
         u32x4 yv[RPI];
 #pragma unroll
         for (int u = 0; u < RPI; ++u) {
@@ -514,25 +562,35 @@ int bgmv_shrink_ranks(int64_t T, int32_t r, int32_t H) {
 
 hipError_t launch_bgmv_shrink(const SegView& seg, const uint16_t* x, int64_t ldx, const uint16_t* A,
                               int32_t H, int32_t r, float* v, int64_t ldv, int dtype, bool vec,
-                              hipStream_t s) {
-  BgShrinkArgs a{seg, x, ldx, A, H, r, v, ldv, 1};
-  const int64_t T = seg.T > 0 ? seg.T : 1;
+                              hipStream_t s, int short_max) {
+  BgShrinkArgs a{seg, x, ldx, A, H, r, v, ldv, 1, short_max > 0 ? short_max : 0};
+  // Items walked: every token, or short_max per segment slot.
+  const int64_t T_walk = a.short_max > 0 ? (int64_t)std::min(seg.L, seg.T) * a.short_max : seg.T;
+  const int64_t T = T_walk > 0 ? T_walk : 1;
   const int rt = bgmv_shrink_ranks(T, r, H);
   a.jb = (r + rt - 1) / rt;
   int64_t grid = T * a.jb;
   if (grid > 8192) grid = 8192;
-#define LORA_BG_SHRINK(DT_, VEC_)                                                                     \
+  // Taking short segments only, most slots may be empty (a batch without
+  // decode requests has none): one round of resident workgroups (two per CU
+  // at these register counts) walks them, so an empty pass costs little.
+  if (a.short_max > 0 && grid > 512) grid = 512;
+  const bool sh = a.short_max > 0;
+#define LORA_BG_SHRINK(DT_, VEC_, SH_)                                                                \
   if (rt == 16)                                                                                      \
-    hipLaunchKernelGGL((bgmv_shrink_kernel<DT_, VEC_, 16>), dim3(grid), dim3(kBgThreads), 0, s, a);  \
+    hipLaunchKernelGGL((bgmv_shrink_kernel<DT_, VEC_, 16, SH_>), dim3(grid), dim3(kBgThreads), 0, s, a); \
   else if (rt == 8)                                                                                  \
-    hipLaunchKernelGGL((bgmv_shrink_kernel<DT_, VEC_, 8>), dim3(grid), dim3(kBgThreads), 0, s, a);   \
+    hipLaunchKernelGGL((bgmv_shrink_kernel<DT_, VEC_, 8, SH_>), dim3(grid), dim3(kBgThreads), 0, s, a); \
   else                                                                                               \
-    hipLaunchKernelGGL((bgmv_shrink_kernel<DT_, VEC_, 4>), dim3(grid), dim3(kBgThreads), 0, s, a);
+    hipLaunchKernelGGL((bgmv_shrink_kernel<DT_, VEC_, 4, SH_>), dim3(grid), dim3(kBgThreads), 0, s, a);
+#define LORA_BG_SHRINK_SH(DT_, VEC_) \
+  if (sh) { LORA_BG_SHRINK(DT_, VEC_, true) } else { LORA_BG_SHRINK(DT_, VEC_, false) }
   if (dtype == 0) {
-    if (vec) { LORA_BG_SHRINK(0, true) } else { LORA_BG_SHRINK(0, false) }
+    if (vec) { LORA_BG_SHRINK_SH(0, true) } else { LORA_BG_SHRINK_SH(0, false) }
   } else {
-    if (vec) { LORA_BG_SHRINK(1, true) } else { LORA_BG_SHRINK(1, false) }
+    if (vec) { LORA_BG_SHRINK_SH(1, true) } else { LORA_BG_SHRINK_SH(1, false) }
   }
+#undef LORA_BG_SHRINK_SH
 #undef LORA_BG_SHRINK
   return hipGetLastError();
 }
@@ -543,12 +601,8 @@ hipError_t launch_bgmv_expand(const SegView& seg, const float* v, int64_t ldv, i
                               int short_max) {
   BgExpandArgs a{};
   a.short_max = short_max > 0 ? short_max : 0;
-  // Tokens walked: every token, or at most min(S, T) * short_max of short
-  // segments (S <= L); the table of short segments lives in LDS.
-  const int64_t T_walk = a.short_max > 0
-                             ? std::min<int64_t>(seg.T, (int64_t)std::min(seg.L, seg.T) * a.short_max)
-                             : seg.T;
-  const size_t lds = a.short_max > 0 ? 4 * (size_t)(short_table_ints(seg.L) + kBgThreads / kWave + 1) : 0;
+  // Items walked: every token, or short_max per segment slot.
+  const int64_t T_walk = a.short_max > 0 ? (int64_t)std::min(seg.L, seg.T) * a.short_max : seg.T;
   a.seg = seg;
   a.v = v;
   a.ldv = ldv;
@@ -580,37 +634,48 @@ hipError_t launch_bgmv_expand(const SegView& seg, const float* v, int64_t ldv, i
     a.cb = (int32_t)cb;
     int64_t grid = T * cb;
     if (grid > 8192) grid = 8192;
-#define LORA_BG_FAST(DT_)                                                                            \
+    if (a.short_max > 0 && grid > 1024) grid = 1024;  // one round (four per CU), as for the shrink
+    const bool sh = a.short_max > 0;
+#define LORA_BG_FAST(DT_, SH_)                                                                       \
   switch (r) {                                                                                      \
     case 8:                                                                                         \
-      if (rpi == 2) hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 1, 2>), dim3(grid), dim3(kBgThreads), lds, s, a); \
-      else hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 1, 1>), dim3(grid), dim3(kBgThreads), lds, s, a); \
+      if (rpi == 2) hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 1, 2, SH_>), dim3(grid), dim3(kBgThreads), 0, s, a); \
+      else hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 1, 1, SH_>), dim3(grid), dim3(kBgThreads), 0, s, a); \
       break;                                                                                        \
     case 16:                                                                                        \
-      if (rpi == 2) hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 2, 2>), dim3(grid), dim3(kBgThreads), lds, s, a); \
-      else hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 2, 1>), dim3(grid), dim3(kBgThreads), lds, s, a); \
+      if (rpi == 2) hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 2, 2, SH_>), dim3(grid), dim3(kBgThreads), 0, s, a); \
+      else hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 2, 1, SH_>), dim3(grid), dim3(kBgThreads), 0, s, a); \
       break;                                                                                        \
-    case 32: hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 4, 1>), dim3(grid), dim3(kBgThreads), lds, s, a); break; \
-    case 64: hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 8, 1>), dim3(grid), dim3(kBgThreads), lds, s, a); break; \
-    default: hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 16, 1>), dim3(grid), dim3(kBgThreads), lds, s, a); break; \
+    case 32: hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 4, 1, SH_>), dim3(grid), dim3(kBgThreads), 0, s, a); break; \
+    case 64: hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 8, 1, SH_>), dim3(grid), dim3(kBgThreads), 0, s, a); break; \
+    default: hipLaunchKernelGGL((bgmv_expand_fast_kernel<DT_, 16, 1, SH_>), dim3(grid), dim3(kBgThreads), 0, s, a); break; \
   }
-    if (dtype == 0) { LORA_BG_FAST(0) } else { LORA_BG_FAST(1) }
+    if (dtype == 0) {
+      if (sh) { LORA_BG_FAST(0, true) } else { LORA_BG_FAST(0, false) }
+    } else {
+      if (sh) { LORA_BG_FAST(1, true) } else { LORA_BG_FAST(1, false) }
+    }
 #undef LORA_BG_FAST
     return hipGetLastError();
   }
-  const int grid = bg_grid((int32_t)T_walk);
-#define LORA_BG_EXPAND(DT_, VEC_)                                                                     \
+  int grid = bg_grid((int32_t)T_walk);
+  if (a.short_max > 0 && grid > 1024) grid = 1024;
+  const bool sh = a.short_max > 0;
+#define LORA_BG_EXPAND(DT_, VEC_, SH_)                                                                \
   if (r <= 16)                                                                                       \
-    hipLaunchKernelGGL((bgmv_expand_kernel<DT_, VEC_, 16>), dim3(grid), dim3(kBgThreads), lds, s, a);  \
+    hipLaunchKernelGGL((bgmv_expand_kernel<DT_, VEC_, 16, SH_>), dim3(grid), dim3(kBgThreads), 0, s, a); \
   else if (r <= 32)                                                                                  \
-    hipLaunchKernelGGL((bgmv_expand_kernel<DT_, VEC_, 32>), dim3(grid), dim3(kBgThreads), lds, s, a);  \
+    hipLaunchKernelGGL((bgmv_expand_kernel<DT_, VEC_, 32, SH_>), dim3(grid), dim3(kBgThreads), 0, s, a); \
   else                                                                                               \
-    hipLaunchKernelGGL((bgmv_expand_kernel<DT_, VEC_, 64>), dim3(grid), dim3(kBgThreads), lds, s, a);
+    hipLaunchKernelGGL((bgmv_expand_kernel<DT_, VEC_, 64, SH_>), dim3(grid), dim3(kBgThreads), 0, s, a);
+#define LORA_BG_EXPAND_SH(DT_, VEC_) \
+  if (sh) { LORA_BG_EXPAND(DT_, VEC_, true) } else { LORA_BG_EXPAND(DT_, VEC_, false) }
   if (dtype == 0) {
-    if (vec) { LORA_BG_EXPAND(0, true) } else { LORA_BG_EXPAND(0, false) }
+    if (vec) { LORA_BG_EXPAND_SH(0, true) } else { LORA_BG_EXPAND_SH(0, false) }
   } else {
-    if (vec) { LORA_BG_EXPAND(1, true) } else { LORA_BG_EXPAND(1, false) }
+    if (vec) { LORA_BG_EXPAND_SH(1, true) } else { LORA_BG_EXPAND_SH(1, false) }
   }
+#undef LORA_BG_EXPAND_SH
 #undef LORA_BG_EXPAND
   return hipGetLastError();
 }

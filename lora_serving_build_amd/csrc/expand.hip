@@ -41,7 +41,9 @@ struct ExpandArgs {
   ExpandSliceDesc slices[kMaxSlices];
   int32_t run_start[kMaxSlices + 1];  // prefix of chunk runs per slice
   int32_t num_slices;
-  int32_t cpr;                        // chunks per run
+  int32_t cpr;                        // chunks per run (from the tile bound)
+  int32_t cpr_fixed;                  // 1: cpr as set, not to be shortened
+  int32_t mt_bound;                   // the host's upper bound on the token tiles
   int32_t r;
   uint16_t* y;
   int64_t ldy;
@@ -100,29 +102,52 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
   const TileTable table =
       build_tile_table<kExpandThreads, DENSE>(a.seg, TT, a.r, s_table, s_scan, a.min_seg_len);
   const int mtiles = table.tiles;
-  const int nruns = a.run_start[a.num_slices];
-  const int n_items = mtiles * nruns;
   const int grid = gridDim.x;
+  // Runs of a slice for cpr chunks per run.
+  auto slice_runs = [&](int q, int cpr) {
+    return ((a.slices[q].n + kExpandCols - 1) / kExpandCols + cpr - 1) / cpr;
+  };
+  auto all_runs = [&](int cpr) {
+    int n = 0;
+    for (int q = 0; q < a.num_slices; ++q) n += slice_runs(q, cpr);
+    return n;
+  };
+  // The host sized the runs for its bound on the tiles; when the batch has
+  // under half as many (an adapter pool far larger than the segments in
+  // use), shorter runs keep two items per workgroup (the same value in every
+  // workgroup).
+  int cpr = a.cpr;
+  int nruns = a.run_start[a.num_slices];
+  if (!a.cpr_fixed && 2 * mtiles <= a.mt_bound) {
+    while (cpr > 1 && mtiles * nruns < 2 * grid) {
+      cpr >>= 1;
+      nruns = all_runs(cpr);
+    }
+  }
+  const int n_items = mtiles * nruns;
 
   for (int item = xcd_first_item(blockIdx.x, grid, n_items); item < n_items; item += grid) {
     // Consecutive items walk the token tiles under one run of columns, so
     // the weight run is reused from the L2 of one XCD.
     const int cr = item / mtiles;
     const int mt = item - cr * mtiles;
-    int q = 0;
-    while (q + 1 < a.num_slices && a.run_start[q + 1] <= cr) ++q;
+    int q = 0, rs = 0;
+    while (q + 1 < a.num_slices && rs + slice_runs(q, cpr) <= cr) {
+      rs += slice_runs(q, cpr);
+      ++q;
+    }
     const int nq = a.slices[q].n;
-    const int c_beg = (cr - a.run_start[q]) * a.cpr;
-    const int c_end = min(c_beg + a.cpr, (nq + kExpandCols - 1) / kExpandCols);
+    const int c_beg = (cr - rs) * cpr;
+    const int c_end = min(c_beg + cpr, (nq + kExpandCols - 1) / kExpandCols);
 
     int p0 = 0, p_end = 0, l = 0;
-    const bool ok = tile_range_lds(table, a.seg.T, a.seg.L, TT, mt, &p0, &p_end, &l);
-    const uint16_t* Bl = a.slices[q].B + (int64_t)l * nq * a.r;
-    uint16_t* ybase = a.y + a.slices[q].col_off;
     // The adapter's live rank: weight pieces and v groups at or beyond it
     // are zero and are not read (their pieces read the row's first one,
     // which is loaded anyway), and their matrix ops are skipped.
-    const int rank_l = ok ? table.rank[l] : 0;
+    int rank_l = 0;
+    const bool ok = tile_range_lds(table, a.seg.T, a.seg.L, TT, mt, &p0, &p_end, &l, &rank_l);
+    const uint16_t* Bl = a.slices[q].B + (int64_t)l * nq * a.r;
+    uint16_t* ybase = a.y + a.slices[q].col_off;
 
     // Weight chunk loader: piece p = tid + 256 i is row p / PPR, columns
     // 8 (p % PPR) .. +8 of the chunk's B_l^T rows.  Rows past the slice read
@@ -477,8 +502,13 @@ hipError_t launch_expand(const SegView& seg, const float* v, int64_t ldv, int64_
     const int64_t want = mt_max * chunks / 4096;
     cpr = want >= 8 ? 8 : (want >= 4 ? 4 : 2);
   }
-  if (tuning().expand_cpr >= 1) cpr = tuning().expand_cpr;
+  a.cpr_fixed = 0;
+  if (tuning().expand_cpr >= 1) {
+    cpr = tuning().expand_cpr;
+    a.cpr_fixed = 1;
+  }
   a.cpr = (int32_t)cpr;
+  a.mt_bound = (int32_t)mt_max;
   int32_t runs = 0;
   for (int q = 0; q < num_slices; ++q) {
     a.slices[q] = slices[q];

@@ -66,6 +66,9 @@ int check_rank(int32_t r, const char* fn) {
 // Kernel path: 0 = automatic, 1 = per-token (BGMV), 2 = segment tiles (SGMV).
 std::atomic<int> g_path{0};
 
+// Largest rank at which a tile shrink hands its one-token segments to the
+// per-token kernel.
+
 // Automatic choice between the kernel families, from timings of both on
 // decode-sized batches (T = 16 .. 512, H = 4096 and 16384, r = 16 .. 64, 4
 // adapters, MI355X).
@@ -186,6 +189,14 @@ int scratch_address(const char* fn, void* stream, void** out) {
   return LORA_OK;
 }
 
+// Whether a segment-tile shrink hands its one-token segments to the
+// per-token kernel (the device-side per-segment choice): automatic path,
+// metadata present, and enough adapters for many one-token segments.  The
+// per-token shrink takes every rank.
+bool shrink_split(const lora::SegView& sv) {
+  return g_path.load(std::memory_order_relaxed) == 0 && !sv.dense && sv.L >= 256;
+}
+
 // lora_shrink, lora_shrink_noalloc and lora_shrink_single, after their
 // batch description (sv) has been checked.  With use_scratch, the H-split
 // partial rows go to this device's static scratch instead of a workspace.
@@ -208,7 +219,9 @@ int shrink_core(const char* fn, const void* x, int64_t ldx, const void* A, int32
                                               vec, static_cast<hipStream_t>(stream));
     return hip_status(err, fn);
   }
-  const lora::ShrinkPlan plan = lora::plan_shrink(T, sv.L, H, r);
+  // The static scratch bounds how far the kernel may raise the H split.
+  const lora::ShrinkPlan plan =
+      lora::plan_shrink(T, sv.L, H, r, use_scratch ? (size_t)LORA_NOALLOC_SCRATCH_BYTES : 0);
   const size_t need = plan.partial_bytes;
   if (use_scratch && need > 0) {
     if (need > (size_t)LORA_NOALLOC_SCRATCH_BYTES)
@@ -226,9 +239,21 @@ int shrink_core(const char* fn, const void* x, int64_t ldx, const void* A, int32
     if (!aligned16(workspace))
       return fail(LORA_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned", fn);
   }
+  // The per-segment choice of the expand (below) applies to the shrink too:
+  // in a batch of at least 256 adapters, one-token segments go to the
+  // per-token kernel, launched last so that the split-H reduce (which writes
+  // every active row from the partial rows) cannot overwrite them.  Measured
+  // on MI355X, 7168 prefill + 1024 decode tokens over 1040 adapters, H =
+  // 4096, tiles alone against tiles on the prefill + per-token on the decode
+  // tokens: 119 -> 52 us at r = 16, 184 -> 132 at r = 64, 268 -> 230 at
+  // r = 128; with no one-token segment the empty per-token pass adds 2.5-4 us.
+  const bool split = shrink_split(sv);
   hipError_t err = lora::launch_shrink(sv, static_cast<const uint16_t*>(x), ldx,
                                        static_cast<const uint16_t*>(A), H, r, v, ldv, workspace,
-                                       plan, dtype, vec, static_cast<hipStream_t>(stream));
+                                       plan, dtype, vec, static_cast<hipStream_t>(stream), split ? 2 : 1);
+  if (err == hipSuccess && split)
+    err = lora::launch_bgmv_shrink(sv, static_cast<const uint16_t*>(x), ldx, static_cast<const uint16_t*>(A),
+                                   H, r, v, ldv, dtype, vec, static_cast<hipStream_t>(stream), 1);
   return hip_status(err, fn);
 }
 
@@ -370,9 +395,9 @@ int expand_core(const char* fn, const float* v, int64_t ldv, int64_t v_slice_str
   // 158 us.  Segments of 2 to 7 tokens measured faster on tiles at r = 64, so
   // only one-token segments move; at r = 128 the per-token expand is about
   // twice as slow as the tiles on small batches (16-512 tokens: 15-20 us
-  // against 10-12), so the split stops at r = 64.  The second launch costs a
-  // few microseconds when it finds nothing, so it is made only when the batch
-  // can hold many one-token segments: at least 256 adapters.
+  // against 10-12), so the split stops at r = 64.  The second launch costs
+  // 2.5-4 us when it finds nothing, so it is made only when the batch can
+  // hold many one-token segments: at least 256 adapters.
   const bool split = g_path.load(std::memory_order_relaxed) == 0 && !sv.dense && sv.L >= 256 &&
                      r <= lora::kBgmvMaxRank;
   hipError_t err = lora::launch_expand(sv, v, ldv, v_slice_stride, desc, num_slices, r,

@@ -59,18 +59,28 @@ hipError_t launch_build_segments(const int32_t* token_lora, int32_t T, int32_t L
 struct ShrinkPlan {
   int32_t jtw;          // 16-row tiles of r per wave (1, 2, 4 or 8)
   int32_t rp;           // rank padded to the rank groups
-  int32_t ksplit;       // number of H chunks split across workgroups
+  int32_t ksplit;       // number of H chunks split across workgroups (from the tile bound)
+  int32_t ks_cap;       // most chunks the kernel may choose from the true tile count
   int32_t kchunk;       // H elements per chunk (multiple of kShrinkKStep)
   int32_t max_tiles;    // upper bound on token tiles
+  int32_t resident;     // workgroups resident at once
   int32_t grid;         // persistent workgroups
-  size_t partial_bytes; // workspace for per-chunk partial rows (ksplit > 1)
+  size_t partial_bytes; // workspace: header + ks_cap chunks of partial rows (ks_cap > 1)
 };
 
-ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r);
+// Bytes at the start of the shrink workspace that hold the split the kernel
+// chose (the partial rows follow, 16-byte aligned).
+constexpr size_t kShrinkWsHeader = 256;
 
+// ws_limit: the workspace available (0 = as much as the plan asks for); a
+// smaller one lowers ks_cap, never below ksplit.
+ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r, size_t ws_limit = 0);
+
+// min_seg_len: segments with fewer tokens are left to another kernel.
 hipError_t launch_shrink(const SegView& seg, const uint16_t* x, int64_t ldx, const uint16_t* A,
                          int32_t H, int32_t r, float* v, int64_t ldv, void* workspace,
-                         const ShrinkPlan& plan, int dtype, bool vec, hipStream_t s);
+                         const ShrinkPlan& plan, int dtype, bool vec, hipStream_t s,
+                         int min_seg_len = 1);
 
 struct ExpandSliceDesc {
   const uint16_t* B;
@@ -90,9 +100,10 @@ inline bool bgmv_supports(bool expand, int32_t r, bool vec) {
 // for H >= 12288), 4 if none does.
 int bgmv_shrink_ranks(int64_t T, int32_t r, int32_t H);
 
+// short_max as for launch_bgmv_expand.
 hipError_t launch_bgmv_shrink(const SegView& seg, const uint16_t* x, int64_t ldx, const uint16_t* A,
                               int32_t H, int32_t r, float* v, int64_t ldv, int dtype, bool vec,
-                              hipStream_t s);
+                              hipStream_t s, int short_max = 0);
 
 // short_max = 0: every token; k >= 1: only the tokens of segments of at most
 // k tokens (found from the segment metadata).

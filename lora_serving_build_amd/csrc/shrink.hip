@@ -22,6 +22,14 @@
 // partial rows to the workspace (indexed by sorted position) and a second
 // small kernel adds the ks partials in chunk order and writes v: the kernel
 // boundary orders the two, and the sum order is fixed.
+//
+// The host picks ks from an upper bound on the tiles (T / 64 plus one partial
+// tile per adapter), since it never sees the segments.  When the adapter pool
+// is much larger than the number of segments in use, that bound is loose and
+// the split leaves most of the GPU idle; every workgroup then recomputes ks
+// from the true tile count (the same value in all of them), up to the number
+// of chunks the workspace holds, and workgroup 0 leaves it in the workspace
+// header for the reduce kernel.
 #include "lora_device.h"
 #include "lora_kernels.h"
 #include "tiles.h"
@@ -51,10 +59,14 @@ struct ShrinkArgs {
   int32_t r;
   float* v;
   int64_t ldv;
-  float* partial;  // [ks][T][rp] when ks > 1
-  int32_t ks;
+  float* partial;  // [ks_cap][T][rp] when ks_cap > 1
+  int32_t* ks_out; // workspace header: the ks used (when ks_cap > 1)
+  int32_t ks;      // chunks chosen on the host
+  int32_t ks_cap;  // chunks the workspace holds (ks when the choice is fixed)
+  int32_t resident;  // workgroups resident at once
   int32_t kchunk;  // H elements per workgroup chunk (multiple of kSkKB)
   int32_t rp;      // padded rank of the partial rows (16 * NJT)
+  int32_t min_seg_len;  // segments with fewer tokens are left to another kernel
 };
 
 template <int NJT>
@@ -100,9 +112,20 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
   const int lrow = tid >> 4;
   const int lcol = (tid & 15) * 8;
 
-  const TileTable table = build_tile_table<kShrinkThreads, DENSE>(a.seg, kSkTile, a.r, s_table, s_scan);
+  const TileTable table =
+      build_tile_table<kShrinkThreads, DENSE>(a.seg, kSkTile, a.r, s_table, s_scan, a.min_seg_len);
   const int tiles = table.tiles;
-  const int n_items = tiles * a.ks;
+  int ks = a.ks, kchunk = a.kchunk;
+  if (a.ks_cap > ks && tiles > 0 && 2 * tiles * ks <= a.resident) {
+    // Under half the resident workgroups busy: the host's bound was loose.
+    int k = (a.resident + tiles - 1) / tiles;
+    if (tiles * k - a.resident > a.resident / 50) k = a.resident / tiles;
+    k = k < ks ? ks : (k > a.ks_cap ? a.ks_cap : k);
+    kchunk = ((a.H + k - 1) / k + kSkKB - 1) / kSkKB * kSkKB;
+    ks = (a.H + kchunk - 1) / kchunk;
+  }
+  if (a.ks_out && blockIdx.x == 0 && tid == 0) *a.ks_out = ks;
+  const int n_items = tiles * ks;
   const int grid = gridDim.x;
 
   for (int item = xcd_first_item(blockIdx.x, grid, n_items); item < n_items; item += grid) {
@@ -111,9 +134,10 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
     const int ksi = item / tiles;
     const int tile = item - ksi * tiles;
     int p0 = 0, p_end = 0, l = 0;
-    const bool ok = tile_range_lds(table, a.seg.T, a.seg.L, kSkTile, tile, &p0, &p_end, &l);
-    const int kbeg = ksi * a.kchunk;
-    const int kend = min(a.H, kbeg + a.kchunk);
+    int rank_l = 0;
+    const bool ok = tile_range_lds(table, a.seg.T, a.seg.L, kSkTile, tile, &p0, &p_end, &l, &rank_l);
+    const int kbeg = ksi * kchunk;
+    const int kend = min(a.H, kbeg + kchunk);
     const int pos = p0 + wave * 16 + m;
     int t = (ok && pos < p_end) ? (DENSE ? pos : a.seg.sorted_token[pos]) : -1;
     t = (t >= 0 && t < a.seg.T) ? t : -1;
@@ -126,7 +150,6 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
     // run on the zeros: skipping them cost 7% on full-rank batches.)
     const uint16_t* xrow = a.x + (int64_t)(tok_ok ? t : 0) * a.ldx;
     const uint16_t* Al = a.A + (int64_t)l * a.r * a.H;
-    const int rank_l = ok ? table.rank[l] : 0;
     const uint16_t* asrc[AL];
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
@@ -236,7 +259,7 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
 #pragma unroll
       for (int jt = 0; jt < NJT; ++jt) {
         const int j0 = jt * 16 + 4 * g;
-        if (a.ks == 1) {
+        if (ks == 1) {
           store4<VEC>(a.v + (int64_t)t * a.ldv + j0, j0, a.r, acc[jt]);
         } else {
           float* part = a.partial + ((int64_t)ksi * a.seg.T + pos) * a.rp + j0;
@@ -247,15 +270,21 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
   }
 }
 
-// v[t, :r] = sum over the ks chunks of the partial rows, in chunk order.
+// v[t, :r] = sum over the ks chunks of the partial rows, in chunk order (ks
+// as the shrink kernel left it in the workspace header; nothing to do when it
+// wrote v itself).
 // Every load of a row -- the active count, its token, eight partial rows at a
 // time -- goes out before any of them is checked, so a reduction of up to
 // eight chunks is one memory trip; positions past the active tokens (whose
 // partial rows were never written) and ranks past r are dropped at the store.
 template <bool VEC>
 __global__ __launch_bounds__(256) void shrink_reduce_kernel(SegView seg, const float* partial,
-                                                            int32_t ks, int32_t rp, int32_t r,
-                                                            float* v, int64_t ldv) {
+                                                            const int32_t* ks_in, int32_t ks_cap,
+                                                            int32_t rp, int32_t r, float* v,
+                                                            int64_t ldv) {
+  int ks = *ks_in;
+  ks = ks > ks_cap ? ks_cap : ks;
+  if (ks <= 1) return;
   const int per_row = rp / 4;
   const int64_t n = (int64_t)seg.T * per_row;
   for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < n;
@@ -315,7 +344,7 @@ hipError_t launch_dense(const ShrinkArgs& args, int njt, int grid, hipStream_t s
 
 }  // namespace
 
-ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r) {
+ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r, size_t ws_limit) {
   ShrinkPlan p{};
   const int njt0 = (r + 15) / 16;
   p.jtw = njt0 <= 1 ? 1 : njt0 <= 2 ? 2 : njt0 <= 4 ? 4 : 8;  // rank tiles (template)
@@ -328,6 +357,7 @@ ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r) {
   const int64_t reg_cu = p.jtw <= 4 ? 4 : 2;
   per_cu = per_cu < 1 ? 1 : (per_cu > reg_cu ? reg_cu : per_cu);
   const int64_t resident = 256 * per_cu;
+  p.resident = (int32_t)resident;
   // Split H across workgroups so that the items fill one round of resident
   // workgroups, with at least four blocks per chunk: the extra partial-row
   // traffic costs less than idle CUs.  Rounding the chunk count up leaves
@@ -337,23 +367,42 @@ ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r) {
   //   8192-token layer, 192 tiles: 6 chunks 56.5 us, 5 chunks 52.5 us;
   //   8192 x 4096 at r = 128, 132 tiles (512 resident): 4 -> 46 us, 3 -> 40 us;
   //   16384 x 4096 at r = 16, 260 tiles: 4 -> 37.8 us, 3 -> 40.5 us.
-  int64_t ks = 1;
-  if (tiles > 0 && tiles < resident) {
-    ks = (resident + tiles - 1) / tiles;
-    if (tiles * ks - resident > resident / 50) ks = resident / tiles;
-  }
+  // The kernel applies the same rule to the true tile count (see the kernel).
   int64_t ks_max = H / (4 * kSkKB);
   if (ks_max < 1) ks_max = 1;
-  if (ks > ks_max) ks = ks_max;
-  if (ks < 1) ks = 1;
-  if (tuning().shrink_ksplit > 0) ks = tuning().shrink_ksplit;
-  int64_t chunk = (H + ks - 1) / ks;
-  chunk = (chunk + kSkKB - 1) / kSkKB * kSkKB;
-  ks = (H + chunk - 1) / chunk;
+  auto split_for = [&](int64_t n) {
+    int64_t ks = 1;
+    if (n > 0 && n < resident) {
+      ks = (resident + n - 1) / n;
+      if (n * ks - resident > resident / 50) ks = resident / n;
+    }
+    ks = ks > ks_max ? ks_max : (ks < 1 ? 1 : ks);
+    const int64_t chunk = ((H + ks - 1) / ks + kSkKB - 1) / kSkKB * kSkKB;
+    return (H + chunk - 1) / chunk;
+  };
+  int64_t ks = split_for(tiles);
+  // The kernel may raise the split up to what the fewest tiles T tokens can
+  // make (all of them in 64-token tiles) would take: about one round of
+  // resident workgroups' partial rows, whatever T.
+  int64_t ks_cap = split_for(T > 0 ? ((int64_t)T + kSkTile - 1) / kSkTile : 0);
+  if (tuning().shrink_ksplit > 0) {
+    const int64_t want = tuning().shrink_ksplit;
+    const int64_t chunk = ((H + want - 1) / want + kSkKB - 1) / kSkKB * kSkKB;
+    ks = (H + chunk - 1) / chunk;
+    ks_cap = ks;  // a fixed split, as set
+  }
+  const int64_t row_bytes = (int64_t)T * p.rp * 4;
+  if (ks_cap > ks && row_bytes > 0 && ws_limit > kShrinkWsHeader) {
+    const int64_t fit = (int64_t)((ws_limit - kShrinkWsHeader) / (size_t)row_bytes);
+    if (ks_cap > fit) ks_cap = fit;
+  }
+  if (ks_cap < ks) ks_cap = ks;
   p.ksplit = (int32_t)ks;
-  p.kchunk = (int32_t)chunk;
-  p.partial_bytes = ks > 1 ? (size_t)(ks * (int64_t)T * p.rp * 4) : 0;
-  int64_t items = tiles * ks;
+  p.ks_cap = (int32_t)ks_cap;
+  p.kchunk = (int32_t)(((H + ks - 1) / ks + kSkKB - 1) / kSkKB * kSkKB);
+  p.partial_bytes = ks_cap > 1 ? kShrinkWsHeader + (size_t)(ks_cap * row_bytes) : 0;
+  // Every resident workgroup is launched when the kernel may raise the split.
+  const int64_t items = ks_cap > ks ? resident : tiles * ks;
   int64_t grid = items < resident ? items : resident;
   grid = (grid + 7) / 8 * 8;
   if (grid < 8) grid = 8;
@@ -363,8 +412,9 @@ ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r) {
 
 hipError_t launch_shrink(const SegView& seg, const uint16_t* x, int64_t ldx, const uint16_t* A,
                          int32_t H, int32_t r, float* v, int64_t ldv, void* workspace,
-                         const ShrinkPlan& plan, int dtype, bool vec, hipStream_t s) {
+                         const ShrinkPlan& plan, int dtype, bool vec, hipStream_t s, int min_seg_len) {
   ShrinkArgs a{};
+  a.min_seg_len = min_seg_len > 1 ? min_seg_len : 1;
   a.seg = seg;
   a.x = x;
   a.ldx = ldx;
@@ -373,8 +423,12 @@ hipError_t launch_shrink(const SegView& seg, const uint16_t* x, int64_t ldx, con
   a.r = r;
   a.v = v;
   a.ldv = ldv;
-  a.partial = plan.ksplit > 1 ? reinterpret_cast<float*>(workspace) : nullptr;
+  const bool split = plan.ks_cap > 1;
+  a.partial = split ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kShrinkWsHeader) : nullptr;
+  a.ks_out = split ? static_cast<int32_t*>(workspace) : nullptr;
   a.ks = plan.ksplit;
+  a.ks_cap = plan.ks_cap;
+  a.resident = plan.resident;
   a.kchunk = plan.kchunk;
   a.rp = plan.rp;
   hipError_t e;
@@ -382,16 +436,16 @@ hipError_t launch_shrink(const SegView& seg, const uint16_t* x, int64_t ldx, con
     e = vec ? launch_dense<0, true>(a, plan.jtw, plan.grid, s) : launch_dense<0, false>(a, plan.jtw, plan.grid, s);
   else
     e = vec ? launch_dense<1, true>(a, plan.jtw, plan.grid, s) : launch_dense<1, false>(a, plan.jtw, plan.grid, s);
-  if (e != hipSuccess || plan.ksplit == 1) return e;
+  if (e != hipSuccess || !split) return e;
   int64_t blocks = ((int64_t)seg.T * (plan.rp / 4) + 255) / 256;
   if (blocks > 1024) blocks = 1024;
   if (blocks < 1) blocks = 1;
   if (vec)
     hipLaunchKernelGGL((shrink_reduce_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, s, seg,
-                       a.partial, plan.ksplit, plan.rp, r, v, ldv);
+                       a.partial, a.ks_out, plan.ks_cap, plan.rp, r, v, ldv);
   else
     hipLaunchKernelGGL((shrink_reduce_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, s, seg,
-                       a.partial, plan.ksplit, plan.rp, r, v, ldv);
+                       a.partial, a.ks_out, plan.ks_cap, plan.rp, r, v, ldv);
   return hipGetLastError();
 }
 

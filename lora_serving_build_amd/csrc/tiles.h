@@ -28,8 +28,11 @@ __device__ __forceinline__ int tile_segment(const int32_t* tile_start, int S, in
 
 // LDS copy of everything a tile lookup needs, so that mapping a work item to
 // its tokens costs no global round trip: tile_start[0..S], seg_start[0..S],
-// seg_lora[0..S) and rank[0..L) (the live rank of each adapter, r when the
-// metadata gives none).  Each array holds L + 1 ints.
+// seg_lora[0..S) and the live ranks (r when the metadata gives none).  Each
+// array has room for L + 1 ints.  The ranks are per adapter (rank[0..L)) for
+// pools of up to kEagerTable adapters, where every array is copied whole in
+// one round of loads; for larger pools only the S segments in use are
+// copied, and the ranks are per segment (rank[0..S)).
 struct TileTable {
   int32_t* tile_start;
   int32_t* seg_start;
@@ -37,7 +40,11 @@ struct TileTable {
   int32_t* rank;
   int S;
   int tiles;
+  bool rank_by_seg;
 };
+
+// Pools up to this many adapters copy their whole metadata at once.
+constexpr int kEagerTable = 256;
 
 // Tiles of tile_tokens tokens that T tokens over at most L segments can make:
 // one partial tile per segment at most.
@@ -60,6 +67,7 @@ __device__ TileTable build_tile_table(const SegView& seg, int tile_tokens, int r
   tt.seg_start = lds + seg.L + 1;
   tt.seg_lora = lds + 2 * (seg.L + 1);
   tt.rank = lds + 3 * (seg.L + 1);
+  tt.rank_by_seg = false;
   if constexpr (DENSE) {
     const int tiles = seg.T > 0 ? (seg.T + tile_tokens - 1) / tile_tokens : 0;
     if (threadIdx.x == 0) {
@@ -75,16 +83,38 @@ __device__ TileTable build_tile_table(const SegView& seg, int tile_tokens, int r
     tt.tiles = tiles;
     return tt;
   }
-  // All L + 1 entries are copied (they exist whatever S is), so these loads
-  // go out together with the load of S instead of one round trip after it.
+  auto clamp_rank = [&](int k) { return k < 0 ? 0 : (k > r ? r : k); };
   int S = seg.counts[0];
-  for (int s = threadIdx.x; s <= seg.L; s += NT) tt.seg_start[s] = seg.seg_start[s];
-  for (int s = threadIdx.x; s < seg.L; s += NT) tt.seg_lora[s] = seg.seg_lora[s];
-  for (int s = threadIdx.x; s < seg.L; s += NT) {
-    const int k = seg.lora_rank ? seg.lora_rank[s] : r;
-    tt.rank[s] = k < 0 ? 0 : (k > r ? r : k);
+  if (seg.L <= kEagerTable) {
+    // All L + 1 entries are copied (they exist whatever S is), so these loads
+    // go out together with the load of S instead of one round trip after it.
+    for (int s = threadIdx.x; s <= seg.L; s += NT) tt.seg_start[s] = seg.seg_start[s];
+    for (int s = threadIdx.x; s < seg.L; s += NT) tt.seg_lora[s] = seg.seg_lora[s];
+    for (int s = threadIdx.x; s < seg.L; s += NT) tt.rank[s] = clamp_rank(seg.lora_rank ? seg.lora_rank[s] : r);
+    S = S < 0 ? 0 : (S > seg.L ? seg.L : S);
+  } else {
+    // A large pool, most of it usually idle: the first NT segments go out with
+    // the load of S, the rest (if S is larger) one round trip later, and each
+    // segment's rank is looked up from its adapter.
+    // (NT <= kEagerTable < L: indices up to NT exist.)
+    static_assert(NT <= kEagerTable, "the eager part of a large pool's table is one entry per thread");
+    tt.seg_start[threadIdx.x] = seg.seg_start[threadIdx.x];
+    tt.seg_lora[threadIdx.x] = seg.seg_lora[threadIdx.x];
+    if (threadIdx.x == NT - 1) tt.seg_start[NT] = seg.seg_start[NT];
+    S = S < 0 ? 0 : (S > seg.L ? seg.L : S);
+    for (int s = NT + 1 + threadIdx.x; s <= S; s += NT) tt.seg_start[s] = seg.seg_start[s];
+    for (int s = NT + threadIdx.x; s < S; s += NT) tt.seg_lora[s] = seg.seg_lora[s];
+    if (seg.lora_rank) {
+      __syncthreads();
+      for (int s = threadIdx.x; s < S; s += NT) {
+        const int l = tt.seg_lora[s];
+        tt.rank[s] = (l >= 0 && l < seg.L) ? clamp_rank(seg.lora_rank[l]) : 0;
+      }
+    } else {
+      for (int s = threadIdx.x; s < S; s += NT) tt.rank[s] = r;
+    }
+    tt.rank_by_seg = true;
   }
-  S = S < 0 ? 0 : (S > seg.L ? seg.L : S);
   __syncthreads();
   const int per = (S + NT - 1) / NT;
   const int lo = min((int)threadIdx.x * per, S);
@@ -114,74 +144,10 @@ __device__ TileTable build_tile_table(const SegView& seg, int tile_tokens, int r
   return tt;
 }
 
-// Tokens of the short segments (1 .. max_len tokens: the decode requests of
-// a batch that mixes decode and prefill), numbered 0 .. count - 1 in sorted
-// order, for a per-token kernel that takes only those.  LDS copy of
-// seg_start[0..S] and seg_lora[0..S) with the prefix of short lengths,
-// 3 (L + 1) ints in all (scratch: NT / 64 + 1 more).
-struct ShortTable {
-  int32_t* start;      // [S + 1] first short-token number of segment s
-  int32_t* seg_start;
-  int32_t* seg_lora;
-  int S;
-  int count;
-};
-
-__host__ __device__ constexpr int64_t short_table_ints(int64_t L) { return 3 * (L + 1); }
-
-// Every thread of the block must call it.
-template <int NT>
-__device__ ShortTable build_short_table(const SegView& seg, int max_len, int32_t* lds, int32_t* scratch) {
-  ShortTable st;
-  st.start = lds;
-  st.seg_start = lds + seg.L + 1;
-  st.seg_lora = lds + 2 * (seg.L + 1);
-  int S = seg.counts[0];
-  for (int s = threadIdx.x; s <= seg.L; s += NT) st.seg_start[s] = seg.seg_start[s];
-  for (int s = threadIdx.x; s < seg.L; s += NT) st.seg_lora[s] = seg.seg_lora[s];
-  S = S < 0 ? 0 : (S > seg.L ? seg.L : S);
-  __syncthreads();
-  auto short_len = [&](int s) {
-    const int len = st.seg_start[s + 1] - st.seg_start[s];
-    return (len >= 1 && len <= max_len) ? len : 0;
-  };
-  const int per = (S + NT - 1) / NT;
-  const int lo = min((int)threadIdx.x * per, S);
-  const int hi = min(lo + per, S);
-  int mine = 0;
-  for (int s = lo; s < hi; ++s) mine += short_len(s);
-  int total;
-  int run = block_exclusive_sum<NT>(mine, scratch, &total);
-  for (int s = lo; s < hi; ++s) {
-    st.start[s] = run;
-    run += short_len(s);
-  }
-  if (threadIdx.x == 0) st.start[S] = total;
-  __syncthreads();
-  st.S = S;
-  // As for the tiles: invalid metadata never claims more than T tokens.
-  st.count = total < 0 ? 0 : (total > seg.T ? seg.T : total);
-  return st;
-}
-
-// Sorted position and adapter of short token k (k < st.count); false when
-// the metadata does not hold one.
-__device__ __forceinline__ bool short_token(const ShortTable& st, int T, int L, int k, int* pos,
-                                            int* lora_id) {
-  if (st.S <= 0) return false;
-  const int s = tile_segment(st.start, st.S, k);
-  if (k < st.start[s] || k >= st.start[s + 1]) return false;
-  const int p = st.seg_start[s] + (k - st.start[s]);
-  const int l = st.seg_lora[s];
-  if (p < 0 || p >= T || l < 0 || l >= L) return false;
-  *pos = p;
-  *lora_id = l;
-  return true;
-}
-
-// tile_range on a TileTable (LDS only).
+// tile_range on a TileTable (LDS only), with the live rank of the tile's
+// adapter.
 __device__ __forceinline__ bool tile_range_lds(const TileTable& tt, int T, int L, int tile_tokens,
-                                               int tile, int* p0, int* p_end, int* lora_id) {
+                                               int tile, int* p0, int* p_end, int* lora_id, int* rank) {
   const int s = tile_segment(tt.tile_start, tt.S, tile);
   const int start = tt.seg_start[s];
   const int end = tt.seg_start[s + 1];
@@ -192,6 +158,7 @@ __device__ __forceinline__ bool tile_range_lds(const TileTable& tt, int T, int L
   *p0 = b;
   *p_end = e;
   *lora_id = l;
+  *rank = tt.rank[tt.rank_by_seg ? s : l];
   return true;
 }
 

@@ -130,19 +130,21 @@ def test_workspace_size_is_zero_when_not_split():
     assert lsb.lora_shrink_workspace_bytes(256, 4, 4096, 16) > 0
 
 
-@pytest.mark.parametrize("T,L,H,r,ks,rp", [
-    (8192, 64, 8192, 64, 5, 64),    # 192 tiles: 6 chunks would leave 128 items for a second round
-    (16384, 4, 4096, 16, 4, 16),    # 260 tiles: 4 chunks leave 16 (under 2% of 1024)
-    (32768, 4, 4096, 16, 2, 16),    # 516 tiles: 2 chunks leave 8
-    (8192, 4, 4096, 128, 3, 128),   # rank 128 holds 512 workgroups: 4 chunks would leave 16 (3%)
-    (2048, 4, 4096, 16, 8, 16),     # 36 tiles: capped at four 128-wide blocks per chunk
+@pytest.mark.parametrize("T,L,H,r,ks_cap,rp", [
+    (8192, 64, 8192, 64, 8, 64),    # 128 tiles at the fewest: 8 chunks fill 1024 workgroups
+    (16384, 4, 4096, 16, 4, 16),    # 256 tiles: 4 chunks
+    (32768, 4, 4096, 16, 2, 16),    # 512 tiles: 2 chunks
+    (8192, 4, 4096, 128, 4, 128),   # rank 128 holds 512 workgroups: 128 tiles take 4 chunks
+    (2048, 4, 4096, 16, 8, 16),     # 32 tiles: capped at four 128-wide blocks per chunk
     (1024, 16, 4096, 128, 8, 128),  # the same cap at rank 128
+    (4096, 1040, 4096, 16, 8, 16),  # a large adapter pool: the bound (1104 tiles) takes no split
 ])
-def test_shrink_split_fills_one_round(T, L, H, r, ks, rp):
-    """The workspace holds ks chunks of fp32 partial rows (rp = r padded to a
-    rank tile): the H split chosen so the items fill one round of resident
-    workgroups."""
-    assert lsb.lora_shrink_workspace_bytes(T, L, H, r) == ks * T * rp * 4
+def test_shrink_split_fills_one_round(T, L, H, r, ks_cap, rp):
+    """The workspace holds a 256-byte header and ks_cap chunks of fp32
+    partial rows (rp = r padded to a rank tile): the most chunks the kernel
+    may choose, the split that the fewest tiles of T tokens (all in 64-token
+    tiles) would take to fill one round of resident workgroups."""
+    assert lsb.lora_shrink_workspace_bytes(T, L, H, r) == 256 + ks_cap * T * rp * 4
 
 
 def _slice_call(lib, sp, Bs, ns, offs, ldy=64, r=16, stride=0, dt=0, nsl=None, ldv=16):

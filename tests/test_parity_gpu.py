@@ -683,17 +683,22 @@ def test_plan_variants(force_path, monkeypatch, tuning_from_env, env, path, dtyp
 
 
 RANK_CASES = [
-    # (dtype, T, H, r, L, slices, ranks_from, integer)
-    ("bf16", 500, 1024, 128, 16, [[1024, 256, 256], [2048]], [8, 16, 32, 64, 128], False),
-    ("f16", 300, 2048, 64, 7, [[1536]], [8, 24, 40, 64], False),       # ranks off the 16 / 32 grid
-    ("bf16", 200, 512, 32, 5, [[512, 128]], [8, 16, 32], True),
-    ("f16", 130, 1001, 16, 3, [[1001]], [8, 16], False),               # unaligned: element-wise loads
+    # (dtype, T, H, r, L, slices, ranks_from, integer, seq_len)
+    ("bf16", 500, 1024, 128, 16, [[1024, 256, 256], [2048]], [8, 16, 32, 64, 128], False, (1, 40)),
+    ("f16", 300, 2048, 64, 7, [[1536]], [8, 24, 40, 64], False, (1, 40)),   # ranks off the 16 / 32 grid
+    ("bf16", 200, 512, 32, 5, [[512, 128]], [8, 16, 32], True, (1, 40)),
+    ("f16", 130, 1001, 16, 3, [[1001]], [8, 16], False, (1, 40)),           # unaligned: element-wise loads
+    # pools of more than 256 adapters: the tile tables copy only the segments
+    # in use and look each segment's rank up from its adapter -- a few
+    # segments, and more than 256 of them
+    ("bf16", 600, 1024, 64, 600, [[1024]], [8, 16, 40, 64], False, (1, 40)),
+    ("f16", 1500, 512, 32, 700, [[512, 256]], [8, 16, 24, 32], True, (1, 4)),
 ]
 
 
 @pytest.mark.parametrize("path", ["sgmv", "bgmv"])
-@pytest.mark.parametrize("dtype,T,H,r,L,slices,ranks_from,integer", RANK_CASES)
-def test_live_ranks(force_path, path, dtype, T, H, r, L, slices, ranks_from, integer):
+@pytest.mark.parametrize("dtype,T,H,r,L,slices,ranks_from,integer,seq_len", RANK_CASES)
+def test_live_ranks(force_path, path, dtype, T, H, r, L, slices, ranks_from, integer, seq_len):
     """Per-adapter live ranks (zero-padded adapters, the issue's mixed-rank
     batch): the segment kernels skip the padding, the per-token kernels read
     the zero padding as it is; both give the same values as without the
@@ -702,8 +707,11 @@ def test_live_ranks(force_path, path, dtype, T, H, r, L, slices, ranks_from, int
         pytest.skip("the per-token kernels take r <= 64 or 128")
     _announce(f"live ranks {path} {dtype} T={T} H={H} r={r} L={L} slices={slices} ranks={ranks_from}")
     force_path(lsb.PATH_SGMV if path == "sgmv" else lsb.PATH_BGMV)
-    w = W.make("ranks", dtype, T, H, r, L, slices, seed=T + r, seq_len=(1, 40), neg_frac=0.1,
+    w = W.make("ranks", dtype, T, H, r, L, slices, seed=T + r, seq_len=seq_len, neg_frac=0.1,
                ranks_from=ranks_from, integer=integer)
+    if L > 256:
+        S = len(np.unique(w.ids[w.ids >= 0]))
+        print(f"  segments in use: {S}")
     plain = DeviceWorkload(w)
     plain.run()
     ranked = DeviceWorkload(w)
@@ -964,14 +972,24 @@ def test_single_adapter_empty_batch():
 # ---------------------------------------------------------------- decode + prefill mixes
 MIXED_CASES = [
     # dtype, n_prefill, prefill_loras, n_decode, L, H, r, slices, integer: batches
-    # of >= 256 adapters, where the expand sends one-token segments to the
-    # per-token kernel and the rest to the tile kernel
+    # of >= 256 adapters, where the shrink and the expand (up to r = 64) send
+    # one-token segments to the per-token kernel and the rest to the tile kernel
     ("bf16", 2000, 16, 700, 1024, 1024, 16, [[1024]], False),
     ("f16", 1500, 8, 600, 700, 2048, 64, [[512, 256]], False),
     ("bf16", 1200, 12, 400, 512, 512, 24, [[300]], False),        # per-token general kernel
     ("bf16", 900, 4, 300, 400, 1024, 32, [[512], [256, 256]], True),
     ("f16", 0, 1, 800, 1024, 512, 16, [[1024]], False),          # decode only, above 512 tokens
-    ("bf16", 3000, 16, 300, 320, 1024, 128, [[512]], False),      # rank 128: tiles for every segment
+    # the tile shrink splits H (a reduce kernel writes every active row) and the
+    # per-token pass then writes the one-token segments' rows
+    ("f16", 400, 4, 200, 256, 2048, 16, [[512]], False),
+    ("bf16", 450, 4, 150, 256, 2048, 32, [[256, 256]], True),
+    ("bf16", 3000, 16, 300, 320, 1024, 128, [[512]], False),      # rank 128: the expand keeps tiles throughout
+    # prefill only, a few segments of a large pool: the tile bound (one partial
+    # tile per adapter) is loose, and the kernels raise the H split and
+    # shorten the column runs from the true tile count
+    ("bf16", 3000, 8, 0, 1024, 4096, 16, [[4096]], False),
+    ("f16", 2500, 6, 0, 2000, 2048, 64, [[1024, 512]], True),
+    ("bf16", 1800, 3, 0, 1500, 4096, 128, [[2048], [512]], False),
 ]
 
 

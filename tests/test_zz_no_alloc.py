@@ -18,6 +18,8 @@ CASES = [
     # the second call smaller than the first
     ("bf16", 4096, 8192, 64, 16, (1, 200)),
     ("f16", 700, 4096, 32, 7, (1, 40)),
+    # a few sequences of a large adapter pool: the kernel raises the split
+    ("bf16", 600, 4096, 16, 900, (100, 300)),
 ]
 
 
@@ -26,7 +28,7 @@ def test_noalloc_shrink_matches_workspace_shrink():
     for dtype, T, H, r, L, sl in CASES:
         print(f"\n[case] noalloc shrink {dtype} T={T} H={H} r={r} L={L}", flush=True)
         need = lsb.lora_shrink_workspace_bytes(T, L, H, r)
-        assert 0 < need <= lsb.LORA_NOALLOC_SCRATCH_BYTES
+        assert need > 0   # the noalloc call fits its split into the scratch
         w = W.make("noalloc", dtype, T, H, r, L, [[64]], seed=T + r, seq_len=sl, neg_frac=0.1)
         ids = torch.from_numpy(w.ids).cuda()
         seg = lsb.lora_build_segments(ids, w.L)
@@ -46,4 +48,4 @@ def test_noalloc_shrink_matches_workspace_shrink():
         v_or = oracle.shrink(dtype, w.x, w.A, w.ids)
         assert tol_ratio(v_na.cpu().numpy()[act].astype(np.float64), v_or[act]) <= 1
         outs.append(b)
-    assert len(outs) == 2
+    assert len(outs) == len(CASES)
