@@ -157,6 +157,26 @@ def step(w, lsb, s, ws):
     op_expand(w, lsb, s, ws)
 
 
+def fused_applies(w):
+    """Whether lora_shrink_expand (shrink and expand in one launch) takes the
+    workload: one output, r in 8..64 by powers of two, aligned sizes, a
+    decode-sized batch."""
+    if len(w.outputs) != 1 or w.r not in (8, 16, 32, 64) or w.H % 8 or w.T > 1024:
+        return False
+    o = w.outputs[0]
+    return o.ldy % 8 == 0 and all(q.n % 8 == 0 and q.col_off % 8 == 0 for q in o.slices)
+
+
+def op_fused(w, lsb, s, ws):
+    o = w.outputs[0]
+    lsb.lora_shrink_expand(s.x, s.A, s.Bs[0], [q.col_off for q in o.slices], s.seg, s.v, s.ys[0], w.add)
+
+
+def fused_step(w, lsb, s, ws):
+    op_build(w, lsb, s, ws)
+    op_fused(w, lsb, s, ws)
+
+
 _evict = None
 
 
@@ -209,7 +229,7 @@ def tol_ratio(got, ref):
     return float(err.max())
 
 
-def parity_check(w, torch, lsb, ws):
+def parity_check(w, torch, lsb, ws, stepfn=step):
     """Checks one fresh step against the oracle before anything is timed:
     metadata bit for bit, every active row of v and of every output in full
     (streamed through the oracle in row blocks, so no fp64 copy of a whole
@@ -218,7 +238,7 @@ def parity_check(w, torch, lsb, ws):
     import oracle
     import workloads as W
     s = make_pool(w, torch, lsb, 1)[0]
-    step(w, lsb, s, ws)
+    stepfn(w, lsb, s, ws)
     torch.cuda.synchronize()
     meta = (s.seg.sorted_token[:w.T].cpu().numpy(), s.seg.seg_lora.cpu().numpy(),
             s.seg.seg_start.cpu().numpy(), s.seg.counts.cpu().numpy())
@@ -1062,6 +1082,23 @@ def measure(w, args, torch, lsb, check=True):
                 "value": round(live_bytes / (ms_live * 1e-3) / 1e9, 2)}
         log(f"live ranks: {ms_live * 1e3:.2f} us/step ({live['speedup']}x)")
     res["live_ranks"] = live
+
+    # Decode batches: the same step with shrink and expand in one launch
+    # (lora_shrink_expand), checked against the oracle first.
+    fused = None
+    if fused_applies(w):
+        ratio = parity_check(w, torch, lsb, ws, stepfn=fused_step) if check else None
+        if ratio is not None and not ratio <= 1.0:
+            print(json.dumps({"error": "parity check failed (fused step)", "workload": w.name, "ratio": ratio}))
+            sys.exit(1)
+        ms_f = graph_time(torch, lambda s: fused_step(w, lsb, s, ws), sets, args.warmup, K) / K
+        t_op = graph_time(torch, lambda s: op_fused(w, lsb, s, ws), sets, args.warmup + K, K) / K
+        fb = w.shrink_bytes() + w.expand_bytes()
+        fused = {"ms_per_step": round(ms_f, 6), "speedup": round(ms_per_step / ms_f, 3),
+                 "value": round(fb / (ms_f * 1e-3) / 1e9, 2), "us_per_op": round(t_op * 1e3, 3),
+                 "parity_ratio": ratio}
+        log(f"fused step: {ms_f * 1e3:.2f} us/step ({fused['speedup']}x), shrink+expand {t_op * 1e3:.2f} us")
+    res["fused"] = fused
     return res, sets
 
 
@@ -1150,7 +1187,7 @@ def main():
         others[wk.name] = {"value": round(bk / (rk["ms_per_step"] * 1e-3) / 1e9, 2), "unit": "GB/s",
                            "ms_per_step": round(rk["ms_per_step"], 6), "ops": rk["ops"],
                            "roofline": rk["roofline"], "parity_ratio": rk["parity_ratio"],
-                           "pool_sets": rk["pool_sets"]}
+                           "pool_sets": rk["pool_sets"], "fused": rk["fused"]}
 
     # Context for the roofline fraction: what plain torch streaming kernels
     # reach on this GPU (a copy and an in-place add over 512 MiB each, twice
@@ -1209,6 +1246,7 @@ def main():
         "cpu_baseline": cpu,
         "parity_ratio": res["parity_ratio"],
         "live_ranks": res["live_ranks"],
+        "fused": res["fused"],
         "other_workloads": others,
         "hbm_context": hbm_context,
     }

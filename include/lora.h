@@ -213,6 +213,30 @@ int lora_expand_slice(const float *v, int64_t ldv, int64_t v_slice_stride,
                       int32_t num_slices, int32_t r, const lora_segments *seg, void *y,
                       int64_t ldy, int add_inputs, int dtype, void *stream);
 
+/* Shrink then expand_slice in one launch, for decode batches (TPU PR summary:
+ * the Pallas kernel was split into separate shrink and expand kernels;
+ * which form is faster depends on the shape -- one launch instead of two
+ * pays where a decode step's calls are bound by their launch and round
+ * trips).  Computes v = x . A_l as lora_shrink (v is written, the same
+ * values up to the order of the fp32 sums) and y (+)= v . B_s[l] for every
+ * slice as lora_expand_slice with v_slice_stride 0.  Each token is handled by
+ * its own workgroups, so the cost grows with T times the adapter's weight
+ * bytes: meant for decode batches (up to a few hundred tokens); larger
+ * batches belong to the separate calls.  Reads token_lora only (the sorted
+ * metadata need not be built).
+ *   r          8, 16, 32 or 64
+ *   x, A       as lora_shrink;  B, n_s, col_off, num_slices, y, ldy as
+ *              lora_expand_slice;  v  [T][ldv] fp32 device, ldv >= r, written
+ * Every row and size must be 16-byte aligned: x, A, B, y 16-byte aligned; H,
+ * ldx, ldy, n_s[] and col_off[] multiples of 8.
+ * Errors: INVALID_ARG (NULL pointers, H < 1, ld too small, bad dtype, slice
+ * errors as lora_expand_slice), UNSUPPORTED (another rank, unaligned data,
+ * num_slices), HIP. */
+int lora_shrink_expand(const void *x, int64_t ldx, const void *A, int32_t H, int32_t r,
+                       const void *const *B, const int32_t *n_s, const int64_t *col_off,
+                       int32_t num_slices, const lora_segments *seg, float *v, int64_t ldv,
+                       void *y, int64_t ldy, int add_inputs, int dtype, void *stream);
+
 /* Single-adapter forms (TPU PR summary: the masking is removed when only one
  * adapter is in use; micro-benchmark PR review thread: with few adapters the
  * kernels should match torch.mm).  Every token t in [0, T) uses the one

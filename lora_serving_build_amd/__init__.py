@@ -96,12 +96,14 @@ def lib() -> ctypes.CDLL:
             L.lora_expand.argtypes = [p, i64, p, i32, i32, seg_p, p, i64, ctypes.c_int, ctypes.c_int, p]
             L.lora_expand_slice.argtypes = [p, i64, i64, p, p, p, i32, i32, seg_p, p, i64,
                                             ctypes.c_int, ctypes.c_int, p]
+            L.lora_shrink_expand.argtypes = [p, i64, p, i32, i32, p, p, p, i32, seg_p, p, i64, p, i64,
+                                             ctypes.c_int, ctypes.c_int, p]
             L.lora_last_error.restype = ctypes.c_char_p
             L.lora_set_path.argtypes = [ctypes.c_int]
             L.lora_set_path.restype = ctypes.c_int
             for f in ("lora_build_segments", "lora_shrink", "lora_shrink_noalloc", "lora_expand",
                       "lora_expand_slice", "lora_shrink_single", "lora_expand_single",
-                      "lora_expand_slice_single"):
+                      "lora_expand_slice_single", "lora_shrink_expand"):
                 getattr(L, f).restype = ctypes.c_int
             _lib = L
     return _lib
@@ -333,6 +335,40 @@ def lora_expand_slice(v: torch.Tensor, Bs, col_offs, seg: Segments, y: torch.Ten
     _check(lib().lora_expand_slice(ctypes.c_void_p(v.data_ptr()), ldv, int(v_slice_stride), ptrs, n_s,
                                    offs, ns, r, seg.ref(), ctypes.c_void_p(y.data_ptr()), ldy,
                                    int(bool(add_inputs)), _dtype_code(y.dtype), _stream(y.device)))
+    return y
+
+
+def lora_shrink_expand(x: torch.Tensor, A: torch.Tensor, Bs, col_offs, seg: Segments, v: torch.Tensor,
+                       y: torch.Tensor, add_inputs: bool = True) -> torch.Tensor:
+    """Shrink then expand_slice in one launch (decode batches): v = x . A_l
+    (written) and y[t, off_s : off_s + n_s] (+)= v[t] . B_s,l for every slice.
+    r must be 8, 16, 32 or 64 and every row and size 16-byte aligned."""
+    if A.dim() != 3 or not A.is_contiguous():
+        raise ValueError("A must be a contiguous [L][r][H] tensor")
+    L, r, H = A.shape
+    if L != seg.num_loras:
+        raise ValueError(f"A holds {L} adapters, segments were built for {seg.num_loras}")
+    if x.dtype != A.dtype or y.dtype != A.dtype:
+        raise TypeError("x, A and y must share a dtype")
+    if v.dtype != torch.float32:
+        raise TypeError("v must be float32")
+    Bs = list(Bs)
+    ns = len(Bs)
+    if ns != len(col_offs):
+        raise ValueError("one column offset per slice")
+    for b in Bs:
+        if b.dim() != 3 or not b.is_contiguous() or b.shape[0] != L or b.shape[2] != r or b.dtype != y.dtype:
+            raise ValueError("every B must be a contiguous [L][n_s][r] tensor in y's dtype")
+    ldx = _row_major(x, "x")
+    ldv = _row_major(v, "v")
+    ldy = _row_major(y, "y")
+    ptrs = (ctypes.c_void_p * ns)(*[b.data_ptr() for b in Bs])
+    n_s = (ctypes.c_int32 * ns)(*[b.shape[1] for b in Bs])
+    offs = (ctypes.c_int64 * ns)(*[int(o) for o in col_offs])
+    _check(lib().lora_shrink_expand(ctypes.c_void_p(x.data_ptr()), ldx, ctypes.c_void_p(A.data_ptr()), H, r,
+                                    ptrs, n_s, offs, ns, seg.ref(), ctypes.c_void_p(v.data_ptr()), ldv,
+                                    ctypes.c_void_p(y.data_ptr()), ldy, int(bool(add_inputs)),
+                                    _dtype_code(y.dtype), _stream(y.device)))
     return y
 
 

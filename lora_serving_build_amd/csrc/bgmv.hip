@@ -147,20 +147,76 @@ __device__ __forceinline__ bool short_item(const SegView& seg, int short_max, in
   return true;
 }
 
-// Work item = (token, block of RT ranks): a small batch is spread over
-// T ceil(r / RT) workgroups, each of which reads the token's x row (again, from
-// L2, for every block after the first) and RT rows of A.  Lane i owns elements
-// 8 (i + 256 k) .. +8 of H; UNR blocks of 2048 elements are in flight per trip,
-// more when RT is small.  SH: the short segments' tokens only (a compile-time
-// variant, so the every-token kernels carry none of its code).
-template <int DT, bool VEC, int RT, bool SH>
-__global__ __launch_bounds__(kBgThreads) void bgmv_shrink_kernel(BgShrinkArgs a) {
+// x . A_l[j0 + j] for j < RT over this thread's pieces of an aligned row:
+// lane i owns elements 8 (i + 256 k) .. +8 of H (each wave instruction reads
+// 1 KB of one row); UNR blocks of 2048 elements are in flight per trip, more
+// when RT is small.  The x row does not depend on the adapter: its loads go
+// out before adapter() (a uniform id, -1 for none) is waited for.  Rows
+// j0 + j >= r read row 0; their sums are never stored.  Returns the adapter.
+template <int DT, int RT, class Adapter>
+__device__ __forceinline__ int token_rank_dots(const uint16_t* xrow, const uint16_t* A, int H, int r, int j0,
+                                               Adapter adapter, float (&acc)[RT]) {
   constexpr int BLK = kBgThreads * 8;
   constexpr int UNR = RT <= 4 ? 8 : RT <= 8 ? 4 : 2;  // blocks per trip (register bound)
+  int l = 0;
+  for (int h0 = threadIdx.x * 8; h0 < H; h0 += UNR * BLK) {
+    u32x4 xv[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u)
+      xv[u] = h0 + u * BLK < H ? *reinterpret_cast<const u32x4*>(xrow + h0 + u * BLK) : u32x4{0u, 0u, 0u, 0u};
+    l = adapter();
+    if (l < 0) return l;
+    const uint16_t* Al = A + (int64_t)l * r * H;
+#pragma unroll
+    for (int j = 0; j < RT; ++j) {
+      const uint16_t* arow = Al + (int64_t)(j0 + j < r ? j0 + j : 0) * H;
+      float s = acc[j];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const u32x4 av = h0 + u * BLK < H ? *reinterpret_cast<const u32x4*>(arow + h0 + u * BLK)
+                                          : u32x4{0u, 0u, 0u, 0u};
+        s = dot2<DT>(xv[u].x, av.x, s);
+        s = dot2<DT>(xv[u].y, av.y, s);
+        s = dot2<DT>(xv[u].z, av.z, s);
+        s = dot2<DT>(xv[u].w, av.w, s);
+      }
+      acc[j] = s;
+    }
+  }
+  if (H > 0) l = adapter();
+  return l;
+}
+
+// Workgroup total of each of RT per-thread partial sums: a transposing wave
+// reduction leaves lane i with its wave's total of rank i >> (6 - log2 RT),
+// one lane of each group parks it in s_red, and thread j < RT returns rank
+// j's sum over the waves (others return 0).  The caller syncs before s_red
+// is written again.
+template <int RT>
+__device__ __forceinline__ float block_rank_sum(float (&acc)[RT], float (*s_red)[RT]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  wave_transpose_sum<RT>(acc);
+  constexpr int kShift = 6 - log2_of<RT>();
+  if ((lane & ((1 << kShift) - 1)) == 0) s_red[wave][lane >> kShift] = acc[0];
+  __syncthreads();
+  float s = 0.f;
+  if ((int)threadIdx.x < RT) {
+#pragma unroll
+    for (int w = 0; w < kBgThreads / kWave; ++w) s += s_red[w][threadIdx.x];
+  }
+  return s;
+}
+
+// Work item = (token, block of RT ranks): a small batch is spread over
+// T ceil(r / RT) workgroups, each of which reads the token's x row (again, from
+// L2, for every block after the first) and RT rows of A (token_rank_dots).
+// SH: the short segments' tokens only (a compile-time variant, so the
+// every-token kernels carry none of its code).
+template <int DT, bool VEC, int RT, bool SH>
+__global__ __launch_bounds__(kBgThreads) void bgmv_shrink_kernel(BgShrinkArgs a) {
   __shared__ float s_red[kBgThreads / kWave][RT];
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
   const int items = bg_items(a.seg, SH ? a.short_max : 0) * a.jb;
   ShortBatch sb;
   int n = 0;
@@ -180,34 +236,7 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_shrink_kernel(BgShrinkArgs a)
     for (int j = 0; j < RT; ++j) acc[j] = 0.f;
     int l = 0;
     if constexpr (VEC) {
-      for (int h0 = tid * 8; h0 < a.H; h0 += UNR * BLK) {
-        // The x row does not depend on the adapter: its loads go first.
-        u32x4 xv[UNR];
-#pragma unroll
-        for (int u = 0; u < UNR; ++u)
-          xv[u] = h0 + u * BLK < a.H ? *reinterpret_cast<const u32x4*>(xrow + h0 + u * BLK)
-                                     : u32x4{0u, 0u, 0u, 0u};
-        l = adapter();
-        if (l < 0) break;
-        const uint16_t* Al = a.A + (int64_t)l * a.r * a.H;
-#pragma unroll
-        for (int j = 0; j < RT; ++j) {
-          // Rows j0 + j >= r read row 0 and are never stored.
-          const uint16_t* arow = Al + (int64_t)(j0 + j < a.r ? j0 + j : 0) * a.H;
-          float s = acc[j];
-#pragma unroll
-          for (int u = 0; u < UNR; ++u) {
-            const u32x4 av = h0 + u * BLK < a.H ? *reinterpret_cast<const u32x4*>(arow + h0 + u * BLK)
-                                                : u32x4{0u, 0u, 0u, 0u};
-            s = dot2<DT>(xv[u].x, av.x, s);
-            s = dot2<DT>(xv[u].y, av.y, s);
-            s = dot2<DT>(xv[u].z, av.z, s);
-            s = dot2<DT>(xv[u].w, av.w, s);
-          }
-          acc[j] = s;
-        }
-      }
-      if (a.H > 0) l = adapter();
+      l = token_rank_dots<DT, RT>(xrow, a.A, a.H, a.r, j0, adapter, acc);
     } else {
       l = adapter();
       if (l >= 0) {
@@ -221,18 +250,8 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_shrink_kernel(BgShrinkArgs a)
       }
     }
     if (l < 0) continue;  // uniform: no adapter, v row left as it is
-    // Transposing wave reduction: lane i ends with the wave's total of rank
-    // j0 + (i >> (6 - log2 RT)); one lane of each group writes it.
-    wave_transpose_sum<RT>(acc);
-    constexpr int kShift = 6 - log2_of<RT>();
-    if ((lane & ((1 << kShift) - 1)) == 0) s_red[wave][lane >> kShift] = acc[0];
-    __syncthreads();
-    if (tid < RT && j0 + tid < a.r) {
-      float s = 0.f;
-#pragma unroll
-      for (int w = 0; w < kBgThreads / kWave; ++w) s += s_red[w][tid];
-      a.v[(int64_t)t * a.ldv + j0 + tid] = s;
-    }
+    const float s = block_rank_sum<RT>(acc, s_red);
+    if (tid < RT && j0 + tid < a.r) a.v[(int64_t)t * a.ldv + j0 + tid] = s;
     __syncthreads();
   }
 }
@@ -408,23 +427,145 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_expand_kernel(BgExpandArgs a)
 // so a small batch still fills the chip: in every slice, block b takes the
 // rounds whose index divided by 4 RPI is b modulo cb.
 constexpr int kRoundCols = kWave * 8;
+// Column c of the staged sums sits at c + 4 (c / 128): each lane reads its
+// 8 columns at 8 lane, and 16-byte LDS reads serve lanes 0-7 with 16-23,
+// whose columns lie 128 apart -- the same banks without the 4-float shift.
+constexpr int kSoRow = kRoundCols + kRoundCols / 32;
 
-template <int DT, int G, int RPI, bool SH>
-__global__ __launch_bounds__(kBgThreads) void bgmv_expand_fast_kernel(BgExpandArgs a) {
+// y of rounds R0 .. R0 + RPI of a token's slice row, 8 columns a lane
+// (zeros past the slice, or when y is not read).
+template <int RPI>
+__device__ __forceinline__ void load_round_y(const uint16_t* yrow, int nq, int add, int R0, int lane,
+                                             u32x4 (&yv)[RPI]) {
+#pragma unroll
+  for (int u = 0; u < RPI; ++u) {
+    const int c0 = (R0 + u) * kRoundCols + lane * 8;
+    yv[u] = (add && c0 + 8 <= nq) ? *reinterpret_cast<const u32x4*>(yrow + c0) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// The first KB weight chunks of rounds R0 .. R0 + RPI for this lane.
+// Chunks past the slice read chunk 0; their columns are never stored.
+template <int G, int RPI, int KB>
+__device__ __forceinline__ void load_round_b(const uint16_t* Bl, int64_t nchunks, int R0, int lane,
+                                             u32x4 (&b)[RPI][KB]) {
+#pragma unroll
+  for (int u = 0; u < RPI; ++u) {
+    const int64_t base = (int64_t)(R0 + u) * kRoundCols * G + lane;
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int64_t idx = base + (int64_t)k * kWave;
+      b[u][k] = *reinterpret_cast<const u32x4*>(Bl + (idx < nchunks ? idx : 0) * 8);
+    }
+  }
+}
+
+// One token's share of an aligned expand: the rounds of column block cb in
+// every slice.  vrow_of(q) points at the token's v for slice q (global memory
+// or LDS); adapter() is its uniform id (-1: y stays as it is); so is this
+// wave's staging row of RPI kSoRow floats.
+template <int DT, int G, int RPI, class VRow, class Adapter>
+__device__ __forceinline__ void expand_token_aligned(const BgExpandArgs& a, int t, int cb, VRow vrow_of,
+                                                     Adapter adapter, float* so) {
   constexpr int LG = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : G == 8 ? 3 : 4;
   constexpr int K = 8 * G;                   // weight loads per lane and round
   constexpr int KB = K < 16 ? K : 16;        // loads per batch (register bound)
   constexpr int CPI = kWave / G;             // columns per load instruction
   constexpr int NW = kBgThreads / kWave;
-  // Column c of the staged sums sits at c + 4 (c / 128): each lane reads its
-  // 8 columns at 8 lane, and 16-byte LDS reads serve lanes 0-7 with 16-23,
-  // whose columns lie 128 apart -- the same banks without the 4-float shift.
-  constexpr int kSoRow = kRoundCols + kRoundCols / 32;
-  __shared__ __align__(16) float s_out[NW][RPI * kSoRow];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int part = lane & (G - 1);
-  float* so = s_out[wave];
+  for (int q = 0; q < a.num_slices; ++q) {
+    const int nq = a.slices[q].n;
+    const float* vrow = vrow_of(q) + part * 8;
+    uint16_t* yrow = a.y + (int64_t)t * a.ldy + a.slices[q].col_off;
+    for (int R0 = (cb * NW + wave) * RPI; R0 * kRoundCols < nq; R0 += a.cb * NW * RPI) {
+      // y and v do not depend on the adapter: they are in flight while the
+      // (scalar) adapter id arrives, and only the id is waited for before
+      // the weight loads go out.
+      const int l = adapter();
+      u32x4 yv[RPI];
+      load_round_y<RPI>(yrow, nq, a.add, R0, lane, yv);
+      f32x4 va = *reinterpret_cast<const f32x4*>(vrow);
+      f32x4 vb = *reinterpret_cast<const f32x4*>(vrow + 4);
+      if (l < 0) break;  // uniform: the row of y stays as it is
+      const uint16_t* Bl = a.slices[q].B + (int64_t)l * nq * (8 * G);
+      const int64_t nchunks = (int64_t)nq * G;
+      u32x4 b[RPI][KB];
+      load_round_b<G, RPI, KB>(Bl, nchunks, R0, lane, b);
+      // All first-batch weight loads are in flight before any arithmetic;
+      // the opaque moves keep the split of v from being hoisted above them.
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" : "+v"(va), "+v"(vb));
+      // Binary16 prescale of the token's v (f16_prescale): the G lanes of
+      // a column group hold the whole row, so their maximum is the row's.
+      float down = 1.f, up = 1.f;
+      if constexpr (DT == 0) {
+        float vmax = fmaxf(fmaxf(fmaxf(fabsf(va.x), fabsf(va.y)), fmaxf(fabsf(va.z), fabsf(va.w))),
+                           fmaxf(fmaxf(fabsf(vb.x), fabsf(vb.y)), fmaxf(fabsf(vb.z), fabsf(vb.w))));
+        if constexpr (G >= 2) vmax = fmaxf(vmax, lane_xor<0>(vmax, lane));
+        if constexpr (G >= 4) vmax = fmaxf(vmax, lane_xor<1>(vmax, lane));
+        if constexpr (G >= 8) vmax = fmaxf(vmax, lane_xor<2>(vmax, lane));
+        if constexpr (G >= 16) vmax = fmaxf(vmax, lane_xor<3>(vmax, lane));
+        f16_prescale(vmax, &down, &up);
+        va *= down;
+        vb *= down;
+      }
+      uint32_t vh[4], vl[4];
+      split_hilo<DT>(va.x, va.y, &vh[0], &vl[0]);
+      split_hilo<DT>(va.z, va.w, &vh[1], &vl[1]);
+      split_hilo<DT>(vb.x, vb.y, &vh[2], &vl[2]);
+      split_hilo<DT>(vb.z, vb.w, &vh[3], &vl[3]);
+#pragma unroll
+      for (int u = 0; u < RPI; ++u) {
+        const int64_t base = (int64_t)(R0 + u) * kRoundCols * G + lane;
+#pragma unroll
+        for (int kb = 0; kb < K; kb += KB) {
+          if (kb > 0) {
+#pragma unroll
+            for (int k = 0; k < KB; ++k) {
+              const int64_t idx = base + (int64_t)(kb + k) * kWave;
+              b[u][k] = *reinterpret_cast<const u32x4*>(Bl + (idx < nchunks ? idx : 0) * 8);
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < KB; ++k) {
+            float p = group_dot<DT>(vh, vl, b[u][k]);
+            if constexpr (G >= 2) p = p + lane_xor<0>(p, lane);
+            if constexpr (G >= 4) p = p + lane_xor<1>(p, lane);
+            if constexpr (G >= 8) p = p + lane_xor<2>(p, lane);
+            if constexpr (G >= 16) p = p + lane_xor<3>(p, lane);
+            if (part == 0) {
+              const int c = (kb + k) * CPI + (lane >> LG);  // a run of CPI columns in one 128
+              so[u * kSoRow + c + ((c >> 7) << 2)] = DT == 0 ? p * up : p;
+            }
+          }
+        }
+      }
+      // LDS operations of one wave execute in order: wave-scope fences
+      // only keep the compiler from moving them.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int u = 0; u < RPI; ++u) {
+        const int c0 = (R0 + u) * kRoundCols + lane * 8;
+        const float* sr = so + u * kSoRow + lane * 8 + ((lane >> 4) << 2);
+        const f32x4 o0 = *reinterpret_cast<const f32x4*>(sr);
+        const f32x4 o1 = *reinterpret_cast<const f32x4*>(sr + 4);
+        float out[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+        if (c0 < nq) bg_store_cols<DT, true>(yrow, nq, c0, a.add, yv[u], out);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+}
+
+template <int DT, int G, int RPI, bool SH>
+__global__ __launch_bounds__(kBgThreads) void bgmv_expand_fast_kernel(BgExpandArgs a) {
+  constexpr int NW = kBgThreads / kWave;
+  __shared__ __align__(16) float s_out[NW][RPI * kSoRow];
+  float* so = s_out[threadIdx.x / kWave];
   const int items = bg_items(a.seg, SH ? a.short_max : 0) * a.cb;
   ShortBatch sb;
   int n = 0;
@@ -437,104 +578,62 @@ __global__ __launch_bounds__(kBgThreads) void bgmv_expand_fast_kernel(BgExpandAr
     if constexpr (SH) {
       if (!short_item(a.seg, a.short_max, a.cb, items, it, n, sb, &t, &l_short)) continue;
     }
-    for (int q = 0; q < a.num_slices; ++q) {
-      const int nq = a.slices[q].n;
-      const float* vrow = a.v + (int64_t)t * a.ldv + (int64_t)q * a.v_slice_stride + part * 8;
-      uint16_t* yrow = a.y + (int64_t)t * a.ldy + a.slices[q].col_off;
-      for (int R0 = (cb * NW + wave) * RPI; R0 * kRoundCols < nq; R0 += a.cb * NW * RPI) {
-        // y and v do not depend on the adapter: they are in flight while the
-        // (scalar) adapter id arrives, and only the id is waited for before
-        // the weight loads go out.
-        const int l = SH ? l_short : token_adapter(a.seg, t);
-        u32x4 yv[RPI];
+    expand_token_aligned<DT, G, RPI>(
+        a, t, cb, [&](int q) { return a.v + (int64_t)t * a.ldv + (int64_t)q * a.v_slice_stride; },
+        [&]() { return SH ? l_short : token_adapter(a.seg, t); }, so);
+  }
+}
+
+struct FusedArgs {
+  BgExpandArgs ex;  // the expand's view (its v is not read: v comes from LDS)
+  const uint16_t* x;
+  int64_t ldx;
+  const uint16_t* A;
+  int32_t H;
+  float* v;         // [T][ex.ldv], written by the first column block of each token
+};
+
+// Shrink then expand of one token in one workgroup, for decode batches: the
+// launch and the round trip of v between two kernels are what a decode
+// step's shrink and expand mostly cost.  The workgroup sums x . A_l for all
+// r = 8 G ranks (token_rank_dots in blocks of up to 16 ranks, then across
+// the waves into LDS), the first column block writes v out, and the expand
+// of its column block (expand_token_aligned) reads v from LDS.  A token's
+// columns are spread over cb workgroups as in the aligned per-token expand;
+// each of them computes the token's v again (x and A_l come from L2 after
+// the first), so no workgroup waits for another.
+template <int DT, int G, int RPI>
+__global__ __launch_bounds__(kBgThreads) void fused_decode_kernel(FusedArgs f) {
+  constexpr int R = 8 * G;
+  constexpr int RT = R < 16 ? R : 16;
+  constexpr int NW = kBgThreads / kWave;
+  __shared__ float s_red[NW][RT];
+  __shared__ __align__(16) float s_v[R];
+  __shared__ __align__(16) float s_out[NW][RPI * kSoRow];
+  float* so = s_out[threadIdx.x / kWave];
+  const BgExpandArgs& a = f.ex;
+  const int items = a.seg.T * a.cb;
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int t = it / a.cb;
+    const int cb = it - t * a.cb;
+    const uint16_t* xrow = f.x + (int64_t)t * f.ldx;
+    auto adapter = [&]() { return token_adapter(a.seg, t); };
+    int l = -1;
+    for (int j0 = 0; j0 < R; j0 += RT) {
+      float acc[RT];
 #pragma unroll
-        for (int u = 0; u < RPI; ++u) {
-          const int c0 = (R0 + u) * kRoundCols + lane * 8;
-          yv[u] = (a.add && c0 + 8 <= nq) ? *reinterpret_cast<const u32x4*>(yrow + c0)
-                                          : u32x4{0u, 0u, 0u, 0u};
-        }
-        f32x4 va = *reinterpret_cast<const f32x4*>(vrow);
-        f32x4 vb = *reinterpret_cast<const f32x4*>(vrow + 4);
-        if (l < 0) break;  // uniform: the row of y stays as it is
-        const uint16_t* Bl = a.slices[q].B + (int64_t)l * nq * (8 * G);
-        const int64_t nchunks = (int64_t)nq * G;
-        u32x4 b[RPI][KB];
-#pragma unroll
-        for (int u = 0; u < RPI; ++u) {
-          const int64_t base = (int64_t)(R0 + u) * kRoundCols * G + lane;
-#pragma unroll
-          for (int k = 0; k < KB; ++k) {
-            // Chunks past the slice read chunk 0; their columns are never stored.
-            const int64_t idx = base + (int64_t)k * kWave;
-            b[u][k] = *reinterpret_cast<const u32x4*>(Bl + (idx < nchunks ? idx : 0) * 8);
-          }
-        }
-        // All first-batch weight loads are in flight before any arithmetic;
-        // the opaque moves keep the split of v from being hoisted above them.
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("" : "+v"(va), "+v"(vb));
-        // Binary16 prescale of the token's v (f16_prescale): the G lanes of
-        // a column group hold the whole row, so their maximum is the row's.
-        float down = 1.f, up = 1.f;
-        if constexpr (DT == 0) {
-          float vmax = fmaxf(fmaxf(fmaxf(fabsf(va.x), fabsf(va.y)), fmaxf(fabsf(va.z), fabsf(va.w))),
-                             fmaxf(fmaxf(fabsf(vb.x), fabsf(vb.y)), fmaxf(fabsf(vb.z), fabsf(vb.w))));
-          if constexpr (G >= 2) vmax = fmaxf(vmax, lane_xor<0>(vmax, lane));
-          if constexpr (G >= 4) vmax = fmaxf(vmax, lane_xor<1>(vmax, lane));
-          if constexpr (G >= 8) vmax = fmaxf(vmax, lane_xor<2>(vmax, lane));
-          if constexpr (G >= 16) vmax = fmaxf(vmax, lane_xor<3>(vmax, lane));
-          f16_prescale(vmax, &down, &up);
-          va *= down;
-          vb *= down;
-        }
-        uint32_t vh[4], vl[4];
-        split_hilo<DT>(va.x, va.y, &vh[0], &vl[0]);
-        split_hilo<DT>(va.z, va.w, &vh[1], &vl[1]);
-        split_hilo<DT>(vb.x, vb.y, &vh[2], &vl[2]);
-        split_hilo<DT>(vb.z, vb.w, &vh[3], &vl[3]);
-#pragma unroll
-        for (int u = 0; u < RPI; ++u) {
-          const int64_t base = (int64_t)(R0 + u) * kRoundCols * G + lane;
-#pragma unroll
-          for (int kb = 0; kb < K; kb += KB) {
-            if (kb > 0) {
-#pragma unroll
-              for (int k = 0; k < KB; ++k) {
-                const int64_t idx = base + (int64_t)(kb + k) * kWave;
-                b[u][k] = *reinterpret_cast<const u32x4*>(Bl + (idx < nchunks ? idx : 0) * 8);
-              }
-            }
-#pragma unroll
-            for (int k = 0; k < KB; ++k) {
-              float p = group_dot<DT>(vh, vl, b[u][k]);
-              if constexpr (G >= 2) p = p + lane_xor<0>(p, lane);
-              if constexpr (G >= 4) p = p + lane_xor<1>(p, lane);
-              if constexpr (G >= 8) p = p + lane_xor<2>(p, lane);
-              if constexpr (G >= 16) p = p + lane_xor<3>(p, lane);
-              if (part == 0) {
-                const int c = (kb + k) * CPI + (lane >> LG);  // a run of CPI columns in one 128
-                so[u * kSoRow + c + ((c >> 7) << 2)] = DT == 0 ? p * up : p;
-              }
-            }
-          }
-        }
-        // LDS operations of one wave execute in order: wave-scope fences
-        // only keep the compiler from moving them.
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int u = 0; u < RPI; ++u) {
-          const int c0 = (R0 + u) * kRoundCols + lane * 8;
-          const float* sr = so + u * kSoRow + lane * 8 + ((lane >> 4) << 2);
-          const f32x4 o0 = *reinterpret_cast<const f32x4*>(sr);
-          const f32x4 o1 = *reinterpret_cast<const f32x4*>(sr + 4);
-          float out[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
-          if (c0 < nq) bg_store_cols<DT, true>(yrow, nq, c0, a.add, yv[u], out);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      }
+      for (int j = 0; j < RT; ++j) acc[j] = 0.f;
+      l = token_rank_dots<DT, RT>(xrow, f.A, f.H, R, j0, adapter, acc);
+      if (l < 0) break;  // uniform
+      const float s = block_rank_sum<RT>(acc, s_red);
+      if ((int)threadIdx.x < RT) s_v[j0 + threadIdx.x] = s;
+      __syncthreads();
     }
+    if (l < 0) continue;  // no adapter: the v and y rows stay as they are
+    if (cb == 0 && (int)threadIdx.x < R) f.v[(int64_t)t * a.ldv + threadIdx.x] = s_v[threadIdx.x];
+    expand_token_aligned<DT, G, RPI>(a, t, cb, [&](int) { return static_cast<const float*>(s_v); },
+                                     [&]() { return l; }, so);
+    __syncthreads();  // s_v and s_red are rewritten by the next item
   }
 }
 
@@ -677,6 +776,53 @@ hipError_t launch_bgmv_expand(const SegView& seg, const float* v, int64_t ldv, i
   }
 #undef LORA_BG_EXPAND_SH
 #undef LORA_BG_EXPAND
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_decode(const SegView& seg, const uint16_t* x, int64_t ldx, const uint16_t* A,
+                               int32_t H, int32_t r, float* v, int64_t ldv, const ExpandSliceDesc* slices,
+                               int32_t num_slices, uint16_t* y, int64_t ldy, int add, int dtype,
+                               hipStream_t s) {
+  FusedArgs f{};
+  f.x = x;
+  f.ldx = ldx;
+  f.A = A;
+  f.H = H;
+  f.v = v;
+  BgExpandArgs& a = f.ex;
+  a.seg = seg;
+  a.v = v;
+  a.ldv = ldv;
+  a.v_slice_stride = 0;
+  for (int q = 0; q < num_slices; ++q) a.slices[q] = slices[q];
+  a.num_slices = num_slices;
+  a.r = r;
+  a.y = y;
+  a.ldy = ldy;
+  a.add = add;
+  a.short_max = 0;
+  // Column blocks per token as in the aligned per-token expand: one round of
+  // 512 columns of the widest slice per wave.
+  constexpr int nw = kBgThreads / kWave;
+  int64_t rounds = 1;
+  for (int q = 0; q < num_slices; ++q) {
+    const int64_t rq = (slices[q].n + kRoundCols - 1) / kRoundCols;
+    rounds = rq > rounds ? rq : rounds;
+  }
+  const int64_t cb = (rounds + nw - 1) / nw;
+  a.cb = (int32_t)cb;
+  int64_t grid = (int64_t)seg.T * cb;
+  if (grid > 8192) grid = 8192;
+  if (grid < 1) grid = 1;
+#define LORA_FUSED(DT_)                                                                              \
+  switch (r) {                                                                                      \
+    case 8: hipLaunchKernelGGL((fused_decode_kernel<DT_, 1, 1>), dim3(grid), dim3(kBgThreads), 0, s, f); break;  \
+    case 16: hipLaunchKernelGGL((fused_decode_kernel<DT_, 2, 1>), dim3(grid), dim3(kBgThreads), 0, s, f); break; \
+    case 32: hipLaunchKernelGGL((fused_decode_kernel<DT_, 4, 1>), dim3(grid), dim3(kBgThreads), 0, s, f); break; \
+    default: hipLaunchKernelGGL((fused_decode_kernel<DT_, 8, 1>), dim3(grid), dim3(kBgThreads), 0, s, f); break; \
+  }
+  if (dtype == 0) { LORA_FUSED(0) } else { LORA_FUSED(1) }
+#undef LORA_FUSED
   return hipGetLastError();
 }
 

@@ -66,8 +66,6 @@ int check_rank(int32_t r, const char* fn) {
 // Kernel path: 0 = automatic, 1 = per-token (BGMV), 2 = segment tiles (SGMV).
 std::atomic<int> g_path{0};
 
-// Largest rank at which a tile shrink hands its one-token segments to the
-// per-token kernel.
 
 // Automatic choice between the kernel families, from timings of both on
 // decode-sized batches (T = 16 .. 512, H = 4096 and 16384, r = 16 .. 64, 4
@@ -331,22 +329,15 @@ int lora_shrink_noalloc(const void* x, int64_t ldx, const void* A, int32_t H, in
 
 namespace {
 
-// lora_expand_slice and lora_expand_slice_single after their batch
-// description (sv) has been checked.
-int expand_core(const char* fn, const float* v, int64_t ldv, int64_t v_slice_stride, const void* const* B,
-                const int32_t* n_s, const int64_t* col_off, int32_t num_slices, int32_t r,
-                const lora::SegView& sv, void* y, int64_t ldy, int add_inputs, int dtype, void* stream) {
-  if (int e = check_dtype(dtype, fn)) return e;
-  if (int e = check_rank(r, fn)) return e;
+// Checks the slices of an expand_slice and fills their descriptors: none
+// NULL or empty, inside [0, ldy), none overlapping another.
+int check_slices(const char* fn, const void* const* B, const int32_t* n_s, const int64_t* col_off,
+                 int32_t num_slices, int64_t ldy, lora::ExpandSliceDesc* desc) {
   if (num_slices < 1 || num_slices > LORA_MAX_SLICES)
     return fail(LORA_ERR_UNSUPPORTED, "%s: num_slices %d outside [1, %d]", fn, num_slices,
                 LORA_MAX_SLICES);
   if (!B || !n_s || !col_off)
     return fail(LORA_ERR_INVALID_ARG, "%s: B, n_s and col_off must not be NULL", fn);
-  if (ldv < r) return fail(LORA_ERR_INVALID_ARG, "%s: ldv %lld < r %d", fn, (long long)ldv, r);
-  if (v_slice_stride < 0)
-    return fail(LORA_ERR_INVALID_ARG, "%s: v_slice_stride %lld < 0", fn, (long long)v_slice_stride);
-  lora::ExpandSliceDesc desc[LORA_MAX_SLICES];
   int order[LORA_MAX_SLICES];
   for (int s = 0; s < num_slices; ++s) {
     if (!B[s]) return fail(LORA_ERR_INVALID_ARG, "%s: B[%d] is NULL", fn, s);
@@ -365,6 +356,21 @@ int expand_core(const char* fn, const float* v, int64_t ldv, int64_t v_slice_str
     if (col_off[a] + n_s[a] > col_off[b])
       return fail(LORA_ERR_INVALID_ARG, "%s: slices %d and %d overlap", fn, a, b);
   }
+  return LORA_OK;
+}
+
+// lora_expand_slice and lora_expand_slice_single after their batch
+// description (sv) has been checked.
+int expand_core(const char* fn, const float* v, int64_t ldv, int64_t v_slice_stride, const void* const* B,
+                const int32_t* n_s, const int64_t* col_off, int32_t num_slices, int32_t r,
+                const lora::SegView& sv, void* y, int64_t ldy, int add_inputs, int dtype, void* stream) {
+  if (int e = check_dtype(dtype, fn)) return e;
+  if (int e = check_rank(r, fn)) return e;
+  if (ldv < r) return fail(LORA_ERR_INVALID_ARG, "%s: ldv %lld < r %d", fn, (long long)ldv, r);
+  if (v_slice_stride < 0)
+    return fail(LORA_ERR_INVALID_ARG, "%s: v_slice_stride %lld < 0", fn, (long long)v_slice_stride);
+  lora::ExpandSliceDesc desc[LORA_MAX_SLICES];
+  if (int e = check_slices(fn, B, n_s, col_off, num_slices, ldy, desc)) return e;
   const int32_t T = sv.T;
   if (T == 0) return ok();
   if (!v || !y) return fail(LORA_ERR_INVALID_ARG, "%s: v and y must not be NULL", fn);
@@ -422,6 +428,40 @@ int lora_expand_slice(const float* v, int64_t ldv, int64_t v_slice_stride, const
   if (int e = check_segments(seg, fn)) return e;
   return expand_core(fn, v, ldv, v_slice_stride, B, n_s, col_off, num_slices, r, view(seg), y, ldy,
                      add_inputs, dtype, stream);
+}
+
+int lora_shrink_expand(const void* x, int64_t ldx, const void* A, int32_t H, int32_t r, const void* const* B,
+                       const int32_t* n_s, const int64_t* col_off, int32_t num_slices,
+                       const lora_segments* seg, float* v, int64_t ldv, void* y, int64_t ldy, int add_inputs,
+                       int dtype, void* stream) {
+  static const char* fn = "lora_shrink_expand";
+  if (int e = check_segments(seg, fn)) return e;
+  if (int e = check_dtype(dtype, fn)) return e;
+  if (int e = check_rank(r, fn)) return e;
+  if (r != 8 && r != 16 && r != 32 && r != 64)
+    return fail(LORA_ERR_UNSUPPORTED,
+                "%s: rank %d is not 8, 16, 32 or 64 (use lora_shrink and lora_expand_slice)", fn, r);
+  if (H < 1) return fail(LORA_ERR_INVALID_ARG, "%s: H %d < 1", fn, H);
+  if (ldx < H) return fail(LORA_ERR_INVALID_ARG, "%s: ldx %lld < H %d", fn, (long long)ldx, H);
+  if (ldv < r) return fail(LORA_ERR_INVALID_ARG, "%s: ldv %lld < r %d", fn, (long long)ldv, r);
+  lora::ExpandSliceDesc desc[LORA_MAX_SLICES];
+  if (int e = check_slices(fn, B, n_s, col_off, num_slices, ldy, desc)) return e;
+  const lora::SegView sv = view(seg);
+  if (sv.T == 0) return ok();
+  if (!x || !A || !v || !y) return fail(LORA_ERR_INVALID_ARG, "%s: x, A, v and y must not be NULL", fn);
+  bool aligned = (H % 8 == 0) && (ldx % 8 == 0) && aligned16(x) && aligned16(A) && (ldy % 8 == 0) &&
+                 aligned16(y);
+  for (int q = 0; q < num_slices; ++q)
+    aligned = aligned && aligned16(B[q]) && (col_off[q] % 8 == 0) && (n_s[q] % 8 == 0);
+  if (!aligned)
+    return fail(LORA_ERR_UNSUPPORTED,
+                "%s: needs 16-byte aligned x, A, B and y with H, ldx, ldy, the slice widths and offsets "
+                "multiples of 8 (use lora_shrink and lora_expand_slice)", fn);
+  hipError_t err = lora::launch_fused_decode(sv, static_cast<const uint16_t*>(x), ldx,
+                                             static_cast<const uint16_t*>(A), H, r, v, ldv, desc, num_slices,
+                                             static_cast<uint16_t*>(y), ldy, add_inputs ? 1 : 0, dtype,
+                                             static_cast<hipStream_t>(stream));
+  return hip_status(err, fn);
 }
 
 int lora_expand_slice_single(const float* v, int64_t ldv, int64_t v_slice_stride, const void* const* B,

@@ -112,6 +112,14 @@ hipError_t launch_bgmv_expand(const SegView& seg, const float* v, int64_t ldv, i
                               uint16_t* y, int64_t ldy, int add, int dtype, bool vec, hipStream_t s,
                               int short_max = 0);
 
+// Shrink then expand_slice of each token in one launch (decode batches): r is
+// 8, 16, 32 or 64 and every row and size is 16-byte aligned; the slices share
+// v, which is written as by the shrink.
+hipError_t launch_fused_decode(const SegView& seg, const uint16_t* x, int64_t ldx, const uint16_t* A,
+                               int32_t H, int32_t r, float* v, int64_t ldv, const ExpandSliceDesc* slices,
+                               int32_t num_slices, uint16_t* y, int64_t ldy, int add, int dtype,
+                               hipStream_t s);
+
 // min_seg_len: segments with fewer tokens are left to another kernel.
 hipError_t launch_expand(const SegView& seg, const float* v, int64_t ldv, int64_t v_slice_stride,
                          const ExpandSliceDesc* slices, int32_t num_slices, int32_t r,

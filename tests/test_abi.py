@@ -241,6 +241,41 @@ def test_noalloc_shrink_rejects_splits_beyond_its_scratch():
     assert lsb.lora_last_error().startswith("lora_shrink_noalloc:")
 
 
+def test_shrink_expand_validation():
+    """The fused decode call refuses, before anything is launched, ranks
+    other than 8, 16, 32 and 64, unaligned data and the usual argument
+    errors; T = 0 launches nothing."""
+    lib = lsb.lib()
+    s = _seg()
+    sp = ctypes.byref(s)
+    B = (ctypes.c_void_p * 1)(FAKE.value)
+    ns = (ctypes.c_int32 * 1)(64)
+    off = (ctypes.c_int64 * 1)(0)
+
+    def call(**k):
+        return lib.lora_shrink_expand(k.get("x", FAKE), k.get("ldx", 64), k.get("A", FAKE), k.get("H", 64),
+                                      k.get("r", 16), k.get("B", B), k.get("ns", ns), k.get("off", off),
+                                      k.get("nsl", 1), k.get("seg", sp), k.get("v", FAKE), k.get("ldv", 16),
+                                      k.get("y", FAKE), k.get("ldy", 64), 1, k.get("dt", 0), None)
+
+    _expect(call(dt=3), lsb.LORA_ERR_INVALID_ARG, "dtype")
+    _expect(call(r=24), lsb.LORA_ERR_UNSUPPORTED, "8, 16, 32 or 64")
+    _expect(call(r=128, ldv=128), lsb.LORA_ERR_UNSUPPORTED, "8, 16, 32 or 64")
+    _expect(call(r=0), lsb.LORA_ERR_UNSUPPORTED, "rank")
+    _expect(call(H=0), lsb.LORA_ERR_INVALID_ARG, "H 0")
+    _expect(call(ldx=60), lsb.LORA_ERR_INVALID_ARG, "ldx")
+    _expect(call(ldv=8), lsb.LORA_ERR_INVALID_ARG, "ldv")
+    _expect(call(nsl=0), lsb.LORA_ERR_UNSUPPORTED, "num_slices")
+    _expect(call(ldy=32), lsb.LORA_ERR_INVALID_ARG, "outside [0, ldy")
+    _expect(call(x=None), lsb.LORA_ERR_INVALID_ARG, "must not be NULL")
+    _expect(call(seg=None), lsb.LORA_ERR_INVALID_ARG, "seg is NULL")
+    _expect(call(H=60, ldx=64), lsb.LORA_ERR_UNSUPPORTED, "aligned")
+    _expect(call(x=ctypes.c_void_p(FAKE.value + 2)), lsb.LORA_ERR_UNSUPPORTED, "aligned")
+    _expect(call(ns=(ctypes.c_int32 * 1)(60)), lsb.LORA_ERR_UNSUPPORTED, "aligned")
+    s0 = _seg(T=0)
+    assert call(seg=ctypes.byref(s0)) == lsb.LORA_OK
+
+
 def test_single_adapter_validation():
     """The single-adapter entry points: T < 0 and the usual argument errors
     are refused before anything is launched."""

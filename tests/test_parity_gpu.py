@@ -1060,3 +1060,84 @@ def test_decode_prefill_mix_graph_replays():
         assert np.array_equal(g_w.v.cpu().numpy()[act].view(np.uint32),
                               eager.v.cpu().numpy()[act].view(np.uint32))
         assert np.array_equal(host_bits(g_w.ys[0]), host_bits(eager.ys[0]))
+
+
+# ---------------------------------------------------------------- fused decode call
+FUSED_CASES = [
+    # dtype, T, H, r, L, slices, add, integer
+    ("f16", 16, 1024, 16, 4, [1024], True, False),         # the 16-token decode shape
+    ("f16", 256, 4096, 16, 4, [4096], True, False),        # the 256-token decode shape
+    ("bf16", 100, 2048, 8, 7, [512, 256, 256], False, False),
+    ("bf16", 300, 1024, 32, 5, [1536, 512], True, True),
+    ("f16", 37, 4096, 64, 3, [4096, 1024, 1024], True, False),
+    ("bf16", 1, 8192, 64, 2, [2048], True, True),
+    ("f16", 700, 512, 16, 600, [2560], True, True),        # a large pool, wider than 2048 columns
+    ("bf16", 64, 3000, 32, 9, [520, 8], True, False),      # H and slices off the 2048 / 512 grids
+]
+
+
+@pytest.mark.parametrize("dtype,T,H,r,L,widths,add,integer", FUSED_CASES)
+def test_fused_decode(dtype, T, H, r, L, widths, add, integer):
+    """lora_shrink_expand (one launch) against the oracle's shrink then
+    expand_slice: v and every slice of y (integer inputs: bit for bit); rows
+    of tokens without an adapter and columns outside the slices keep their
+    values."""
+    _announce(f"fused decode {dtype} T={T} H={H} r={r} L={L} slices={widths} add={add} integer={integer}")
+    w = W.make("fused", dtype, T, H, r, L, [widths], seed=T + H + r, seq_len=1, neg_frac=0.1, add=add,
+               integer=integer)
+    dw = DeviceWorkload(w)
+    seg = lsb.lora_build_segments(dw.ids, w.L)
+    o = w.outputs[0]
+    offs = [q.col_off for q in o.slices]
+    lsb.lora_shrink_expand(dw.x, dw.A, dw.Bs[0], offs, seg, dw.v, dw.ys[0], add)
+    torch.cuda.synchronize()
+    act = np.nonzero(w.active)[0]
+    cols = _slice_cols(o)
+    v_gpu = dw.v.cpu().numpy()
+    v_or = oracle.shrink(dtype, w.x, w.A, w.ids)
+    Bh = [q.B for q in o.slices]
+    ref = oracle.expand_slice(dtype, v_or, Bh, offs, w.ids, o.y0, add)
+    if integer:
+        assert np.array_equal(v_gpu[act].astype(np.float64), v_or[act])
+        ref_bits = W.f32_to_bits(ref[:, cols].astype(np.float32), dtype) if dtype == "bf16" else \
+            ref[:, cols].astype(np.float16).view(np.uint16)
+        assert np.array_equal(host_bits(dw.ys[0])[:, cols][act], ref_bits[act])
+    else:
+        assert tol_ratio(v_gpu[act].astype(np.float64), v_or[act]) <= 1
+        got = decode(host_bits(dw.ys[0]), dtype)[:, cols]
+        assert tol_ratio(got[act], ref[:, cols][act]) <= 1
+        # the expand alone, from the GPU's own v
+        ref_i = oracle.expand_slice(dtype, np.ascontiguousarray(v_gpu[:, :r].astype(np.float64)), Bh, offs,
+                                    w.ids, o.y0, add)
+        assert tol_ratio(got[act], ref_i[:, cols][act]) <= 1
+    check_neg_rows(dw)
+    check_outside_slices(dw)
+
+
+def test_fused_decode_graph_replays():
+    """lora_shrink_expand captured in a HIP graph: three replays, with v and
+    y overwritten between them, give the eager call's bits."""
+    _announce("fused decode, graph replays")
+    w = W.make("fusedg", "bf16", 200, 4096, 16, 4, [[4096, 1024]], seed=9, seq_len=1, neg_frac=0.1)
+    o = w.outputs[0]
+    offs = [q.col_off for q in o.slices]
+    eager = DeviceWorkload(w)
+    seg_e = lsb.lora_build_segments(eager.ids, w.L)
+    lsb.lora_shrink_expand(eager.x, eager.A, eager.Bs[0], offs, seg_e, eager.v, eager.ys[0], True)
+    torch.cuda.synchronize()
+    g_w = DeviceWorkload(w)
+    seg = lsb.lora_build_segments(g_w.ids, w.L)
+    y0 = g_w.ys[0].clone()
+    v0 = g_w.v.clone()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        lsb.lora_shrink_expand(g_w.x, g_w.A, g_w.Bs[0], offs, seg, g_w.v, g_w.ys[0], True)
+    for _ in range(3):
+        g_w.ys[0].copy_(y0)
+        g_w.v.copy_(v0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(g_w.v.cpu().numpy().view(np.uint32), eager.v.cpu().numpy().view(np.uint32))
+        assert np.array_equal(host_bits(g_w.ys[0]), host_bits(eager.ys[0]))
