@@ -1141,3 +1141,44 @@ def test_fused_decode_graph_replays():
         torch.cuda.synchronize()
         assert np.array_equal(g_w.v.cpu().numpy().view(np.uint32), eager.v.cpu().numpy().view(np.uint32))
         assert np.array_equal(host_bits(g_w.ys[0]), host_bits(eager.ys[0]))
+
+
+# ---------------------------------------------------------------- metadata that breaks its invariants
+@pytest.mark.parametrize("L", [5, 300])
+@pytest.mark.parametrize("path", ["auto", "bgmv", "sgmv"])
+def test_invalid_metadata_stays_in_bounds(force_path, L, path):
+    """The caller may fill lora_segments itself.  Metadata that breaks its
+    invariants (random values, S past L, descending starts, counts out of
+    range) gives unspecified rows but no error and no access outside the
+    buffers, through every kernel family, the lazy tile tables of pools over
+    256 adapters and the short-segment pass; a valid step afterwards still
+    matches the oracle."""
+    _announce(f"invalid metadata L={L} path={path}")
+    force_path({"auto": lsb.PATH_AUTO, "bgmv": lsb.PATH_BGMV, "sgmv": lsb.PATH_SGMV}[path])
+    T, H, r = 700, 1024, 16
+    w = W.make("badmeta", "bf16", T, H, r, L, [[512, 256]], seed=L + 3, seq_len=(1, 8), neg_frac=0.1)
+    dw = DeviceWorkload(w)
+    o = w.outputs[0]
+    offs = [q.col_off for q in o.slices]
+    seg = lsb.Segments(dw.ids, L)
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(L)
+    fills = [
+        lambda t: t.copy_(torch.randint(-2 * T, 2 * T, t.shape, generator=gen, dtype=torch.int32)),
+        lambda t: t.fill_(L + 5),
+        lambda t: t.copy_(torch.arange(t.numel(), 0, -1, dtype=torch.int32).reshape(t.shape) * 3),
+        lambda t: t.fill_(-7),
+    ]
+    for fill in fills:
+        for b in (seg.sorted_token, seg.seg_lora, seg.seg_start, seg.counts):
+            host = torch.empty(b.shape, dtype=torch.int32)
+            fill(host)
+            b.copy_(host)
+        lsb.lora_shrink(dw.x, dw.A, seg, dw.v)
+        lsb.lora_expand_slice(dw.v, dw.Bs[0], offs, seg, dw.ys[0], True)
+        lsb.lora_shrink_expand(dw.x, dw.A, dw.Bs[0], offs, seg, dw.v, dw.ys[0], True)
+        torch.cuda.synchronize()
+    fresh = DeviceWorkload(w)
+    fresh.run()
+    rv, ry, ryi = compare_with_oracle(fresh)
+    assert rv <= 1 and ry <= 1 and ryi <= 1
