@@ -9,9 +9,12 @@ compares with the oracle run on the same bits:
   * integer-valued inputs bit for bit against the oracle rounded once,
   * rows of tokens without an adapter and columns outside the slices
     untouched, bit for bit.
-The five named workloads run at full size; the largest is compared on a
-sample of rows (plus every untouched row in full).
+The five named workloads run at full size, each compared on every row
+(the largest streamed through the oracle in row blocks).
 """
+import math
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -403,7 +406,6 @@ def test_add_inputs_false():
 
 
 def _rank_pairs():
-    import os
     pairs = []
     with open(os.path.join(os.path.dirname(__file__), "golden", "rank_bins.txt")) as f:
         for line in f:
@@ -1182,3 +1184,58 @@ def test_invalid_metadata_stays_in_bounds(force_path, L, path):
     fresh.run()
     rv, ry, ryi = compare_with_oracle(fresh)
     assert rv <= 1 and ry <= 1 and ryi <= 1
+
+
+# ---------------------------------------------------------------- the micro-benchmark PR's shapes
+def _golden_shapes():
+    out = []
+    with open(os.path.join(os.path.dirname(__file__), "golden", "microbench_shapes.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                src, bs, sl, m, k, n, L, srt, ns = line.split()
+                out.append((src, int(bs), int(sl), int(m), int(k), int(n), int(L), bool(int(srt)), int(ns)))
+    return out
+
+
+@pytest.mark.parametrize("src,bs,sl,m,rank,n,L,sort,ns", _golden_shapes())
+def test_microbench_shapes(src, bs, sl, m, rank, n, L, sort, ns):
+    """The problem shapes the micro-benchmark PR prints (tests/golden/
+    microbench_shapes.txt): bs sequences of sl tokens (m = bs sl tokens),
+    rank k, n columns, sorted by adapter, shrink n -> k then expand k -> n.
+    The console table's shape is compared in full; the review thread's
+    65536-token example (2 GiB of x) is drawn on the GPU and compared on 256
+    sampled rows, each row's inputs copied to the host for the oracle."""
+    _announce(f"micro-benchmark shape {src}: {bs} x {sl} tokens, rank {rank}, {n} columns, {L} adapters")
+    assert bs * sl == m and ns == 1
+    if m <= 4096:
+        w = W.make(f"golden_{src}", "f16", m, n, rank, L, [[n]], seed=m + n, seq_len=sl, sort_by_id=sort)
+        dw = DeviceWorkload(w)
+        dw.run()
+        rv, ry, ryi = compare_all_rows(dw)
+        assert rv <= 1 and ry <= 1 and ryi <= 1
+        return
+    ids_np = W.make(f"golden_{src}", "f16", m, 8, 8, L, [[8]], seed=m + n, seq_len=sl, sort_by_id=sort).ids
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(m + n)
+    x = torch.randn(m, n, generator=gen, device="cuda").half()
+    A = (torch.randn(L, rank, n, generator=gen, device="cuda") / math.sqrt(n)).half()
+    B = (torch.randn(L, n, rank, generator=gen, device="cuda") / math.sqrt(rank)).half()
+    y = torch.randn(m, n, generator=gen, device="cuda").half()
+    rows = np.sort(np.random.default_rng(m).choice(m, 256, replace=False)).astype(np.int64)
+    ridx = torch.from_numpy(rows).cuda()
+    y0_rows = host_bits(y.index_select(0, ridx))
+    x_rows = host_bits(x.index_select(0, ridx))
+    ids = torch.from_numpy(ids_np).cuda()
+    seg = lsb.lora_build_segments(ids, L)
+    v = sentinel_v(m, rank)
+    lsb.lora_shrink(x, A, seg, v)
+    lsb.lora_expand(v, B, seg, y, True)
+    torch.cuda.synchronize()
+    sub_ids = ids_np[rows]
+    A_h, B_h = host_bits(A), host_bits(B)
+    v_or = oracle.shrink("f16", x_rows, A_h, sub_ids)
+    v_gpu = v.index_select(0, ridx).cpu().numpy().astype(np.float64)
+    assert tol_ratio(v_gpu, v_or) <= 1
+    y_or = oracle.expand("f16", v_or, B_h, sub_ids, y0_rows, 0, True)
+    got = decode(host_bits(y.index_select(0, ridx)), "f16")
+    assert tol_ratio(got, y_or) <= 1
