@@ -1187,7 +1187,7 @@ def main():
         others[wk.name] = {"value": round(bk / (rk["ms_per_step"] * 1e-3) / 1e9, 2), "unit": "GB/s",
                            "ms_per_step": round(rk["ms_per_step"], 6), "ops": rk["ops"],
                            "roofline": rk["roofline"], "parity_ratio": rk["parity_ratio"],
-                           "pool_sets": rk["pool_sets"], "fused": rk["fused"]}
+                           "pool_sets": rk["pool_sets"], "live_ranks": rk["live_ranks"], "fused": rk["fused"]}
 
     # Context for the roofline fraction: what plain torch streaming kernels
     # reach on this GPU (a copy and an in-place add over 512 MiB each, twice
