@@ -26,6 +26,7 @@
 #include "lora_device.h"
 #include "lora_kernels.h"
 #include "tiles.h"
+#include "token_path.h"
 
 namespace lora {
 
@@ -49,7 +50,14 @@ struct ExpandArgs {
   int64_t ldy;
   int32_t add;
   int32_t min_seg_len;  // segments with fewer tokens are left to another kernel
+  int32_t short_cb;     // SG > 0: column blocks of each one-token segment's per-token items
 };
+
+static_assert(kExpandThreads == kBgThreads, "per-token items run the per-token expand's body");
+
+// LDS of the per-token items' staging rows (one per wave), which reuse the
+// weight buffers.
+constexpr size_t kShortStageBytes = (size_t)(kBgThreads / kWave) * kSoRow * sizeof(float);
 
 template <int NKS>
 struct ExpandLds {
@@ -62,9 +70,22 @@ struct ExpandLds {
   static constexpr int BP = (RK / 32) * 32 + 16;
   static constexpr int NB = NKS <= 4 ? 2 : 1;    // weight buffers
   static constexpr size_t weight_bytes = (size_t)NB * kExpandCols * BP * 2;
-  // weights, then the tile table and scan scratch
-  static size_t bytes(int L) { return weight_bytes + 4 * ((size_t)tile_table_ints(L) + 8); }
+  // weights (or, with per-token items, at least their staging rows), then
+  // the tile table and scan scratch
+  static constexpr size_t region(bool with_short) {
+    return with_short && weight_bytes < kShortStageBytes ? kShortStageBytes : weight_bytes;
+  }
+  static size_t bytes(int L, bool with_short) {
+    return region(with_short) + 4 * ((size_t)tile_table_ints(L) + 8);
+  }
 };
+
+// Resident workgroups per CU the registers allow: four up to r = 32, three
+// at r = 64 (and at r = 32 with per-token items, whose expand body needs a
+// few more registers), two at r = 128 or with 128-token tiles.
+constexpr int expand_wgs_per_cu(int nks, int tb, int sg) {
+  return (tb == 2 || nks == 8) ? 2 : ((nks == 1 || (nks == 2 && sg == 0)) ? 4 : 3);
+}
 
 // Column offset (inside a 32-column pair of op tiles) of the 8 columns a lane
 // of lane group g holds after the swap.
@@ -76,8 +97,16 @@ __device__ __forceinline__ int pair_col(int g) { return 8 * (((g & 1) << 1) | (g
 // the slice offsets multiples of 8, ldy a multiple of 8.
 // DENSE: one adapter (0) for every token, token index = position (the
 // single-adapter form): no metadata is read.
-template <int DT, bool VEC, int NKS, int TB, bool DENSE>
-__global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <= 2 ? 4 : 3)) void expand_kernel(ExpandArgs a) {
+// SG > 0 (r = 8 SG, aligned data, with segment metadata): the launch also
+// takes the batch's one-token segments, which its tile table skips, as
+// per-token work items after the tile items: (segment slot, column block),
+// checked 64 at a time (short_item) and expanded with the per-token expand's
+// body, staging through this workgroup's weight buffers.  One launch then
+// covers both kinds of segment, and the per-token items fill the tail of the
+// tile items.
+template <int DT, bool VEC, int NKS, int TB, bool DENSE, int SG>
+__global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) void expand_kernel(ExpandArgs a) {
+  static_assert(SG == 0 || (VEC && !DENSE), "per-token items need aligned data and segment metadata");
   using Lds = ExpandLds<NKS>;
   constexpr int BP = Lds::BP;
   constexpr int NB = Lds::NB;
@@ -89,7 +118,7 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
   constexpr bool kPack = NKS >= 2;                           // 32 ranks per weight operand
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* s_b = reinterpret_cast<uint16_t*>(smem);
-  int32_t* s_table = reinterpret_cast<int32_t*>(smem + Lds::weight_bytes);
+  int32_t* s_table = reinterpret_cast<int32_t*>(smem + Lds::region(SG > 0));
   int32_t* s_scan = s_table + tile_table_ints(a.seg.L);
 
   const int tid = threadIdx.x;
@@ -124,9 +153,29 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
       nruns = all_runs(cpr);
     }
   }
-  const int n_items = mtiles * nruns;
+  const int n_tile_items = mtiles * nruns;
+  const int n_short = SG > 0 ? min(a.seg.L, a.seg.T) * a.short_cb : 0;
+  const int n_items = n_tile_items + n_short;
+  ShortBatch sb;
+  int n_short_seen = 0;
 
   for (int item = xcd_first_item(blockIdx.x, grid, n_items); item < n_items; item += grid) {
+    if constexpr (SG > 0) {
+      if (item >= n_tile_items) {
+        // A per-token item: its slot's segment, if it holds one token.
+        const int it = item - n_tile_items;
+        int t = 0, l = -1;
+        if (short_item(a.seg, 1, a.short_cb, n_short, it, n_short_seen++, sb, &t, &l)) {
+          const int k = it / a.short_cb;
+          expand_token_aligned<DT, SG, 1>(
+              a, t, it - k * a.short_cb, a.short_cb,
+              [&](int q) { return a.v + (int64_t)t * a.ldv + (int64_t)q * a.v_slice_stride; },
+              [&]() { return l; }, reinterpret_cast<float*>(smem) + wave * kSoRow);
+        }
+        __syncthreads();  // the staging rows are the next tile item's weight buffers
+        continue;
+      }
+    }
     // Consecutive items walk the token tiles under one run of columns, so
     // the weight run is reused from the L2 of one XCD.
     const int cr = item / mtiles;
@@ -449,12 +498,31 @@ __global__ __launch_bounds__(kExpandThreads, (TB == 2 || NKS == 8) ? 2 : (NKS <=
 
 }  // namespace
 
+namespace {
+
+// The tile expand with per-token items for r = 8, 16, 32, 64 (aligned, with
+// metadata).
+template <int DT, int TB>
+void launch_with_short(int r, int64_t grid, size_t lds, hipStream_t s, const ExpandArgs& a) {
+  switch (r) {
+    case 8: hipLaunchKernelGGL((expand_kernel<DT, true, 1, TB, false, 1>), dim3(grid), dim3(kExpandThreads), lds, s, a); break;
+    case 16: hipLaunchKernelGGL((expand_kernel<DT, true, 1, TB, false, 2>), dim3(grid), dim3(kExpandThreads), lds, s, a); break;
+    case 32: hipLaunchKernelGGL((expand_kernel<DT, true, 2, TB, false, 4>), dim3(grid), dim3(kExpandThreads), lds, s, a); break;
+    default: hipLaunchKernelGGL((expand_kernel<DT, true, 4, TB, false, 8>), dim3(grid), dim3(kExpandThreads), lds, s, a); break;
+  }
+}
+
+}  // namespace
+
 hipError_t launch_expand(const SegView& seg, const float* v, int64_t ldv, int64_t v_slice_stride,
                          const ExpandSliceDesc* slices, int32_t num_slices, int32_t r,
                          uint16_t* y, int64_t ldy, int add, int dtype, bool vec, hipStream_t s,
-                         int min_seg_len) {
+                         int min_seg_len, bool short_items) {
   ExpandArgs a{};
   a.min_seg_len = min_seg_len > 1 ? min_seg_len : 1;
+  // Per-token items for the one-token segments: aligned data, segment
+  // metadata and r = 8 SG only (the caller checks).
+  const int sg = short_items ? r / 8 : 0;
   a.seg = seg;
   a.v = v;
   a.ldv = ldv;
@@ -518,24 +586,47 @@ hipError_t launch_expand(const SegView& seg, const float* v, int64_t ldv, int64_
   }
   a.run_start[num_slices] = runs;
   int64_t items = mt_max * runs;
-  const size_t lds = nks == 1 ? ExpandLds<1>::bytes(seg.L)
-                     : nks == 2 ? ExpandLds<2>::bytes(seg.L)
-                     : nks == 4 ? ExpandLds<4>::bytes(seg.L) : ExpandLds<8>::bytes(seg.L);
+  if (sg > 0) {
+    // Column blocks of a one-token segment's items: one round of 512 columns
+    // of the widest slice per wave, as in the per-token expand.
+    int64_t rounds = 1;
+    for (int q = 0; q < num_slices; ++q) {
+      const int64_t rq = (slices[q].n + kRoundCols - 1) / kRoundCols;
+      rounds = rq > rounds ? rq : rounds;
+    }
+    const int64_t nw = kBgThreads / kWave;
+    a.short_cb = (int32_t)((rounds + nw - 1) / nw);
+    items += (int64_t)(seg.L < seg.T ? seg.L : seg.T) * a.short_cb;
+  }
+  const bool ws = sg > 0;
+  const size_t lds = nks == 1 ? ExpandLds<1>::bytes(seg.L, ws)
+                     : nks == 2 ? ExpandLds<2>::bytes(seg.L, ws)
+                     : nks == 4 ? ExpandLds<4>::bytes(seg.L, ws) : ExpandLds<8>::bytes(seg.L, ws);
   // Persistent workgroups: as many as fit on the 256 CUs (LDS and register
   // bound), at most four per CU.
   int64_t per_cu = (int64_t)(160 * 1024 / lds);
-  const int64_t reg_cu = tb == 2 || nks == 8 ? 2 : (nks <= 2 ? 4 : 3);
+  const int64_t reg_cu = expand_wgs_per_cu(nks, tb, sg);
   per_cu = per_cu < 1 ? 1 : (per_cu > reg_cu ? reg_cu : per_cu);
   if (tuning().expand_wgs_per_cu >= 1 && tuning().expand_wgs_per_cu < per_cu) per_cu = tuning().expand_wgs_per_cu;
   int64_t grid = items < 256 * per_cu ? items : 256 * per_cu;
   grid = (grid + 7) / 8 * 8;
   if (grid < 8) grid = 8;
+  if (sg > 0) {
+    if (dtype == 0) {
+      if (tb == 2) launch_with_short<0, 2>(r, grid, lds, s, a);
+      else launch_with_short<0, 1>(r, grid, lds, s, a);
+    } else {
+      if (tb == 2) launch_with_short<1, 2>(r, grid, lds, s, a);
+      else launch_with_short<1, 1>(r, grid, lds, s, a);
+    }
+    return hipGetLastError();
+  }
 #define LORA_EXPAND_LAUNCH(DT_, VEC_, TB_, DN_)                                                      \
   switch (nks) {                                                                                    \
-    case 1: hipLaunchKernelGGL((expand_kernel<DT_, VEC_, 1, TB_, DN_>), dim3(grid), dim3(kExpandThreads), lds, s, a); break; \
-    case 2: hipLaunchKernelGGL((expand_kernel<DT_, VEC_, 2, TB_, DN_>), dim3(grid), dim3(kExpandThreads), lds, s, a); break; \
-    case 4: hipLaunchKernelGGL((expand_kernel<DT_, VEC_, 4, TB_, DN_>), dim3(grid), dim3(kExpandThreads), lds, s, a); break; \
-    default: hipLaunchKernelGGL((expand_kernel<DT_, VEC_, 8, 1, DN_>), dim3(grid), dim3(kExpandThreads), lds, s, a); break; \
+    case 1: hipLaunchKernelGGL((expand_kernel<DT_, VEC_, 1, TB_, DN_, 0>), dim3(grid), dim3(kExpandThreads), lds, s, a); break; \
+    case 2: hipLaunchKernelGGL((expand_kernel<DT_, VEC_, 2, TB_, DN_, 0>), dim3(grid), dim3(kExpandThreads), lds, s, a); break; \
+    case 4: hipLaunchKernelGGL((expand_kernel<DT_, VEC_, 4, TB_, DN_, 0>), dim3(grid), dim3(kExpandThreads), lds, s, a); break; \
+    default: hipLaunchKernelGGL((expand_kernel<DT_, VEC_, 8, 1, DN_, 0>), dim3(grid), dim3(kExpandThreads), lds, s, a); break; \
   }
 #define LORA_EXPAND_TYPED(DN_)                                                                       \
   if (tb == 2) {                                                                                    \

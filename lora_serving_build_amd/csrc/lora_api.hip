@@ -404,12 +404,17 @@ int expand_core(const char* fn, const float* v, int64_t ldv, int64_t v_slice_str
   // against 10-12), so the split stops at r = 64.  The second launch costs
   // 2.5-4 us when it finds nothing, so it is made only when the batch can
   // hold many one-token segments: at least 256 adapters.
+  // With aligned data and r = 8, 16, 32 or 64 the tile launch itself takes
+  // the one-token segments as per-token work items (the aligned per-token
+  // expand's body), so both kinds of segment share one launch; other shapes
+  // take a second, per-token launch.
   const bool split = g_path.load(std::memory_order_relaxed) == 0 && !sv.dense && sv.L >= 256 &&
                      r <= lora::kBgmvMaxRank;
+  const bool one_launch = split && vec && (r == 8 || r == 16 || r == 32 || r == 64);
   hipError_t err = lora::launch_expand(sv, v, ldv, v_slice_stride, desc, num_slices, r,
                                        static_cast<uint16_t*>(y), ldy, add_inputs ? 1 : 0, dtype,
-                                       vec, static_cast<hipStream_t>(stream), split ? 2 : 1);
-  if (err == hipSuccess && split)
+                                       vec, static_cast<hipStream_t>(stream), split ? 2 : 1, one_launch);
+  if (err == hipSuccess && split && !one_launch)
     err = lora::launch_bgmv_expand(sv, v, ldv, v_slice_stride, desc, num_slices, r,
                                    static_cast<uint16_t*>(y), ldy, add_inputs ? 1 : 0, dtype, vec,
                                    static_cast<hipStream_t>(stream), 1);

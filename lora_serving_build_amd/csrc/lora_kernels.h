@@ -121,9 +121,11 @@ hipError_t launch_fused_decode(const SegView& seg, const uint16_t* x, int64_t ld
                                hipStream_t s);
 
 // min_seg_len: segments with fewer tokens are left to another kernel.
+// short_items (vec, segment metadata, r = 8, 16, 32 or 64, with min_seg_len
+// 2): the same launch takes the one-token segments as per-token items.
 hipError_t launch_expand(const SegView& seg, const float* v, int64_t ldv, int64_t v_slice_stride,
                          const ExpandSliceDesc* slices, int32_t num_slices, int32_t r,
                          uint16_t* y, int64_t ldy, int add, int dtype, bool vec, hipStream_t s,
-                         int min_seg_len = 1);
+                         int min_seg_len = 1, bool short_items = false);
 
 }  // namespace lora
