@@ -265,10 +265,15 @@ int lora_expand_slice_single(const float *v, int64_t ldv, int64_t v_slice_stride
  * per-token (BGMV) kernels -- a shrink when a cost fitted to measured times of
  * both families (from T, H and r) favours it, an expand when r <= 16 and
  * T n <= 4M or r <= 32 and T n <= 1M -- everything else the segment-tile
- * (SGMV) kernels; 1 = always per-token (shrink: any r; expand: r <= 64, or
- * r = 128 with 16-byte aligned rows and sizes that are multiples of 8, else
- * LORA_ERR_UNSUPPORTED); 2 = always segment tiles.  Process-wide, meant for tests and measurement.
- * Returns the previous mode, or LORA_ERR_INVALID_ARG for an unknown mode. */
+ * (SGMV) kernels.  In automatic mode, a segment-tile call of at least 256
+ * adapters also chooses per segment on the device (punica issue, BGMV vs
+ * SGMV): its one-token segments go to per-token work (the shrink at every
+ * rank, the expand up to r = 64), its longer segments to the tiles.
+ * 1 = always per-token (shrink: any r; expand: r <= 64, or r = 128 with
+ * 16-byte aligned rows and sizes that are multiples of 8, else
+ * LORA_ERR_UNSUPPORTED); 2 = always segment tiles, every segment.
+ * Process-wide, meant for tests and measurement.  Returns the previous mode,
+ * or LORA_ERR_INVALID_ARG for an unknown mode. */
 int lora_set_path(int mode);
 
 /* Re-reads the launch-plan overrides (LORA_SHRINK_KSPLIT, LORA_EXPAND_TB,
