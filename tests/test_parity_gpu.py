@@ -986,6 +986,7 @@ MIXED_CASES = [
     ("f16", 400, 4, 200, 256, 2048, 16, [[512]], False),
     ("bf16", 450, 4, 150, 256, 2048, 32, [[256, 256]], True),
     ("bf16", 3000, 16, 300, 320, 1024, 128, [[512]], False),      # rank 128: the expand keeps tiles throughout
+    ("f16", 1200, 8, 500, 600, 1024, 8, [[1024, 512]], True),     # rank 8: one-token items with one lane a column
     # prefill only, a few segments of a large pool: the tile bound (one partial
     # tile per adapter) is loose, and the kernels raise the H split and
     # shorten the column runs from the true tile count
