@@ -3,12 +3,15 @@
 // The punica issue describes BGMV as each input using its own model, with the
 // speed-up coming from spreading many small products over many compute units.
 // Here a workgroup takes one token (with a small batch, one block of its ranks
-// or of its output columns) at a time, in token order.  These kernels
-// read only token_lora: for a small batch, the sorted metadata would add
-// dependent round trips before the first weight load, and every adapter of the
-// batch fits in L2 anyway.  Rows that do not depend on the adapter (x, y, v)
-// are loaded before the adapter id is needed.  The whole H-sum of a token
-// stays inside its workgroup, so no partial sums leave it.
+// or of its output columns) at a time, in token order.  Over a whole batch
+// these kernels read only token_lora: for a small batch, the sorted metadata
+// would add dependent round trips before the first weight load, and every
+// adapter of the batch fits in L2 anyway.  (A compile-time variant takes only
+// the one-token segments of a mixed batch, from the metadata.)  Rows that do
+// not depend on the adapter (x, y, v) are loaded before the adapter id is
+// needed.  The whole H-sum of a token stays inside its workgroup, so no
+// partial sums leave it.  The pieces the tile expand shares live in
+// token_path.h.
 //
 // shrink: a workgroup takes one token and a block of up to 16 ranks; lane i
 //   owns elements 8 (i + 256 k) .. +8 of H (each wave instruction reads 1 KB

@@ -8,10 +8,11 @@
 // type, so v keeps about 16 significant bits.  For r <= 16, lane groups 0 and
 // 1 carry hi and groups 2 and 3 carry lo against the same 16 weights, so one
 // 16x16x32 op adds B^T (hi + lo).  For larger r, one weight operand covers 32
-// ranks and two ops apply it to hi and to lo, which halves the LDS reads.  Per chunk, the weight block (128 rows of B_l^T, one
-// contiguous 128 x r run in memory) is loaded by the whole workgroup with
-// linear 16-byte loads one chunk ahead and staged in LDS (two buffers up to
-// r = 64, so one barrier per chunk), so all waves share one copy.
+// ranks and two ops apply it to hi and to lo, which halves the LDS reads.  Per
+// chunk, the weight block (128 rows of B_l^T, one contiguous 128 x r run in
+// memory) is loaded by the whole workgroup with linear 16-byte loads one
+// chunk ahead and staged in LDS (two buffers up to r = 64, so one barrier per
+// chunk), so all waves share one copy.
 //
 // The product is computed transposed, D[c][token]: lane (m, g) of op tile q
 // holds columns 16 q + 4 g .. +4 of token m.  One lane-row swap between the
@@ -23,6 +24,10 @@
 // first chunk's with v, in the item's set-up); y is rounded once, to nearest
 // even.  LDS and registers leave room for four workgroups per CU up to
 // r = 32, three at r = 64 and two at r = 128 or with 128-token tiles.
+//
+// In a batch of many adapters the same launch can also take the one-token
+// segments, which a 64- or 128-token tile would waste, as per-token work
+// items after the tile items (SG > 0, see expand_kernel).
 #include "lora_device.h"
 #include "lora_kernels.h"
 #include "tiles.h"
