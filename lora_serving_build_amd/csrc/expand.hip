@@ -56,6 +56,7 @@ struct ExpandArgs {
   int32_t add;
   int32_t min_seg_len;  // segments with fewer tokens are left to another kernel
   int32_t short_cb;     // SG > 0: column blocks of each one-token segment's per-token items
+  int32_t balanced;     // tile schedule: 0 chosen per call, 1 round-robin items, 2 balanced ranges
 };
 
 static_assert(kExpandThreads == kBgThreads, "per-token items run the per-token expand's body");
@@ -160,39 +161,77 @@ __global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) voi
   }
   const int n_tile_items = mtiles * nruns;
   const int n_short = SG > 0 ? min(a.seg.L, a.seg.T) * a.short_cb : 0;
-  const int n_items = n_tile_items + n_short;
-  ShortBatch sb;
-  int n_short_seen = 0;
 
-  for (int item = xcd_first_item(blockIdx.x, grid, n_items); item < n_items; item += grid) {
-    if constexpr (SG > 0) {
-      if (item >= n_tile_items) {
-        // A per-token item: its slot's segment, if it holds one token.
-        const int it = item - n_tile_items;
-        int t = 0, l = -1;
-        if (short_item(a.seg, 1, a.short_cb, n_short, it, n_short_seen++, sb, &t, &l)) {
-          const int k = it / a.short_cb;
-          expand_token_aligned<DT, SG, 1>(
-              a, t, it - k * a.short_cb, a.short_cb,
-              [&](int q) { return a.v + (int64_t)t * a.ldv + (int64_t)q * a.v_slice_stride; },
-              [&]() { return l; }, reinterpret_cast<float*>(smem) + wave * kSoRow);
-        }
-        __syncthreads();  // the staging rows are the next tile item's weight buffers
-        continue;
+  // Tile work, in one of two schedules (the same choice in every
+  // workgroup).  Round-robin: item = (run, tile); consecutive items walk the
+  // token tiles under one run of columns, so the weight run is reused from
+  // the L2 of one XCD.  Balanced: the same order cut into (run, tile, chunk)
+  // units, each workgroup taking one contiguous range of U / grid units
+  // (neighbouring ranges on one XCD).  Round-robin spends a whole round on a
+  // last round that is only partly filled; a balanced range rarely starts or
+  // ends on a run boundary, so it pays about one more item set-up (about 1.5
+  // chunk times: token ids, v and the first y).  Balanced is taken when it
+  // is estimated 5% faster.  Measured on MI355X (us, round-robin ->
+  // balanced): 8192 x 16384 over 4 segments of 1952-2288 tokens, r = 16 /
+  // 64: 135.5 / 145.2 -> 123.4 / 131.3 (66 tiles, 4.1 rounds); 8192 x 4096,
+  // r = 64: 47.6 -> 40.7 (1.03 rounds); but 4 aligned segments of 2048
+  // tokens: 133.0 -> 136.1, and the 8192-token layer's gate_up call (7.8
+  // rounds): 442.9 -> 461.6.
+  int64_t chunks = 0;
+  for (int q = 0; q < a.num_slices; ++q) chunks += (a.slices[q].n + kExpandCols - 1) / kExpandCols;
+  const int64_t units = (int64_t)mtiles * chunks;
+  bool balanced = a.balanced == 2;
+  if (a.balanced == 0 && n_tile_items > grid) {
+    constexpr float kSetup = 1.5f;
+    const float per = (float)units / (float)grid;
+    const float rr = ceilf((float)n_tile_items / (float)grid) * ((float)cpr + kSetup);
+    const float bal = per + kSetup * (ceilf(per / (float)cpr) + 1.f);
+    balanced = bal < 0.95f * rr;
+  }
+  int item = xcd_first_item(blockIdx.x, grid, n_tile_items);
+  int64_t u = 0, u_end = 0;
+  if (balanced) {
+    const int w = (grid & 7) == 0 ? (blockIdx.x & 7) * (grid >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+    u = units * w / grid;
+    u_end = units * (w + 1) / grid;
+  }
+  for (;;) {
+    int q = 0, mt = 0, c_beg = 0, c_end = 0;
+    if (balanced) {
+      if (u >= u_end) break;
+      // Slice, run inside the slice (full runs of cpr chunks, then one
+      // shorter run), tile, chunk inside the run.
+      int64_t base = 0;
+      int cq = (a.slices[0].n + kExpandCols - 1) / kExpandCols;
+      while (q + 1 < a.num_slices && base + (int64_t)mtiles * cq <= u) {
+        base += (int64_t)mtiles * cq;
+        ++q;
+        cq = (a.slices[q].n + kExpandCols - 1) / kExpandCols;
       }
-    }
-    // Consecutive items walk the token tiles under one run of columns, so
-    // the weight run is reused from the L2 of one XCD.
-    const int cr = item / mtiles;
-    const int mt = item - cr * mtiles;
-    int q = 0, rs = 0;
-    while (q + 1 < a.num_slices && rs + slice_runs(q, cpr) <= cr) {
-      rs += slice_runs(q, cpr);
-      ++q;
+      const int64_t o = u - base;
+      const int j = (int)(o / ((int64_t)mtiles * cpr));
+      const int len = min(cpr, cq - j * cpr);
+      const int o2 = (int)(o - (int64_t)j * mtiles * cpr);
+      mt = o2 / len;
+      const int c = o2 - mt * len;
+      c_beg = j * cpr + c;
+      const int64_t left = u_end - u;
+      c_end = c_beg + (int)(left < len - c ? left : len - c);
+      u += c_end - c_beg;
+    } else {
+      if (item >= n_tile_items) break;
+      const int cr = item / mtiles;
+      mt = item - cr * mtiles;
+      int rs = 0;
+      while (q + 1 < a.num_slices && rs + slice_runs(q, cpr) <= cr) {
+        rs += slice_runs(q, cpr);
+        ++q;
+      }
+      c_beg = (cr - rs) * cpr;
+      c_end = min(c_beg + cpr, (a.slices[q].n + kExpandCols - 1) / kExpandCols);
+      item += grid;
     }
     const int nq = a.slices[q].n;
-    const int c_beg = (cr - rs) * cpr;
-    const int c_end = min(c_beg + cpr, (nq + kExpandCols - 1) / kExpandCols);
 
     int p0 = 0, p_end = 0, l = 0;
     // The adapter's live rank: weight pieces and v groups at or beyond it
@@ -499,6 +538,25 @@ __global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) voi
     if (c_beg < c_end) chunk(c_beg, true);
     for (int c = c_beg + 1; c < c_end; ++c) chunk(c, false);
   }
+
+  if constexpr (SG > 0) {
+    // Per-token items, in a grid-stride walk of their own: each takes its
+    // slot's segment if it holds one token.  Every chunk above ended with a
+    // barrier, so the staging rows (the weight buffers) are free.
+    ShortBatch sb;
+    int n_seen = 0;
+    for (int it = xcd_first_item(blockIdx.x, grid, n_short); it < n_short; it += grid) {
+      int t = 0, l = -1;
+      if (short_item(a.seg, 1, a.short_cb, n_short, it, n_seen++, sb, &t, &l)) {
+        const int k = it / a.short_cb;
+        expand_token_aligned<DT, SG, 1>(
+            a, t, it - k * a.short_cb, a.short_cb,
+            [&](int qs) { return a.v + (int64_t)t * a.ldv + (int64_t)qs * a.v_slice_stride; },
+            [&]() { return l; }, reinterpret_cast<float*>(smem) + wave * kSoRow);
+      }
+      __syncthreads();  // the staging rows are reused by the next item
+    }
+  }
 }
 
 }  // namespace
@@ -575,6 +633,7 @@ hipError_t launch_expand(const SegView& seg, const float* v, int64_t ldv, int64_
     const int64_t want = mt_max * chunks / 4096;
     cpr = want >= 8 ? 8 : (want >= 4 ? 4 : 2);
   }
+  a.balanced = tuning().expand_balance == 1 || tuning().expand_balance == 2 ? tuning().expand_balance : 0;
   a.cpr_fixed = 0;
   if (tuning().expand_cpr >= 1) {
     cpr = tuning().expand_cpr;

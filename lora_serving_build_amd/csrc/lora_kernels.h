@@ -24,7 +24,8 @@ constexpr int kShrinkKStep = 128;
 // Launch-plan overrides for tests and measurement, read from the
 // environment once when the library is loaded (and again on
 // lora_reload_tuning): LORA_SHRINK_KSPLIT, LORA_EXPAND_TB, LORA_EXPAND_CPR,
-// LORA_EXPAND_WGS_PER_CU, LORA_BGMV_SHRINK_RT, LORA_BGMV_RPI, LORA_BGMV_CB.  0 = not set: the
+// LORA_EXPAND_WGS_PER_CU, LORA_EXPAND_BALANCE (1 round-robin items, 2 balanced
+// ranges), LORA_BGMV_SHRINK_RT, LORA_BGMV_RPI, LORA_BGMV_CB.  0 = not set: the
 // launchers' own choice.
 struct Tuning {
   int shrink_ksplit;
@@ -34,6 +35,7 @@ struct Tuning {
   int bgmv_rpi;
   int bgmv_cb;
   int expand_wgs_per_cu;
+  int expand_balance;
 };
 const Tuning& tuning();
 void reload_tuning();

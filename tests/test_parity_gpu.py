@@ -631,6 +631,15 @@ PLAN_VARIANTS = [
     ({"LORA_EXPAND_CPR": "1"}, "sgmv", "bf16", 400, 1024, 32, 6, [[1536, 256]]),
     ({"LORA_EXPAND_CPR": "3"}, "sgmv", "f16", 400, 1024, 32, 6, [[1536, 256]]),
     ({"LORA_EXPAND_CPR": "40"}, "sgmv", "bf16", 400, 1024, 32, 6, [[1536, 256]]),
+    # the tile expand's two schedules, forced: balanced ranges of (run, tile,
+    # chunk) units cut runs anywhere (ragged slice ends, 3-chunk runs, 128-token
+    # tiles, rank 128, the element-wise path) -- and round-robin items
+    ({"LORA_EXPAND_BALANCE": "2"}, "sgmv", "bf16", 700, 1024, 64, 5, [[2048, 520, 136]]),
+    ({"LORA_EXPAND_BALANCE": "2", "LORA_EXPAND_CPR": "3"}, "sgmv", "f16", 400, 1024, 32, 6, [[1536, 256]]),
+    ({"LORA_EXPAND_BALANCE": "2", "LORA_EXPAND_TB": "2"}, "sgmv", "f16", 900, 1024, 16, 6, [[1000]]),
+    ({"LORA_EXPAND_BALANCE": "2"}, "sgmv", "bf16", 300, 512, 128, 3, [[384]]),
+    ({"LORA_EXPAND_BALANCE": "2"}, "sgmv", "f16", 77, 2049, 20, 3, [[300]]),
+    ({"LORA_EXPAND_BALANCE": "1"}, "sgmv", "bf16", 700, 1024, 64, 5, [[2048, 520, 136]]),
     # per-token expand: rounds of 512 columns per wave and column blocks per token
     ({"LORA_BGMV_RPI": "2"}, "bgmv", "f16", 20, 1024, 16, 3, [[4096, 1024]]),
     ({"LORA_BGMV_RPI": "2"}, "bgmv", "bf16", 9, 512, 8, 3, [[2048, 4096]]),
@@ -1024,6 +1033,42 @@ def test_decode_prefill_mix(dtype, n_pre, pre_l, n_dec, L, H, r, slices, integer
         assert rv <= 1 and ry <= 1 and ryi <= 1
     check_neg_rows(dw)
     check_outside_slices(dw)
+
+
+@pytest.mark.parametrize("case", [MIXED_CASES[i] for i in (1, 3, 6, 8, 10)])
+@pytest.mark.parametrize("balance", ["1", "2"])
+def test_decode_prefill_mix_schedules(monkeypatch, tuning_from_env, case, balance):
+    """Mixed batches with the tile expand's schedule forced (round-robin
+    items, balanced ranges), its per-token items walked after the tile work:
+    bit for bit against the automatic choice's result, and against the
+    oracle as in the automatic case."""
+    dtype, n_pre, pre_l, n_dec, L, H, r, slices, integer = case
+    _announce(f"decode+prefill mix, expand schedule {balance}: {dtype} prefill={n_pre}/{pre_l} "
+              f"decode={n_dec} L={L} r={r} slices={slices} integer={integer}")
+    w = W.make_mixed("mix", dtype, n_pre, pre_l, n_dec, L, H, r, slices, seed=n_pre + n_dec + r,
+                     neg_frac=0.05, integer=integer)
+    auto = DeviceWorkload(w)
+    auto.run()
+    monkeypatch.setenv("LORA_EXPAND_BALANCE", balance)
+    tuning_from_env()
+    forced = DeviceWorkload(w)
+    forced.run()
+    for ya, yf in zip(auto.ys, forced.ys):
+        assert np.array_equal(host_bits(ya), host_bits(yf))
+    if integer:
+        act = np.nonzero(w.active)[0]
+        v_or = oracle.shrink(w.dtype, w.x, w.A, w.ids)
+        for o, y in zip(w.outputs, forced.ys):
+            ref = oracle.expand_slice(w.dtype, np.nan_to_num(v_or), [s.B for s in o.slices],
+                                      [s.col_off for s in o.slices], w.ids, o.y0, w.add)
+            ref_bits = W.f32_to_bits(ref.astype(np.float32), dtype) if dtype == "bf16" else \
+                ref.astype(np.float16).view(np.uint16)
+            assert np.array_equal(host_bits(y)[:, _slice_cols(o)][act], ref_bits[act])
+    else:
+        rv, ry, ryi = compare_all_rows(forced)
+        assert rv <= 1 and ry <= 1 and ryi <= 1
+    check_neg_rows(forced)
+    check_outside_slices(forced)
 
 
 def test_decode_prefill_mix_graph_replays():
