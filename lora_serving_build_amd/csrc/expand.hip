@@ -188,7 +188,9 @@ __global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) voi
     const float bal = per + kSetup * (ceilf(per / (float)cpr) + 1.f);
     balanced = bal < 0.95f * rr;
   }
-  int item = xcd_first_item(blockIdx.x, grid, n_tile_items);
+  // Round-robin numbers the per-token items after the tile items in one
+  // walk, so the workgroups without a last-round tile item take them first.
+  int item = xcd_first_item(blockIdx.x, grid, balanced ? n_tile_items : n_tile_items + n_short);
   int64_t u = 0, u_end = 0;
   if (balanced) {
     const int w = (grid & 7) == 0 ? (blockIdx.x & 7) * (grid >> 3) + (blockIdx.x >> 3) : blockIdx.x;
@@ -540,12 +542,14 @@ __global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) voi
   }
 
   if constexpr (SG > 0) {
-    // Per-token items, in a grid-stride walk of their own: each takes its
-    // slot's segment if it holds one token.  Every chunk above ended with a
+    // Per-token items: each takes its slot's segment if it holds one token.
+    // Round-robin goes on with the walk above; balanced ranges start a
+    // grid-stride walk of their own.  Every chunk above ended with a
     // barrier, so the staging rows (the weight buffers) are free.
     ShortBatch sb;
     int n_seen = 0;
-    for (int it = xcd_first_item(blockIdx.x, grid, n_short); it < n_short; it += grid) {
+    for (int it = balanced ? xcd_first_item(blockIdx.x, grid, n_short) : item - n_tile_items; it < n_short;
+         it += grid) {
       int t = 0, l = -1;
       if (short_item(a.seg, 1, a.short_cb, n_short, it, n_seen++, sb, &t, &l)) {
         const int k = it / a.short_cb;
