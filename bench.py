@@ -1210,9 +1210,31 @@ def main():
             rates[name] = round(2 * (512 << 20) * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
         del src, dst
         torch.cuda.empty_cache()
+        # The launch floor the decode-sized ops sit on: 64 launches of a
+        # one-element add (an empty kernel in all but name) captured in one
+        # graph, replayed once untimed and once between two events.
+        tiny = torch.zeros(1, dtype=torch.int32, device="cuda")
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for _ in range(64):
+                tiny.add_(1)
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        floor_us = round(e0.elapsed_time(e1) * 1e3 / 64, 2)
+        del g, tiny
         hbm_context = {"copy_GB_s": rates["copy"], "rmw_GB_s": rates["rmw"],
-                       "how": "torch copy_ and in-place add_ over 512 MiB int32, read + write bytes"}
-        log(f"torch streaming context: copy {rates['copy']} GB/s, rmw {rates['rmw']} GB/s")
+                       "how": "torch copy_ and in-place add_ over 512 MiB int32, read + write bytes",
+                       "launch_floor_us": floor_us,
+                       "launch_floor_how": "graph replay of 64 one-element torch add_ launches, per launch"}
+        log(f"torch streaming context: copy {rates['copy']} GB/s, rmw {rates['rmw']} GB/s; "
+            f"launch floor {floor_us} us per launch in a graph")
 
     cpu = None
     if not args.no_cpu_baseline:

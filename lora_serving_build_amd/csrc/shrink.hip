@@ -271,18 +271,20 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
 }
 
 // v[t, :r] = sum over the ks chunks of the partial rows, in chunk order (ks
-// as the shrink kernel left it in the workspace header; nothing to do when it
-// wrote v itself).
+// as the shrink kernel left it in the workspace header, or ks_fixed when the
+// host's split is the most the workspace holds, so the kernel cannot have
+// raised it: then the partial rows' loads need not wait for the header;
+// nothing to do when the shrink kernel wrote v itself).
 // Every load of a row -- the active count, its token, eight partial rows at a
 // time -- goes out before any of them is checked, so a reduction of up to
 // eight chunks is one memory trip; positions past the active tokens (whose
 // partial rows were never written) and ranks past r are dropped at the store.
 template <bool VEC>
 __global__ __launch_bounds__(256) void shrink_reduce_kernel(SegView seg, const float* partial,
-                                                            const int32_t* ks_in, int32_t ks_cap,
-                                                            int32_t rp, int32_t r, float* v,
+                                                            const int32_t* ks_in, int32_t ks_fixed,
+                                                            int32_t ks_cap, int32_t rp, int32_t r, float* v,
                                                             int64_t ldv) {
-  int ks = *ks_in;
+  int ks = ks_fixed > 0 ? ks_fixed : *ks_in;
   ks = ks > ks_cap ? ks_cap : ks;
   if (ks <= 1) return;
   const int per_row = rp / 4;
@@ -440,12 +442,13 @@ hipError_t launch_shrink(const SegView& seg, const uint16_t* x, int64_t ldx, con
   int64_t blocks = ((int64_t)seg.T * (plan.rp / 4) + 255) / 256;
   if (blocks > 1024) blocks = 1024;
   if (blocks < 1) blocks = 1;
+  const int32_t ks_fixed = plan.ks_cap == plan.ksplit ? plan.ksplit : 0;
   if (vec)
     hipLaunchKernelGGL((shrink_reduce_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, s, seg,
-                       a.partial, a.ks_out, plan.ks_cap, plan.rp, r, v, ldv);
+                       a.partial, a.ks_out, ks_fixed, plan.ks_cap, plan.rp, r, v, ldv);
   else
     hipLaunchKernelGGL((shrink_reduce_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, s, seg,
-                       a.partial, a.ks_out, plan.ks_cap, plan.rp, r, v, ldv);
+                       a.partial, a.ks_out, ks_fixed, plan.ks_cap, plan.rp, r, v, ldv);
   return hipGetLastError();
 }
 
