@@ -169,61 +169,70 @@ __global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) voi
   // units, each workgroup taking one contiguous range of U / grid units
   // (neighbouring ranges on one XCD).  Round-robin spends a whole round on a
   // last round that is only partly filled; a balanced range rarely starts or
-  // ends on a run boundary, so it pays about one more item set-up (about 1.5
-  // chunk times: token ids, v and the first y).  Balanced is taken when it
-  // is estimated 5% faster.  Measured on MI355X (us, round-robin ->
-  // balanced): 8192 x 16384 over 4 segments of 1952-2288 tokens, r = 16 /
-  // 64: 135.5 / 145.2 -> 123.4 / 131.3 (66 tiles, 4.1 rounds); 8192 x 4096,
-  // r = 64: 47.6 -> 40.7 (1.03 rounds); but 4 aligned segments of 2048
-  // tokens: 133.0 -> 136.1, and the 8192-token layer's gate_up call (7.8
-  // rounds): 442.9 -> 461.6.
+  // ends on a run boundary, so it pays about one more item set-up (token ids,
+  // v and the first y: a few memory trips, about 1.5 chunk times with
+  // 128-token tiles).  Balanced is taken when it is estimated 5% faster.
+  // Measured on MI355X (us, round-robin -> balanced): 8192 x 16384 over 4 segments of
+  // 1952-2288 tokens, r = 16 / 64: 135.5 / 145.2 -> 123.4 / 131.3 (66 tiles,
+  // 4.1 rounds); 8192 x 4096, r = 64: 47.6 -> 40.7 (1.03 rounds); but 4
+  // aligned segments of 2048 tokens: 133.0 -> 136.1, the 8192-token layer's
+  // gate_up call (7.8 rounds): 442.9 -> 461.6, and with 64-token tiles and
+  // 2-chunk runs 8192 x 1024 at r = 128 (1.02 rounds): 21.6 -> 24.0.
+  // (Balanced ranges count units in 32 bits: beyond that, round-robin.  The
+  // forms with 64-token tiles are always round-robin: there a set-up costs
+  // about 3 chunk times, so balanced ranges rarely pay, and the code of the
+  // other walk cost them 1-7% (rank 128: 21.8 -> 23.5 us on 8192 x 1024).)
+  constexpr bool kCanBalance = TB == 2 && NKS <= 4;
   int64_t chunks = 0;
   for (int q = 0; q < a.num_slices; ++q) chunks += (a.slices[q].n + kExpandCols - 1) / kExpandCols;
   const int64_t units = (int64_t)mtiles * chunks;
-  bool balanced = a.balanced == 2;
-  if (a.balanced == 0 && n_tile_items > grid) {
+  bool balanced = kCanBalance && a.balanced == 2 && units < INT32_MAX;
+  if (kCanBalance && a.balanced == 0 && n_tile_items > grid && units < INT32_MAX) {
     constexpr float kSetup = 1.5f;
     const float per = (float)units / (float)grid;
     const float rr = ceilf((float)n_tile_items / (float)grid) * ((float)cpr + kSetup);
     const float bal = per + kSetup * (ceilf(per / (float)cpr) + 1.f);
     balanced = bal < 0.95f * rr;
   }
-  // Round-robin numbers the per-token items after the tile items in one
-  // walk, so the workgroups without a last-round tile item take them first.
-  int item = xcd_first_item(blockIdx.x, grid, balanced ? n_tile_items : n_tile_items + n_short);
-  int64_t u = 0, u_end = 0;
+  // The walk's position and end: item and tile-item count (round-robin,
+  // which numbers the per-token items after the tile items in one walk, so
+  // the workgroups without a last-round tile item take them first), or unit
+  // range (balanced).
+  int cur, end;
   if (balanced) {
     const int w = (grid & 7) == 0 ? (blockIdx.x & 7) * (grid >> 3) + (blockIdx.x >> 3) : blockIdx.x;
-    u = units * w / grid;
-    u_end = units * (w + 1) / grid;
+    cur = (int)(units * w / grid);
+    end = (int)(units * (w + 1) / grid);
+  } else {
+    cur = xcd_first_item(blockIdx.x, grid, n_tile_items + n_short);
+    end = n_tile_items;
   }
   for (;;) {
+    if (cur >= end) break;
     int q = 0, mt = 0, c_beg = 0, c_end = 0;
     if (balanced) {
-      if (u >= u_end) break;
+      const int u = cur;
       // Slice, run inside the slice (full runs of cpr chunks, then one
       // shorter run), tile, chunk inside the run.
-      int64_t base = 0;
+      int base = 0;  // units before slice q (all below 2^31 here)
       int cq = (a.slices[0].n + kExpandCols - 1) / kExpandCols;
-      while (q + 1 < a.num_slices && base + (int64_t)mtiles * cq <= u) {
-        base += (int64_t)mtiles * cq;
+      while (q + 1 < a.num_slices && base + mtiles * cq <= u) {
+        base += mtiles * cq;
         ++q;
         cq = (a.slices[q].n + kExpandCols - 1) / kExpandCols;
       }
-      const int64_t o = u - base;
-      const int j = (int)(o / ((int64_t)mtiles * cpr));
+      const int o = u - base;
+      const int j = o / (mtiles * cpr);
       const int len = min(cpr, cq - j * cpr);
-      const int o2 = (int)(o - (int64_t)j * mtiles * cpr);
+      const int o2 = o - j * mtiles * cpr;
       mt = o2 / len;
       const int c = o2 - mt * len;
       c_beg = j * cpr + c;
-      const int64_t left = u_end - u;
-      c_end = c_beg + (int)(left < len - c ? left : len - c);
-      u += c_end - c_beg;
+      c_end = c_beg + min(end - u, len - c);
+      cur += c_end - c_beg;
     } else {
-      if (item >= n_tile_items) break;
-      const int cr = item / mtiles;
-      mt = item - cr * mtiles;
+      const int cr = cur / mtiles;
+      mt = cur - cr * mtiles;
       int rs = 0;
       while (q + 1 < a.num_slices && rs + slice_runs(q, cpr) <= cr) {
         rs += slice_runs(q, cpr);
@@ -231,7 +240,7 @@ __global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) voi
       }
       c_beg = (cr - rs) * cpr;
       c_end = min(c_beg + cpr, (a.slices[q].n + kExpandCols - 1) / kExpandCols);
-      item += grid;
+      cur += grid;
     }
     const int nq = a.slices[q].n;
 
@@ -548,7 +557,7 @@ __global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) voi
     // barrier, so the staging rows (the weight buffers) are free.
     ShortBatch sb;
     int n_seen = 0;
-    for (int it = balanced ? xcd_first_item(blockIdx.x, grid, n_short) : item - n_tile_items; it < n_short;
+    for (int it = balanced ? xcd_first_item(blockIdx.x, grid, n_short) : cur - n_tile_items; it < n_short;
          it += grid) {
       int t = 0, l = -1;
       if (short_item(a.seg, 1, a.short_cb, n_short, it, n_seen++, sb, &t, &l)) {

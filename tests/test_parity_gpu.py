@@ -632,13 +632,17 @@ PLAN_VARIANTS = [
     ({"LORA_EXPAND_CPR": "3"}, "sgmv", "f16", 400, 1024, 32, 6, [[1536, 256]]),
     ({"LORA_EXPAND_CPR": "40"}, "sgmv", "bf16", 400, 1024, 32, 6, [[1536, 256]]),
     # the tile expand's two schedules, forced: balanced ranges of (run, tile,
-    # chunk) units cut runs anywhere (ragged slice ends, 3-chunk runs, 128-token
-    # tiles, rank 128, the element-wise path) -- and round-robin items
-    ({"LORA_EXPAND_BALANCE": "2"}, "sgmv", "bf16", 700, 1024, 64, 5, [[2048, 520, 136]]),
-    ({"LORA_EXPAND_BALANCE": "2", "LORA_EXPAND_CPR": "3"}, "sgmv", "f16", 400, 1024, 32, 6, [[1536, 256]]),
+    # chunk) units (128-token tiles) cut runs anywhere (ragged slice ends,
+    # 3-chunk runs, the element-wise path); the forms that always walk
+    # round-robin (64-token tiles, rank 128) ignore the override; and
+    # round-robin items
+    ({"LORA_EXPAND_BALANCE": "2", "LORA_EXPAND_TB": "2"}, "sgmv", "bf16", 700, 1024, 64, 5, [[2048, 520, 136]]),
+    ({"LORA_EXPAND_BALANCE": "2", "LORA_EXPAND_TB": "2", "LORA_EXPAND_CPR": "3"}, "sgmv", "f16", 400, 1024, 32, 6,
+     [[1536, 256]]),
     ({"LORA_EXPAND_BALANCE": "2", "LORA_EXPAND_TB": "2"}, "sgmv", "f16", 900, 1024, 16, 6, [[1000]]),
+    ({"LORA_EXPAND_BALANCE": "2", "LORA_EXPAND_TB": "2"}, "sgmv", "f16", 77, 2049, 20, 3, [[300]]),
     ({"LORA_EXPAND_BALANCE": "2"}, "sgmv", "bf16", 300, 512, 128, 3, [[384]]),
-    ({"LORA_EXPAND_BALANCE": "2"}, "sgmv", "f16", 77, 2049, 20, 3, [[300]]),
+    ({"LORA_EXPAND_BALANCE": "2", "LORA_EXPAND_TB": "1"}, "sgmv", "bf16", 400, 1024, 32, 6, [[1536, 256]]),
     ({"LORA_EXPAND_BALANCE": "1"}, "sgmv", "bf16", 700, 1024, 64, 5, [[2048, 520, 136]]),
     # per-token expand: rounds of 512 columns per wave and column blocks per token
     ({"LORA_BGMV_RPI": "2"}, "bgmv", "f16", 20, 1024, 16, 3, [[4096, 1024]]),
