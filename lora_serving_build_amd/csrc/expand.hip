@@ -358,6 +358,11 @@ __global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) voi
     // not hold it back and it is in flight through v's conversion and the
     // first barrier.
     u32x4 yfirst[TB][NP];
+    // With 64-token tiles an item is short (a few chunks, often one item per
+    // workgroup), so its chain of memory trips sets the time: the second
+    // chunk's y goes out with the first's.
+    constexpr bool kPeel = TB == 1;
+    u32x4 ysecond[TB][NP];
     // Per token: 2^k of the binary16 prescale (1 for bfloat16, whose range is
     // fp32's), applied to the fp32 products before y is added.
     float vscale[TB];
@@ -383,6 +388,7 @@ __global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) voi
         }
       }
       gload_y(c_beg, yfirst);  // unconditional: addresses are clamped, c_beg < c_end
+      if constexpr (kPeel) gload_y(c_beg + 1, ysecond);  // clamped too, also past c_end
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int b = 0; b < TB; ++b) {
@@ -436,16 +442,23 @@ __global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) voi
     // the y update.  The latency of y is covered by the other workgroups on
     // the CU (up to four), not by a longer prefetch: a longer prefetch would
     // not survive the compiler's conservative load counting across the loop.
-    auto chunk = [&](int c, bool first) {
+    // src (a constant at every call): 0 the set-up's first y, 1 its second,
+    // 2 loaded here.
+    auto chunk = [&](int c, int src) {
       const int buf = NB == 2 ? ((c - c_beg) & 1) : 0;
       const bool has_next = c + 1 < c_end;
       if (has_next) gload_b(c + 1);
       u32x4 ycur[TB][NP];
-      if (first) {
+      if (src == 0) {
 #pragma unroll
         for (int b = 0; b < TB; ++b)
 #pragma unroll
           for (int p = 0; p < NP; ++p) ycur[b][p] = yfirst[b][p];
+      } else if (src == 1) {
+#pragma unroll
+        for (int b = 0; b < TB; ++b)
+#pragma unroll
+          for (int p = 0; p < NP; ++p) ycur[b][p] = ysecond[b][p];
       } else {
         gload_y(c, ycur);
       }
@@ -546,8 +559,13 @@ __global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) voi
         __syncthreads();
       }
     };
-    if (c_beg < c_end) chunk(c_beg, true);
-    for (int c = c_beg + 1; c < c_end; ++c) chunk(c, false);
+    if (c_beg < c_end) chunk(c_beg, 0);
+    if constexpr (kPeel) {
+      if (c_beg + 1 < c_end) chunk(c_beg + 1, 1);
+      for (int c = c_beg + 2; c < c_end; ++c) chunk(c, 2);
+    } else {
+      for (int c = c_beg + 1; c < c_end; ++c) chunk(c, 2);
+    }
   }
 
   if constexpr (SG > 0) {
