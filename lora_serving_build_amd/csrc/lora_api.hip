@@ -121,6 +121,7 @@ lora::Tuning read_tuning() {
   t.bgmv_cb = read_env_int("LORA_BGMV_CB");
   t.expand_wgs_per_cu = read_env_int("LORA_EXPAND_WGS_PER_CU");
   t.expand_balance = read_env_int("LORA_EXPAND_BALANCE");
+  t.shrink_tb = read_env_int("LORA_SHRINK_TB");
   return t;
 }
 

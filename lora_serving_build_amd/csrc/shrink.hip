@@ -41,6 +41,11 @@ namespace {
 constexpr int kShrinkThreads = 256;
 constexpr int kSkTile = 64;              // tokens per tile (4 waves x 16)
 constexpr int kSkKB = kShrinkKStep;      // H elements per block
+// Resident workgroups per CU the registers allow, by rank tiles (NJT) and
+// 16-token blocks per wave (TB).
+constexpr int shrink_wgs_per_cu(int njt, int tb) {
+  return tb == 1 ? (njt <= 4 ? 4 : 2) : (njt <= 2 ? 4 : njt <= 4 ? 3 : 2);
+}
 // 16-bit elements per LDS row of A.  A 16-byte LDS read is served for 16
 // lanes at a time, lanes 0-7 with 16-23 (and so on); here those are rows 0-7
 // of the operand at two 16-byte columns.  A row stride that is an odd
@@ -67,7 +72,41 @@ struct ShrinkArgs {
   int32_t kchunk;  // H elements per workgroup chunk (multiple of kSkKB)
   int32_t rp;      // padded rank of the partial rows (16 * NJT)
   int32_t min_seg_len;  // segments with fewer tokens are left to another kernel
+  int32_t fixed;   // 1: the split is as set (an override), not re-planned
 };
+
+// H split for 128-token tiles.  The CUs stream their items concurrently, so
+// a CU's time is about its share of the work: ceil(items / 256) items times
+// the blocks of one plus about two blocks' worth per item (its set-up and its
+// partial rows, as many bytes as one block of x).  Measured on MI355X, 8192 x
+// 16384 at r = 64, one adapter: 4 chunks 62.3 us, 8 chunks 63.6, 5 chunks
+// 83.8; over four segments of 1952-2288 tokens: 11 chunks 73.6, 4 chunks
+// 97.6; 8192 x 4096: 3 chunks 28.3, 7 chunks 32.5; the 8192-token layer (71
+// tiles): 3 chunks 48.2, 7 chunks 50.6.  Splits that give a CU more items
+// than it holds workgroups run far slower (their items wait for a second
+// round) and are not taken, except one chunk.  Among the rest, the least
+// time, ties to fewer chunks.
+// (32-bit divisions, two per candidate: in the kernel every workgroup runs
+// this before its first item, and 64-bit divisions are long sequences there.)
+__host__ __device__ inline int split_by_cu(int tiles, int H, int ks_max, int per_cu, int* chunk_out) {
+  int best = 1;
+  int64_t best_cost = -1;
+  int best_chunk = (((H - 1) >> 7) + 1) << 7;
+  for (int k = 1; k <= ks_max; ++k) {
+    const int ch = ((((H - 1) / k) >> 7) + 1) << 7;  // ceil(H / k) rounded up to a block
+    if ((H - 1) / ch + 1 != k) continue;               // this chunk size makes fewer chunks: counted there
+    const int64_t per = ((int64_t)tiles * k + 255) >> 8;
+    if (per > per_cu && k > 1) continue;
+    const int64_t cost = per * ((ch >> 7) + 2);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = k;
+      best_chunk = ch;
+    }
+  }
+  *chunk_out = best_chunk;
+  return best;
+}
 
 template <int NJT>
 struct ShrinkLds {
@@ -93,9 +132,10 @@ __device__ __forceinline__ void store4(float* p, int j0, int r, f32x4 val) {
 // and ldx multiples of 8 (otherwise element-wise loads).
 // DENSE: one adapter (0) for every token, token index = position (the
 // single-adapter form): no metadata is read.
-template <int DT, bool VEC, int NJT, bool DENSE>
-__global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kernel(ShrinkArgs a) {
+template <int DT, bool VEC, int NJT, bool DENSE, int TB>
+__global__ __launch_bounds__(kShrinkThreads, shrink_wgs_per_cu(NJT, TB)) void shrink_kernel(ShrinkArgs a) {
   constexpr int RP = 16 * NJT;
+  constexpr int TT = kSkTile * TB;  // tokens per tile
   constexpr int AL = RP * kSkChunks / kShrinkThreads;  // A pieces per thread per block (NJT)
   constexpr int KS = kSkKB / 32;                        // 32-wide k steps per block
   extern __shared__ __align__(16) unsigned char smem[];
@@ -113,10 +153,16 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
   const int lcol = (tid & 15) * 8;
 
   const TileTable table =
-      build_tile_table<kShrinkThreads, DENSE>(a.seg, kSkTile, a.r, s_table, s_scan, a.min_seg_len);
+      build_tile_table<kShrinkThreads, DENSE>(a.seg, TT, a.r, s_table, s_scan, a.min_seg_len);
   const int tiles = table.tiles;
   int ks = a.ks, kchunk = a.kchunk;
-  if (a.ks_cap > ks && tiles > 0 && 2 * tiles * ks <= a.resident) {
+  if constexpr (TB == 2) {
+    // The split from the true tile count, by the CUs' share of the blocks
+    // (the same in every workgroup; within what the workspace holds).
+    if (!a.fixed && a.ks_cap > 1 && tiles > 0) {
+      ks = split_by_cu(tiles, a.H, a.ks_cap, a.resident >> 8, &kchunk);
+    }
+  } else if (a.ks_cap > ks && tiles > 0 && 2 * tiles * ks <= a.resident) {
     // Under half the resident workgroups busy: the host's bound was loose.
     int k = (a.resident + tiles - 1) / tiles;
     if (tiles * k - a.resident > a.resident / 50) k = a.resident / tiles;
@@ -135,20 +181,30 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
     const int tile = item - ksi * tiles;
     int p0 = 0, p_end = 0, l = 0;
     int rank_l = 0;
-    const bool ok = tile_range_lds(table, a.seg.T, a.seg.L, kSkTile, tile, &p0, &p_end, &l, &rank_l);
+    const bool ok = tile_range_lds(table, a.seg.T, a.seg.L, TT, tile, &p0, &p_end, &l, &rank_l);
     const int kbeg = ksi * kchunk;
     const int kend = min(a.H, kbeg + kchunk);
-    const int pos = p0 + wave * 16 + m;
-    int t = (ok && pos < p_end) ? (DENSE ? pos : a.seg.sorted_token[pos]) : -1;
-    t = (t >= 0 && t < a.seg.T) ? t : -1;
-    const bool tok_ok = t >= 0;
-    const bool wave_live = ok && p0 + wave * 16 < p_end;
+    // Wave w takes tokens [16 TB w, 16 TB (w + 1)) of the tile, block b the
+    // 16 from 16 (TB w + b).
+    int pos[TB], t[TB];
+    bool tok_ok[TB], blk_live[TB];
+#pragma unroll
+    for (int b = 0; b < TB; ++b) {
+      pos[b] = p0 + 16 * (TB * wave + b) + m;
+      int tb = (ok && pos[b] < p_end) ? (DENSE ? pos[b] : a.seg.sorted_token[pos[b]]) : -1;
+      t[b] = (tb >= 0 && tb < a.seg.T) ? tb : -1;
+      tok_ok[b] = t[b] >= 0;
+      blk_live[b] = ok && p0 + 16 * (TB * wave + b) < p_end;
+    }
+    const bool wave_live = blk_live[0];
     // A missing token reads row 0 (its output column is dropped).  Rows
     // at or beyond the adapter's live rank (and the padding of r to 16 NJT)
     // read row 0 -- lines this block loads anyway, so they cost no HBM
     // traffic -- and are zeroed when written to LDS.  (Their matrix ops still
     // run on the zeros: skipping them cost 7% on full-rank batches.)
-    const uint16_t* xrow = a.x + (int64_t)(tok_ok ? t : 0) * a.ldx;
+    const uint16_t* xrow[TB];
+#pragma unroll
+    for (int b = 0; b < TB; ++b) xrow[b] = a.x + (int64_t)(tok_ok[b] ? t[b] : 0) * a.ldx;
     const uint16_t* Al = a.A + (int64_t)l * a.r * a.H;
     const uint16_t* asrc[AL];
 #pragma unroll
@@ -180,22 +236,27 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
         *reinterpret_cast<u32x4*>(&s_a[(buf * RP + lrow + 16 * i) * kSkPitch + lcol]) = w;
       }
     };
-    auto gload_x = [&](int kb, u32x4* xr) {
+    auto gload_x = [&](int kb, u32x4 (*xr)[KS]) {
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        const int off = kb + 32 * kk + 8 * g;
-        if constexpr (VEC) {
-          const int oc = off < kend ? off : kend - 8;
-          xr[kk] = *reinterpret_cast<const u32x4*>(xrow + oc);
-        } else {
-          xr[kk] = tok_ok ? load8_16<false>(xrow + off, kend - off) : u32x4{0u, 0u, 0u, 0u};
+      for (int b = 0; b < TB; ++b) {
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          const int off = kb + 32 * kk + 8 * g;
+          if constexpr (VEC) {
+            const int oc = off < kend ? off : kend - 8;
+            xr[b][kk] = *reinterpret_cast<const u32x4*>(xrow[b] + oc);
+          } else {
+            xr[b][kk] = tok_ok[b] ? load8_16<false>(xrow[b] + off, kend - off) : u32x4{0u, 0u, 0u, 0u};
+          }
         }
       }
     };
 
-    f32x4 acc[NJT];
+    f32x4 acc[TB][NJT];
 #pragma unroll
-    for (int jt = 0; jt < NJT; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < TB; ++b)
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt) acc[b][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int nblk = kend > kbeg ? (kend - kbeg + kSkKB - 1) / kSkKB : 0;
     // The blocks of the chunk are walked in a rotated order that starts at
     // block (tile mod nblk).  The concurrent items otherwise read x at the
@@ -215,7 +276,7 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
 
     // One block: the next block's A and x go out first, then the ops of this
     // one from LDS (A) and registers (x).
-    auto block = [&](int b, u32x4* xcur, u32x4* xnext) {
+    auto block = [&](int b, u32x4 (*xcur)[KS], u32x4 (*xnext)[KS]) {
       const int buf = b & 1;
       const int kb = kb_of(b);
       const bool has_next = b + 1 < nblk;
@@ -230,11 +291,16 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
           // Elements past the chunk (last block only) are zero.
-          const u32x4 xop = (kb + 32 * kk + 8 * g < kend) ? xcur[kk] : u32x4{0u, 0u, 0u, 0u};
+          const bool in = kb + 32 * kk + 8 * g < kend;
 #pragma unroll
           for (int jt = 0; jt < NJT; ++jt) {
+            // One A operand from LDS feeds the ops of all TB token blocks.
             const u32x4 aop = *reinterpret_cast<const u32x4*>(as + jt * 16 * kSkPitch + 32 * kk);
-            acc[jt] = mfma16x16x32<DT>(aop, xop, acc[jt]);
+#pragma unroll
+            for (int bb = 0; bb < TB; ++bb) {
+              const u32x4 xop = in ? xcur[bb][kk] : u32x4{0u, 0u, 0u, 0u};
+              acc[bb][jt] = mfma16x16x32<DT>(aop, xop, acc[bb][jt]);
+            }
           }
         }
       }
@@ -242,7 +308,7 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
       __syncthreads();
     };
 
-    u32x4 xa[KS], xb[KS];
+    u32x4 xa[TB][KS], xb[TB][KS];
     if (nblk > 0) {
       gload_a(kb_of(0));
       gload_x(kb_of(0), xa);
@@ -254,16 +320,18 @@ __global__ __launch_bounds__(kShrinkThreads, NJT <= 4 ? 4 : 2) void shrink_kerne
       if (b + 1 < nblk) block(b + 1, xb, xa);
     }
 
-    // Lane (m, g) holds D[j = 16 jt + 4 g + e][token 16 wave + m].
-    if (wave_live && tok_ok) {
+    // Lane (m, g) holds D[j = 16 jt + 4 g + e][token 16 (TB wave + b) + m].
+#pragma unroll
+    for (int bb = 0; bb < TB; ++bb) {
+      if (!(blk_live[bb] && tok_ok[bb])) continue;
 #pragma unroll
       for (int jt = 0; jt < NJT; ++jt) {
         const int j0 = jt * 16 + 4 * g;
         if (ks == 1) {
-          store4<VEC>(a.v + (int64_t)t * a.ldv + j0, j0, a.r, acc[jt]);
+          store4<VEC>(a.v + (int64_t)t[bb] * a.ldv + j0, j0, a.r, acc[bb][jt]);
         } else {
-          float* part = a.partial + ((int64_t)ksi * a.seg.T + pos) * a.rp + j0;
-          *reinterpret_cast<f32x4*>(part) = acc[jt];
+          float* part = a.partial + ((int64_t)ksi * a.seg.T + pos[bb]) * a.rp + j0;
+          *reinterpret_cast<f32x4*>(part) = acc[bb][jt];
         }
       }
     }
@@ -319,29 +387,32 @@ size_t shrink_lds_bytes(int njt, int L) {
 }
 
 template <int DT, bool VEC, bool DENSE>
-hipError_t launch_typed(const ShrinkArgs& args, int njt, int grid, hipStream_t s) {
+hipError_t launch_typed(const ShrinkArgs& args, int njt, int tb, int grid, hipStream_t s) {
   const size_t lds = shrink_lds_bytes(njt, args.seg.L);
   switch (njt) {
     case 1:
-      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 1, DENSE>), dim3(grid), dim3(kShrinkThreads), lds, s, args);
+      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 1, DENSE, 1>), dim3(grid), dim3(kShrinkThreads), lds, s, args);
       break;
     case 2:
-      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 2, DENSE>), dim3(grid), dim3(kShrinkThreads), lds, s, args);
+      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 2, DENSE, 1>), dim3(grid), dim3(kShrinkThreads), lds, s, args);
       break;
     case 4:
-      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 4, DENSE>), dim3(grid), dim3(kShrinkThreads), lds, s, args);
+      if (tb == 2)
+        hipLaunchKernelGGL((shrink_kernel<DT, VEC, 4, DENSE, 2>), dim3(grid), dim3(kShrinkThreads), lds, s, args);
+      else
+        hipLaunchKernelGGL((shrink_kernel<DT, VEC, 4, DENSE, 1>), dim3(grid), dim3(kShrinkThreads), lds, s, args);
       break;
     default:
-      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 8, DENSE>), dim3(grid), dim3(kShrinkThreads), lds, s, args);
+      hipLaunchKernelGGL((shrink_kernel<DT, VEC, 8, DENSE, 1>), dim3(grid), dim3(kShrinkThreads), lds, s, args);
       break;
   }
   return hipGetLastError();
 }
 
 template <int DT, bool VEC>
-hipError_t launch_dense(const ShrinkArgs& args, int njt, int grid, hipStream_t s) {
-  return args.seg.dense ? launch_typed<DT, VEC, true>(args, njt, grid, s)
-                        : launch_typed<DT, VEC, false>(args, njt, grid, s);
+hipError_t launch_dense(const ShrinkArgs& args, int njt, int tb, int grid, hipStream_t s) {
+  return args.seg.dense ? launch_typed<DT, VEC, true>(args, njt, tb, grid, s)
+                        : launch_typed<DT, VEC, false>(args, njt, tb, grid, s);
 }
 
 }  // namespace
@@ -351,12 +422,21 @@ ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r, size_t ws_lim
   const int njt0 = (r + 15) / 16;
   p.jtw = njt0 <= 1 ? 1 : njt0 <= 2 ? 2 : njt0 <= 4 ? 4 : 8;  // rank tiles (template)
   p.rp = 16 * p.jtw;
-  const int64_t tiles = max_token_tiles(T, L, kSkTile);
+  // 16-token blocks per wave: two at r = 33..64 from 4096 tokens up (tiles
+  // of 128 tokens, each A operand read from LDS feeding two matrix ops: half
+  // the A traffic and LDS reads per x byte).  Measured on MI355X, each call
+  // alone (64-token tiles -> 128-token tiles at their best split): the
+  // 8192-token layer 50.5 -> 48.2 us, 8192 x 16384 one adapter 74.9 -> 62.3,
+  // over four segments 81.8 -> 73.6, 8192 x 4096 32.7 -> 28.3; but 512 x
+  // 4096 12.4 -> 14.6 (fewer, longer items).
+  p.tb = (p.jtw == 4 && ((tuning().shrink_tb == 0 && T >= 4096) || tuning().shrink_tb == 2)) ? 2 : 1;
+  const int64_t tt = (int64_t)kSkTile * p.tb;
+  const int64_t tiles = max_token_tiles(T, L, tt);
   p.max_tiles = (int32_t)tiles;
   // Persistent workgroups: as many as are resident at once (LDS and register
   // bound: four per CU up to r = 64, two beyond).
   int64_t per_cu = (int64_t)(160 * 1024 / shrink_lds_bytes(p.jtw, L));
-  const int64_t reg_cu = p.jtw <= 4 ? 4 : 2;
+  const int64_t reg_cu = shrink_wgs_per_cu(p.jtw, p.tb);
   per_cu = per_cu < 1 ? 1 : (per_cu > reg_cu ? reg_cu : per_cu);
   const int64_t resident = 256 * per_cu;
   p.resident = (int32_t)resident;
@@ -386,14 +466,32 @@ ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r, size_t ws_lim
   // The kernel may raise the split up to what the fewest tiles T tokens can
   // make (all of them in 64-token tiles) would take: about one round of
   // resident workgroups' partial rows, whatever T.
-  int64_t ks_cap = split_for(T > 0 ? ((int64_t)T + kSkTile - 1) / kSkTile : 0);
+  int64_t ks_cap = split_for(T > 0 ? ((int64_t)T + tt - 1) / tt : 0);
+  const int64_t row_bytes = (int64_t)T * p.rp * 4;
+  if (p.tb == 2) {
+    // By the CUs' share of the blocks (see split_by_cu); every split it can
+    // take has tiles * ks <= per_cu * 256, so the fewest tiles bound it.  A
+    // caller's workspace limit bounds it too.
+    int64_t lim = ks_max;
+    if (row_bytes > 0 && ws_limit > kShrinkWsHeader) {
+      const int64_t fit = (int64_t)((ws_limit - kShrinkWsHeader) / (size_t)row_bytes);
+      lim = fit < lim ? (fit < 1 ? 1 : fit) : lim;
+    }
+    int ch = 0;
+    ks = split_by_cu((int)(tiles < INT32_MAX ? tiles : INT32_MAX), H, (int)lim, (int)per_cu, &ch);
+    const int64_t n_min = T > 0 ? ((int64_t)T + tt - 1) / tt : 1;
+    ks_cap = per_cu * 256 / n_min;
+    ks_cap = ks_cap > lim ? lim : (ks_cap < 1 ? 1 : ks_cap);
+    if (ks_cap < ks) ks_cap = ks;
+  }
+  p.fixed = 0;
   if (tuning().shrink_ksplit > 0) {
+    p.fixed = 1;
     const int64_t want = tuning().shrink_ksplit;
     const int64_t chunk = ((H + want - 1) / want + kSkKB - 1) / kSkKB * kSkKB;
     ks = (H + chunk - 1) / chunk;
     ks_cap = ks;  // a fixed split, as set
   }
-  const int64_t row_bytes = (int64_t)T * p.rp * 4;
   if (ks_cap > ks && row_bytes > 0 && ws_limit > kShrinkWsHeader) {
     const int64_t fit = (int64_t)((ws_limit - kShrinkWsHeader) / (size_t)row_bytes);
     if (ks_cap > fit) ks_cap = fit;
@@ -403,8 +501,8 @@ ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r, size_t ws_lim
   p.ks_cap = (int32_t)ks_cap;
   p.kchunk = (int32_t)(((H + ks - 1) / ks + kSkKB - 1) / kSkKB * kSkKB);
   p.partial_bytes = ks_cap > 1 ? kShrinkWsHeader + (size_t)(ks_cap * row_bytes) : 0;
-  // Every resident workgroup is launched when the kernel may raise the split.
-  const int64_t items = ks_cap > ks ? resident : tiles * ks;
+  // Every resident workgroup is launched when the kernel may change the split.
+  const int64_t items = (ks_cap > ks || (p.tb == 2 && !p.fixed && ks_cap > 1)) ? resident : tiles * ks;
   int64_t grid = items < resident ? items : resident;
   grid = (grid + 7) / 8 * 8;
   if (grid < 8) grid = 8;
@@ -433,16 +531,24 @@ hipError_t launch_shrink(const SegView& seg, const uint16_t* x, int64_t ldx, con
   a.resident = plan.resident;
   a.kchunk = plan.kchunk;
   a.rp = plan.rp;
+  a.fixed = plan.fixed;
   hipError_t e;
   if (dtype == 0)
-    e = vec ? launch_dense<0, true>(a, plan.jtw, plan.grid, s) : launch_dense<0, false>(a, plan.jtw, plan.grid, s);
+    e = vec ? launch_dense<0, true>(a, plan.jtw, plan.tb, plan.grid, s)
+            : launch_dense<0, false>(a, plan.jtw, plan.tb, plan.grid, s);
   else
-    e = vec ? launch_dense<1, true>(a, plan.jtw, plan.grid, s) : launch_dense<1, false>(a, plan.jtw, plan.grid, s);
+    e = vec ? launch_dense<1, true>(a, plan.jtw, plan.tb, plan.grid, s)
+            : launch_dense<1, false>(a, plan.jtw, plan.tb, plan.grid, s);
   if (e != hipSuccess || !split) return e;
   int64_t blocks = ((int64_t)seg.T * (plan.rp / 4) + 255) / 256;
   if (blocks > 1024) blocks = 1024;
   if (blocks < 1) blocks = 1;
-  const int32_t ks_fixed = plan.ks_cap == plan.ksplit ? plan.ksplit : 0;
+  // The split is known here only when the kernel cannot change it: with
+  // 64-token tiles when the workspace holds no more chunks than the host's
+  // split, with 128-token tiles (re-planned from the true tile count in
+  // every call) only when an override fixes it or nothing is split.
+  const bool kernel_may_change = plan.tb == 2 ? (!plan.fixed && plan.ks_cap > 1) : plan.ks_cap > plan.ksplit;
+  const int32_t ks_fixed = kernel_may_change ? 0 : plan.ksplit;
   if (vec)
     hipLaunchKernelGGL((shrink_reduce_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, s, seg,
                        a.partial, a.ks_out, ks_fixed, plan.ks_cap, plan.rp, r, v, ldv);

@@ -131,7 +131,10 @@ def test_workspace_size_is_zero_when_not_split():
 
 
 @pytest.mark.parametrize("T,L,H,r,ks_cap,rp", [
-    (8192, 64, 8192, 64, 8, 64),    # 128 tiles at the fewest: 8 chunks fill 1024 workgroups
+    (8192, 64, 8192, 64, 12, 64),   # r = 64 from 4096 tokens: 128-token tiles, 64 at the fewest,
+                                    # 3 workgroups per CU: up to 12 chunks
+    (2048, 4, 8192, 64, 16, 64),    # r = 64 below 4096 tokens: 64-token tiles, 32 at the fewest,
+                                    # capped at 16 chunks (512-wide)
     (16384, 4, 4096, 16, 4, 16),    # 256 tiles: 4 chunks
     (32768, 4, 4096, 16, 2, 16),    # 512 tiles: 2 chunks
     (8192, 4, 4096, 128, 4, 128),   # rank 128 holds 512 workgroups: 128 tiles take 4 chunks
@@ -142,8 +145,10 @@ def test_workspace_size_is_zero_when_not_split():
 def test_shrink_split_fills_one_round(T, L, H, r, ks_cap, rp):
     """The workspace holds a 256-byte header and ks_cap chunks of fp32
     partial rows (rp = r padded to a rank tile): the most chunks the kernel
-    may choose, the split that the fewest tiles of T tokens (all in 64-token
-    tiles) would take to fill one round of resident workgroups."""
+    may choose.  With 64-token tiles that is the split the fewest tiles of T
+    tokens would take to fill one round of resident workgroups; with
+    128-token tiles (r = 33..64 from 4096 tokens), the most chunks that keep
+    the fewest tiles' items within the resident workgroups."""
     assert lsb.lora_shrink_workspace_bytes(T, L, H, r) == 256 + ks_cap * T * rp * 4
 
 
@@ -225,7 +230,9 @@ def test_noalloc_shrink_rejects_splits_beyond_its_scratch():
     """lora_shrink_noalloc refuses, before anything is launched or looked up
     on a device, a shrink whose H split needs more than the static scratch."""
     lib = lsb.lib()
-    T, L, H, r = 16392, 4, 8192, 64
+    # rank 128 (64-token tiles): 65 tiles at the bound take 8 chunks of
+    # 4096 x 128 fp32 partial rows, 256 bytes past 16 MiB with the header
+    T, L, H, r = 4096, 1, 8192, 128
     assert lsb.lora_shrink_workspace_bytes(T, L, H, r) > lsb.LORA_NOALLOC_SCRATCH_BYTES
     s = _seg(T=T, L=L)
     prev = lib.lora_set_path(2)

@@ -491,6 +491,31 @@ def test_shrink_repeatable_and_workspace_reuse(force_path):
     assert np.array_equal(res[0], res[2])
 
 
+@pytest.mark.parametrize("dtype,T,H,r,L,sl", [
+    ("bf16", 4096, 8192, 64, 16, (1, 200)),   # the host's split equals what the workspace holds
+    ("f16", 5000, 4096, 48, 5, (1, 600)),
+    ("bf16", 6000, 2048, 64, 40, (1, 300)),
+])
+def test_shrink_128_token_tiles_every_row(dtype, T, H, r, L, sl):
+    """The shrink at r = 33..64 from 4096 tokens (128-token tiles, the H split
+    chosen in the kernel from the true tile count): every active row against
+    the oracle, with a workspace that starts full of garbage, so a reduce that
+    summed chunks the kernel did not write would show."""
+    _announce(f"shrink, 128-token tiles: {dtype} T={T} H={H} r={r} L={L}")
+    w = W.make("tb2", dtype, T, H, r, L, [[64]], seed=T + H + r, seq_len=sl, neg_frac=0.1)
+    ids = torch.from_numpy(w.ids).cuda()
+    seg = lsb.lora_build_segments(ids, w.L)
+    need = lsb.lora_shrink_workspace_bytes(T, L, H, r)
+    ws = torch.from_numpy(np.random.default_rng(T).integers(0, 256, need, dtype=np.uint8)).cuda()
+    v = sentinel_v(T, r)
+    lsb.lora_shrink(dev_bits(w.x, dtype), dev_bits(w.A, dtype), seg, v, workspace=ws)
+    torch.cuda.synchronize()
+    act = w.active
+    v_or = oracle.shrink(dtype, w.x, w.A, w.ids)
+    assert tol_ratio(v.cpu().numpy()[act].astype(np.float64), v_or[act]) <= 1
+    assert np.all(v.cpu().numpy().view(np.uint32)[~act] == V_SENTINEL)
+
+
 WIDE_V_CASES = [
     # dtype, r, n, path: each expand kernel form (per-token aligned r = 16 / 64,
     # per-token general, tiles at r <= 16, 64, 128, tiles on the scalar path)
@@ -625,6 +650,12 @@ PLAN_VARIANTS = [
     ({"LORA_SHRINK_KSPLIT": "1"}, "sgmv", "f16", 300, 1408, 16, 5, [[256]]),
     ({"LORA_SHRINK_KSPLIT": "3"}, "sgmv", "bf16", 300, 2000, 40, 5, [[256]]),
     ({"LORA_SHRINK_KSPLIT": "2"}, "sgmv", "bf16", 260, 1152, 128, 4, [[128]]),
+    # 128-token shrink tiles at r = 33..64 (two 16-token blocks per wave):
+    # ragged tiles, split and unsplit H, the element-wise path
+    ({"LORA_SHRINK_TB": "2"}, "sgmv", "bf16", 700, 2048, 64, 5, [[512]]),
+    ({"LORA_SHRINK_TB": "2", "LORA_SHRINK_KSPLIT": "1"}, "sgmv", "f16", 300, 1024, 48, 4, [[256]]),
+    ({"LORA_SHRINK_TB": "2", "LORA_SHRINK_KSPLIT": "3"}, "sgmv", "bf16", 500, 4096, 64, 9, [[1024]]),
+    ({"LORA_SHRINK_TB": "2"}, "sgmv", "f16", 200, 2001, 40, 3, [[256]]),
     ({"LORA_EXPAND_TB": "2"}, "sgmv", "bf16", 700, 1024, 64, 5, [[2048, 512]]),
     ({"LORA_EXPAND_TB": "2"}, "sgmv", "f16", 300, 1024, 16, 3, [[1000]]),
     ({"LORA_EXPAND_TB": "2"}, "sgmv", "bf16", 300, 512, 128, 3, [[384]]),

@@ -1,7 +1,9 @@
 """lora_shrink_noalloc (the shrink whose H-split partial rows go to the
 library's static device scratch, for callers that cannot allocate) against
-lora_shrink with a workspace: identical bits, on two calls in a row, the
-second with a smaller batch, and both within the oracle's tolerance."""
+lora_shrink with a workspace, on calls in a row, the later ones smaller:
+identical bits where the workspace holds no more chunks of the H split than
+the scratch does (both calls then take the same split), else the same
+within the tolerance, and both within the oracle's tolerance."""
 import numpy as np
 import pytest
 import torch
@@ -42,8 +44,16 @@ def test_noalloc_shrink_matches_workspace_shrink():
         torch.cuda.synchronize()
         a = v_ws.cpu().numpy().view(np.uint32)
         b = v_na.cpu().numpy().view(np.uint32)
-        assert np.array_equal(a, b)
         act = w.active
+        if need <= lsb.LORA_NOALLOC_SCRATCH_BYTES:
+            # the same bound on the split: the same split, the same bits
+            assert np.array_equal(a, b)
+        else:
+            # the scratch holds fewer chunks than the workspace, so the kernel
+            # may take another split: the sums differ by rounding only
+            assert np.array_equal(a[~act], b[~act])
+            assert tol_ratio(v_na.cpu().numpy()[act].astype(np.float64),
+                             v_ws.cpu().numpy()[act].astype(np.float64)) <= 1
         assert np.all(b[~act] == V_SENTINEL)
         v_or = oracle.shrink(dtype, w.x, w.A, w.ids)
         assert tol_ratio(v_na.cpu().numpy()[act].astype(np.float64), v_or[act]) <= 1
