@@ -136,11 +136,11 @@ int lora_build_segments(const int32_t *token_lora, int32_t T, int32_t L, lora_se
  * size H and rank r (0 if it needs none).  Only batches with too few token
  * tiles to occupy the GPU split the H-sum across workgroups; the workspace
  * then holds a 256-byte header (the split the kernel chose) and one fp32
- * partial row per token and H chunk, for as many chunks as the fewest tiles
- * of T tokens would take.  The host sees only an upper bound on the tiles
- * (one partial tile per adapter of the pool); the kernel sets the split from
- * the true count, so a batch that uses few adapters of a large pool still
- * fills the GPU. */
+ * partial row per token and H chunk, for as many chunks as the kernel may
+ * choose for the fewest tiles T tokens can make.  The host sees only an
+ * upper bound on the tiles (one partial tile per adapter of the pool); the
+ * kernel sets the split from the true count, so a batch that uses few
+ * adapters of a large pool still fills the GPU. */
 size_t lora_shrink_workspace_bytes(int32_t T, int32_t L, int32_t H, int32_t r);
 
 /* Shrink (micro-benchmark PR: bgmv_shrink / sgmv_shrink; TPU PR: the
