@@ -422,14 +422,15 @@ ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r, size_t ws_lim
   const int njt0 = (r + 15) / 16;
   p.jtw = njt0 <= 1 ? 1 : njt0 <= 2 ? 2 : njt0 <= 4 ? 4 : 8;  // rank tiles (template)
   p.rp = 16 * p.jtw;
-  // 16-token blocks per wave: two at r = 33..64 from 4096 tokens up (tiles
-  // of 128 tokens, each A operand read from LDS feeding two matrix ops: half
-  // the A traffic and LDS reads per x byte).  Measured on MI355X, each call
-  // alone (64-token tiles -> 128-token tiles at their best split): the
-  // 8192-token layer 50.5 -> 48.2 us, 8192 x 16384 one adapter 74.9 -> 62.3,
-  // over four segments 81.8 -> 73.6, 8192 x 4096 32.7 -> 28.3; but 512 x
-  // 4096 12.4 -> 14.6 (fewer, longer items).
-  p.tb = (p.jtw == 4 && ((tuning().shrink_tb == 0 && T >= 4096) || tuning().shrink_tb == 2)) ? 2 : 1;
+  // 16-token blocks per wave: two at r = 33..64 from 4096 tokens and H =
+  // 2048 up (tiles of 128 tokens, each A operand read from LDS feeding two
+  // matrix ops: half the A traffic and LDS reads per x byte).  Measured on
+  // MI355X, each call alone (64-token tiles -> 128-token tiles at their best
+  // split): the 8192-token layer 50.5 -> 48.2 us, 8192 x 16384 one adapter
+  // 74.9 -> 62.3, over four segments 81.8 -> 73.6, 8192 x 4096 32.7 -> 28.3;
+  // but 512 x 4096 12.4 -> 14.6 (fewer, longer items) and 8192 x 1024
+  // 17.0 -> 17.7 (two chunks at most).
+  p.tb = (p.jtw == 4 && ((tuning().shrink_tb == 0 && T >= 4096 && H >= 2048) || tuning().shrink_tb == 2)) ? 2 : 1;
   const int64_t tt = (int64_t)kSkTile * p.tb;
   const int64_t tiles = max_token_tiles(T, L, tt);
   p.max_tiles = (int32_t)tiles;
