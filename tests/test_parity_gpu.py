@@ -495,6 +495,8 @@ def test_shrink_repeatable_and_workspace_reuse(force_path):
     ("bf16", 4096, 8192, 64, 16, (1, 200)),   # the host's split equals what the workspace holds
     ("f16", 5000, 4096, 48, 5, (1, 600)),
     ("bf16", 6000, 2048, 64, 40, (1, 300)),
+    ("f16", 4096, 2048, 40, 7, (1, 100)),     # the smallest batch and H that take 128-token tiles
+    ("bf16", 4500, 4096, 64, 600, (1, 60)),   # a pool of 600 adapters: lazy tile table
 ])
 def test_shrink_128_token_tiles_every_row(dtype, T, H, r, L, sl):
     """The shrink at r = 33..64 from 4096 tokens (128-token tiles, the H split
@@ -514,6 +516,21 @@ def test_shrink_128_token_tiles_every_row(dtype, T, H, r, L, sl):
     v_or = oracle.shrink(dtype, w.x, w.A, w.ids)
     assert tol_ratio(v.cpu().numpy()[act].astype(np.float64), v_or[act]) <= 1
     assert np.all(v.cpu().numpy().view(np.uint32)[~act] == V_SENTINEL)
+
+
+def test_single_adapter_shrink_128_token_tiles():
+    """lora_shrink_single (no metadata) at r = 64, 8192 tokens: the dense form
+    of the 128-token-tile kernel, every row against the oracle."""
+    _announce("single-adapter shrink, 128-token tiles: f16 T=8192 H=2048 r=64")
+    T, H, r = 8192, 2048, 64
+    w = W.make("single_tb2", "f16", T, H, r, 1, [[64]], seed=77)
+    x = dev_bits(w.x, "f16")
+    A = dev_bits(w.A, "f16")[0]
+    v = sentinel_v(T, r)
+    lsb.lora_shrink_single(x, A, v)
+    torch.cuda.synchronize()
+    v_or = oracle.shrink("f16", w.x, w.A, np.zeros(T, np.int32))
+    assert tol_ratio(v.cpu().numpy().astype(np.float64), v_or) <= 1
 
 
 WIDE_V_CASES = [
