@@ -13,6 +13,10 @@
 //    row) is loaded cooperatively one block ahead and written to a
 //    double-buffered LDS tile (row pitch 288 B, see kSkPitch), so A_l is read
 //    from L2 once per 64 tokens.
+// At r = 33..64 from 4096 tokens and H = 2048 (TB = 2), tiles hold 128
+// tokens: wave w takes tokens 32w..32w+31 as two blocks of 16, and each A
+// operand read from LDS feeds both blocks' ops (half the A reads per x byte;
+// three workgroups per CU for the registers).
 // Loads are unconditional (addresses clamped into the chunk): values past the
 // end of the chunk are zeroed where they are used, so the compiler can count
 // the loads in flight exactly.  LDS holds only A and the tile table, which
@@ -29,7 +33,9 @@
 // the split leaves most of the GPU idle; every workgroup then recomputes ks
 // from the true tile count (the same value in all of them), up to the number
 // of chunks the workspace holds, and workgroup 0 leaves it in the workspace
-// header for the reduce kernel.
+// header for the reduce kernel.  With 128-token tiles the kernel always
+// chooses ks itself, from the true tile count, by the CUs' share of the work
+// (split_by_cu).
 #include "lora_device.h"
 #include "lora_kernels.h"
 #include "tiles.h"
@@ -340,9 +346,9 @@ __global__ __launch_bounds__(kShrinkThreads, shrink_wgs_per_cu(NJT, TB)) void sh
 
 // v[t, :r] = sum over the ks chunks of the partial rows, in chunk order (ks
 // as the shrink kernel left it in the workspace header, or ks_fixed when the
-// host's split is the most the workspace holds, so the kernel cannot have
-// raised it: then the partial rows' loads need not wait for the header;
-// nothing to do when the shrink kernel wrote v itself).
+// kernel cannot have changed the host's split: then the partial rows' loads
+// need not wait for the header; nothing to do when the shrink kernel wrote v
+// itself).
 // Every load of a row -- the active count, its token, eight partial rows at a
 // time -- goes out before any of them is checked, so a reduction of up to
 // eight chunks is one memory trip; positions past the active tokens (whose
@@ -435,7 +441,8 @@ ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r, size_t ws_lim
   const int64_t tiles = max_token_tiles(T, L, tt);
   p.max_tiles = (int32_t)tiles;
   // Persistent workgroups: as many as are resident at once (LDS and register
-  // bound: four per CU up to r = 64, two beyond).
+  // bound: four per CU up to r = 64 with 64-token tiles, three with 128-token
+  // tiles, two at r = 128).
   int64_t per_cu = (int64_t)(160 * 1024 / shrink_lds_bytes(p.jtw, L));
   const int64_t reg_cu = shrink_wgs_per_cu(p.jtw, p.tb);
   per_cu = per_cu < 1 ? 1 : (per_cu > reg_cu ? reg_cu : per_cu);
@@ -464,9 +471,9 @@ ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r, size_t ws_lim
     return (H + chunk - 1) / chunk;
   };
   int64_t ks = split_for(tiles);
-  // The kernel may raise the split up to what the fewest tiles T tokens can
-  // make (all of them in 64-token tiles) would take: about one round of
-  // resident workgroups' partial rows, whatever T.
+  // With 64-token tiles the kernel may raise the split up to what the fewest
+  // tiles T tokens can make (all of them in whole tiles) would take: about
+  // one round of resident workgroups' partial rows, whatever T.
   int64_t ks_cap = split_for(T > 0 ? ((int64_t)T + tt - 1) / tt : 0);
   const int64_t row_bytes = (int64_t)T * p.rp * 4;
   if (p.tb == 2) {
