@@ -1123,41 +1123,47 @@ def test_decode_prefill_mix_schedules(monkeypatch, tuning_from_env, case, balanc
     check_outside_slices(forced)
 
 
-@pytest.mark.parametrize("dtype,n,r", [("f16", 4096, 64), ("bf16", 16384, 16)])
-def test_expand_balanced_choice_at_size(monkeypatch, tuning_from_env, dtype, n, r):
+@pytest.mark.parametrize("dtype,widths,r", [("f16", [4096], 64), ("bf16", [16384], 16),
+                                           ("bf16", [16384, 4096], 64)])
+def test_expand_balanced_choice_at_size(monkeypatch, tuning_from_env, dtype, widths, r):
     """8192 tokens over four sorted segments of 1952-2288 tokens (66 token
     tiles of 128 against 64 for aligned ones): the tile expand takes balanced
-    ranges by itself here.  Its result is bit for bit the forced round-robin
-    one, and sampled rows (first and last of every segment, and random ones)
-    match the oracle."""
-    _announce(f"expand, balanced ranges chosen at 8192 tokens: {dtype} n={n} r={r}")
+    ranges by itself here, also over two slices, whose runs the ranges cross.
+    Its result is bit for bit the forced round-robin one, and sampled rows
+    (first and last of every segment, and random ones) match the oracle in
+    every slice."""
+    _announce(f"expand, balanced ranges chosen at 8192 tokens: {dtype} slices={widths} r={r}")
     T, L = 8192, 4
     ids_np = W.sweep_point("sgmv", T, 8, 8, L=L).ids
     counts = np.bincount(ids_np, minlength=L)
     assert sum(-(-int(c) // 128) for c in counts) == 66
     tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    n = sum(widths)
+    offs = [int(o) for o in np.cumsum([0] + widths[:-1])]
     gen = torch.Generator(device="cuda")
     gen.manual_seed(n + r)
     v = torch.randn(T, r, generator=gen, device="cuda")
-    B = (torch.randn(L, n, r, generator=gen, device="cuda") / math.sqrt(r)).to(tdt)
+    Bs = [(torch.randn(L, wd, r, generator=gen, device="cuda") / math.sqrt(r)).to(tdt) for wd in widths]
     y0 = torch.randn(T, n, generator=gen, device="cuda").to(tdt)
     seg = lsb.lora_build_segments(torch.from_numpy(ids_np).cuda(), L)
     y_auto = y0.clone()
-    lsb.lora_expand(v, B, seg, y_auto, True)
+    lsb.lora_expand_slice(v, Bs, offs, seg, y_auto, True)
     monkeypatch.setenv("LORA_EXPAND_BALANCE", "1")
     tuning_from_env()
     y_rr = y0.clone()
-    lsb.lora_expand(v, B, seg, y_rr, True)
+    lsb.lora_expand_slice(v, Bs, offs, seg, y_rr, True)
     torch.cuda.synchronize()
     assert torch.equal(y_auto.view(torch.int16), y_rr.view(torch.int16))
     starts = np.concatenate([[0], np.cumsum(counts)])
     rows = np.unique(np.concatenate([starts[:-1], starts[1:] - 1,
                                      np.random.default_rng(r).choice(T, 128, replace=False)])).astype(np.int64)
     ridx = torch.from_numpy(rows).cuda()
-    ref = oracle.expand(dtype, v.index_select(0, ridx).cpu().numpy().astype(np.float64), host_bits(B),
-                        ids_np[rows], host_bits(y0.index_select(0, ridx)), 0, True)
+    v_rows = v.index_select(0, ridx).cpu().numpy().astype(np.float64)
+    y0_rows = host_bits(y0.index_select(0, ridx))
     got = decode(host_bits(y_auto.index_select(0, ridx)), dtype)
-    assert tol_ratio(got, ref) <= 1
+    for B, off, wd in zip(Bs, offs, widths):
+        ref = oracle.expand(dtype, v_rows, host_bits(B), ids_np[rows], y0_rows, off, True)
+        assert tol_ratio(got[:, off:off + wd], ref) <= 1
 
 
 def test_decode_prefill_mix_graph_replays():
