@@ -200,6 +200,15 @@ __global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) voi
   // range (balanced).
   int cur, end;
   if (balanced) {
+    // A range breaks at run boundaries, so longer runs leave fewer item
+    // set-ups per workgroup; but a run longer than one XCD's share of the
+    // units (chunks / 8 per tile) splits each run's tiles over two XCDs, and
+    // that measured far slower (8192 x 16384 over four segments, r = 64:
+    // runs of 4 / 16 / 32 chunks 129.8 / 118.9 / 177.3 us; 8192 x 4096:
+    // runs of 4 / 8 40.1 / 51.3).  So the runs double while they fit.
+    if (!a.cpr_fixed) {
+      while (2 * (int64_t)cpr <= (chunks >> 3)) cpr *= 2;
+    }
     const int w = (grid & 7) == 0 ? (blockIdx.x & 7) * (grid >> 3) + (blockIdx.x >> 3) : blockIdx.x;
     cur = (int)(units * w / grid);
     end = (int)(units * (w + 1) / grid);
