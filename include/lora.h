@@ -134,7 +134,9 @@ int lora_build_segments(const int32_t *token_lora, int32_t T, int32_t L, lora_se
 
 /* Workspace bytes that lora_shrink needs for T tokens, L adapters, hidden
  * size H and rank r (0 if it needs none).  Only batches with too few token
- * tiles to occupy the GPU split the H-sum across workgroups; the workspace
+ * tiles to occupy the GPU split the H-sum across workgroups (mid-size
+ * batches at r <= 32 and small H split it across the waves of one workgroup
+ * instead, and need none); the workspace
  * then holds a 256-byte header (the split the kernel chose) and one fp32
  * partial row per token and H chunk, for as many chunks as the kernel may
  * choose for the fewest tiles T tokens can make.  The host sees only an

@@ -122,6 +122,7 @@ lora::Tuning read_tuning() {
   t.expand_wgs_per_cu = read_env_int("LORA_EXPAND_WGS_PER_CU");
   t.expand_balance = read_env_int("LORA_EXPAND_BALANCE");
   t.shrink_tb = read_env_int("LORA_SHRINK_TB");
+  t.shrink_group = read_env_int("LORA_SHRINK_GROUP");
   return t;
 }
 

@@ -25,8 +25,10 @@ constexpr int kShrinkKStep = 128;
 // environment once when the library is loaded (and again on
 // lora_reload_tuning): LORA_SHRINK_KSPLIT, LORA_EXPAND_TB, LORA_EXPAND_CPR,
 // LORA_EXPAND_WGS_PER_CU, LORA_EXPAND_BALANCE (1 round-robin items, 2 balanced
-// ranges), LORA_SHRINK_TB (2: 128-token shrink tiles at r = 33..64), LORA_BGMV_SHRINK_RT, LORA_BGMV_RPI, LORA_BGMV_CB.  0 = not set: the
-// launchers' own choice.
+// ranges), LORA_SHRINK_TB (2: 128-token shrink tiles at r = 33..64),
+// LORA_SHRINK_GROUP (1: 16-token groups with the H split inside the
+// workgroup at r <= 32, 2: never), LORA_BGMV_SHRINK_RT, LORA_BGMV_RPI,
+// LORA_BGMV_CB.  0 = not set: the launchers' own choice.
 struct Tuning {
   int shrink_ksplit;
   int expand_tb;
@@ -37,6 +39,7 @@ struct Tuning {
   int expand_wgs_per_cu;
   int expand_balance;
   int shrink_tb;
+  int shrink_group;
 };
 const Tuning& tuning();
 void reload_tuning();
@@ -62,6 +65,7 @@ hipError_t launch_build_segments(const int32_t* token_lora, int32_t T, int32_t L
 struct ShrinkPlan {
   int32_t jtw;          // 16-row tiles of r per wave (1, 2, 4 or 8)
   int32_t tb;           // 16-token blocks per wave (tiles of 64 tb tokens)
+  int32_t group;        // 1: 16-token groups, H split inside the workgroup (no workspace)
   int32_t fixed;        // 1: the split is set by an override (the kernel keeps it)
   int32_t rp;           // rank padded to the rank groups
   int32_t ksplit;       // number of H chunks split across workgroups (from the tile bound)

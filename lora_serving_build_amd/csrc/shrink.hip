@@ -344,6 +344,139 @@ __global__ __launch_bounds__(kShrinkThreads, shrink_wgs_per_cu(NJT, TB)) void sh
   }
 }
 
+// 16-token groups with the H split inside the workgroup (r <= 32).  Item =
+// one 16-token tile of a segment; its eight waves take the 256-element blocks
+// of H in turn (wave w: blocks w, w + 8, ...), each streaming its blocks of x
+// and of the adapter's A rows straight into matrix-op operands (no wave
+// shares a weight block, so nothing is staged in LDS), one block ahead.  The
+// eight partial sums meet in LDS and are added in wave order, so v is written
+// in the same launch: no partial rows, no workspace, no reduce launch.  For
+// mid-size batches, where the tile kernel's H split pays a second launch and a
+// chain of memory trips per item.
+constexpr int kGrpThreads = 512;
+constexpr int kGrpWaves = kGrpThreads / kWave;
+constexpr int kGrpKB = 256;  // H elements per wave block
+
+template <int NJT>
+struct GroupLds {
+  static constexpr size_t red_bytes = (size_t)kGrpWaves * NJT * kWave * 16;
+  // the partial sums, then the tile table and the scan's scratch (one int per
+  // wave and the total)
+  static size_t bytes(int L) { return red_bytes + 4 * ((size_t)tile_table_ints(L) + kGrpWaves + 1); }
+};
+
+template <int DT, bool VEC, int NJT, bool DENSE>
+__global__ __launch_bounds__(kGrpThreads) void shrink_group_kernel(ShrinkArgs a) {
+  constexpr int KS = kGrpKB / 32;  // 32-wide k steps per block
+  extern __shared__ __align__(16) unsigned char smem[];
+  f32x4* s_red = reinterpret_cast<f32x4*>(smem);  // [wave][NJT][lane]
+  int32_t* s_table = reinterpret_cast<int32_t*>(smem + GroupLds<NJT>::red_bytes);
+  int32_t* s_scan = s_table + tile_table_ints(a.seg.L);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int m = lane & 15;  // token of the tile / row of A inside a 16-row tile
+  const int g = lane >> 4;  // which 8 of the 32 elements of an op
+
+  const TileTable table =
+      build_tile_table<kGrpThreads, DENSE>(a.seg, 16, a.r, s_table, s_scan, a.min_seg_len);
+  const int tiles = table.tiles;
+  const int grid = gridDim.x;
+  const int nb = (a.H + kGrpKB - 1) / kGrpKB;
+  const int nbw = wave < nb ? (nb - 1 - wave) / kGrpWaves + 1 : 0;  // blocks of this wave
+
+  for (int item = xcd_first_item(blockIdx.x, grid, tiles); item < tiles; item += grid) {
+    int p0 = 0, p_end = 0, l = 0, rank_l = 0;
+    const bool ok = tile_range_lds(table, a.seg.T, a.seg.L, 16, item, &p0, &p_end, &l, &rank_l);
+    const int pos = p0 + m;
+    int t = (ok && pos < p_end) ? (DENSE ? pos : a.seg.sorted_token[pos]) : -1;
+    t = (t >= 0 && t < a.seg.T) ? t : -1;
+    const bool tok_ok = t >= 0;
+    // A missing token reads row 0 and a rank row at or past the live rank
+    // reads the adapter's row 0; their outputs are dropped or zeroed below.
+    const uint16_t* xrow = a.x + (int64_t)(tok_ok ? t : 0) * a.ldx;
+    const uint16_t* Al = a.A + (int64_t)(ok ? l : 0) * a.r * a.H;
+    const uint16_t* arow[NJT];
+    bool row_ok[NJT];
+#pragma unroll
+    for (int jt = 0; jt < NJT; ++jt) {
+      const int j = 16 * jt + m;
+      row_ok[jt] = ok && j < rank_l;
+      arow[jt] = Al + (int64_t)(row_ok[jt] ? j : 0) * a.H;
+    }
+    // Block i of this wave (i may be past its last block: the prefetch after
+    // the last one reads clamped addresses and is dropped).
+    auto gload = [&](int i, u32x4* xr, u32x4 (*ar)[KS]) {
+      const int kb = (wave + kGrpWaves * i) * kGrpKB;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const int off = kb + 32 * kk + 8 * g;
+        if constexpr (VEC) {
+          const int oc = off < a.H ? off : a.H - 8;  // H is a multiple of 8 here
+          xr[kk] = *reinterpret_cast<const u32x4*>(xrow + oc);
+#pragma unroll
+          for (int jt = 0; jt < NJT; ++jt) ar[jt][kk] = *reinterpret_cast<const u32x4*>(arow[jt] + oc);
+        } else {
+          xr[kk] = tok_ok ? load8_16<false>(xrow + off, a.H - off) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int jt = 0; jt < NJT; ++jt)
+            ar[jt][kk] = row_ok[jt] ? load8_16<false>(arow[jt] + off, a.H - off) : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    };
+    f32x4 acc[NJT];
+#pragma unroll
+    for (int jt = 0; jt < NJT; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int i, const u32x4* xr, const u32x4 (*ar)[KS]) {
+      const int kb = (wave + kGrpWaves * i) * kGrpKB;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        // Elements past H (the last block) are zero.
+        const bool in = kb + 32 * kk + 8 * g < a.H;
+        const u32x4 xop = in ? xr[kk] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt) acc[jt] = mfma16x16x32<DT>(ar[jt][kk], xop, acc[jt]);
+      }
+    };
+    if (nbw > 0) {
+      u32x4 x0[KS], x1[KS], a0[NJT][KS], a1[NJT][KS];
+      gload(0, x0, a0);
+      for (int i = 0; i < nbw; i += 2) {
+        gload(i + 1, x1, a1);
+        compute(i, x0, a0);
+        if (i + 1 < nbw) {
+          gload(i + 2, x0, a0);
+          compute(i + 1, x1, a1);
+        }
+      }
+    }
+    // Lane (m, g) holds D[j = 16 jt + 4 g + e][token m] of this wave's blocks.
+#pragma unroll
+    for (int jt = 0; jt < NJT; ++jt) s_red[(wave * NJT + jt) * kWave + lane] = acc[jt];
+    __syncthreads();
+    if (wave < NJT && tok_ok) {
+      const int jt = wave;
+      f32x4 sum = s_red[jt * kWave + lane];
+#pragma unroll
+      for (int w = 1; w < kGrpWaves; ++w) {
+        const f32x4 o = s_red[(w * NJT + jt) * kWave + lane];
+        sum.x += o.x;
+        sum.y += o.y;
+        sum.z += o.z;
+        sum.w += o.w;
+      }
+      const int j0 = 16 * jt + 4 * g;
+      if (j0 + 0 >= rank_l) sum.x = 0.f;
+      if (j0 + 1 >= rank_l) sum.y = 0.f;
+      if (j0 + 2 >= rank_l) sum.z = 0.f;
+      if (j0 + 3 >= rank_l) sum.w = 0.f;
+      store4<VEC>(a.v + (int64_t)t * a.ldv + j0, j0, a.r, sum);
+    }
+    __syncthreads();  // the partial sums' rows are reused by the next item
+  }
+}
+
 // v[t, :r] = sum over the ks chunks of the partial rows, in chunk order (ks
 // as the shrink kernel left it in the workspace header, or ks_fixed when the
 // kernel cannot have changed the host's split: then the partial rows' loads
@@ -415,6 +548,24 @@ hipError_t launch_typed(const ShrinkArgs& args, int njt, int tb, int grid, hipSt
   return hipGetLastError();
 }
 
+size_t group_lds_bytes(int njt, int L) { return njt == 1 ? GroupLds<1>::bytes(L) : GroupLds<2>::bytes(L); }
+
+template <int DT, bool VEC, bool DENSE>
+hipError_t launch_group_typed(const ShrinkArgs& args, int njt, int grid, hipStream_t s) {
+  const size_t lds = group_lds_bytes(njt, args.seg.L);
+  if (njt == 1)
+    hipLaunchKernelGGL((shrink_group_kernel<DT, VEC, 1, DENSE>), dim3(grid), dim3(kGrpThreads), lds, s, args);
+  else
+    hipLaunchKernelGGL((shrink_group_kernel<DT, VEC, 2, DENSE>), dim3(grid), dim3(kGrpThreads), lds, s, args);
+  return hipGetLastError();
+}
+
+template <int DT, bool VEC>
+hipError_t launch_group(const ShrinkArgs& args, int njt, int grid, hipStream_t s) {
+  return args.seg.dense ? launch_group_typed<DT, VEC, true>(args, njt, grid, s)
+                        : launch_group_typed<DT, VEC, false>(args, njt, grid, s);
+}
+
 template <int DT, bool VEC>
 hipError_t launch_dense(const ShrinkArgs& args, int njt, int tb, int grid, hipStream_t s) {
   return args.seg.dense ? launch_typed<DT, VEC, true>(args, njt, tb, grid, s)
@@ -436,6 +587,36 @@ ShrinkPlan plan_shrink(int32_t T, int32_t L, int32_t H, int32_t r, size_t ws_lim
   // 74.9 -> 62.3, over four segments 81.8 -> 73.6, 8192 x 4096 32.7 -> 28.3;
   // but 512 x 4096 12.4 -> 14.6 (fewer, longer items) and 8192 x 1024
   // 17.0 -> 17.7 (two chunks at most).
+  // 16-token groups with the H split inside the workgroup (shrink_group_kernel)
+  // at r <= 32, when the groups fit one round of workgroups (one per CU) and
+  // each moves at most 128 KB of x and A (H (16 + r) <= 65536 elements).  A
+  // CU sustains only so many lines in flight, so a group's bytes set its
+  // time; past that size the tile kernel's H split over every CU wins.
+  // Measured on MI355X (fp16, 4 adapters, each call alone, tiles -> groups):
+  // r = 16, H = 1024: 1024 tokens 10.5 -> 6.3 us, 2048 11.1 -> 6.6; H = 2048:
+  // 1024 tokens 11.1 -> 8.6, 2048 11.5 -> 9.0; r = 32, H = 1024: 2048 tokens
+  // 11.4 -> 7.8; but r = 32, H = 2048: 4096 tokens 13.6 -> 17.5, and the
+  // 2048-token prefill at H = 4096, r = 16: 13.0 -> 16.3.
+  {
+    const int64_t g_tiles = max_token_tiles(T, L, 16);
+    const bool fit = p.jtw <= 2 && group_lds_bytes(p.jtw, L) <= 64 * 1024 && g_tiles < INT32_MAX;
+    const bool want = tuning().shrink_group == 1 ||
+                      (tuning().shrink_group == 0 && g_tiles <= 256 && (int64_t)H * (16 + r) <= 65536);
+    if (fit && want) {
+      p.group = 1;
+      p.tb = 1;
+      p.ksplit = 1;
+      p.ks_cap = 1;
+      p.kchunk = (int32_t)H;
+      p.max_tiles = (int32_t)g_tiles;
+      p.resident = 256;  // one eight-wave workgroup per CU
+      p.partial_bytes = 0;
+      int64_t grid = g_tiles < 256 ? g_tiles : 256;
+      grid = (grid + 7) / 8 * 8;
+      p.grid = (int32_t)(grid < 8 ? 8 : grid);
+      return p;
+    }
+  }
   p.tb = (p.jtw == 4 && ((tuning().shrink_tb == 0 && T >= 4096 && H >= 2048) || tuning().shrink_tb == 2)) ? 2 : 1;
   const int64_t tt = (int64_t)kSkTile * p.tb;
   const int64_t tiles = max_token_tiles(T, L, tt);
@@ -540,6 +721,13 @@ hipError_t launch_shrink(const SegView& seg, const uint16_t* x, int64_t ldx, con
   a.kchunk = plan.kchunk;
   a.rp = plan.rp;
   a.fixed = plan.fixed;
+  if (plan.group) {
+    a.partial = nullptr;
+    a.ks_out = nullptr;
+    if (dtype == 0)
+      return vec ? launch_group<0, true>(a, plan.jtw, plan.grid, s) : launch_group<0, false>(a, plan.jtw, plan.grid, s);
+    return vec ? launch_group<1, true>(a, plan.jtw, plan.grid, s) : launch_group<1, false>(a, plan.jtw, plan.grid, s);
+  }
   hipError_t e;
   if (dtype == 0)
     e = vec ? launch_dense<0, true>(a, plan.jtw, plan.tb, plan.grid, s)

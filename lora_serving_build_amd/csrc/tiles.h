@@ -93,17 +93,19 @@ __device__ TileTable build_tile_table(const SegView& seg, int tile_tokens, int r
     for (int s = threadIdx.x; s < seg.L; s += NT) tt.rank[s] = clamp_rank(seg.lora_rank ? seg.lora_rank[s] : r);
     S = S < 0 ? 0 : (S > seg.L ? seg.L : S);
   } else {
-    // A large pool, most of it usually idle: the first NT segments go out with
+    // A large pool, most of it usually idle: the first NE segments go out with
     // the load of S, the rest (if S is larger) one round trip later, and each
     // segment's rank is looked up from its adapter.
-    // (NT <= kEagerTable < L: indices up to NT exist.)
-    static_assert(NT <= kEagerTable, "the eager part of a large pool's table is one entry per thread");
-    tt.seg_start[threadIdx.x] = seg.seg_start[threadIdx.x];
-    tt.seg_lora[threadIdx.x] = seg.seg_lora[threadIdx.x];
-    if (threadIdx.x == NT - 1) tt.seg_start[NT] = seg.seg_start[NT];
+    // (NE <= kEagerTable < L: indices up to NE exist.)
+    constexpr int NE = NT < kEagerTable ? NT : kEagerTable;
+    if (threadIdx.x < NE) {
+      tt.seg_start[threadIdx.x] = seg.seg_start[threadIdx.x];
+      tt.seg_lora[threadIdx.x] = seg.seg_lora[threadIdx.x];
+    }
+    if (threadIdx.x == NE - 1) tt.seg_start[NE] = seg.seg_start[NE];
     S = S < 0 ? 0 : (S > seg.L ? seg.L : S);
-    for (int s = NT + 1 + threadIdx.x; s <= S; s += NT) tt.seg_start[s] = seg.seg_start[s];
-    for (int s = NT + threadIdx.x; s < S; s += NT) tt.seg_lora[s] = seg.seg_lora[s];
+    for (int s = NE + 1 + threadIdx.x; s <= S; s += NT) tt.seg_start[s] = seg.seg_start[s];
+    for (int s = NE + threadIdx.x; s < S; s += NT) tt.seg_lora[s] = seg.seg_lora[s];
     if (seg.lora_rank) {
       __syncthreads();
       for (int s = threadIdx.x; s < S; s += NT) {

@@ -128,6 +128,10 @@ def test_workspace_size_is_zero_when_not_split():
     assert lsb.lora_shrink_workspace_bytes(0, 4, 4096, 16) == 0
     assert lsb.lora_shrink_workspace_bytes(65536, 4, 4096, 16) == 0
     assert lsb.lora_shrink_workspace_bytes(256, 4, 4096, 16) > 0
+    # 16-token groups (r <= 32, one round of groups, small H): the H split
+    # stays inside the workgroup, so no partial rows either.
+    assert lsb.lora_shrink_workspace_bytes(2048, 4, 1024, 16) == 0
+    assert lsb.lora_shrink_workspace_bytes(1024, 4, 2048, 32) > 0
 
 
 @pytest.mark.parametrize("T,L,H,r,ks_cap,rp", [

@@ -518,6 +518,29 @@ def test_shrink_128_token_tiles_every_row(dtype, T, H, r, L, sl):
     assert np.all(v.cpu().numpy().view(np.uint32)[~act] == V_SENTINEL)
 
 
+@pytest.mark.parametrize("dtype,T,H,r", [("bf16", 700, 4096, 16), ("f16", 301, 2001, 32)])
+def test_single_adapter_shrink_groups(force_path, monkeypatch, tuning_from_env, dtype, T, H, r):
+    """lora_shrink_single in the 16-token-group form (forced): bit for bit
+    the segment entry point on the same batch with every id 0 (the same
+    groups and block order), and the oracle's result."""
+    _announce(f"single-adapter shrink, 16-token groups: {dtype} T={T} H={H} r={r}")
+    monkeypatch.setenv("LORA_SHRINK_GROUP", "1")
+    tuning_from_env()
+    force_path(lsb.PATH_SGMV)
+    w = W.make("grp_single", dtype, T, H, r, 1, [[64]], seed=T + H + r)
+    x = dev_bits(w.x, dtype)
+    A = dev_bits(w.A, dtype)
+    v = sentinel_v(T, r)
+    lsb.lora_shrink_single(x, A[0], v)
+    seg = lsb.lora_build_segments(torch.zeros(T, dtype=torch.int32, device="cuda"), 1)
+    v_seg = sentinel_v(T, r)
+    lsb.lora_shrink(x, A, seg, v_seg)
+    torch.cuda.synchronize()
+    assert np.array_equal(v.cpu().numpy().view(np.uint32), v_seg.cpu().numpy().view(np.uint32))
+    v_or = oracle.shrink(dtype, w.x, w.A, np.zeros(T, np.int32))
+    assert tol_ratio(v.cpu().numpy().astype(np.float64), v_or) <= 1
+
+
 def test_single_adapter_shrink_128_token_tiles():
     """lora_shrink_single (no metadata) at r = 64, 8192 tokens: the dense form
     of the 128-token-tile kernel, every row against the oracle."""
@@ -588,10 +611,13 @@ def test_expand_wide_range_v(force_path, dtype, r, n, path):
 
 # ---------------------------------------------------------------- BGMV and SGMV paths
 @pytest.fixture
-def tuning_from_env():
+def tuning_from_env(monkeypatch):
     """Reloads the library's launch-plan overrides after a test has set them
-    in the environment, and again (with them removed) afterwards."""
+    in the environment (through monkeypatch), and again afterwards, once the
+    environment is restored: this teardown runs before monkeypatch's own, so
+    it undoes the environment first."""
     yield lsb.lora_reload_tuning
+    monkeypatch.undo()
     lsb.lora_reload_tuning()
 
 
@@ -673,6 +699,16 @@ PLAN_VARIANTS = [
     ({"LORA_SHRINK_TB": "2", "LORA_SHRINK_KSPLIT": "1"}, "sgmv", "f16", 300, 1024, 48, 4, [[256]]),
     ({"LORA_SHRINK_TB": "2", "LORA_SHRINK_KSPLIT": "3"}, "sgmv", "bf16", 500, 4096, 64, 9, [[1024]]),
     ({"LORA_SHRINK_TB": "2"}, "sgmv", "f16", 200, 2001, 40, 3, [[256]]),
+    # 16-token groups with the H split inside the workgroup (r <= 32): H in
+    # whole 256-element blocks, a ragged last block, the element-wise path,
+    # waves with no block (H = 1024), eight blocks per wave (the pipelined
+    # loop), one and two rank tiles, and a pool past the eagerly copied table
+    ({"LORA_SHRINK_GROUP": "1"}, "sgmv", "bf16", 300, 4096, 16, 7, [[512]]),
+    ({"LORA_SHRINK_GROUP": "1"}, "sgmv", "f16", 500, 2000, 32, 9, [[256]]),
+    ({"LORA_SHRINK_GROUP": "1"}, "sgmv", "bf16", 200, 2001, 20, 3, [[256]]),
+    ({"LORA_SHRINK_GROUP": "1"}, "sgmv", "f16", 77, 1024, 8, 4, [[128]]),
+    ({"LORA_SHRINK_GROUP": "1"}, "sgmv", "bf16", 260, 16384, 32, 5, [[256]]),
+    ({"LORA_SHRINK_GROUP": "1"}, "sgmv", "f16", 600, 1024, 16, 300, [[256]]),
     ({"LORA_EXPAND_TB": "2"}, "sgmv", "bf16", 700, 1024, 64, 5, [[2048, 512]]),
     ({"LORA_EXPAND_TB": "2"}, "sgmv", "f16", 300, 1024, 16, 3, [[1000]]),
     ({"LORA_EXPAND_TB": "2"}, "sgmv", "bf16", 300, 512, 128, 3, [[384]]),
