@@ -518,6 +518,30 @@ def test_shrink_128_token_tiles_every_row(dtype, T, H, r, L, sl):
     assert np.all(v.cpu().numpy().view(np.uint32)[~act] == V_SENTINEL)
 
 
+@pytest.mark.parametrize("dtype,T,H,r,L,sl", [
+    ("f16", 2048, 1024, 16, 4, 8),        # 2048 tokens in 8-token sequences, sorted by the builder
+    ("bf16", 1024, 2048, 16, 4, 1),       # one token per sequence
+    ("bf16", 3000, 1024, 32, 9, (1, 40)),  # ragged segments, two rank tiles, 10 % without adapter
+])
+def test_shrink_groups_chosen_at_size(force_path, dtype, T, H, r, L, sl):
+    """Mid-size batches at small H, where the launcher itself takes the
+    16-token groups (no workspace): every active row against the oracle, and
+    the rows without an adapter left as they were."""
+    _announce(f"shrink, 16-token groups by the launcher: {dtype} T={T} H={H} r={r} L={L}")
+    force_path(lsb.PATH_SGMV)
+    assert lsb.lora_shrink_workspace_bytes(T, L, H, r) == 0
+    w = W.make("grp", dtype, T, H, r, L, [[64]], seed=T + H + r, seq_len=sl,
+               neg_frac=0.1 if isinstance(sl, tuple) else 0.0)
+    seg = lsb.lora_build_segments(torch.from_numpy(w.ids).cuda(), w.L)
+    v = sentinel_v(T, r)
+    lsb.lora_shrink(dev_bits(w.x, dtype), dev_bits(w.A, dtype), seg, v)
+    torch.cuda.synchronize()
+    act = w.active
+    v_or = oracle.shrink(dtype, w.x, w.A, w.ids)
+    assert tol_ratio(v.cpu().numpy()[act].astype(np.float64), v_or[act]) <= 1
+    assert np.all(v.cpu().numpy().view(np.uint32)[~act] == V_SENTINEL)
+
+
 @pytest.mark.parametrize("dtype,T,H,r", [("bf16", 700, 4096, 16), ("f16", 301, 2001, 32)])
 def test_single_adapter_shrink_groups(force_path, monkeypatch, tuning_from_env, dtype, T, H, r):
     """lora_shrink_single in the 16-token-group form (forced): bit for bit
