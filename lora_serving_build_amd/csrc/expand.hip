@@ -57,6 +57,7 @@ struct ExpandArgs {
   int32_t min_seg_len;  // segments with fewer tokens are left to another kernel
   int32_t short_cb;     // SG > 0: column blocks of each one-token segment's per-token items
   int32_t balanced;     // tile schedule: 0 chosen per call, 1 round-robin items, 2 balanced ranges
+  int32_t line_y;       // 128-token tiles, aligned data: y loaded in whole lines (staged in LDS)
 };
 
 static_assert(kExpandThreads == kBgThreads, "per-token items run the per-token expand's body");
@@ -97,6 +98,17 @@ constexpr int expand_wgs_per_cu(int nks, int tb, int sg) {
 // of lane group g holds after the swap.
 __device__ __forceinline__ int pair_col(int g) { return 8 * (((g & 1) << 1) | (g >> 1)); }
 
+// y of a chunk loaded in whole 128-byte lines (128-token tiles): each load
+// instruction covers 8 rows x 128 B, where the op layout above covers 16
+// rows x 64 B, so every line is read by one instruction instead of two.
+// Measured on MI355X, a tiled read-modify-write of a 57344-column bf16 y
+// (8192 rows, 128-row x 1024-column items): 398.5 -> 380.3 us, whether the
+// loads or the stores take the whole lines, and the same with the loads
+// passed through LDS into the op layout.  Each wave passes one half chunk
+// (16 TB rows x 128 B) at a time through its own LDS rows.
+constexpr int kYsPitch = 144;  // bytes per staged row (128 + 16)
+constexpr size_t kYStageBytes = (size_t)(kExpandThreads / kWave) * 32 * kYsPitch;  // 128-token tiles
+
 // NKS = 16-wide steps of r (r <= 16 * NKS).  TB = 16-token blocks per wave
 // (tile = 64 TB tokens; two blocks share every weight operand read from LDS
 // and halve the weight traffic per token).  VEC: 16-byte aligned rows, r and
@@ -124,7 +136,12 @@ __global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) voi
   constexpr bool kPack = NKS >= 2;                           // 32 ranks per weight operand
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* s_b = reinterpret_cast<uint16_t*>(smem);
-  int32_t* s_table = reinterpret_cast<int32_t*>(smem + Lds::region(SG > 0));
+  // The y staging rows (when the launch takes whole-line y loads) follow the
+  // weights, then the tile table.
+  const bool line_y = VEC && TB == 2 && a.line_y != 0;
+  unsigned char* s_ys = smem + Lds::region(SG > 0) + (size_t)(threadIdx.x / kWave) * (16 * TB * kYsPitch);
+  int32_t* s_table =
+      reinterpret_cast<int32_t*>(smem + Lds::region(SG > 0) + (TB == 2 && a.line_y ? kYStageBytes : 0));
   int32_t* s_scan = s_table + tile_table_ints(a.seg.L);
 
   const int tid = threadIdx.x;
@@ -335,6 +352,19 @@ __global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) voi
       yrow[b] = ybase + (int64_t)(tok_ok[b] ? t : 0) * a.ldy;
     }
     const bool wave_live = blk_live[0];
+    // Whole-line y loads: instruction i covers rows 8 (i / 2) + lane / 8 of
+    // the wave's 16 TB rows and the 128-byte half i % 2 of the chunk; a row's
+    // token comes from the lane that holds it in the op layout (row 16 b + m
+    // of block b is lane m's).
+    uint16_t* yline[2 * TB];
+    if (line_y) {
+#pragma unroll
+      for (int hh = 0; hh < 2 * TB; ++hh) {
+        const int src = (8 * hh + (lane >> 3)) & 15;  // row 8 hh + lane / 8 is in block hh / 2
+        const int row = __shfl(tok_ok[hh >> 1] ? tok[hh >> 1] : 0, src, kWave);
+        yline[hh] = ybase + (int64_t)row * a.ldy;
+      }
+    }
 
     // y of this lane for chunk c: pair p covers columns 32 p + pc .. +8.  The
     // vector path loads unconditionally (rows of inactive lanes point at row
@@ -342,6 +372,16 @@ __global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) voi
     // counts the loads in flight exactly; values that no store uses are
     // simply ignored.
     auto gload_y = [&](int c, u32x4 (*yv)[NP]) {
+      if (line_y) {
+        // register i = (b, p) with b = i / NP, p = i % NP holds line load i
+#pragma unroll
+        for (int i = 0; i < TB * NP; ++i) {
+          const int col = c * kExpandCols + 64 * (i & 1) + 8 * (lane & 7);
+          const int cs = col + 8 <= nq ? col : nq - 8;
+          yv[i / NP][i % NP] = *reinterpret_cast<const u32x4*>(yline[i >> 1] + cs);
+        }
+        return;
+      }
 #pragma unroll
       for (int b = 0; b < TB; ++b) {
 #pragma unroll
@@ -507,6 +547,29 @@ __global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) voi
               for (int b = 0; b < TB; ++b) acc[b][qq] = mfma16x16x32<DT>(aop, bop[b][0], acc[b][qq]);
             }
           }
+          // This half's y in the op layout: straight from the registers, or
+          // (whole-line loads) the half's lines through the wave's LDS rows.
+          u32x4 yh[TB][NP / 2];
+          if (line_y) {
+#pragma unroll
+            for (int hh = 0; hh < 2 * TB; ++hh) {
+              const int i = 2 * hh + h;
+              *reinterpret_cast<u32x4*>(s_ys + (8 * hh + (lane >> 3)) * kYsPitch + 16 * (lane & 7)) =
+                  ycur[i / NP][i % NP];
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int b = 0; b < TB; ++b)
+#pragma unroll
+              for (int pp = 0; pp < NP / 2; ++pp)
+                yh[b][pp] = *reinterpret_cast<const u32x4*>(s_ys + (16 * b + m) * kYsPitch + 2 * (32 * pp + pc));
+            __builtin_amdgcn_wave_barrier();
+          } else {
+#pragma unroll
+            for (int b = 0; b < TB; ++b)
+#pragma unroll
+              for (int pp = 0; pp < NP / 2; ++pp) yh[b][pp] = ycur[b][h * (NP / 2) + pp];
+          }
 #pragma unroll
           for (int b = 0; b < TB; ++b) {
             if (!tok_ok[b]) continue;
@@ -531,7 +594,7 @@ __global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) voi
               uint16_t* yp = yrow[b] + col;
               if constexpr (VEC) {  // n % 8 == 0: the lane's 8 columns are all in the slice
                 if (a.add) {
-                  const uint32_t d[4] = {ycur[b][p].x, ycur[b][p].y, ycur[b][p].z, ycur[b][p].w};
+                  const uint32_t d[4] = {yh[b][pp].x, yh[b][pp].y, yh[b][pp].z, yh[b][pp].w};
 #pragma unroll
                   for (int e = 0; e < 4; ++e) {
                     float y0, y1;
@@ -703,14 +766,25 @@ hipError_t launch_expand(const SegView& seg, const float* v, int64_t ldv, int64_
     items += (int64_t)(seg.L < seg.T ? seg.L : seg.T) * a.short_cb;
   }
   const bool ws = sg > 0;
-  const size_t lds = nks == 1 ? ExpandLds<1>::bytes(seg.L, ws)
-                     : nks == 2 ? ExpandLds<2>::bytes(seg.L, ws)
-                     : nks == 4 ? ExpandLds<4>::bytes(seg.L, ws) : ExpandLds<8>::bytes(seg.L, ws);
+  size_t lds = nks == 1 ? ExpandLds<1>::bytes(seg.L, ws)
+               : nks == 2 ? ExpandLds<2>::bytes(seg.L, ws)
+               : nks == 4 ? ExpandLds<4>::bytes(seg.L, ws) : ExpandLds<8>::bytes(seg.L, ws);
   // Persistent workgroups: as many as fit on the 256 CUs (LDS and register
   // bound), at most four per CU.
-  int64_t per_cu = (int64_t)(160 * 1024 / lds);
   const int64_t reg_cu = expand_wgs_per_cu(nks, tb, sg);
-  per_cu = per_cu < 1 ? 1 : (per_cu > reg_cu ? reg_cu : per_cu);
+  auto fit_cu = [&](size_t bytes) {
+    const int64_t n = (int64_t)(160 * 1024 / bytes);
+    return n < 1 ? 1 : (n > reg_cu ? reg_cu : n);
+  };
+  int64_t per_cu = fit_cu(lds);
+  // Whole-line y loads with 128-token tiles on aligned data, when their LDS
+  // rows keep as many workgroups per CU (a large adapter pool's table may
+  // not leave room).
+  a.line_y = 0;
+  if (tb == 2 && vec && tuning().expand_line_y != 2 && fit_cu(lds + kYStageBytes) >= per_cu) {
+    a.line_y = 1;
+    lds += kYStageBytes;
+  }
   if (tuning().expand_wgs_per_cu >= 1 && tuning().expand_wgs_per_cu < per_cu) per_cu = tuning().expand_wgs_per_cu;
   int64_t grid = items < 256 * per_cu ? items : 256 * per_cu;
   grid = (grid + 7) / 8 * 8;

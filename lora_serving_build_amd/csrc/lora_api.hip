@@ -123,6 +123,7 @@ lora::Tuning read_tuning() {
   t.expand_balance = read_env_int("LORA_EXPAND_BALANCE");
   t.shrink_tb = read_env_int("LORA_SHRINK_TB");
   t.shrink_group = read_env_int("LORA_SHRINK_GROUP");
+  t.expand_line_y = read_env_int("LORA_EXPAND_LINE_Y");
   return t;
 }
 
