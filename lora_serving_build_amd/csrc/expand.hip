@@ -57,7 +57,7 @@ struct ExpandArgs {
   int32_t min_seg_len;  // segments with fewer tokens are left to another kernel
   int32_t short_cb;     // SG > 0: column blocks of each one-token segment's per-token items
   int32_t balanced;     // tile schedule: 0 chosen per call, 1 round-robin items, 2 balanced ranges
-  int32_t line_y;       // 128-token tiles, aligned data: y loaded in whole lines (staged in LDS)
+  int32_t line_y;       // aligned data: y loaded in whole lines (staged in LDS)
 };
 
 static_assert(kExpandThreads == kBgThreads, "per-token items run the per-token expand's body");
@@ -98,7 +98,7 @@ constexpr int expand_wgs_per_cu(int nks, int tb, int sg) {
 // of lane group g holds after the swap.
 __device__ __forceinline__ int pair_col(int g) { return 8 * (((g & 1) << 1) | (g >> 1)); }
 
-// y of a chunk loaded in whole 128-byte lines (128-token tiles): each load
+// y of a chunk loaded in whole 128-byte lines (aligned data): each load
 // instruction covers 8 rows x 128 B, where the op layout above covers 16
 // rows x 64 B, so every line is read by one instruction instead of two.
 // Measured on MI355X, a tiled read-modify-write of a 57344-column bf16 y
@@ -107,7 +107,7 @@ __device__ __forceinline__ int pair_col(int g) { return 8 * (((g & 1) << 1) | (g
 // passed through LDS into the op layout.  Each wave passes one half chunk
 // (16 TB rows x 128 B) at a time through its own LDS rows.
 constexpr int kYsPitch = 144;  // bytes per staged row (128 + 16)
-constexpr size_t kYStageBytes = (size_t)(kExpandThreads / kWave) * 32 * kYsPitch;  // 128-token tiles
+constexpr size_t y_stage_bytes(int tb) { return (size_t)(kExpandThreads / kWave) * 16 * tb * kYsPitch; }
 
 // NKS = 16-wide steps of r (r <= 16 * NKS).  TB = 16-token blocks per wave
 // (tile = 64 TB tokens; two blocks share every weight operand read from LDS
@@ -138,10 +138,10 @@ __global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) voi
   uint16_t* s_b = reinterpret_cast<uint16_t*>(smem);
   // The y staging rows (when the launch takes whole-line y loads) follow the
   // weights, then the tile table.
-  const bool line_y = VEC && TB == 2 && a.line_y != 0;
+  const bool line_y = VEC && a.line_y != 0;
   unsigned char* s_ys = smem + Lds::region(SG > 0) + (size_t)(threadIdx.x / kWave) * (16 * TB * kYsPitch);
   int32_t* s_table =
-      reinterpret_cast<int32_t*>(smem + Lds::region(SG > 0) + (TB == 2 && a.line_y ? kYStageBytes : 0));
+      reinterpret_cast<int32_t*>(smem + Lds::region(SG > 0) + (a.line_y ? y_stage_bytes(TB) : 0));
   int32_t* s_scan = s_table + tile_table_ints(a.seg.L);
 
   const int tid = threadIdx.x;
@@ -777,13 +777,13 @@ hipError_t launch_expand(const SegView& seg, const float* v, int64_t ldv, int64_
     return n < 1 ? 1 : (n > reg_cu ? reg_cu : n);
   };
   int64_t per_cu = fit_cu(lds);
-  // Whole-line y loads with 128-token tiles on aligned data, when their LDS
+  // Whole-line y loads on aligned data, when their LDS
   // rows keep as many workgroups per CU (a large adapter pool's table may
   // not leave room).
   a.line_y = 0;
-  if (tb == 2 && vec && tuning().expand_line_y != 2 && fit_cu(lds + kYStageBytes) >= per_cu) {
+  if (vec && tuning().expand_line_y != 2 && fit_cu(lds + y_stage_bytes(tb)) >= per_cu) {
     a.line_y = 1;
-    lds += kYStageBytes;
+    lds += y_stage_bytes(tb);
   }
   if (tuning().expand_wgs_per_cu >= 1 && tuning().expand_wgs_per_cu < per_cu) per_cu = tuning().expand_wgs_per_cu;
   int64_t grid = items < 256 * per_cu ? items : 256 * per_cu;

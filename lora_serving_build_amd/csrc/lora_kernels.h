@@ -28,7 +28,7 @@ constexpr int kShrinkKStep = 128;
 // ranges), LORA_SHRINK_TB (2: 128-token shrink tiles at r = 33..64),
 // LORA_SHRINK_GROUP (1: 16-token groups with the H split inside the
 // workgroup at r <= 32, 2: never), LORA_EXPAND_LINE_Y (2: no whole-line y
-// loads in the 128-token-tile expand), LORA_BGMV_SHRINK_RT, LORA_BGMV_RPI,
+// loads in the tile expand), LORA_BGMV_SHRINK_RT, LORA_BGMV_RPI,
 // LORA_BGMV_CB.  0 = not set: the launchers' own choice.
 struct Tuning {
   int shrink_ksplit;
