@@ -105,8 +105,12 @@ __device__ __forceinline__ int pair_col(int g) { return 8 * (((g & 1) << 1) | (g
 // (8192 rows, 128-row x 1024-column items): 398.5 -> 380.3 us, whether the
 // loads or the stores take the whole lines, and the same with the loads
 // passed through LDS into the op layout.  Each wave passes one half chunk
-// (16 TB rows x 128 B) at a time through its own LDS rows.
-constexpr int kYsPitch = 144;  // bytes per staged row (128 + 16)
+// (16 TB rows x 128 B) at a time through its own LDS rows.  Row pitch 192 B
+// with the 16-byte slot XORed by bit 2 of the row: the line writes (rows two
+// apart start 8 bank quads apart) and the op-layout reads (16 rows, two slots)
+// are both free of bank conflicts.
+constexpr int kYsPitch = 192;  // bytes per staged row
+__device__ __forceinline__ int ys_off(int row, int slot) { return row * kYsPitch + 16 * (slot ^ ((row >> 2) & 1)); }
 constexpr size_t y_stage_bytes(int tb) { return (size_t)(kExpandThreads / kWave) * 16 * tb * kYsPitch; }
 
 // NKS = 16-wide steps of r (r <= 16 * NKS).  TB = 16-token blocks per wave
@@ -554,15 +558,14 @@ __global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) voi
 #pragma unroll
             for (int hh = 0; hh < 2 * TB; ++hh) {
               const int i = 2 * hh + h;
-              *reinterpret_cast<u32x4*>(s_ys + (8 * hh + (lane >> 3)) * kYsPitch + 16 * (lane & 7)) =
-                  ycur[i / NP][i % NP];
+              *reinterpret_cast<u32x4*>(s_ys + ys_off(8 * hh + (lane >> 3), lane & 7)) = ycur[i / NP][i % NP];
             }
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int b = 0; b < TB; ++b)
 #pragma unroll
               for (int pp = 0; pp < NP / 2; ++pp)
-                yh[b][pp] = *reinterpret_cast<const u32x4*>(s_ys + (16 * b + m) * kYsPitch + 2 * (32 * pp + pc));
+                yh[b][pp] = *reinterpret_cast<const u32x4*>(s_ys + ys_off(16 * b + m, 4 * pp + (pc >> 3)));
             __builtin_amdgcn_wave_barrier();
           } else {
 #pragma unroll
