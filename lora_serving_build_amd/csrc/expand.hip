@@ -57,7 +57,7 @@ struct ExpandArgs {
   int32_t min_seg_len;  // segments with fewer tokens are left to another kernel
   int32_t short_cb;     // SG > 0: column blocks of each one-token segment's per-token items
   int32_t balanced;     // tile schedule: 0 chosen per call, 1 round-robin items, 2 balanced ranges
-  int32_t line_y;       // aligned data: y loaded in whole lines (staged in LDS)
+  int32_t line_y;       // aligned data: y loaded (1), or loaded and stored (2), in whole lines (staged in LDS)
 };
 
 static_assert(kExpandThreads == kBgThreads, "per-token items run the per-token expand's body");
@@ -105,7 +105,8 @@ __device__ __forceinline__ int pair_col(int g) { return 8 * (((g & 1) << 1) | (g
 // (8192 rows, 128-row x 1024-column items): 398.5 -> 380.3 us, whether the
 // loads or the stores take the whole lines, and the same with the loads
 // passed through LDS into the op layout.  Each wave passes one half chunk
-// (16 TB rows x 128 B) at a time through its own LDS rows.  Row pitch 192 B
+// (16 TB rows x 128 B) at a time through its own LDS rows; the stores take
+// whole lines too, through the same rows, where that measured faster.  Row pitch 192 B
 // with the 16-byte slot XORed by bit 2 of the row: the line writes (rows two
 // apart start 8 bank quads apart) and the op-layout reads (16 rows, two slots)
 // are both free of bank conflicts.
@@ -215,6 +216,13 @@ __global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) voi
     const float bal = per + kSetup * (ceilf(per / (float)cpr) + 1.f);
     balanced = bal < 0.95f * rr;
   }
+  // Whole-line stores too (the results pass back through the same LDS rows)
+  // at r <= 32 and on round-robin walks at r = 33..64: the 8192-token
+  // layer's gate_up call 442.7 -> 432.1 us, r <= 32 1-2.5% faster; but
+  // balanced ranges at r = 64 measured 1-2% slower (8192 x 16384 / 8192 /
+  // 4096: 120.9 / 66.1 / 41.5 -> 122.4 / 67.0 / 42.4 us) and r = 128 2-3%
+  // (8192 x 1024: 22.5 -> 23.1).
+  const bool line_st = line_y && a.line_y == 2 && (NKS <= 2 || (NKS == 4 && !balanced));
   // The walk's position and end: item and tile-item count (round-robin,
   // which numbers the per-token items after the tile items in one walk, so
   // the workgroups without a last-round tile item take them first), or unit
@@ -361,12 +369,14 @@ __global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) voi
     // token comes from the lane that holds it in the op layout (row 16 b + m
     // of block b is lane m's).
     uint16_t* yline[2 * TB];
+    bool rowok[2 * TB];
     if (line_y) {
 #pragma unroll
       for (int hh = 0; hh < 2 * TB; ++hh) {
         const int src = (8 * hh + (lane >> 3)) & 15;  // row 8 hh + lane / 8 is in block hh / 2
         const int row = __shfl(tok_ok[hh >> 1] ? tok[hh >> 1] : 0, src, kWave);
         yline[hh] = ybase + (int64_t)row * a.ldy;
+        rowok[hh] = line_st && __shfl(tok_ok[hh >> 1] ? 1 : 0, src, kWave) != 0;
       }
     }
 
@@ -606,9 +616,12 @@ __global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) voi
                     out[2 * e + 1] += y1;
                   }
                 }
-                *reinterpret_cast<u32x4*>(yp) =
-                    u32x4{cvt_pack2<DT>(out[0], out[1]), cvt_pack2<DT>(out[2], out[3]),
-                          cvt_pack2<DT>(out[4], out[5]), cvt_pack2<DT>(out[6], out[7])};
+                const u32x4 res = u32x4{cvt_pack2<DT>(out[0], out[1]), cvt_pack2<DT>(out[2], out[3]),
+                                        cvt_pack2<DT>(out[4], out[5]), cvt_pack2<DT>(out[6], out[7])};
+                if (line_st)  // back to the slot its y came from; stored in whole lines below
+                  *reinterpret_cast<u32x4*>(s_ys + ys_off(16 * b + m, 4 * pp + (pc >> 3))) = res;
+                else
+                  *reinterpret_cast<u32x4*>(yp) = res;
               } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -620,6 +633,18 @@ __global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) voi
                 }
               }
             }
+          }
+          if (line_st) {
+            // The half's results in whole lines: every row with a token and
+            // every column inside the slice (n % 8 == 0).
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int hh = 0; hh < 2 * TB; ++hh) {
+              const u32x4 res = *reinterpret_cast<const u32x4*>(s_ys + ys_off(8 * hh + (lane >> 3), lane & 7));
+              const int col = c * kExpandCols + 64 * h + 8 * (lane & 7);
+              if (rowok[hh] && col < nq) *reinterpret_cast<u32x4*>(yline[hh] + col) = res;
+            }
+            __builtin_amdgcn_wave_barrier();
           }
         }
       }
@@ -785,7 +810,7 @@ hipError_t launch_expand(const SegView& seg, const float* v, int64_t ldv, int64_
   // not leave room).
   a.line_y = 0;
   if (vec && tuning().expand_line_y != 2 && fit_cu(lds + y_stage_bytes(tb)) >= per_cu) {
-    a.line_y = 1;
+    a.line_y = tuning().expand_line_y == 1 ? 1 : 2;
     lds += y_stage_bytes(tb);
   }
   if (tuning().expand_wgs_per_cu >= 1 && tuning().expand_wgs_per_cu < per_cu) per_cu = tuning().expand_wgs_per_cu;

@@ -27,8 +27,8 @@ constexpr int kShrinkKStep = 128;
 // LORA_EXPAND_WGS_PER_CU, LORA_EXPAND_BALANCE (1 round-robin items, 2 balanced
 // ranges), LORA_SHRINK_TB (2: 128-token shrink tiles at r = 33..64),
 // LORA_SHRINK_GROUP (1: 16-token groups with the H split inside the
-// workgroup at r <= 32, 2: never), LORA_EXPAND_LINE_Y (2: no whole-line y
-// loads in the tile expand), LORA_BGMV_SHRINK_RT, LORA_BGMV_RPI,
+// workgroup at r <= 32, 2: never), LORA_EXPAND_LINE_Y (whole-line y in the
+// tile expand; 1: loads only, 2: neither), LORA_BGMV_SHRINK_RT, LORA_BGMV_RPI,
 // LORA_BGMV_CB.  0 = not set: the launchers' own choice.
 struct Tuning {
   int shrink_ksplit;

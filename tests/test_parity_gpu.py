@@ -805,6 +805,46 @@ def test_plan_variants(force_path, monkeypatch, tuning_from_env, env, path, dtyp
     check_outside_slices(dw)
 
 
+LINE_CASES = [
+    # (dtype, T, r, slice widths, LORA_EXPAND_TB, LORA_EXPAND_BALANCE): whole-line
+    # y loads and stores on round-robin walks at r = 64, loads only on balanced
+    # ranges at r = 64 and at r = 128, both at r <= 32; ragged slice ends
+    ("bf16", 1500, 64, [2048, 520], "2", "1"),
+    ("bf16", 1500, 64, [2048, 520], "2", "2"),
+    ("f16", 900, 16, [1000], "2", "2"),
+    ("f16", 700, 32, [1536, 256], "1", "0"),
+    ("bf16", 500, 128, [384, 136], "0", "0"),
+]
+
+
+@pytest.mark.parametrize("dtype,T,r,widths,tb,balance", LINE_CASES)
+def test_expand_whole_line_y_bit_identical(force_path, monkeypatch, tuning_from_env, dtype, T, r, widths, tb, balance):
+    """The tile expand's whole-line y paths (loads and stores, loads only)
+    leave y bit for bit as the op-layout loads and stores do: the same sums,
+    only the memory access shape differs."""
+    _announce(f"whole-line y: {dtype} T={T} r={r} slices={widths} tb={tb} balance={balance}")
+    force_path(lsb.PATH_SGMV)
+    monkeypatch.setenv("LORA_EXPAND_TB", tb)
+    monkeypatch.setenv("LORA_EXPAND_BALANCE", balance)
+    w = W.make("line", dtype, T, 64, r, 6, [widths], seed=T + r, seq_len=(1, 40), neg_frac=0.1)
+    o = w.outputs[0]
+    seg = lsb.lora_build_segments(torch.from_numpy(w.ids).cuda(), w.L)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(T)
+    v = torch.randn(T, r, generator=gen, device="cuda")
+    Bs = [dev_bits(q.B, dtype) for q in o.slices]
+    got = []
+    for mode in ("2", "1", "0"):
+        monkeypatch.setenv("LORA_EXPAND_LINE_Y", mode)
+        tuning_from_env()
+        y = dev_bits(o.y0, dtype).clone()
+        lsb.lora_expand_slice(v, Bs, [q.col_off for q in o.slices], seg, y, True)
+        torch.cuda.synchronize()
+        got.append(host_bits(y))
+    assert np.array_equal(got[0], got[1]) and np.array_equal(got[0], got[2])
+    assert np.array_equal(got[2][~w.active], host_bits(dev_bits(o.y0, dtype))[~w.active])
+
+
 RANK_CASES = [
     # (dtype, T, H, r, L, slices, ranks_from, integer, seq_len)
     ("bf16", 500, 1024, 128, 16, [[1024, 256, 256], [2048]], [8, 16, 32, 64, 128], False, (1, 40)),
