@@ -112,6 +112,15 @@ __device__ __forceinline__ int pair_col(int g) { return 8 * (((g & 1) << 1) | (g
 // are both free of bank conflicts.
 constexpr int kYsPitch = 192;  // bytes per staged row
 __device__ __forceinline__ int ys_off(int row, int slot) { return row * kYsPitch + 16 * (slot ^ ((row >> 2) & 1)); }
+// Between one pass's LDS writes and the reads of other lanes' data: a
+// wavefront-scope release / acquire keeps the compiler from moving the LDS
+// accesses across it (no wait is needed: a wave's LDS operations run in
+// order).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 constexpr size_t y_stage_bytes(int tb) { return (size_t)(kExpandThreads / kWave) * 16 * tb * kYsPitch; }
 
 // NKS = 16-wide steps of r (r <= 16 * NKS).  TB = 16-token blocks per wave
@@ -570,13 +579,13 @@ __global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) voi
               const int i = 2 * hh + h;
               *reinterpret_cast<u32x4*>(s_ys + ys_off(8 * hh + (lane >> 3), lane & 7)) = ycur[i / NP][i % NP];
             }
-            __builtin_amdgcn_wave_barrier();
+            wave_lds_sync();
 #pragma unroll
             for (int b = 0; b < TB; ++b)
 #pragma unroll
               for (int pp = 0; pp < NP / 2; ++pp)
                 yh[b][pp] = *reinterpret_cast<const u32x4*>(s_ys + ys_off(16 * b + m, 4 * pp + (pc >> 3)));
-            __builtin_amdgcn_wave_barrier();
+            wave_lds_sync();
           } else {
 #pragma unroll
             for (int b = 0; b < TB; ++b)
@@ -637,14 +646,14 @@ __global__ __launch_bounds__(kExpandThreads, expand_wgs_per_cu(NKS, TB, SG)) voi
           if (line_st) {
             // The half's results in whole lines: every row with a token and
             // every column inside the slice (n % 8 == 0).
-            __builtin_amdgcn_wave_barrier();
+            wave_lds_sync();
 #pragma unroll
             for (int hh = 0; hh < 2 * TB; ++hh) {
               const u32x4 res = *reinterpret_cast<const u32x4*>(s_ys + ys_off(8 * hh + (lane >> 3), lane & 7));
               const int col = c * kExpandCols + 64 * h + 8 * (lane & 7);
               if (rowok[hh] && col < nq) *reinterpret_cast<u32x4*>(yline[hh] + col) = res;
             }
-            __builtin_amdgcn_wave_barrier();
+            wave_lds_sync();
           }
         }
       }
